@@ -1,0 +1,417 @@
+// Memory-bound decode path (fp32 VALU): quantised matvec, routed gate/up +
+// SwiGLU, down projection and the routing-weighted combine.
+//
+// Work layout.  A row of C = 64*L values is split into L "chunks" of 64 values,
+// one per lane; L consecutive lanes of a wave64 share a row, so a wave covers
+// 64/L rows per row slot.  A Q2_K chunk is one quarter of a 256-value block
+// (16 code bytes + its 4 scale bytes + d/dmin), a Q4_1 chunk is two 32-value
+// blocks (40 contiguous bytes).  Each lane keeps the 64 activations its chunk
+// multiplies in registers for the whole row loop and streams only weights.
+//
+// Arithmetic per chunk (Q2_K): sum_k d*sc_k*(sum_i q_i x_i) - dmin*mn_k*(sum_i x_i)
+// over its four 16-value sub-blocks, with sum_i x_i precomputed once per token
+// (the min term hoisted out of the row loop); Q4_1: d*(sum q x) + m*(sum x).
+// Partial sums are combined with an xor-butterfly over the row's L lanes.
+//
+// Expert FFN ("【#2】ds4.c 해독하기": routed experts w1 = gate, w3 = up,
+// w2 = down; SwiGLU; the down input is the routed SwiGLU row, weighted):
+//   h = silu(W1 x) * (W3 x),  y += sum_j p_j * W2[e_j] h_j.
+#include "common.h"
+#include "launch.h"
+
+namespace ds4q {
+namespace {
+
+constexpr int WAVES = 4;
+
+// ---------------------------------------------------------------- x slices
+
+template <int TYPE>
+struct XSlice {
+  float v[64];
+  float s[TYPE == TYPE_Q2_K ? 4 : 2];
+
+  // Activations multiplied by chunk c of a row, scaled by `scale`.
+  __device__ __forceinline__ void load(const float *__restrict__ X, int c, float scale) {
+    if constexpr (TYPE == TYPE_Q2_K) {
+      // quarter g = c&3 of block c>>2: values 128h + 32k + 16p + l'
+      const int b = c >> 2, g = c & 3, h = g >> 1, p = g & 1;
+      const float *base = X + 256 * b + 128 * h + 16 * p;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 t = *reinterpret_cast<const float4 *>(base + 32 * k + 4 * j);
+          v[16 * k + 4 * j + 0] = t.x * scale;
+          v[16 * k + 4 * j + 1] = t.y * scale;
+          v[16 * k + 4 * j + 2] = t.z * scale;
+          v[16 * k + 4 * j + 3] = t.w * scale;
+        }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a += v[16 * k + i];
+        s[k] = a;
+      }
+    } else {
+      const float *base = X + 64 * c;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 t = *reinterpret_cast<const float4 *>(base + 4 * j);
+        v[4 * j + 0] = t.x * scale;
+        v[4 * j + 1] = t.y * scale;
+        v[4 * j + 2] = t.z * scale;
+        v[4 * j + 3] = t.w * scale;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) a += v[32 * b + i];
+        s[b] = a;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- weight chunks
+
+template <int TYPE>
+struct Chunk;
+
+template <>
+struct Chunk<TYPE_Q2_K> {
+  uint32_t q[4], s0, s1, dd;
+  int p;
+  // row: first byte of the row; c: chunk index within the row
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ row, int c) {
+    const uint8_t *blk = row + (c >> 2) * BB_Q2K;
+    const int g = c & 3, h = g >> 1;
+    p = g & 1;
+    const uint8_t *qs = blk + 16 + 16 * g;
+    q[0] = ld32(qs); q[1] = ld32(qs + 4); q[2] = ld32(qs + 8); q[3] = ld32(qs + 12);
+    s0 = ld32(blk + 8 * h);
+    s1 = ld32(blk + 8 * h + 4);
+    dd = ld32(blk + 80);
+  }
+  __device__ __forceinline__ float dot(const XSlice<TYPE_Q2_K> &x) const {
+    float acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t t = (q[j] >> (2 * k)) & 0x03030303u;
+        a = fmaf(ub0(t), x.v[16 * k + 4 * j + 0], a);
+        a = fmaf(ub1(t), x.v[16 * k + 4 * j + 1], a);
+        a = fmaf(ub2(t), x.v[16 * k + 4 * j + 2], a);
+        a = fmaf(ub3(t), x.v[16 * k + 4 * j + 3], a);
+      }
+      acc[k] = a;
+    }
+    // sub-block 8h + 2k + p: bytes p, 2+p of s0 (k = 0, 1), of s1 (k = 2, 3)
+    const uint32_t a0 = s0 >> (8 * p), a1 = s1 >> (8 * p);
+    float sc = (float)(a0 & 15u) * acc[0];
+    sc = fmaf((float)((a0 >> 16) & 15u), acc[1], sc);
+    sc = fmaf((float)(a1 & 15u), acc[2], sc);
+    sc = fmaf((float)((a1 >> 16) & 15u), acc[3], sc);
+    float mn = (float)((a0 >> 4) & 15u) * x.s[0];
+    mn = fmaf((float)((a0 >> 20) & 15u), x.s[1], mn);
+    mn = fmaf((float)((a1 >> 4) & 15u), x.s[2], mn);
+    mn = fmaf((float)((a1 >> 20) & 15u), x.s[3], mn);
+    return f16lo(dd) * sc - f16hi(dd) * mn;
+  }
+};
+
+template <>
+struct Chunk<TYPE_Q4_1> {
+  uint32_t w[10];
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ row, int c) {
+    const uint8_t *p = row + c * (2 * BB_Q41);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) w[i] = ld32(p + 4 * i);
+  }
+  __device__ __forceinline__ float dot(const XSlice<TYPE_Q4_1> &x) const {
+    float r = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t qw = w[5 * b + 1 + j];
+        const uint32_t lo = qw & 0x0F0F0F0Fu, hi = (qw >> 4) & 0x0F0F0F0Fu;
+        const float *xl = x.v + 32 * b + 4 * j, *xh = x.v + 32 * b + 16 + 4 * j;
+        a = fmaf(ub0(lo), xl[0], a); a = fmaf(ub1(lo), xl[1], a);
+        a = fmaf(ub2(lo), xl[2], a); a = fmaf(ub3(lo), xl[3], a);
+        a = fmaf(ub0(hi), xh[0], a); a = fmaf(ub1(hi), xh[1], a);
+        a = fmaf(ub2(hi), xh[2], a); a = fmaf(ub3(hi), xh[3], a);
+      }
+      r = fmaf(f16lo(w[5 * b]), a, r);
+      r = fmaf(f16hi(w[5 * b]), x.s[b], r);
+    }
+    return r;
+  }
+};
+
+// ---------------------------------------------------------------- matvec
+
+// y[t][r] = sum_c W[r][c] x[t][c].  L lanes per row, RS row slots per wave.
+template <int TYPE, int L, int RS>
+__global__ __launch_bounds__(256) void matvec_kernel(const uint8_t *__restrict__ W, int64_t rows,
+                                                     const float *__restrict__ x, int n_tok,
+                                                     float *__restrict__ y) {
+  constexpr int RPW = 64 / L;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c = lane % L, rs = lane / L;
+  const int64_t rbytes = row_bytes(TYPE, 64 * L);
+  const int64_t row0 = ((int64_t)blockIdx.x * WAVES + wv) * RS * RPW;
+  for (int t = 0; t < n_tok; ++t) {
+    XSlice<TYPE> xs;
+    xs.load(x + (int64_t)t * 64 * L, c, 1.0f);
+    Chunk<TYPE> ch[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int64_t r = row0 + i * RPW + rs;
+      if (r < rows) ch[i].load(W + r * rbytes, c);
+    }
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int64_t r = row0 + i * RPW + rs;
+      float v = r < rows ? ch[i].dot(xs) : 0.f;
+      v = group_sum<L>(v);
+      if (c == 0 && r < rows) y[(int64_t)t * rows + r] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- decode gate/up
+
+// Grid: x = row blocks of F (WAVES * RS * RPW rows each), y = active experts.
+template <int TYPE, int L, int RS>
+__global__ __launch_bounds__(256) void gateup_kernel(const uint8_t *__restrict__ gate,
+                                                     const uint8_t *__restrict__ up, int F, int k,
+                                                     const float *__restrict__ x,
+                                                     const float *__restrict__ inv_rms,
+                                                     RouteBufs rb, float *__restrict__ h) {
+  constexpr int RPW = 64 / L;
+  const int j = blockIdx.y;
+  if (j >= *rb.n_active) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c = lane % L, rs = lane / L;
+  const int64_t rbytes = row_bytes(TYPE, 64 * L);
+  const int e = rb.act_expert[j];
+  const uint8_t *W1 = gate + (int64_t)e * F * rbytes;
+  const uint8_t *W3 = up + (int64_t)e * F * rbytes;
+  const int row0 = (blockIdx.x * WAVES + wv) * RS * RPW;
+  const int pb = rb.act_begin[j], pe = rb.act_begin[j + 1];
+  for (int pi = pb; pi < pe; ++pi) {
+    const int p = rb.pairs[pi];
+    const int t = p / k;
+    XSlice<TYPE> xs;
+    xs.load(x + (int64_t)t * 64 * L, c, inv_rms ? inv_rms[t] : 1.0f);
+    Chunk<TYPE> cg[RS], cu[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int r = row0 + i * RPW + rs;
+      cg[i].load(W1 + r * rbytes, c);
+      cu[i].load(W3 + r * rbytes, c);
+    }
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int r = row0 + i * RPW + rs;
+      const float g = group_sum<L>(cg[i].dot(xs));
+      const float u = group_sum<L>(cu[i].dot(xs));
+      if (c == 0) h[(int64_t)p * F + r] = silu(g) * u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- decode down
+
+// Single token: one wave per routing slot (blockDim = 64*k); slot partials
+// meet in LDS and are summed in slot order: y (+)= sum_j w_j * (W2[e_j] h_j).
+template <int TYPE, int L, int RS>
+__global__ __launch_bounds__(512) void down_slots_kernel(const uint8_t *__restrict__ down, int D,
+                                                         int k, const float *__restrict__ h,
+                                                         RouteBufs rb, float *__restrict__ y,
+                                                         int accumulate) {
+  constexpr int RPW = 64 / L;
+  constexpr int ROWS = RS * RPW;
+  __shared__ float part[8][ROWS];
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int c = lane % L, rs = lane / L;
+  const int F = 64 * L;
+  const int64_t rbytes = row_bytes(TYPE, F);
+  const int row0 = blockIdx.x * ROWS;
+  const int e = rb.ids[j];
+  const uint8_t *W2 = down + (int64_t)e * D * rbytes;
+  XSlice<TYPE> hs;
+  hs.load(h + (int64_t)j * F, c, 1.0f);
+  Chunk<TYPE> ch[RS];
+#pragma unroll
+  for (int i = 0; i < RS; ++i) ch[i].load(W2 + (int64_t)(row0 + i * RPW + rs) * rbytes, c);
+#pragma unroll
+  for (int i = 0; i < RS; ++i) {
+    const float v = group_sum<L>(ch[i].dot(hs));
+    if (c == 0) part[j][i * RPW + rs] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < ROWS) {
+    const int r = row0 + threadIdx.x;
+    float acc = 0.f;
+    for (int s = 0; s < k; ++s) acc = fmaf(rb.w[s], part[s][threadIdx.x], acc);
+    y[r] = accumulate ? y[r] + acc : acc;
+  }
+}
+
+// Several tokens: grid x = row blocks of D, y = active experts; every pair of
+// the expert writes o[p][row] (unweighted); launch_combine sums the slots.
+template <int TYPE, int L, int RS>
+__global__ __launch_bounds__(256) void down_grouped_kernel(const uint8_t *__restrict__ down, int D,
+                                                           const float *__restrict__ h, RouteBufs rb,
+                                                           float *__restrict__ o) {
+  constexpr int RPW = 64 / L;
+  const int j = blockIdx.y;
+  if (j >= *rb.n_active) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c = lane % L, rs = lane / L;
+  const int F = 64 * L;
+  const int64_t rbytes = row_bytes(TYPE, F);
+  const int e = rb.act_expert[j];
+  const uint8_t *W2 = down + (int64_t)e * D * rbytes;
+  const int row0 = (blockIdx.x * WAVES + wv) * RS * RPW;
+  const int pb = rb.act_begin[j], pe = rb.act_begin[j + 1];
+  for (int pi = pb; pi < pe; ++pi) {
+    const int p = rb.pairs[pi];
+    XSlice<TYPE> hs;
+    hs.load(h + (int64_t)p * F, c, 1.0f);
+    Chunk<TYPE> ch[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) ch[i].load(W2 + (int64_t)(row0 + i * RPW + rs) * rbytes, c);
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const float v = group_sum<L>(ch[i].dot(hs));
+      if (c == 0) o[(int64_t)p * D + row0 + i * RPW + rs] = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o, RouteBufs rb,
+                                                      int T, int k, int D, int by_pos,
+                                                      float *__restrict__ y, int accumulate) {
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int D4 = D / 4;
+  if (i4 >= (int64_t)T * D4) return;
+  const int t = (int)(i4 / D4), c = (int)(i4 % D4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int p = t * k + j;
+    const int64_t row = by_pos ? rb.pair_pos[p] : p;
+    const float4 v = *reinterpret_cast<const float4 *>(o + row * D + 4 * c);
+    const float w = rb.w[p];
+    acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+  }
+  float4 *yp = reinterpret_cast<float4 *>(y + (int64_t)t * D + 4 * c);
+  if (accumulate) {
+    const float4 old = *yp;
+    acc.x += old.x; acc.y += old.y; acc.z += old.z; acc.w += old.w;
+  }
+  *yp = acc;
+}
+
+// ---------------------------------------------------------------- dispatch
+
+#define DS4Q_DISPATCH_L(L_VAL, ...)                     \
+  switch (L_VAL) {                                      \
+    case 4: { constexpr int LL = 4; __VA_ARGS__; break; }   \
+    case 8: { constexpr int LL = 8; __VA_ARGS__; break; }   \
+    case 16: { constexpr int LL = 16; __VA_ARGS__; break; } \
+    case 32: { constexpr int LL = 32; __VA_ARGS__; break; } \
+    case 64: { constexpr int LL = 64; __VA_ARGS__; break; } \
+    default: return hipErrorInvalidValue;               \
+  }
+
+// Row slots per wave: enough rows in flight per wave, while keeping >= 8
+// waves per CU on the largest grids.
+template <int L>
+constexpr int row_slots() { return L == 64 ? 2 : 1; }
+
+}  // namespace
+
+hipError_t launch_matvec(int w_type, const void *w, int64_t rows, int64_t cols, const float *x,
+                         int n_tok, float *y, hipStream_t s) {
+  if (rows == 0 || n_tok == 0) return hipSuccess;
+  const uint8_t *W = static_cast<const uint8_t *>(w);
+  const int L = (int)(cols / 64);
+  DS4Q_DISPATCH_L(L, {
+    constexpr int RS = 1;
+    const int64_t per_wg = (int64_t)WAVES * RS * (64 / LL);
+    const unsigned grid = (unsigned)((rows + per_wg - 1) / per_wg);
+    if (w_type == TYPE_Q2_K)
+      hipLaunchKernelGGL((matvec_kernel<TYPE_Q2_K, LL, RS>), dim3(grid), dim3(256), 0, s, W, rows, x, n_tok, y);
+    else
+      hipLaunchKernelGGL((matvec_kernel<TYPE_Q4_1, LL, RS>), dim3(grid), dim3(256), 0, s, W, rows, x, n_tok, y);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_gateup(const MoeDims &m, const float *x, const float *inv_rms, int T,
+                                const RouteBufs &rb, float *h, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int L = m.D / 64;
+  const int max_active = T * m.k < m.E ? T * m.k : m.E;
+  DS4Q_DISPATCH_L(L, {
+    constexpr int RS = row_slots<LL>();
+    const int per_wg = WAVES * RS * (64 / LL);
+    const dim3 grid(m.F / per_wg, max_active);
+    if (m.tg == TYPE_Q2_K)
+      hipLaunchKernelGGL((gateup_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(256), 0, s, m.gate, m.up, m.F, m.k, x, inv_rms, rb, h);
+    else
+      hipLaunchKernelGGL((gateup_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(256), 0, s, m.gate, m.up, m.F, m.k, x, inv_rms, rb, h);
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const RouteBufs &rb,
+                              float *o, float *y, bool accumulate, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int L = m.F / 64;
+  if (T == 1) {
+    DS4Q_DISPATCH_L(L, {
+      constexpr int RS = LL == 64 ? 2 : 4;
+      const int per_wg = RS * (64 / LL);
+      const dim3 grid(m.D / per_wg);
+      if (m.td == TYPE_Q2_K)
+        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0);
+      else
+        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0);
+    });
+    return hipGetLastError();
+  }
+  const int max_active = T * m.k < m.E ? T * m.k : m.E;
+  DS4Q_DISPATCH_L(L, {
+    constexpr int RS = row_slots<LL>();
+    const int per_wg = WAVES * RS * (64 / LL);
+    const dim3 grid(m.D / per_wg, max_active);
+    if (m.td == TYPE_Q2_K)
+      hipLaunchKernelGGL((down_grouped_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(256), 0, s, m.down, m.D, h, rb, o);
+    else
+      hipLaunchKernelGGL((down_grouped_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(256), 0, s, m.down, m.D, h, rb, o);
+  });
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_combine(o, rb, T, m.k, m.D, false, y, accumulate, s);
+}
+
+hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
+                          float *y, bool accumulate, hipStream_t s) {
+  const int64_t n4 = (int64_t)T * (D / 4);
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, o, rb, T,
+                     k, D, by_pos ? 1 : 0, y, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace ds4q

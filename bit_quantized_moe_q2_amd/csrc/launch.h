@@ -1,0 +1,66 @@
+// Host-side launchers of the gfx950 kernels (one translation unit per kernel
+// family).  Called only from abi.cpp after argument validation.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ds4q {
+
+hipError_t launch_dequant(int src_type, const void *src, int64_t rows, int64_t cols, bool bf16,
+                          void *dst, hipStream_t s);
+
+hipError_t launch_matvec(int w_type, const void *w, int64_t rows, int64_t cols, const float *x,
+                         int n_tok, float *y, hipStream_t s);
+
+// Routing workspace views (all device pointers).
+struct RouteBufs {
+  int32_t *ids;        // [T][k]
+  float *w;            // [T][k]
+  float *inv_rms;      // [T]  (written when x != NULL)
+  int32_t *counts;     // [E]
+  int32_t *offsets;    // [E+1]
+  int32_t *pairs;      // [T*k] sorted by (expert, token, slot)
+  int32_t *pair_pos;   // [T*k] inverse of pairs
+  int32_t *act_expert; // [E]   active experts (count > 0), in expert order
+  int32_t *act_begin;  // [E+1] start of each active expert's run in pairs
+  int32_t *n_active;   // [1]
+  int32_t *tiles;      // [max_tiles][2] (expert, first sorted position) m-tiles
+  int32_t *n_tiles;    // [1]
+};
+
+// Top-k + softmax per token; with x != NULL also the per-token inverse RMS.
+hipError_t launch_topk(const float *logits, int T, int E, int k, const float *x, int D, float eps,
+                       const RouteBufs &rb, bool single_token_lists, hipStream_t s);
+// Counting-sort grouping of the T*k pairs; tile_m > 0 also builds m-tiles.
+hipError_t launch_group(int T, int E, int k, int tile_m, const RouteBufs &rb, hipStream_t s);
+
+struct MoeDims {
+  int D, F, E, k;
+  int tg, tu, td;  // block types of gate, up, down
+  const uint8_t *gate, *up, *down;
+};
+
+// Decode path (T <= 64): gate/up + SwiGLU -> h [T*k][F] f32 (pair-indexed).
+hipError_t launch_decode_gateup(const MoeDims &m, const float *x, const float *inv_rms, int T,
+                                const RouteBufs &rb, float *h, hipStream_t s);
+// Decode path: down projection.  T == 1: fused weighted combine into y.
+// T > 1: o [T*k][D] f32 (pair-indexed), then launch_combine.
+hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const RouteBufs &rb,
+                              float *o, float *y, bool accumulate, hipStream_t s);
+// y[t] (+)= sum_j w[t][j] * o[row(t, j)]; row = pair index, or sorted
+// position (via pair_pos) when by_pos.
+hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
+                          float *y, bool accumulate, hipStream_t s);
+
+// Prefill path.
+hipError_t launch_prep_bf16(const float *x, const float *inv_rms, int T, int D, uint16_t *xb,
+                            hipStream_t s);
+hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, const RouteBufs &rb,
+                                 int max_tiles, uint16_t *hb, hipStream_t s);
+hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, const RouteBufs &rb,
+                               int max_tiles, float *o, hipStream_t s);
+
+constexpr int PREFILL_TILE_M = 128;
+
+}  // namespace ds4q

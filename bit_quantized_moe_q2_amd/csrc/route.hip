@@ -1,0 +1,168 @@
+// Routing: top-k of n_expert router logits per token with softmax weights over
+// the selected k ("ds4.c 해독하기 1/8", DS4_SHAPE_FLASH passage: 6 of 256
+// routed experts per token), and the token->expert grouping (counting sort of
+// the T*k (token, slot) pairs by expert, stable in pair index).
+//
+// Selection order is (logit desc, index asc): each candidate is packed into a
+// 64-bit key (order-preserving fp32 bits << 32 | ~index) and the wave takes
+// k rounds of a 64-bit max; -0.0 is folded onto +0.0 so that equal logits
+// tie exactly as floating-point comparison says.
+#include "common.h"
+#include "launch.h"
+
+namespace ds4q {
+namespace {
+
+constexpr int MAX_E = 1024;
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per token.
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
+                                                   int k, const float *__restrict__ x, int D,
+                                                   float eps, RouteBufs rb, int single) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float *lg = logits + (int64_t)t * E;
+  uint64_t key[MAX_E / 64];
+#pragma unroll
+  for (int i = 0; i < MAX_E / 64; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? ((uint64_t)ordered_bits(lg[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  float my_val = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < MAX_E / 64; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+#pragma unroll
+    for (int i = 0; i < MAX_E / 64; ++i)
+      if (lane + 64 * i == e) key[i] = 0ull;
+    if (lane == j) { my_id = e; my_val = lg[e]; }
+  }
+  // softmax over the k selected logits, max-subtracted (slot 0 holds the max)
+  const float top = __shfl(my_val, 0, 64);
+  const float ex = lane < k ? expf(my_val - top) : 0.f;
+  const float den = group_sum<64>(ex);
+  if (lane < k) {
+    rb.ids[t * k + lane] = my_id;
+    rb.w[t * k + lane] = ex / den;
+    if (single) {
+      rb.act_expert[lane] = my_id;
+      rb.act_begin[lane] = lane;
+      rb.pairs[lane] = lane;
+    }
+  }
+  if (single && lane == 0) {
+    rb.act_begin[k] = k;
+    *rb.n_active = k;
+  }
+  if (x) {
+    const float *xr = x + (int64_t)t * D;
+    float ss = 0.f;
+    for (int i = lane; i < D; i += 64) ss = fmaf(xr[i], xr[i], ss);
+    ss = group_sum<64>(ss);
+    if (lane == 0) rb.inv_rms[t] = 1.0f / sqrtf(ss / (float)D + eps);
+  }
+}
+
+// One workgroup per expert: histogram of all pair experts (for its offset),
+// then a stable, order-preserving compaction of its own pairs.  Workgroup 0
+// also writes counts, offsets, the active-expert list and the m-tile list.
+__global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int tile_m, RouteBufs rb) {
+  __shared__ int hist[MAX_E];
+  __shared__ int wave_tot[16];
+  __shared__ int s_off;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int P = T * k;
+  for (int i = tid; i < E; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) atomicAdd(&hist[rb.ids[p]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int off = 0;
+    for (int i = 0; i < e; ++i) off += hist[i];
+    s_off = off;
+    if (e == 0) {
+      int acc = 0, na = 0, nt = 0;
+      for (int i = 0; i < E; ++i) {
+        rb.counts[i] = hist[i];
+        rb.offsets[i] = acc;
+        if (hist[i] > 0) {
+          rb.act_expert[na] = i;
+          rb.act_begin[na] = acc;
+          ++na;
+          if (tile_m > 0)
+            for (int m0 = 0; m0 < hist[i]; m0 += tile_m) {
+              rb.tiles[2 * nt] = i;
+              rb.tiles[2 * nt + 1] = acc + m0;
+              ++nt;
+            }
+        }
+        acc += hist[i];
+      }
+      rb.offsets[E] = acc;
+      rb.act_begin[na] = acc;
+      *rb.n_active = na;
+      if (tile_m > 0) *rb.n_tiles = nt;
+    }
+  }
+  __syncthreads();
+  int running = s_off;
+  for (int base = 0; base < P; base += 1024) {
+    const int p = base + tid;
+    const bool mine = p < P && rb.ids[p] == e;
+    const uint64_t bal = __ballot(mine);
+    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wv] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int i = 0; i < 16; ++i) {
+      before += i < wv ? wave_tot[i] : 0;
+      total += wave_tot[i];
+    }
+    if (mine) {
+      const int pos = running + before + rank;
+      rb.pairs[pos] = p;
+      rb.pair_pos[p] = pos;
+    }
+    running += total;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float *logits, int T, int E, int k, const float *x, int D, float eps,
+                       const RouteBufs &rb, bool single_token_lists, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, x, D, eps,
+                     rb, single_token_lists ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_group(int T, int E, int k, int tile_m, const RouteBufs &rb, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(group_kernel, dim3(E), dim3(1024), 0, s, T, E, k, tile_m, rb);
+  return hipGetLastError();
+}
+
+}  // namespace ds4q

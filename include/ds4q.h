@@ -1,0 +1,178 @@
+/* ds4q — routed-MoE expert FFN on Q2_K / Q4_1 block-quantised weights for
+ * AMD Instinct MI355X (gfx950).  C ABI of libds4q.so.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P1] "【#2】ds4.c 해독하기" (molayo1419.me): the Q2_K block-layout table
+ *       (scales @0, qs @16, d @80, dmin @82; 256 values in 84 B) and the
+ *       printed code-packing expression; routed-expert tensors
+ *       blk.N.ffn_{gate,up,down}_exps with w1 = gate, w2 = down, w3 = up;
+ *       the imatrix passage stating that the down projection's input is the
+ *       routed SwiGLU row after the routing weight.
+ *  [P2] "ds4.c 해독하기 1/8" (molayo1419.me): the DS4_SHAPE_FLASH passage —
+ *       256 routed experts per layer, 6 used per token, 43 layers.
+ *  [P5] ThakiCloud, "자체 저비트 포맷을 llama.cpp로 옮기기: 복원값이 비트까지
+ *       같은 GGUF Q4_1 재부호화": the Q4_1 block section (fp16 d, fp16 m,
+ *       qs[16]; low nibble = value j, high nibble = value j+16;
+ *       y = d*q + m); the section on reading bits/group from metadata, never
+ *       from byte counts; the raw_shape section (byte shape vs element shape);
+ *       the tensor-name section (GGUF ne[0] is the input dimension).
+ *
+ * Conventions for every entry point:
+ *  - Types are always explicit (never inferred from a byte count, [P5]).
+ *  - Shapes are ELEMENT shapes; the library derives byte strides
+ *    (row bytes = cols / QK * block_bytes).  A matrix [rows][cols] stores its
+ *    rows one after another, each row a run of blocks along cols (the input
+ *    dimension, [P5]).  An expert tensor is [n_expert][rows][cols], expert
+ *    major ([P1] ffn_*_exps).
+ *  - Every pointer argument named *_dev or documented "device" is device memory
+ *    the caller owns; the library allocates no device memory and keeps no
+ *    device state.  Structs are read on the host during the call only.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; the call returns once it is enqueued.
+ *  - All validation happens on the host before anything is enqueued; on an
+ *    error nothing is launched.  Block contents are never validated: every bit
+ *    pattern is a valid block, and NaN/Inf in fp16 fields propagate.
+ *  - Calls on distinct streams with disjoint outputs and workspaces may run
+ *    concurrently.
+ */
+#ifndef DS4Q_H
+#define DS4Q_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS4Q_ABI_VERSION 1
+
+/* Tensor types.  Numeric values follow the public GGML/GGUF type ids. */
+typedef enum {
+  DS4Q_TYPE_F32 = 0,
+  DS4Q_TYPE_F16 = 1,      /* not accepted by any entry point */
+  DS4Q_TYPE_Q4_1 = 3,     /* 32 values in 20 B, [P5] */
+  DS4Q_TYPE_Q2_K = 10,    /* 256 values in 84 B, [P1] */
+  DS4Q_TYPE_IQ2_XXS = 16, /* known but unsupported: its grid codebook is not on the pages */
+  DS4Q_TYPE_BF16 = 30
+} ds4q_type;
+
+/* Status codes (0 = success, negative = error). */
+enum {
+  DS4Q_OK = 0,
+  DS4Q_E_INVAL = -1,        /* NULL pointer, negative size, bad k / n_expert, unknown flag */
+  DS4Q_E_UNSUPPORTED = -2,  /* type not handled (IQ2_XXS, F16, unknown); no fallback path */
+  DS4Q_E_SHAPE = -3,        /* cols not a multiple of the block size, or a shape the path does not take */
+  DS4Q_E_ALIGN = -4,        /* a pointer misses its required alignment */
+  DS4Q_E_WORKSPACE = -5,    /* workspace NULL or smaller than ds4q_moe_workspace_size() */
+  DS4Q_E_ALIAS = -6,        /* an output overlaps an input or the workspace */
+  DS4Q_E_HIP = -7           /* a HIP runtime call or launch failed */
+};
+
+/* Flags of ds4q_moe_layer.flags. */
+#define DS4Q_F_ACCUMULATE 0x1u    /* y += MoE(x) instead of y = MoE(x) */
+#define DS4Q_F_RMSNORM_INPUT 0x2u /* experts see x / sqrt(mean(x^2) + norm_eps) (per token) */
+
+/* One routed-MoE layer.  gate/up: [n_expert][n_ff][n_embd]; down:
+ * [n_expert][n_embd][n_ff] (element shapes; rows run along the last index).
+ * w1 = gate, w3 = up, w2 = down ([P1]).  Each tensor is Q2_K or Q4_1; gate
+ * and up must share a type, down may differ.  Device pointers, 16-byte
+ * aligned.  n_embd and n_ff each one of 256, 512, 1024, 2048, 4096
+ * (DS4_SHAPE_FLASH: 4096 and 2048); n_expert 1..1024; n_expert_used 1..8 and
+ * <= n_expert; norm_eps finite and >= 0. */
+typedef struct {
+  int32_t n_embd, n_ff, n_expert, n_expert_used;
+  int32_t type_gate, type_up, type_down; /* ds4q_type */
+  const void *gate, *up, *down;
+  uint32_t flags;
+  float norm_eps;
+} ds4q_moe_layer;
+
+/* Optional routing outputs (device pointers; any may be NULL). */
+typedef struct {
+  int32_t *topk_ids;       /* [T][k]  experts by (logit desc, index asc) */
+  float *topk_w;           /* [T][k]  softmax over the k selected logits */
+  int32_t *expert_counts;  /* [n_expert]   pairs per expert */
+  int32_t *expert_offsets; /* [n_expert+1] exclusive prefix of counts */
+  int32_t *sorted_pairs;   /* [T*k]  p = token*k + slot, ordered by (expert, token, slot) */
+} ds4q_route_out;
+
+/* Dequantise a [rows][cols] tensor ([P1] Q2_K table, [P5] Q4_1 section).
+ * src_type: Q2_K (cols % 256 == 0) or Q4_1 (cols % 32 == 0); src 4-byte
+ * aligned device pointer to rows*cols/QK blocks.  dst_type: F32 (value =
+ * fp32 of d*sc*q - dmin*mn, resp. d*q + m, rounded once) or BF16 (that fp32
+ * value rounded to nearest even); dst device [rows][cols], 16-byte aligned,
+ * not overlapping src.  rows == 0 is a no-op. */
+int ds4q_dequant(int32_t src_type, const void *src, int64_t rows, int64_t cols,
+                 int32_t dst_type, void *dst, void *stream);
+
+/* y[t][r] = sum_c W[r][c] * x[t][c] for t < n_tok, fp32 accumulation
+ * (one token per call in the decode use; [P1] layouts).  w: device blocks of
+ * a [rows][cols] Q2_K or Q4_1 tensor, 16-byte aligned, cols one of 256, 512,
+ * 1024, 2048, 4096; x: device f32 [n_tok][cols], 16-byte aligned; y: device
+ * f32 [n_tok][rows], must not overlap x or w.  n_tok in 0..64. */
+int ds4q_matvec(int32_t w_type, const void *w, int64_t rows, int64_t cols,
+                const float *x, int32_t n_tok, float *y, void *stream);
+
+/* Bytes of device workspace ds4q_route needs for n_tok tokens; 0 for invalid
+ * arguments. */
+size_t ds4q_route_workspace_size(int32_t n_tok, int32_t n_expert, int32_t k);
+
+/* Routing alone ([P2]: k of n_expert experts per token; n_expert 1..1024,
+ * k 1..8, n_tok 0..65536).  logits: device f32 [n_tok][n_expert], finite
+ * values expected.  Writes the non-NULL members of *out (device arrays; see
+ * ds4q_route_out).  workspace: device, 256-byte aligned, at least
+ * ds4q_route_workspace_size() bytes, overlapping nothing else. */
+int ds4q_route(const float *logits, int32_t n_tok, int32_t n_expert, int32_t k,
+               const ds4q_route_out *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace a decode (mode 0) or prefill (mode 1) call with
+ * up to max_tok tokens needs; 0 for an invalid layer. */
+size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t mode);
+
+/* Decode-path MoE layer ([P1] SwiGLU expert FFN with the routing weight on the
+ * down input; [P2] top-k routing): for each token t,
+ *   y_t (+)= sum_j p_tj * W2[e_tj] (silu(W1[e_tj] n_t) * (W3[e_tj] n_t)),
+ * n_t = x_t (or its RMS norm with DS4Q_F_RMSNORM_INPUT); fp32 arithmetic.
+ * x: device f32 [n_tok][n_embd]; logits: device f32 [n_tok][n_expert];
+ * y: device f32 [n_tok][n_embd] — may be the same pointer as x (in-place
+ * residual with DS4Q_F_ACCUMULATE), must not partially overlap it.
+ * n_tok in 0..64.  route may be NULL.  workspace: device, 256-byte aligned,
+ * >= ds4q_moe_workspace_size(L, n_tok, 0) bytes, not overlapping any other
+ * argument. */
+int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int32_t n_tok,
+                    float *y, const ds4q_route_out *route, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Prefill-path MoE layer: same mathematics as ds4q_moe_decode for a chunk
+ * of n_tok tokens (0..65536), computed as grouped GEMMs on bf16 matrix cores
+ * with fp32 accumulation: the expert input rows are bf16 (x_type BF16, or
+ * x_type F32 which is normalised per DS4Q_F_RMSNORM_INPUT if set and rounded
+ * to bf16), dequantised weights are rounded to bf16, the SwiGLU row is
+ * rounded to bf16 before the down projection; routing and the final
+ * weighted combine are fp32.  x: device [n_tok][n_embd] of x_type; y: device
+ * f32 [n_tok][n_embd] (may equal x only when x_type is F32).  workspace
+ * >= ds4q_moe_workspace_size(L, n_tok, 1). */
+int ds4q_moe_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const float *logits,
+                     int32_t n_tok, float *y, const ds4q_route_out *route, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Layer stack ([P2]: 43 layers in the Flash shape): for l in 0..n_layers-1,
+ *   x <- x + MoE_l(rmsnorm(x))
+ * with layer l's descriptor layers[l] (its flags are ignored: RMSNORM_INPUT
+ * and ACCUMULATE are implied) and router logits logits + l*n_tok*n_expert.
+ * mode 0 = decode path (n_tok <= 64), 1 = prefill path.  x: device f32
+ * [n_tok][n_embd], updated in place.  All layers must share n_embd, n_ff,
+ * n_expert, n_expert_used.  workspace >= max over layers of
+ * ds4q_moe_workspace_size(layers[l], n_tok, mode). */
+int ds4q_moe_stack(const ds4q_moe_layer *layers, int32_t n_layers, int32_t mode, float *x,
+                   const float *logits, int32_t n_tok, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/* Static description of a status code. */
+const char *ds4q_strerror(int status);
+/* DS4Q_ABI_VERSION of the loaded library. */
+int ds4q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DS4Q_H */

@@ -198,3 +198,75 @@ def logits_zipf(key: int, T: int, E: int, s: float = 1.1) -> np.ndarray:
     u = uniform01(stream_key(key, 0x6B), T * E).reshape(T, E)
     g = -np.log(-np.log(u))
     return (-s * np.log(rank.astype(np.float64))[None, :] + g).astype(np.float32)
+
+
+# ---------------------------------------------------------------- device twin
+
+_dev_lib = None
+_DEV_LIB_PATH = __import__("os").path.join(__import__("os").path.dirname(__file__), "libds4q_synth.so")
+
+
+def build_device(force: bool = True) -> str:
+    """Compile the HIP twin of the block generators (gfx950)."""
+    import os
+    import subprocess
+    if force or not os.path.exists(_DEV_LIB_PATH):
+        src = os.path.join(os.path.dirname(__file__), "csrc", "synth_gen.hip")
+        hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+        cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-o", _DEV_LIB_PATH + ".tmp", src]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(r.stderr)
+        os.replace(_DEV_LIB_PATH + ".tmp", _DEV_LIB_PATH)
+    return _DEV_LIB_PATH
+
+
+def _device_lib():
+    global _dev_lib
+    if _dev_lib is None:
+        import ctypes
+        import os
+        if not os.path.exists(_DEV_LIB_PATH):
+            raise ImportError(f"{_DEV_LIB_PATH} is not built")
+        L = ctypes.CDLL(_DEV_LIB_PATH)
+        P, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.synth_q2k_fill.restype = ctypes.c_int
+        L.synth_q2k_fill.argtypes = [P, P, i64, i64, P, P]
+        L.synth_q41_fill.restype = ctypes.c_int
+        L.synth_q41_fill.argtypes = [P, P, i64, i64, P, P, P]
+        _dev_lib = L
+    return _dev_lib
+
+
+_dev_tables: dict = {}
+
+
+def device_fill(qtype: str, dst, keys, blocks_per_tensor: int):
+    """Fill ``len(keys)`` consecutive tensors of ``blocks_per_tensor`` blocks in
+    the uint8 CUDA tensor ``dst`` (on its device, current stream) with the
+    same bytes q2k_blocks / q41_blocks draw for those stream keys."""
+    import torch
+    dev = dst.device
+    if dev not in _dev_tables:
+        half, full = f16_tables()
+        _dev_tables[dev] = (torch.from_numpy(half.view(np.int16).copy()).to(dev),
+                            torch.from_numpy(full.view(np.int16).copy()).to(dev))
+    half_t, full_t = _dev_tables[dev]
+    bb = Q2K_BLOCK_BYTES if qtype == "q2_k" else Q41_BLOCK_BYTES
+    n = len(keys)
+    assert dst.dtype == torch.uint8 and dst.is_contiguous()
+    assert dst.numel() >= n * blocks_per_tensor * bb
+    assert dst.data_ptr() % 4 == 0
+    k = torch.tensor(np.array([int(v) for v in keys], dtype=np.uint64).view(np.int64), device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    L = _device_lib()
+    if qtype == "q2_k":
+        rc = L.synth_q2k_fill(dst.data_ptr(), k.data_ptr(), n, blocks_per_tensor, half_t.data_ptr(), s)
+    else:
+        rc = L.synth_q41_fill(dst.data_ptr(), k.data_ptr(), n, blocks_per_tensor, half_t.data_ptr(),
+                              full_t.data_ptr(), s)
+    if rc != 0:
+        raise RuntimeError(f"synth device fill failed: hip error {rc}")
+    return k            # keep alive until the stream has consumed it

@@ -1,0 +1,255 @@
+"""GPU parity of the decode path through the C ABI against the oracle:
+device generator, dequant (bit-exact), matvec, routing (bit-exact ids and
+grouping), decode MoE layer (normwise <= 2e-3)."""
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import SynthLayer, normwise_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL_FP32 = 2e-3
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- generator twin
+
+@pytest.mark.parametrize("qname,bb,per", [("q2_k", 84, 256), ("q4_1", 20, 32)])
+def test_device_generator_matches_host(gpu, qname, bb, per):
+    keys = [synth.layer_key(77, 3, "gate", e) for e in (0, 1, 255)]
+    nblk = 2048 * 4096 // per // 16
+    t = torch.empty(len(keys) * nblk * bb, dtype=torch.uint8, device=DEV)
+    synth.device_fill(qname, t, keys, nblk)
+    torch.cuda.synchronize()
+    got = t.cpu().numpy().reshape(len(keys), -1)
+    gen = synth.q2k_blocks if qname == "q2_k" else synth.q41_blocks
+    for i, kk in enumerate(keys):
+        assert np.array_equal(got[i], gen(kk, nblk).ravel())
+
+
+# ---------------------------------------------------------------- dequant
+
+def _special_q2k_blocks(n):
+    b = synth.q2k_blocks(synth.stream_key(5, 5), n)
+    fields = [0x7E00, 0x7C00, 0xFC00, 0x0001, 0x03FF, 0x8000, 0x0000, 0xBC00]
+    for i in range(n):
+        d, dm = fields[i % len(fields)], fields[(i // len(fields)) % len(fields)]
+        b[i, 80:84] = np.frombuffer(struct.pack("<HH", d, dm), np.uint8)
+    return b
+
+
+def _compare_f32_bits(got, ref):
+    gn, rn = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(gn, rn)
+    assert np.array_equal(got[~gn].view(np.uint32), ref[~rn].view(np.uint32))
+
+
+@pytest.mark.parametrize("qt", [10, 3])
+@pytest.mark.parametrize("rows,cols", [(2048, 4096), (3, 256), (7, 512), (1, 4096)])
+def test_dequant_bitexact(gpu, qt, rows, cols):
+    ds4q = gpu
+    _log(f"dequant qt={qt} rows={rows} cols={cols}")
+    qname = "q2_k" if qt == 10 else "q4_1"
+    w = synth.expert_tensor_blocks(qname, synth.stream_key(6, qt, rows, cols), rows, cols)
+    if rows <= 8 and qt == 10:
+        w = _special_q2k_blocks(rows * cols // 256).reshape(rows, -1)
+    wd = torch.from_numpy(w.ravel().copy()).to(DEV)
+    f = torch.empty(rows, cols, dtype=torch.float32, device=DEV)
+    b = torch.empty(rows, cols, dtype=torch.int16, device=DEV)
+    ds4q.ds4q_dequant(qt, wd, rows, cols, ds4q.TYPE_F32, f)
+    ds4q.ds4q_dequant(qt, wd, rows, cols, ds4q.TYPE_BF16, b)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_f32(qt, w, rows, cols)
+    _compare_f32_bits(f.cpu().numpy(), ref)
+    refb = oracle.dequant_bf16(qt, w, rows, cols)
+    gb = b.cpu().numpy().view(np.uint16)
+    nan = np.isnan(ref)
+    assert np.array_equal(gb[~nan], refb[~nan])
+    assert np.all((gb[nan] & 0x7F80) == 0x7F80) and np.all((gb[nan] & 0x7F) != 0)
+
+
+def test_dequant_q41_special_fields(gpu):
+    ds4q = gpu
+    w = synth.q41_blocks(synth.stream_key(8), 64)
+    fields = [0x7E00, 0x7C00, 0xFC00, 0x0001, 0x03FF, 0x8000, 0x0000, 0xBC00]
+    for i in range(64):
+        w[i, 0:4] = np.frombuffer(struct.pack("<HH", fields[i % 8], fields[i // 8]), np.uint8)
+    wd = torch.from_numpy(w.ravel().copy()).to(DEV)
+    f = torch.empty(2, 1024, dtype=torch.float32, device=DEV)
+    ds4q.ds4q_dequant(3, wd, 2, 1024, ds4q.TYPE_F32, f)
+    torch.cuda.synchronize()
+    _compare_f32_bits(f.cpu().numpy(), oracle.dequant_f32(3, w, 2, 1024))
+
+
+def test_dequant_empty_is_noop(gpu):
+    ds4q = gpu
+    ds4q.ds4q_dequant(10, 0, 0, 256, ds4q.TYPE_F32, 0)
+
+
+# ---------------------------------------------------------------- matvec
+
+@pytest.mark.parametrize("qt", [10, 3])
+@pytest.mark.parametrize("rows,cols,T", [(2048, 4096, 1), (2048, 4096, 3), (5, 256, 1),
+                                         (37, 512, 2), (130, 2048, 1), (64, 1024, 1)])
+def test_matvec_parity(gpu, qt, rows, cols, T):
+    ds4q = gpu
+    _log(f"matvec qt={qt} rows={rows} cols={cols} T={T}")
+    qname = "q2_k" if qt == 10 else "q4_1"
+    w = synth.expert_tensor_blocks(qname, synth.stream_key(7, qt, rows, cols), rows, cols)
+    x = synth.x_f32(synth.stream_key(8, cols, T), T, cols)
+    y = torch.full((T, rows), float("nan"), dtype=torch.float32, device=DEV)
+    ds4q.ds4q_matvec(qt, torch.from_numpy(w.ravel().copy()).to(DEV), rows, cols,
+                     torch.from_numpy(x).to(DEV), T, y)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.matvec(qt, w, rows, cols, x[t]) for t in range(T)])
+    assert normwise_err(y.cpu().numpy(), ref) <= TOL_FP32
+
+
+# ---------------------------------------------------------------- routing
+
+def _route_gpu(ds4q, lg, k):
+    T, E = lg.shape
+    ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    cnt = torch.empty(E, dtype=torch.int32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    pairs = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    out = ds4q.RouteOut.from_tensors(ids, w, cnt, off, pairs)
+    ws = torch.empty(ds4q.ds4q_route_workspace_size(T, E, k), dtype=torch.uint8, device=DEV)
+    ds4q.ds4q_route(torch.from_numpy(lg).to(DEV), T, E, k, out, ws)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in (ids, w, cnt, off, pairs)]
+
+
+@pytest.mark.parametrize("T,kind", [(1, "n"), (7, "n"), (64, "n"), (4096, "n"), (4096, "zipf")])
+def test_route_parity(gpu, T, kind):
+    ds4q = gpu
+    E, k = 256, 6
+    gen = synth.logits_normal if kind == "n" else synth.logits_zipf
+    lg = gen(synth.stream_key(9, T), T, E)
+    ids, w, cnt, off, pairs = _route_gpu(ds4q, lg, k)
+    rids, rw = oracle.route(lg, k)
+    assert np.array_equal(ids, rids)
+    assert np.max(np.abs(w - rw)) <= 1e-6
+    rc, ro, rp = oracle.group(rids, E)
+    assert np.array_equal(cnt, rc) and np.array_equal(off, ro) and np.array_equal(pairs, rp)
+
+
+def test_route_ties_and_signed_zero(gpu):
+    ds4q = gpu
+    lg = synth.logits_normal(synth.stream_key(10), 8, 256)
+    lg[0] = 0.0
+    lg[1, [200, 10, 99]] = 9.0
+    lg[2, :] = -0.0
+    lg[2, 3] = 0.0                       # +0 and -0 compare equal: index order decides
+    lg[3, [5, 6, 7, 8, 9, 10, 11]] = 3.5  # tie across the 6/7 boundary
+    ids, w, cnt, off, pairs = _route_gpu(ds4q, lg, 6)
+    rids, rw = oracle.route(lg, 6)
+    assert np.array_equal(ids, rids)
+    assert np.max(np.abs(w - rw)) <= 1e-6
+    rc, ro, rp = oracle.group(rids, 256)
+    assert np.array_equal(pairs, rp)
+
+
+@pytest.mark.parametrize("E,k", [(16, 1), (16, 8), (1024, 6), (8, 8)])
+def test_route_shapes(gpu, E, k):
+    ds4q = gpu
+    lg = synth.logits_normal(synth.stream_key(11, E, k), 33, E)
+    ids, w, cnt, off, pairs = _route_gpu(ds4q, lg, k)
+    rids, rw = oracle.route(lg, k)
+    assert np.array_equal(ids, rids)
+    rc, ro, rp = oracle.group(rids, E)
+    assert np.array_equal(pairs, rp) and np.array_equal(off, ro)
+
+
+# ---------------------------------------------------------------- decode MoE
+
+def _decode(ds4q, lay, x, lg, flags=0, y0=None, in_place=False):
+    T = x.shape[0]
+    lay.L.flags = flags
+    xd = torch.from_numpy(x).to(DEV)
+    if in_place:
+        y = xd
+    else:
+        y = torch.from_numpy(y0).to(DEV) if y0 is not None else torch.empty(T, lay.D, device=DEV)
+    ws = torch.empty(ds4q.ds4q_moe_workspace_size(lay.L, T, 0), dtype=torch.uint8, device=DEV)
+    ids = torch.empty(T, lay.k, dtype=torch.int32, device=DEV)
+    ds4q.ds4q_moe_decode(lay.L, xd, torch.from_numpy(lg).to(DEV), T, y,
+                         ds4q.RouteOut.from_tensors(topk_ids=ids), ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ids.cpu().numpy()
+
+
+@pytest.mark.parametrize("qt,qtd", [(10, 10), (3, 3), (10, 3), (3, 10)])
+@pytest.mark.parametrize("T", [1, 2, 5, 64])
+def test_decode_small(gpu, qt, qtd, T):
+    ds4q = gpu
+    _log(f"decode small qt={qt} qtd={qtd} T={T}")
+    lay = SynthLayer(ds4q, DEV, 512, 256, 16, 6, qt, seed=100 + T, qtype_down=qtd)
+    x = synth.x_f32(synth.stream_key(12, T), T, 512)
+    lg = synth.logits_normal(synth.stream_key(13, T), T, 16)
+    y, ids = _decode(ds4q, lay, x, lg)
+    assert np.array_equal(ids, oracle.route(lg, 6)[0])
+    assert normwise_err(y, lay.oracle_moe(x, lg)) <= TOL_FP32
+
+
+@pytest.mark.parametrize("D,F", [(256, 4096), (4096, 256), (1024, 512), (2048, 1024)])
+def test_decode_shapes(gpu, D, F):
+    ds4q = gpu
+    _log(f"decode shapes D={D} F={F}")
+    lay = SynthLayer(ds4q, DEV, D, F, 8, 2, 10, seed=200 + D)
+    x = synth.x_f32(synth.stream_key(14, D), 3, D)
+    lg = synth.logits_normal(synth.stream_key(15, D), 3, 8)
+    y, _ = _decode(ds4q, lay, x, lg)
+    assert normwise_err(y, lay.oracle_moe(x, lg)) <= TOL_FP32
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_flags_residual_rmsnorm(gpu, T):
+    ds4q = gpu
+    lay = SynthLayer(ds4q, DEV, 512, 256, 16, 6, 10, seed=300)
+    x = synth.x_f32(synth.stream_key(16, T), T, 512) * 3.0
+    lg = synth.logits_normal(synth.stream_key(17, T), T, 16)
+    n = np.stack([oracle.rmsnorm(x[t]) for t in range(T)]).astype(np.float32)
+    ref = lay.oracle_moe(n, lg)
+    y0 = synth.x_f32(synth.stream_key(18, T), T, 512)
+    y, _ = _decode(ds4q, lay, x, lg, flags=ds4q.F_RMSNORM_INPUT | ds4q.F_ACCUMULATE, y0=y0)
+    assert normwise_err(y - y0, ref) <= TOL_FP32
+    y2, _ = _decode(ds4q, lay, x, lg, flags=ds4q.F_RMSNORM_INPUT | ds4q.F_ACCUMULATE, in_place=True)
+    assert normwise_err(y2 - x, ref) <= TOL_FP32
+
+
+def test_decode_full_layer_one_token(gpu):
+    """One-layer decode, 1 token, DeepSeek-V4-Flash expert shape (Q2_K)."""
+    ds4q = gpu
+    _log("decode full T=1")
+    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, 10, seed=400)
+    x = synth.x_f32(synth.stream_key(19), 1, 4096)
+    lg = synth.logits_normal(synth.stream_key(20), 1, 256)
+    y, ids = _decode(ds4q, lay, x, lg)
+    assert np.array_equal(ids, oracle.route(lg, 6)[0])
+    assert normwise_err(y, lay.oracle_moe(x, lg, n_threads=16)) <= TOL_FP32
+
+
+@pytest.mark.parametrize("qt", [10, 3])
+def test_decode_full_layer_64_tokens(gpu, qt):
+    """One-layer batched decode, 64 tokens, full shape; 8 sampled tokens are
+    checked against the oracle (tokens are independent given the logits)."""
+    ds4q = gpu
+    _log(f"decode full T=64 qt={qt}")
+    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, qt, seed=500 + qt)
+    x = synth.x_f32(synth.stream_key(21), 64, 4096)
+    lg = synth.logits_normal(synth.stream_key(22), 64, 256)
+    y, ids = _decode(ds4q, lay, x, lg)
+    assert np.array_equal(ids, oracle.route(lg, 6)[0])
+    sample = np.array([0, 9, 17, 30, 41, 52, 60, 63])
+    ref = lay.oracle_moe(x[sample], lg[sample], n_threads=16)
+    assert normwise_err(y[sample], ref) <= TOL_FP32
