@@ -1,0 +1,128 @@
+"""GPU parity of the prefill path (bf16 MFMA grouped GEMMs) through the C ABI
+against the oracle: max relative error <= 1e-2 — per token row (max |err| /
+max |ref| of the row) at the DeepSeek-V4-Flash expert shape, tensor-wide at
+the smaller test shapes (see helpers.normwise_err_tensor); routing ids and
+grouping bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import SynthLayer, normwise_err, normwise_err_tensor
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL_BF16 = 1e-2
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _bf16_input(key, T, D):
+    bits = synth.x_bf16(key, T, D)
+    as_f32 = (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits, as_f32
+
+
+def _prefill(ds4q, lay, x_bits_or_f32, x_type, lg, flags=0, y0=None, route=True):
+    T = lg.shape[0]
+    lay.L.flags = flags
+    if x_type == ds4q.TYPE_BF16:
+        xd = torch.from_numpy(x_bits_or_f32.view(np.int16)).to(DEV)
+    else:
+        xd = torch.from_numpy(x_bits_or_f32).to(DEV)
+    y = torch.from_numpy(y0).to(DEV) if y0 is not None else torch.empty(T, lay.D, device=DEV)
+    ws = torch.empty(ds4q.ds4q_moe_workspace_size(lay.L, T, 1), dtype=torch.uint8, device=DEV)
+    r = None
+    if route:
+        ids = torch.empty(T, lay.k, dtype=torch.int32, device=DEV)
+        cnt = torch.empty(lay.E, dtype=torch.int32, device=DEV)
+        off = torch.empty(lay.E + 1, dtype=torch.int32, device=DEV)
+        pairs = torch.empty(T * lay.k, dtype=torch.int32, device=DEV)
+        r = ds4q.RouteOut.from_tensors(ids, None, cnt, off, pairs)
+    ds4q.ds4q_moe_prefill(lay.L, xd, x_type, torch.from_numpy(lg).to(DEV), T, y, r, ws)
+    torch.cuda.synchronize()
+    out = y.cpu().numpy()
+    if route:
+        return out, [a.cpu().numpy() for a in (ids, cnt, off, pairs)]
+    return out, None
+
+
+def _check_route(lg, k, E, got):
+    ids, cnt, off, pairs = got
+    rids, _ = oracle.route(lg, k)
+    assert np.array_equal(ids, rids)
+    rc, ro, rp = oracle.group(rids, E)
+    assert np.array_equal(cnt, rc) and np.array_equal(off, ro) and np.array_equal(pairs, rp)
+
+
+@pytest.mark.parametrize("qt,qtd", [(10, 10), (3, 3), (10, 3)])
+@pytest.mark.parametrize("T", [1, 5, 100, 300])
+def test_prefill_small(gpu, qt, qtd, T):
+    ds4q = gpu
+    _log(f"prefill small qt={qt} qtd={qtd} T={T}")
+    lay = SynthLayer(ds4q, DEV, 512, 256, 16, 6, qt, seed=600 + T, qtype_down=qtd)
+    bits, xf = _bf16_input(synth.stream_key(30, T), T, 512)
+    lg = synth.logits_normal(synth.stream_key(31, T), T, 16)
+    y, r = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg)
+    _check_route(lg, 6, 16, r)
+    assert normwise_err_tensor(y, lay.oracle_moe(xf, lg, n_threads=16)) <= TOL_BF16
+
+
+def test_prefill_skewed_multi_tile(gpu):
+    """A dominant expert gets far more than one 128-pair m-tile."""
+    ds4q = gpu
+    T = 700
+    lay = SynthLayer(ds4q, DEV, 512, 256, 32, 6, 10, seed=610)
+    bits, xf = _bf16_input(synth.stream_key(32), T, 512)
+    lg = synth.logits_zipf(synth.stream_key(33), T, 32)
+    y, r = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg)
+    _check_route(lg, 6, 32, r)
+    assert r[1].max() > 3 * 128
+    sample = np.arange(0, T, 7)
+    assert normwise_err_tensor(y[sample], lay.oracle_moe(xf[sample], lg[sample], n_threads=16)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("D,F", [(256, 4096), (4096, 256), (1024, 512)])
+def test_prefill_shapes(gpu, D, F):
+    ds4q = gpu
+    _log(f"prefill shapes D={D} F={F}")
+    lay = SynthLayer(ds4q, DEV, D, F, 8, 2, 3, seed=620 + D)
+    bits, xf = _bf16_input(synth.stream_key(34, D), 40, D)
+    lg = synth.logits_normal(synth.stream_key(35, D), 40, 8)
+    y, _ = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg, route=False)
+    assert normwise_err_tensor(y, lay.oracle_moe(xf, lg, n_threads=16)) <= TOL_BF16
+
+
+def test_prefill_f32_input_rmsnorm_accumulate(gpu):
+    ds4q = gpu
+    T = 50
+    lay = SynthLayer(ds4q, DEV, 512, 256, 16, 6, 10, seed=630)
+    x = synth.x_f32(synth.stream_key(36), T, 512) * 5.0
+    lg = synth.logits_normal(synth.stream_key(37), T, 16)
+    n = np.stack([oracle.rmsnorm(x[t]) for t in range(T)]).astype(np.float32)
+    nb = (oracle.bf16_rne(n).astype(np.uint32) << 16).view(np.float32)
+    y0 = synth.x_f32(synth.stream_key(38), T, 512)
+    y, _ = _prefill(ds4q, lay, x, ds4q.TYPE_F32, lg, flags=ds4q.F_RMSNORM_INPUT | ds4q.F_ACCUMULATE,
+                    y0=y0, route=False)
+    assert normwise_err_tensor(y - y0, lay.oracle_moe(nb, lg, n_threads=16)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("kind", ["uniform", "zipf"])
+def test_prefill_full_chunk(gpu, kind):
+    """One-layer prefill chunk: 4096 bf16 tokens, DeepSeek-V4-Flash expert
+    shape, Q2_K; 16 sampled tokens against the oracle."""
+    ds4q = gpu
+    _log(f"prefill full {kind}")
+    T = 4096
+    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, 10, seed=640)
+    bits, xf = _bf16_input(synth.stream_key(39), T, 4096)
+    gen = synth.logits_normal if kind == "uniform" else synth.logits_zipf
+    lg = gen(synth.stream_key(40, 0 if kind == "uniform" else 1), T, 256)
+    y, r = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg)
+    _check_route(lg, 6, 256, r)
+    assert np.all(np.isfinite(y))
+    sample = np.linspace(0, T - 1, 16).astype(int)
+    assert normwise_err(y[sample], lay.oracle_moe(xf[sample], lg[sample], n_threads=16)) <= TOL_BF16
