@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE expert path on Q2_K weights, one MI355X.
+
+Headline workload: one MoE layer decode of one token in the DeepSeek-V4-Flash
+routed-expert shape (256 experts, top-6, gate/up 4096->2048, SwiGLU, down
+2048->4096), weights Q2_K, activations fp32.  A step is one full layer call
+(routing, gate/up + SwiGLU, down + weighted combine) through the C ABI.
+Steps cycle over --layers distinct seeded weight sets (2.11 GB each, far more
+than the 256 MB MALL) and fresh seeded router logits / activations, so weight
+bytes come from HBM.  Steps are replayed from a HIP graph (one graph holds one
+step per layer).
+
+Also measured in the same run: the 4096-token prefill chunk (bf16, uniform
+routing) as a secondary figure, the dominant kernels' durations from HIP
+events the library records around its own launches, and the CPU oracle on a
+bounded sample of the same decode workload.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE expert tokens/s + achieved HBM GB/s (decode); TFLOP/s (4096-tok prefill)"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+D, F, E, K = 4096, 2048, 256, 6
+Q2K_ROW_D = D // 256 * 84       # bytes of one gate/up row (1344)
+Q2K_ROW_F = F // 256 * 84       # bytes of one down row (672)
+PAIR_FLOPS = 2 * 2 * D * F + 2 * F * D
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(T_pairs, T):
+    """Algorithmic HBM bytes of one decode step (T tokens, T_pairs pairs over
+    distinct experts counted once each in the grouped path)."""
+    gateup_w = T_pairs * 2 * F * Q2K_ROW_D
+    down_w = T_pairs * D * Q2K_ROW_F
+    acts = T * D * 4 * 2 + T * E * 4          # x read, y write, logits read
+    return gateup_w + down_w + acts
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--layers", type=int, default=8, help="distinct weight sets cycled")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=96, help="tokens the oracle runs")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run plain device copies of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md, 'How the path would shard'); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_moe_q2_amd as ds4q
+    import synth
+
+    ds4q.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed = 20260601
+    NL = args.layers
+
+    # ------------------------------------------------------------ weights
+    log(f"generating {NL} layers of Q2_K experts on the device ...")
+    layers, keep = [], []
+    for l in range(NL):
+        t = {}
+        for name, rows, cols in (("gate", F, D), ("up", F, D), ("down", D, F)):
+            buf = torch.empty(E * rows * cols // 256 * 84, dtype=torch.uint8, device=dev)
+            keep.append(synth.device_fill("q2_k", buf, [synth.layer_key(seed, l, name, e) for e in range(E)],
+                                          rows * cols // 256))
+            t[name] = buf
+        layers.append(ds4q.MoeLayer.from_tensors(t["gate"], t["up"], t["down"], D, F, E, K,
+                                                 ds4q.TYPE_Q2_K))
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ decode inputs
+    xs = torch.from_numpy(np.stack([synth.x_f32(synth.stream_key(seed, 1, l), 1, D) for l in range(NL)])).to(dev)
+    lgs = torch.from_numpy(np.stack([synth.logits_normal(synth.stream_key(seed, 2, l), 1, E)
+                                     for l in range(NL)])).to(dev)
+    ys = torch.empty(NL, 1, D, dtype=torch.float32, device=dev)
+    ws_dec = torch.empty(ds4q.ds4q_moe_workspace_size(layers[0], 1, 0), dtype=torch.uint8, device=dev)
+
+    def decode_step(l):
+        ds4q.ds4q_moe_decode(layers[l], xs[l], lgs[l], 1, ys[l], None, ws_dec)
+
+    for l in range(NL):
+        decode_step(l)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(NL):
+            decode_step(l)
+    torch.cuda.synchronize()
+
+    reps_w = max(1, args.warmup // NL)
+    reps = max(1, args.steps // NL)
+    for _ in range(reps_w):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    dec_ms = ev0.elapsed_time(ev1)
+    steps_done = reps * NL
+    ms_per_step = dec_ms / steps_done
+    tok_s = steps_done / (dec_ms / 1e3)
+    step_bytes = decode_bytes(K, 1)
+    log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s, "
+        f"{step_bytes / (ms_per_step / 1e3) / 1e9:.0f} GB/s algorithmic")
+
+    # per-kernel durations: HIP events the library records around its launches
+    ds4q.ds4q_timing_enable(True)
+    n_timed = min(steps_done, 64 * NL)
+    for i in range(n_timed):
+        decode_step(i % NL)
+    torch.cuda.synchronize()
+    kt = ds4q.ds4q_timing_read()
+    ds4q.ds4q_timing_enable(False)
+    gu_ms = kt["decode_gateup"][0] / kt["decode_gateup"][1]
+    dn_ms = kt["decode_down"][0] / kt["decode_down"][1]
+    tk_ms = kt["topk"][0] / kt["topk"][1]
+    gu_bytes = K * 2 * F * Q2K_ROW_D + D * 4 + K * F * 4
+    dn_bytes = K * D * Q2K_ROW_F + K * F * 4 + D * 4
+    gu_gbps = gu_bytes / (gu_ms / 1e3) / 1e9
+    log(f"kernels: topk {tk_ms * 1e3:.2f} us, gateup {gu_ms * 1e3:.2f} us ({gu_gbps:.0f} GB/s), "
+        f"down {dn_ms * 1e3:.2f} us ({dn_bytes / (dn_ms / 1e3) / 1e9:.0f} GB/s)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps_done,
+        "warmup": reps_w * NL,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Q2_K blocks: codes U{0..3}, scale/min nibbles U{0..15}, "
+                "d/dmin |N(0,0.01)|; x, logits N(0,1))",
+        "config": {"workload": "moe_layer_decode_1tok", "weights": "q2_k", "n_expert": E,
+                   "top_k": K, "n_embd": D, "n_ff": F, "tokens": 1,
+                   "weight_sets_cycled": NL, "graph_replay": True},
+        "hbm_gbps_step": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_gateup", "achieved": round(gu_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": gu_bytes,
+                     "avg_launch_us": round(gu_ms * 1e3, 3)},
+        "kernels_us": {k: round(v[0] / v[1] * 1e3, 3) for k, v in kt.items()},
+    }
+
+    # ------------------------------------------------------------ prefill (secondary)
+    if not args.no_prefill:
+        T = 4096
+        xb = torch.from_numpy(synth.x_bf16(synth.stream_key(seed, 3), T, D).view(np.int16)).to(dev)
+        lgp = torch.from_numpy(synth.logits_normal(synth.stream_key(seed, 4), T, E)).to(dev)
+        yp = torch.empty(T, D, dtype=torch.float32, device=dev)
+        ws_p = torch.empty(ds4q.ds4q_moe_workspace_size(layers[0], T, 1), dtype=torch.uint8, device=dev)
+
+        def prefill_step():
+            ds4q.ds4q_moe_prefill(layers[0], xb, ds4q.TYPE_BF16, lgp, T, yp, None, ws_p)
+
+        prefill_step()
+        torch.cuda.synchronize()
+        gp = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gp):
+            prefill_step()
+        for _ in range(3):
+            gp.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.prefill_steps):
+            gp.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        p_ms = ev0.elapsed_time(ev1) / args.prefill_steps
+        flops = T * K * PAIR_FLOPS
+        ds4q.ds4q_timing_enable(True)
+        for _ in range(5):
+            prefill_step()
+        torch.cuda.synchronize()
+        pt = ds4q.ds4q_timing_read()
+        ds4q.ds4q_timing_enable(False)
+        g1_ms = pt["prefill_gateup"][0] / pt["prefill_gateup"][1]
+        g1_tf = T * K * 2 * 2 * D * F / (g1_ms / 1e3) / 1e12
+        log(f"prefill: {p_ms:.3f} ms/chunk, {flops / (p_ms / 1e3) / 1e12:.1f} TFLOP/s; "
+            f"gateup {g1_ms:.3f} ms ({g1_tf:.1f} TFLOP/s)")
+        result["prefill"] = {
+            "workload": "moe_layer_prefill_4096tok_bf16_uniform", "ms_per_chunk": round(p_ms, 4),
+            "tflops": round(flops / (p_ms / 1e3) / 1e12, 2),
+            "tokens_per_s": round(T / (p_ms / 1e3), 1),
+            "roofline": {"bound": "mfma", "kernel": "prefill_gateup", "achieved": round(g1_tf, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(g1_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+            "kernels_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in pt.items()},
+        }
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n * 4
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        S = args.cpu_sample
+        threads = min(16, os.cpu_count() or 1)
+        x = np.stack([synth.x_f32(synth.stream_key(seed, 5, i), 1, D)[0] for i in range(S)])
+        lg = np.stack([synth.logits_normal(synth.stream_key(seed, 6, i), 1, E)[0] for i in range(S)])
+        ids, _ = oracle.route(lg, K)
+        host = {n: np.zeros((E, (F if n != "down" else D) * (D if n != "down" else F) // 256 * 84),
+                            dtype=np.uint8) for n in ("gate", "up", "down")}
+        for e in np.unique(ids):
+            for n, rows, cols in (("gate", F, D), ("up", F, D), ("down", D, F)):
+                host[n][e] = synth.expert_tensor_blocks("q2_k", synth.layer_key(seed, 0, n, int(e)),
+                                                        rows, cols).ravel()
+        orc = oracle.Layer(D, F, E, K, oracle.Q2_K, host["gate"], host["up"], host["down"])
+        t0 = time.perf_counter()
+        oracle.moe(orc, x, lg, n_threads=threads)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(S / dt, 3), "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"{S} decode tokens through layer-0 weights (fp64 C oracle, "
+                                            f"OpenMP over tokens), {dt:.1f} s wall"}
+        log(f"cpu oracle: {S / dt:.2f} tok/s on {threads} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

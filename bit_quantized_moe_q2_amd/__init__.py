@@ -18,7 +18,8 @@ __all__ = [
     "F_ACCUMULATE", "F_RMSNORM_INPUT", "Ds4qError", "MoeLayer", "RouteOut", "load",
     "ds4q_abi_version", "ds4q_strerror", "ds4q_dequant", "ds4q_matvec", "ds4q_route",
     "ds4q_route_workspace_size", "ds4q_moe_workspace_size", "ds4q_moe_decode",
-    "ds4q_moe_prefill", "ds4q_moe_stack", "QK", "BLOCK_BYTES", "row_bytes",
+    "ds4q_moe_prefill", "ds4q_moe_stack", "ds4q_timing_enable", "ds4q_timing_read",
+    "QK", "BLOCK_BYTES", "row_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -99,6 +100,9 @@ def load():
         "ds4q_moe_decode": (ctypes.c_int, [LP, P, P, i32, P, RP, P, sz, P]),
         "ds4q_moe_prefill": (ctypes.c_int, [LP, P, i32, P, i32, P, RP, P, sz, P]),
         "ds4q_moe_stack": (ctypes.c_int, [LP, i32, i32, P, P, i32, P, sz, P]),
+        "ds4q_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "ds4q_timing_read": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -187,3 +191,24 @@ def ds4q_moe_stack(layers, mode, x, logits, n_tok, workspace, workspace_bytes=No
     _check("ds4q_moe_stack", load().ds4q_moe_stack(
         arr, len(layers), mode, _ptr(x), _ptr(logits), n_tok, _ptr(workspace),
         _ws_bytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def ds4q_timing_enable(on: bool):
+    _check("ds4q_timing_enable", load().ds4q_timing_enable(1 if on else 0))
+
+
+def ds4q_timing_read() -> dict:
+    """{launch site: (total_ms, count)} since the last read."""
+    n_max, name_len = 32, 32
+    names = ctypes.create_string_buffer(n_max * name_len)
+    tot = (ctypes.c_double * n_max)()
+    cnt = (ctypes.c_int64 * n_max)()
+    n = ctypes.c_int(0)
+    _check("ds4q_timing_read", load().ds4q_timing_read(
+        ctypes.cast(names, ctypes.c_void_p), name_len, ctypes.cast(tot, ctypes.c_void_p),
+        ctypes.cast(cnt, ctypes.c_void_p), n_max, ctypes.byref(n)))
+    out = {}
+    for i in range(n.value):
+        nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (tot[i], cnt[i])
+    return out

@@ -109,8 +109,52 @@ MoeDims dims_of(const ds4q_moe_layer *L) {
   return m;
 }
 
+// ---------------------------------------------------------------- timing
+// While enabled, each launcher call is bracketed by two HIP events recorded on
+// the caller's stream; ds4q_timing_read() resolves them per launcher name.
+struct TimingRec {
+  const char *name;
+  hipEvent_t start, stop;
+};
+constexpr int MAX_TIMING = 1 << 16;
+constexpr int MAX_NAMES = 32;
+bool g_timing = false;
+int g_n_rec = 0;
+TimingRec g_rec[MAX_TIMING];
+
+struct Timed {
+  TimingRec *rec = nullptr;
+  hipStream_t s;
+  Timed(const char *name, hipStream_t st) : s(st) {
+    if (!g_timing || g_n_rec >= MAX_TIMING) return;
+    TimingRec &r = g_rec[g_n_rec];
+    if (hipEventCreate(&r.start) != hipSuccess) return;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return;
+    }
+    r.name = name;
+    if (hipEventRecord(r.start, s) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      (void)hipEventDestroy(r.stop);
+      return;
+    }
+    rec = &r;
+    ++g_n_rec;
+  }
+  ~Timed() {
+    if (rec) (void)hipEventRecord(rec->stop, s);
+  }
+};
+
 #define HIP_TRY(expr)                                \
   do {                                               \
+    if ((expr) != hipSuccess) return DS4Q_E_HIP;     \
+  } while (0)
+
+#define TIMED_TRY(name, expr)                        \
+  do {                                               \
+    Timed timed_(name, s);                           \
     if ((expr) != hipSuccess) return DS4Q_E_HIP;     \
   } while (0)
 
@@ -184,12 +228,12 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
   const MoeDims m = dims_of(L);
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
-  HIP_TRY(launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));
+  TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));
   // For T == 1 the top-k kernel already wrote the active-expert lists (slot
   // order); the grouping pass (expert order) runs only when asked for.
-  if (T > 1 || wants_grouping(route)) HIP_TRY(launch_group(T, m.E, m.k, 0, w.rb, s));
-  HIP_TRY(launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
-  HIP_TRY(launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, s));
+  if (T > 1 || wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+  TIMED_TRY("decode_gateup", launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
+  TIMED_TRY("decode_down", launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, s));
   return copy_route(route, w.rb, T, m.E, m.k, s);
 }
 
@@ -200,17 +244,17 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
-  HIP_TRY(launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, false, s));
-  HIP_TRY(launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
+  TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, false, s));
+  TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   if (xf) {
-    HIP_TRY(launch_prep_bf16(xf, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xb, s));
+    TIMED_TRY("prep_bf16", launch_prep_bf16(xf, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xb, s));
     xb = w.xb;
   }
   const int mt = max_tiles(T, m.E, m.k);
-  HIP_TRY(launch_prefill_gateup(m, xb, T, w.rb, mt, w.hb, s));
-  HIP_TRY(launch_prefill_down(m, w.hb, T, w.rb, mt, w.o, s));
-  HIP_TRY(launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, s));
+  TIMED_TRY("prefill_gateup", launch_prefill_gateup(m, xb, T, w.rb, mt, w.hb, s));
+  TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.o, s));
+  TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, s));
   return copy_route(route, w.rb, T, m.E, m.k, s);
 }
 
@@ -359,4 +403,42 @@ DS4Q_API int ds4q_moe_stack(const ds4q_moe_layer *layers, int32_t n_layers, int3
     if (rc) return rc;
   }
   return DS4Q_OK;
+}
+
+DS4Q_API int ds4q_timing_enable(int on) {
+  g_timing = on != 0;
+  return DS4Q_OK;
+}
+
+DS4Q_API int ds4q_timing_read(char *names, int name_len, double *total_ms, int64_t *count,
+                              int max_names, int *n_names) {
+  if (!names || !total_ms || !count || !n_names || name_len < 2 || max_names < 1)
+    return DS4Q_E_INVAL;
+  const char *seen[MAX_NAMES];
+  int n = 0, rc = DS4Q_OK;
+  for (int i = 0; i < g_n_rec; ++i) {
+    TimingRec &r = g_rec[i];
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      rc = DS4Q_E_HIP;
+    int j = 0;
+    while (j < n && strcmp(seen[j], r.name) != 0) ++j;
+    if (j == n && n < max_names && n < MAX_NAMES) {
+      seen[n] = r.name;
+      strncpy(names + (size_t)n * name_len, r.name, (size_t)name_len - 1);
+      names[(size_t)n * name_len + name_len - 1] = 0;
+      total_ms[n] = 0.0;
+      count[n] = 0;
+      ++n;
+    }
+    if (j < n) {
+      total_ms[j] += ms;
+      count[j] += 1;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_n_rec = 0;
+  *n_names = n;
+  return rc;
 }

@@ -167,6 +167,20 @@ int ds4q_moe_stack(const ds4q_moe_layer *layers, int32_t n_layers, int32_t mode,
                    const float *logits, int32_t n_tok, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* Per-kernel timing for profiling harnesses (not thread-safe; intended for a
+ * single benchmarking thread).  While enabled, every kernel launch made by
+ * the calls above is bracketed by two HIP events recorded on the call's
+ * stream (the kernels themselves are unchanged; the gaps between launches
+ * grow by the event records).  At most 65536 launches are recorded. */
+int ds4q_timing_enable(int on);
+/* Waits for the recorded events, then returns one entry per launch site:
+ * names (max_names x name_len chars, NUL-terminated: "topk", "group",
+ * "decode_gateup", "decode_down", "prep_bf16", "prefill_gateup",
+ * "prefill_down", "combine"), summed milliseconds and launch counts (host
+ * arrays).  Clears the record. */
+int ds4q_timing_read(char *names, int name_len, double *total_ms, int64_t *count, int max_names,
+                     int *n_names);
+
 /* Static description of a status code. */
 const char *ds4q_strerror(int status);
 /* DS4Q_ABI_VERSION of the loaded library. */
