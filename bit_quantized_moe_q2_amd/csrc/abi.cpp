@@ -44,6 +44,7 @@ int max_tiles(int T, int E, int k) {
 struct Workspace {
   RouteBufs rb{};
   float *h = nullptr;      // decode: [T*k][F] f32
+  void *qbuf = nullptr;    // decode T == 1: quantised activations
   uint16_t *hb = nullptr;  // prefill: [T*k][F] bf16 (sorted order)
   float *o = nullptr;      // [T*k][D] f32
   uint16_t *xb = nullptr;  // prefill: [T][D] bf16
@@ -72,6 +73,7 @@ struct Workspace {
       // routing only
     } else if (mode == 0) {
       h = (float *)take(P * F * 4);
+      qbuf = take(qact_bytes(1, D));
       if (T > 1) o = (float *)take(P * D * 4);
     } else {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
@@ -228,6 +230,14 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
   const MoeDims m = dims_of(L);
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
+  if (T == 1 && m.tg == DS4Q_TYPE_Q2_K && m.td == DS4Q_TYPE_Q2_K) {
+    TIMED_TRY("decode_prologue", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 0, s));
+    TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 1, s));
+    TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 2, s));
+    // the grouping pass (expert order) runs only when asked for
+    if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+    return copy_route(route, w.rb, T, m.E, m.k, s);
+  }
   TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));
   // For T == 1 the top-k kernel already wrote the active-expert lists (slot
   // order); the grouping pass (expert order) runs only when asked for.

@@ -64,4 +64,128 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// ---------------------------------------------------------------- routing
+
+// Order-preserving uint32 of an fp32 value, with -0.0 folded onto +0.0 so
+// that equal logits tie exactly as floating-point comparison says.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+constexpr int ROUTE_MAX_E = 1024;
+
+// DPP (data-parallel primitives) lane exchanges: results stay in VALU
+// registers, no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Wave-wide unsigned max / min; the result is uniform.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, dpp<DPP_XOR1>(v));
+  v = max(v, dpp<DPP_XOR2>(v));
+  v = max(v, dpp<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp<DPP_MIRROR>(v));
+  return max(max(readlane(v, 0), readlane(v, 16)), max(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = min(v, dpp<DPP_XOR1>(v));
+  v = min(v, dpp<DPP_XOR2>(v));
+  v = min(v, dpp<DPP_HALF_MIRROR>(v));
+  v = min(v, dpp<DPP_MIRROR>(v));
+  return min(min(readlane(v, 0), readlane(v, 16)), min(readlane(v, 32), readlane(v, 48)));
+}
+
+__device__ __forceinline__ float float_from_ordered(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __builtin_bit_cast(float, u);
+}
+
+// Top-k for E <= 256 logits (four per lane: expert lane + 64i): each round
+// takes the wave max of the order-preserving keys, then the smallest expert
+// index holding it (ties -> lower index).  Lane j < k returns slot j's expert
+// and softmax weight.
+__device__ __forceinline__ void wave_topk256(const float *__restrict__ lg, int E, int k, int lane,
+                                             int *id, float *w) {
+  uint32_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? ordered_bits(lg[e]) : 0u;
+  }
+  uint32_t my_id = 0, my_key = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t gm = wave_umax(max(max(key[0], key[1]), max(key[2], key[3])));
+    uint32_t cand = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cand = key[i] == gm ? min(cand, (uint32_t)(lane + 64 * i)) : cand;
+    const uint32_t ew = wave_umin(cand);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(lane + 64 * i) == ew ? 0u : key[i];
+    if (lane == j) { my_id = ew; my_key = gm; }
+  }
+  const float top = float_from_ordered(readlane(my_key, 0));
+  const float ex = lane < k ? expf(float_from_ordered(my_key) - top) : 0.f;
+  float den = 0.f;
+  for (int j = 0; j < k; ++j) den += __builtin_bit_cast(float, readlane(__builtin_bit_cast(uint32_t, ex), j));
+  *id = (int)my_id;
+  *w = ex / den;
+}
+
+// Top-k of E logits by (logit desc, index asc) for one token, computed by a
+// whole wave64; softmax weights over the k selected (max-subtracted).  Lane
+// j < k returns slot j's expert in *id and weight in *w; every lane returns
+// the same values for the slot it asks for through the arrays.
+template <int MAXE>
+__device__ __forceinline__ void wave_topk(const float *__restrict__ lg, int E, int k, int lane,
+                                          int *id, float *w) {
+  uint64_t key[MAXE / 64];
+#pragma unroll
+  for (int i = 0; i < MAXE / 64; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? ((uint64_t)ordered_bits(lg[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  int my_id = 0;
+  float my_val = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < MAXE / 64; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+#pragma unroll
+    for (int i = 0; i < MAXE / 64; ++i)
+      if (lane + 64 * i == e) key[i] = 0ull;
+    if (lane == j) { my_id = e; my_val = lg[e]; }
+  }
+  const float top = __shfl(my_val, 0, 64);
+  const float ex = lane < k ? expf(my_val - top) : 0.f;
+  float den = ex;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+  *id = my_id;
+  *w = ex / den;
+}
+
 }  // namespace ds4q

@@ -13,23 +13,7 @@
 namespace ds4q {
 namespace {
 
-constexpr int MAX_E = 1024;
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ uint32_t ordered_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int MAX_E = ROUTE_MAX_E;
 
 // One wave per token.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
@@ -39,32 +23,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *lg = logits + (int64_t)t * E;
-  uint64_t key[MAX_E / 64];
-#pragma unroll
-  for (int i = 0; i < MAX_E / 64; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? ((uint64_t)ordered_bits(lg[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
-  }
-  float my_val = 0.f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < MAX_E / 64; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-#pragma unroll
-    for (int i = 0; i < MAX_E / 64; ++i)
-      if (lane + 64 * i == e) key[i] = 0ull;
-    if (lane == j) { my_id = e; my_val = lg[e]; }
-  }
-  // softmax over the k selected logits, max-subtracted (slot 0 holds the max)
-  const float top = __shfl(my_val, 0, 64);
-  const float ex = lane < k ? expf(my_val - top) : 0.f;
-  const float den = group_sum<64>(ex);
+  int my_id;
+  float my_w;
+  wave_topk<MAX_E>(lg, E, k, lane, &my_id, &my_w);
   if (lane < k) {
     rb.ids[t * k + lane] = my_id;
-    rb.w[t * k + lane] = ex / den;
+    rb.w[t * k + lane] = my_w;
     if (single) {
       rb.act_expert[lane] = my_id;
       rb.act_begin[lane] = lane;

@@ -201,13 +201,14 @@ def test_decode_small(gpu, qt, qtd, T):
     assert normwise_err(y, lay.oracle_moe(x, lg)) <= TOL_FP32
 
 
-@pytest.mark.parametrize("D,F", [(256, 4096), (4096, 256), (1024, 512), (2048, 1024)])
-def test_decode_shapes(gpu, D, F):
+@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("D,F", [(256, 4096), (4096, 256), (1024, 512), (2048, 1024), (512, 2048)])
+def test_decode_shapes(gpu, D, F, T):
     ds4q = gpu
-    _log(f"decode shapes D={D} F={F}")
+    _log(f"decode shapes D={D} F={F} T={T}")
     lay = SynthLayer(ds4q, DEV, D, F, 8, 2, 10, seed=200 + D)
-    x = synth.x_f32(synth.stream_key(14, D), 3, D)
-    lg = synth.logits_normal(synth.stream_key(15, D), 3, 8)
+    x = synth.x_f32(synth.stream_key(14, D), T, D)
+    lg = synth.logits_normal(synth.stream_key(15, D), T, 8)
     y, _ = _decode(ds4q, lay, x, lg)
     assert normwise_err(y, lay.oracle_moe(x, lg)) <= TOL_FP32
 
