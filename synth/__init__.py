@@ -25,8 +25,10 @@ Recipes (all seeded)
   bytes 80..81 and 82..83 are 16-bit indices into the |N(0, 0.01)| fp16
   quantile table, bytes 84..87 are unused.
 * Q4_1 block (20 B): ``d`` (bytes 0..1) from |N(0, 0.01)|, ``m`` (bytes 2..3)
-  from N(0, 0.01), 16 code bytes (bytes 4..19) uniform, i.e. nibbles
-  U{0..15}.  Block ``b`` consumes words ``3b .. 3b+2``.
+  from -7.5 * |N(0, 0.01)| (an independent draw: the block offset is the
+  group minimum, so that d*q + m is centred near zero like a real group of
+  weights), 16 code bytes (bytes 4..19) uniform, i.e. nibbles U{0..15}.
+  Block ``b`` consumes words ``3b .. 3b+2``.
 * fp16 draws use 65536-entry quantile tables (value at the midpoint of each of
   65536 equal-probability cells, rounded to fp16), so host and device produce
   identical bits without evaluating transcendental functions on the device.
@@ -115,7 +117,8 @@ _TABLES: dict = {}
 
 
 def f16_tables(sigma: float = 0.01):
-    """(half_normal, normal) fp16 quantile tables as uint16[65536] bit patterns.
+    """(half_normal, q41_min) fp16 quantile tables as uint16[65536] bit patterns:
+    |N(0, sigma)| and -7.5 * |N(0, sigma)|.
 
     Entry ``u`` is the distribution's quantile at the midpoint of cell ``u``
     of 65536 equal-probability cells, rounded to fp16 (RNE)."""
@@ -124,9 +127,8 @@ def f16_tables(sigma: float = 0.01):
         from scipy.special import ndtri
         u = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
         half = sigma * ndtri(0.5 + 0.5 * u)
-        full = sigma * ndtri(u)
         _TABLES[key] = (half.astype(np.float16).view(np.uint16).copy(),
-                        full.astype(np.float16).view(np.uint16).copy())
+                        (-7.5 * half).astype(np.float16).view(np.uint16).copy())
     return _TABLES[key]
 
 
@@ -145,12 +147,12 @@ def q2k_blocks(key: int, n_blocks: int, start_block: int = 0) -> np.ndarray:
 
 def q41_blocks(key: int, n_blocks: int, start_block: int = 0) -> np.ndarray:
     """``n_blocks`` Q4_1 blocks (uint8 [n, 20]) of stream ``key``."""
-    half, full = f16_tables()
+    half, mtab = f16_tables()
     w = words(key, start_block * Q41_WORDS_PER_BLOCK, n_blocks * Q41_WORDS_PER_BLOCK)
     raw = w.astype("<u8").view(np.uint8).reshape(n_blocks, 24)
     out = np.empty((n_blocks, Q41_BLOCK_BYTES), dtype=np.uint8)
     idx = raw[:, 0:4].copy().view("<u2")
-    dm = np.stack([half[idx[:, 0]], full[idx[:, 1]]], axis=1)
+    dm = np.stack([half[idx[:, 0]], mtab[idx[:, 1]]], axis=1)
     out[:, 0:4] = dm.astype("<u2").view(np.uint8).reshape(n_blocks, 4)
     out[:, 4:20] = raw[:, 4:20]
     return out
@@ -250,10 +252,10 @@ def device_fill(qtype: str, dst, keys, blocks_per_tensor: int):
     import torch
     dev = dst.device
     if dev not in _dev_tables:
-        half, full = f16_tables()
+        half, mtab = f16_tables()
         _dev_tables[dev] = (torch.from_numpy(half.view(np.int16).copy()).to(dev),
-                            torch.from_numpy(full.view(np.int16).copy()).to(dev))
-    half_t, full_t = _dev_tables[dev]
+                            torch.from_numpy(mtab.view(np.int16).copy()).to(dev))
+    half_t, mtab_t = _dev_tables[dev]
     bb = Q2K_BLOCK_BYTES if qtype == "q2_k" else Q41_BLOCK_BYTES
     n = len(keys)
     assert dst.dtype == torch.uint8 and dst.is_contiguous()
@@ -266,7 +268,7 @@ def device_fill(qtype: str, dst, keys, blocks_per_tensor: int):
         rc = L.synth_q2k_fill(dst.data_ptr(), k.data_ptr(), n, blocks_per_tensor, half_t.data_ptr(), s)
     else:
         rc = L.synth_q41_fill(dst.data_ptr(), k.data_ptr(), n, blocks_per_tensor, half_t.data_ptr(),
-                              full_t.data_ptr(), s)
+                              mtab_t.data_ptr(), s)
     if rc != 0:
         raise RuntimeError(f"synth device fill failed: hip error {rc}")
     return k            # keep alive until the stream has consumed it

@@ -44,7 +44,7 @@ __global__ void synth_q2k_kernel(uint32_t *__restrict__ dst, const uint64_t *__r
 __global__ void synth_q41_kernel(uint32_t *__restrict__ dst, const uint64_t *__restrict__ keys,
                                  int64_t blocks_per_tensor, int64_t n_total,
                                  const uint16_t *__restrict__ half_tab,
-                                 const uint16_t *__restrict__ full_tab) {
+                                 const uint16_t *__restrict__ m_tab) {
   int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_total) return;
   int64_t t = g / blocks_per_tensor;
@@ -54,7 +54,7 @@ __global__ void synth_q41_kernel(uint32_t *__restrict__ dst, const uint64_t *__r
   uint64_t base = (uint64_t)b * 3ull;
   uint64_t w0 = sm64(key, base), w1 = sm64(key, base + 1), w2 = sm64(key, base + 2);
   uint32_t d = half_tab[(uint32_t)w0 & 0xFFFFu];
-  uint32_t m = full_tab[((uint32_t)w0 >> 16) & 0xFFFFu];
+  uint32_t m = m_tab[((uint32_t)w0 >> 16) & 0xFFFFu];
   o[0] = d | (m << 16);
   o[1] = (uint32_t)(w0 >> 32);
   o[2] = (uint32_t)w1;
@@ -79,11 +79,11 @@ extern "C" int synth_q2k_fill(void *dst, const uint64_t *keys, int64_t n_tensors
 
 extern "C" int synth_q41_fill(void *dst, const uint64_t *keys, int64_t n_tensors,
                               int64_t blocks_per_tensor, const uint16_t *half_tab,
-                              const uint16_t *full_tab, void *stream) {
+                              const uint16_t *m_tab, void *stream) {
   int64_t n = n_tensors * blocks_per_tensor;
   if (n <= 0) return 0;
   int64_t grid = (n + 255) / 256;
   hipLaunchKernelGGL(synth_q41_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
-                     (uint32_t *)dst, keys, blocks_per_tensor, n, half_tab, full_tab);
+                     (uint32_t *)dst, keys, blocks_per_tensor, n, half_tab, m_tab);
   return (int)hipGetLastError();
 }

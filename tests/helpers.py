@@ -11,6 +11,12 @@ import synth
 QTYPE_NAME = {10: "q2_k", 3: "q4_1"}
 
 
+# Denominator floor of the relative measures: far below any magnitude fp32
+# arithmetic resolves (a SwiGLU row can underflow exactly to zero in fp32 while
+# the fp64 value is ~1e-76).
+REL_FLOOR = 1e-30
+
+
 def normwise_err_tensor(y, ref):
     """Tensor-wide: max |y - ref| / max |ref| over all elements.  Used for the
     bf16 prefill path at shapes smaller than the DeepSeek-V4-Flash expert
@@ -18,13 +24,13 @@ def normwise_err_tensor(y, ref):
     pipeline exceed 1e-2 on single rows (1.32e-2 measured by emulation at
     512 x 256, against 4.2e-3 at 4096 x 2048)."""
     y = np.asarray(y, dtype=np.float64).reshape(ref.shape)
-    return float(np.max(np.abs(y - ref)) / np.max(np.abs(ref)))
+    return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), REL_FLOOR))
 
 
 def normwise_err(y, ref):
     """Per token row: max_i |y_i - ref_i| / max_i |ref_i|; returns the max over rows."""
     y = np.asarray(y, dtype=np.float64).reshape(ref.shape)
-    den = np.max(np.abs(ref), axis=-1, keepdims=True)
+    den = np.maximum(np.max(np.abs(ref), axis=-1, keepdims=True), REL_FLOOR)
     return float(np.max(np.max(np.abs(y - ref), axis=-1, keepdims=True) / den))
 
 
