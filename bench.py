@@ -20,6 +20,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -42,6 +43,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Algorithmic bytes of one gate/up launch at one token: the six experts'
+# gate and up rows, the input vector and the SwiGLU rows written.
+GATEUP_BYTES = K * 2 * F * Q2K_ROW_D + D * 4 + K * F * 4
+COUNTER_FILE = os.path.join(ROOT, "profiles", "decode_q2k_1tok_hbm_counters.txt")
+KERNEL_SOURCES = ("bit_quantized_moe_q2_amd/csrc/decode_mfma.hip",
+                  "bit_quantized_moe_q2_amd/csrc/common.h")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
+    WRITE_SIZE summary, each scaled by its plain-copy calibration factor;
+    None when there is no summary or the kernel sources have changed since
+    the counters were taken."""
+    try:
+        with open(COUNTER_FILE) as f:
+            rows = [json.loads(ln.split(":", 1)[1]) for ln in f if ln.startswith("traffic_json:")]
+    except OSError:
+        return None
+    for r in rows:
+        if r.get("kernel") == kernel and r.get("src_sha256") == kernel_source_hash():
+            return int(round((r["fetch_kib"] * r["fetch_factor"] + r["write_kib"] * r["write_factor"])
+                             * 1024))
+    return None
+
+
 def decode_bytes(T_pairs, T):
     """Algorithmic HBM bytes of one decode step (T tokens, T_pairs pairs over
     distinct experts counted once each in the grouped path)."""
@@ -54,17 +88,20 @@ def decode_bytes(T_pairs, T):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4000)
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=4300)
+    ap.add_argument("--warmup", type=int, default=430)
     ap.add_argument("--layers", type=int, default=43,
                     help="distinct weight sets cycled (43 = DeepSeek-V4-Flash depth, 91 GB of Q2_K)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=96, help="tokens the oracle runs")
+    ap.add_argument("--cpu-sample", type=int, default=1024,
+                    help="decode tokens the oracle runs (about 15 s on 16 host threads)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run plain device copies of this size (counter calibration)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.layers < 1:
+        ap.error("--steps and --layers must be positive, --warmup non-negative")
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md, 'How the path would shard'); run with --gpus 1.", file=sys.stderr)
@@ -101,56 +138,91 @@ def main():
     lgs = torch.from_numpy(np.stack([synth.logits_normal(synth.stream_key(seed, 2, l), 1, E)
                                      for l in range(NL)])).to(dev)
     ys = torch.empty(NL, 1, D, dtype=torch.float32, device=dev)
-    ws_dec = torch.empty(ds4q.ds4q_moe_workspace_size(layers[0], 1, 0), dtype=torch.uint8, device=dev)
+    # one workspace per layer, so that a graph of one phase over all layers
+    # finds each layer's routing and activations where its full step left them
+    ws_bytes = ds4q.ds4q_moe_workspace_size(layers[0], 1, 0)
+    ws_dec = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(NL)]
 
     def decode_step(l):
-        ds4q.ds4q_moe_decode(layers[l], xs[l], lgs[l], 1, ys[l], None, ws_dec)
+        ds4q.ds4q_moe_decode(layers[l], xs[l], lgs[l], 1, ys[l], None, ws_dec[l])
+
+    def decode_phase(l, ph):
+        ds4q.ds4q_moe_decode_phases(layers[l], xs[l], lgs[l], 1, ys[l], None, ws_dec[l], ph)
 
     for l in range(NL):
         decode_step(l)
     torch.cuda.synchronize()
 
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for l in range(NL):
-            decode_step(l)
-    torch.cuda.synchronize()
+    def capture(fn):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        return gr
 
-    reps_w = max(1, args.warmup // NL)
-    reps = max(1, args.steps // NL)
-    for _ in range(reps_w):
-        g.replay()
+    # a graph of NL steps (one per layer) plus one for the remainder, so that
+    # exactly --steps steps are timed
+    g = capture(lambda: [decode_step(l) for l in range(NL)])
+
+    def run_steps(n):
+        for _ in range(n // NL):
+            g.replay()
+        if n % NL:
+            capture_rem(n % NL).replay()
+
+    rem_graphs = {}
+
+    def capture_rem(r):
+        if r not in rem_graphs:
+            rem_graphs[r] = capture(lambda: [decode_step(l) for l in range(r)])
+        return rem_graphs[r]
+
+    if args.steps % NL:
+        capture_rem(args.steps % NL)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     ev0.record()
-    for _ in range(reps):
-        g.replay()
+    run_steps(args.steps)
     ev1.record()
     torch.cuda.synchronize()
     dec_ms = ev0.elapsed_time(ev1)
-    steps_done = reps * NL
+    steps_done = args.steps
+    reps = max(1, args.steps // NL)
     ms_per_step = dec_ms / steps_done
     tok_s = steps_done / (dec_ms / 1e3)
     step_bytes = decode_bytes(K, 1)
     log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tok_s:.0f} tok/s, "
         f"{step_bytes / (ms_per_step / 1e3) / 1e9:.0f} GB/s algorithmic")
 
-    # per-kernel durations: HIP events the library records around its launches
-    ds4q.ds4q_timing_enable(True)
-    n_timed = min(steps_done, 64 * NL)
-    for i in range(n_timed):
-        decode_step(i % NL)
+    # Per-kernel durations: a graph of one kernel launch per layer (the same
+    # launches as in the step graph, on the same stream), replayed between
+    # two events; launch gaps inside a graph are far below a microsecond.
+    phases = (("decode_prologue", ds4q.PHASE_ROUTE), ("decode_gateup", ds4q.PHASE_GATEUP),
+              ("decode_down", ds4q.PHASE_DOWN))
+    k_us = {}
+    k_reps = max(1, min(reps, 40))
+    for name, ph in phases:
+        gk = capture(lambda ph=ph: [decode_phase(l, ph) for l in range(NL)])
+        for _ in range(2):
+            gk.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(k_reps):
+            gk.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        k_us[name] = ev0.elapsed_time(ev1) * 1e3 / (k_reps * NL)
+        del gk
+    g.replay()                      # leave every layer's outputs consistent
     torch.cuda.synchronize()
-    kt = ds4q.ds4q_timing_read()
-    ds4q.ds4q_timing_enable(False)
-    gu_ms = kt["decode_gateup"][0] / kt["decode_gateup"][1]
-    dn_ms = kt["decode_down"][0] / kt["decode_down"][1]
-    gu_bytes = K * 2 * F * Q2K_ROW_D + D * 4 + K * F * 4
+    gu_us, dn_us = k_us["decode_gateup"], k_us["decode_down"]
+    gu_bytes = GATEUP_BYTES
     dn_bytes = K * D * Q2K_ROW_F + K * F * 4 + D * 4
-    gu_gbps = gu_bytes / (gu_ms / 1e3) / 1e9
-    log(f"kernels: gateup {gu_ms * 1e3:.2f} us ({gu_gbps:.0f} GB/s), "
-        f"down {dn_ms * 1e3:.2f} us ({dn_bytes / (dn_ms / 1e3) / 1e9:.0f} GB/s)")
+    gu_gbps = gu_bytes / (gu_us / 1e6) / 1e9
+    log(f"kernels: prologue {k_us['decode_prologue']:.2f} us, gateup {gu_us:.2f} us "
+        f"({gu_gbps:.0f} GB/s), down {dn_us:.2f} us ({dn_bytes / (dn_us / 1e6) / 1e9:.0f} GB/s)")
+    traffic = counter_traffic("decode_gateup")
 
     result = {
         "metric": METRIC,
@@ -158,7 +230,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps_done,
-        "warmup": reps_w * NL,
+        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -172,9 +244,9 @@ def main():
         "hbm_gbps_step": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "decode_gateup", "achieved": round(gu_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": gu_bytes,
-                     "avg_launch_us": round(gu_ms * 1e3, 3)},
-        "kernels_us": {k: round(v[0] / v[1] * 1e3, 3) for k, v in kt.items()},
+                     "traffic": traffic, "bytes_per_launch": gu_bytes,
+                     "avg_launch_us": round(gu_us, 3)},
+        "kernels_us": {k: round(v, 3) for k, v in k_us.items()},
     }
 
     # ------------------------------------------------------------ prefill (secondary)

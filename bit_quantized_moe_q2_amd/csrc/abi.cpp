@@ -225,26 +225,38 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
   return DS4Q_OK;
 }
 
+// The decode launches in three phases (DS4Q_PHASE_*): routing and input
+// preparation, gate/up + SwiGLU, down + combine.  Each phase reads only what
+// the earlier ones left in the workspace.
 int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int32_t T, float *y,
-               const ds4q_route_out *route, void *ws, hipStream_t s, uint32_t flags) {
+               const ds4q_route_out *route, void *ws, hipStream_t s, uint32_t flags,
+               uint32_t phases = DS4Q_PHASE_ALL) {
   const MoeDims m = dims_of(L);
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
+  const bool p_route = phases & DS4Q_PHASE_ROUTE, p_gu = phases & DS4Q_PHASE_GATEUP,
+             p_down = phases & DS4Q_PHASE_DOWN;
   if (T == 1 && m.tg == DS4Q_TYPE_Q2_K && m.td == DS4Q_TYPE_Q2_K) {
-    TIMED_TRY("decode_prologue", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 0, s));
-    TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 1, s));
-    TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 2, s));
+    if (p_route)
+      TIMED_TRY("decode_prologue", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 0, s));
+    if (p_gu)
+      TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 1, s));
+    if (p_down)
+      TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 2, s));
     // the grouping pass (expert order) runs only when asked for
-    if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
-    return copy_route(route, w.rb, T, m.E, m.k, s);
+    if (p_route && wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+    return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
-  TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));
-  // For T == 1 the top-k kernel already wrote the active-expert lists (slot
-  // order); the grouping pass (expert order) runs only when asked for.
-  if (T > 1 || wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
-  TIMED_TRY("decode_gateup", launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
-  TIMED_TRY("decode_down", launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, s));
-  return copy_route(route, w.rb, T, m.E, m.k, s);
+  if (p_route) {
+    TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));
+    // For T == 1 the top-k kernel already wrote the active-expert lists (slot
+    // order); the grouping pass (expert order) runs only when asked for.
+    if (T > 1 || wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+  }
+  if (p_gu)
+    TIMED_TRY("decode_gateup", launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
+  if (p_down) TIMED_TRY("decode_down", launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, s));
+  return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
 }
 
 int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const float *logits,
@@ -364,6 +376,17 @@ DS4Q_API int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const floa
   if (rc || n_tok == 0) return rc;
   return run_decode(L, x, logits, n_tok, y, route, workspace, static_cast<hipStream_t>(stream),
                     L->flags);
+}
+
+DS4Q_API int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float *logits,
+                                    int32_t n_tok, float *y, const ds4q_route_out *route,
+                                    void *workspace, size_t workspace_bytes, uint32_t phases,
+                                    void *stream) {
+  if (phases == 0 || (phases & ~(uint32_t)DS4Q_PHASE_ALL)) return DS4Q_E_INVAL;
+  int rc = check_call(L, x, 4, logits, n_tok, 64, y, route, workspace, workspace_bytes, 0);
+  if (rc || n_tok == 0) return rc;
+  return run_decode(L, x, logits, n_tok, y, route, workspace, static_cast<hipStream_t>(stream),
+                    L->flags, phases);
 }
 
 DS4Q_API int ds4q_moe_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type,

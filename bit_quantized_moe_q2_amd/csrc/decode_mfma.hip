@@ -37,6 +37,7 @@ namespace ds4q {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float INV254 = 1.0f / 254.0f;
 constexpr float INV254SQ = 1.0f / (254.0f * 254.0f);
@@ -168,11 +169,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int NBW>
 struct QActStage {
   static constexpr int NF = (NBW * 48 + 63) / 64, NS = (NBW * 16 + 63) / 64;
-  uint4 f[NF];
+  u32x4 f[NF];
   float sm[NS];
   float sg;
   __device__ __forceinline__ void load(const QAct &q, int b0, int lane) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(q.frag + b0 * 192);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(q.frag + b0 * 192);
 #pragma unroll
     for (int i = 0; i < NF; ++i)
       if (lane + 64 * i < NBW * 48) f[i] = src[lane + 64 * i];
@@ -183,7 +184,7 @@ struct QActStage {
   }
   __device__ __forceinline__ void store(int lane, uint32_t *__restrict__ frag, float *__restrict__ sum,
                                         float *__restrict__ sig) const {
-    uint4 *dst = reinterpret_cast<uint4 *>(frag);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(frag);
 #pragma unroll
     for (int i = 0; i < NF; ++i)
       if (lane + 64 * i < NBW * 48) dst[lane + 64 * i] = f[i];

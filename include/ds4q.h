@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DS4Q_ABI_VERSION 1
+#define DS4Q_ABI_VERSION 2
 
 /* Tensor types.  Numeric values follow the public GGML/GGUF type ids. */
 typedef enum {
@@ -142,6 +142,25 @@ int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits
                     float *y, const ds4q_route_out *route, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* Phases of the decode launches, for ds4q_moe_decode_phases. */
+#define DS4Q_PHASE_ROUTE 0x1u  /* routing (and, for one Q2_K token, the quantised input) */
+#define DS4Q_PHASE_GATEUP 0x2u /* gate/up projections + SwiGLU into the workspace */
+#define DS4Q_PHASE_DOWN 0x4u   /* down projection + weighted combine into y */
+#define DS4Q_PHASE_ALL 0x7u
+
+/* ds4q_moe_decode restricted to the launches of the phases set in `phases`
+ * (a non-empty subset of DS4Q_PHASE_ALL, else DS4Q_E_INVAL), for timing one
+ * kernel family at a time.  A phase reads only what the earlier phases left
+ * in the workspace, so a sequence of calls with the same arguments and
+ * workspace that covers ROUTE, GATEUP and DOWN in that order computes
+ * exactly what one ds4q_moe_decode call computes.  Repeating GATEUP or DOWN
+ * alone is idempotent without DS4Q_F_ACCUMULATE; with it each DOWN adds
+ * again.  Same argument rules and errors as ds4q_moe_decode; route is
+ * written by the ROUTE phase only. */
+int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float *logits,
+                           int32_t n_tok, float *y, const ds4q_route_out *route, void *workspace,
+                           size_t workspace_bytes, uint32_t phases, void *stream);
+
 /* Prefill-path MoE layer: same mathematics as ds4q_moe_decode for a chunk
  * of n_tok tokens (0..65536), computed as grouped GEMMs on bf16 matrix cores
  * with fp32 accumulation: the expert input rows are bf16 (x_type BF16, or
@@ -175,9 +194,9 @@ int ds4q_moe_stack(const ds4q_moe_layer *layers, int32_t n_layers, int32_t mode,
 int ds4q_timing_enable(int on);
 /* Waits for the recorded events, then returns one entry per launch site:
  * names (max_names x name_len chars, NUL-terminated: "topk", "group",
- * "decode_gateup", "decode_down", "prep_bf16", "prefill_gateup",
- * "prefill_down", "combine"), summed milliseconds and launch counts (host
- * arrays).  Clears the record. */
+ * "decode_prologue", "decode_gateup", "decode_down", "prep_bf16",
+ * "prefill_gateup", "prefill_down", "combine"), summed milliseconds and
+ * launch counts (host arrays).  Clears the record. */
 int ds4q_timing_read(char *names, int name_len, double *total_ms, int64_t *count, int max_names,
                      int *n_names);
 

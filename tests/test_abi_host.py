@@ -1,0 +1,150 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/ds4q.h declares, and rejects bad arguments on the host with the
+documented status codes.  Every call here is chosen so that validation fails
+before anything is enqueued (the fake device addresses are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_moe_q2_amd as ds4q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds4q.h")
+
+OK, E_INVAL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ALIAS = 0, -1, -2, -3, -4, -5, -6
+BASE = 1 << 40          # fake, 4 KiB-aligned device addresses, never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds4q_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return ds4q.load()
+    except ImportError as e:      # the build step must have run
+        pytest.fail(str(e))
+
+
+def _layer(**kw):
+    a = dict(n_embd=4096, n_ff=2048, n_expert=256, n_expert_used=6, type_gate=ds4q.TYPE_Q2_K,
+             type_up=ds4q.TYPE_Q2_K, type_down=ds4q.TYPE_Q2_K, gate=BASE, up=BASE + (1 << 32),
+             down=BASE + (2 << 32), flags=0, norm_eps=1e-6)
+    a.update(kw)
+    return ds4q.MoeLayer(**a)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert "ds4q_moe_decode" in names and "ds4q_dequant" in names and len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    m = re.search(r"#define DS4Q_ABI_VERSION (\d+)", open(HEADER).read())
+    assert ds4q.ds4q_abi_version() == int(m.group(1))
+    for code in (OK, E_INVAL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ALIAS, -7):
+        assert ds4q.ds4q_strerror(code) != "unknown status"
+    assert ds4q.ds4q_strerror(-99) == "unknown status"
+
+
+def test_dequant_validation(lib):
+    f = lib.ds4q_dequant
+    src, dst = BASE, BASE + (1 << 32)
+    assert f(ds4q.TYPE_IQ2_XXS, src, 4, 256, ds4q.TYPE_F32, dst, None) == E_UNSUPPORTED
+    assert f(ds4q.TYPE_Q2_K, src, 4, 256, ds4q.TYPE_F16, dst, None) == E_UNSUPPORTED
+    assert f(ds4q.TYPE_Q2_K, src, 4, 200, ds4q.TYPE_F32, dst, None) == E_SHAPE
+    assert f(ds4q.TYPE_Q4_1, src, 4, 48, ds4q.TYPE_F32, dst, None) == E_SHAPE
+    assert f(ds4q.TYPE_Q2_K, src, -1, 256, ds4q.TYPE_F32, dst, None) == E_SHAPE
+    assert f(ds4q.TYPE_Q2_K, src, 0, 256, ds4q.TYPE_F32, dst, None) == OK       # no-op
+    assert f(ds4q.TYPE_Q2_K, None, 4, 256, ds4q.TYPE_F32, dst, None) == E_INVAL
+    assert f(ds4q.TYPE_Q2_K, src, 4, 256, ds4q.TYPE_F32, dst + 8, None) == E_ALIGN
+    assert f(ds4q.TYPE_Q2_K, src, 4, 256, ds4q.TYPE_BF16, src + 64, None) == E_ALIAS
+
+
+def test_matvec_and_route_validation(lib):
+    assert lib.ds4q_matvec(ds4q.TYPE_Q2_K, BASE, 8, 300, BASE + (1 << 32), 1,
+                           BASE + (2 << 32), None) == E_SHAPE
+    assert lib.ds4q_route_workspace_size(10, 256, 9) == 0
+    assert lib.ds4q_route_workspace_size(10, 256, 6) > 0
+    out = ds4q.RouteOut(BASE, BASE + 4096, 0, 0, 0)
+    assert lib.ds4q_route(BASE + (1 << 32), 10, 256, 9, ctypes.byref(out), BASE + (2 << 32),
+                          1 << 20, None) == E_INVAL
+    assert lib.ds4q_route(BASE + (1 << 32), 65537, 256, 6, ctypes.byref(out), BASE + (2 << 32),
+                          1 << 20, None) == E_SHAPE
+
+
+def test_layer_descriptor_validation(lib):
+    ws = lambda L: lib.ds4q_moe_workspace_size(ctypes.byref(L), 1, 0)
+    assert ws(_layer()) > 0
+    assert ws(_layer(type_gate=ds4q.TYPE_IQ2_XXS, type_up=ds4q.TYPE_IQ2_XXS)) == 0
+    assert lib.ds4q_moe_workspace_size(None, 1, 0) == 0
+    assert lib.ds4q_moe_workspace_size(ctypes.byref(_layer()), 1, 2) == 0
+    x, lg, y, w = BASE + (8 << 32), BASE + (9 << 32), BASE + (10 << 32), BASE + (11 << 32)
+    dec = lambda L, T=1: lib.ds4q_moe_decode(ctypes.byref(L), x, lg, T, y, None, w, 1 << 30, None)
+    assert dec(_layer(type_gate=ds4q.TYPE_IQ2_XXS, type_up=ds4q.TYPE_IQ2_XXS)) == E_UNSUPPORTED
+    assert dec(_layer(type_up=ds4q.TYPE_Q4_1)) == E_UNSUPPORTED        # gate and up share a type
+    assert dec(_layer(n_embd=3072)) == E_SHAPE
+    assert dec(_layer(n_ff=128)) == E_SHAPE
+    assert dec(_layer(n_expert_used=9)) == E_INVAL
+    assert dec(_layer(n_expert=2000)) == E_INVAL
+    assert dec(_layer(gate=0)) == E_INVAL
+    assert dec(_layer(down=BASE + 8)) == E_ALIGN
+    assert dec(_layer(flags=0x8)) == E_INVAL
+    assert dec(_layer(norm_eps=float("nan"))) == E_INVAL
+
+
+def test_decode_call_validation(lib):
+    L = _layer()
+    need = lib.ds4q_moe_workspace_size(ctypes.byref(L), 4, 0)
+    assert need > lib.ds4q_moe_workspace_size(ctypes.byref(L), 1, 0) > 0
+    x, lg, y, w = BASE + (8 << 32), BASE + (9 << 32), BASE + (10 << 32), BASE + (11 << 32)
+
+    def dec(x=x, lg=lg, T=4, y=y, w=w, wb=need):
+        return lib.ds4q_moe_decode(ctypes.byref(L), x, lg, T, y, None, w, wb, None)
+
+    assert dec(T=65) == E_SHAPE
+    assert dec(T=-1) == E_SHAPE
+    assert dec(T=0) == OK                                   # nothing to do
+    assert dec(x=None) == E_INVAL
+    assert dec(w=None) == E_WORKSPACE
+    assert dec(wb=need - 1) == E_WORKSPACE
+    assert dec(x=x + 4) == E_ALIGN
+    assert dec(w=w + 16) == E_ALIGN
+    assert dec(y=x + 4096 * 4) == E_ALIAS                   # partial overlap of x and y
+    assert dec(w=y) == E_ALIAS                              # workspace over the output
+    assert dec(lg=y + 64) == E_ALIAS
+    ph = lambda p: lib.ds4q_moe_decode_phases(ctypes.byref(L), x, lg, 4, y, None, w, need, p, None)
+    assert ph(0) == E_INVAL and ph(8) == E_INVAL and ph(0x17) == E_INVAL
+    assert lib.ds4q_moe_decode_phases(ctypes.byref(L), x, lg, 65, y, None, w, need,
+                                      ds4q.PHASE_GATEUP, None) == E_SHAPE
+
+
+def test_prefill_and_stack_validation(lib):
+    L = _layer()
+    need = lib.ds4q_moe_workspace_size(ctypes.byref(L), 4096, 1)
+    x, lg, y, w = BASE + (8 << 32), BASE + (9 << 32), BASE + (10 << 32), BASE + (11 << 32)
+    pre = lambda xt, L=L, T=4096: lib.ds4q_moe_prefill(ctypes.byref(L), x, xt, lg, T, y, None, w,
+                                                       need, None)
+    assert pre(ds4q.TYPE_F16) == E_UNSUPPORTED
+    assert pre(ds4q.TYPE_BF16, _layer(flags=ds4q.F_RMSNORM_INPUT)) == E_INVAL
+    assert pre(ds4q.TYPE_BF16, T=65537) == E_SHAPE
+    assert lib.ds4q_moe_prefill(ctypes.byref(L), x, ds4q.TYPE_BF16, lg, 4096, y, None, w,
+                                need - 256, None) == E_WORKSPACE
+    arr = (ds4q.MoeLayer * 2)(_layer(), _layer(n_ff=1024))
+    wsd = lib.ds4q_moe_workspace_size(ctypes.byref(L), 1, 0)
+    assert lib.ds4q_moe_stack(arr, 2, 0, x, lg, 1, w, wsd, None) == E_SHAPE
+    assert lib.ds4q_moe_stack(arr, 2, 2, x, lg, 1, w, wsd, None) == E_INVAL
+    assert lib.ds4q_moe_stack(arr, 0, 0, x, lg, 1, w, wsd, None) == OK
+    same = (ds4q.MoeLayer * 2)(_layer(), _layer())
+    assert lib.ds4q_moe_stack(same, 2, 0, x, x + 64, 1, w, wsd, None) == E_ALIAS
+
+
+def test_timing_read_empty(lib):
+    assert ds4q.ds4q_timing_read() == {}

@@ -254,3 +254,30 @@ def test_decode_full_layer_64_tokens(gpu, qt):
     sample = np.array([0, 9, 17, 30, 41, 52, 60, 63])
     ref = lay.oracle_moe(x[sample], lg[sample], n_threads=16)
     assert normwise_err(y[sample], ref) <= TOL_FP32
+
+
+@pytest.mark.parametrize("qt,T", [(10, 1), (10, 3), (3, 1)])
+def test_decode_phases_compose(gpu, qt, T):
+    """ROUTE, GATEUP and DOWN run as separate calls on one workspace give the
+    bits of a single ds4q_moe_decode call; repeating GATEUP + DOWN alone is
+    idempotent (the form the per-kernel timing uses)."""
+    ds4q = gpu
+    _log(f"decode phases qt={qt} T={T}")
+    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, qt, seed=600 + T)
+    x = torch.from_numpy(synth.x_f32(synth.stream_key(23, T), T, 4096)).to(DEV)
+    lg = torch.from_numpy(synth.logits_normal(synth.stream_key(24, T), T, 256)).to(DEV)
+    ws = torch.empty(ds4q.ds4q_moe_workspace_size(lay.L, T, 0), dtype=torch.uint8, device=DEV)
+    y_ref = torch.empty(T, 4096, dtype=torch.float32, device=DEV)
+    ds4q.ds4q_moe_decode(lay.L, x, lg, T, y_ref, None, ws)
+    ws.zero_()
+    y = torch.full((T, 4096), float("nan"), dtype=torch.float32, device=DEV)
+    for ph in (ds4q.PHASE_ROUTE, ds4q.PHASE_GATEUP, ds4q.PHASE_DOWN):
+        ds4q.ds4q_moe_decode_phases(lay.L, x, lg, T, y, None, ws, ph)
+    torch.cuda.synchronize()
+    a, b = y_ref.cpu().numpy(), y.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for _ in range(2):
+        ds4q.ds4q_moe_decode_phases(lay.L, x, lg, T, y, None, ws, ds4q.PHASE_GATEUP)
+        ds4q.ds4q_moe_decode_phases(lay.L, x, lg, T, y, None, ws, ds4q.PHASE_DOWN)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.view(np.uint32), y.cpu().numpy().view(np.uint32))
