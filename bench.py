@@ -198,8 +198,9 @@ def main():
     # Per-kernel durations: a graph of one kernel launch per layer (the same
     # launches as in the step graph, on the same stream), replayed between
     # two events; launch gaps inside a graph are far below a microsecond.
-    phases = (("decode_prologue", ds4q.PHASE_ROUTE), ("decode_gateup", ds4q.PHASE_GATEUP),
-              ("decode_down", ds4q.PHASE_DOWN))
+    # (one token on Q2_K: the gate/up launch also routes; the routing phase
+    # launches nothing of its own)
+    phases = (("decode_gateup", ds4q.PHASE_GATEUP), ("decode_down", ds4q.PHASE_DOWN))
     k_us = {}
     k_reps = max(1, min(reps, 40))
     for name, ph in phases:
@@ -220,7 +221,7 @@ def main():
     gu_bytes = GATEUP_BYTES
     dn_bytes = K * D * Q2K_ROW_F + K * F * 4 + D * 4
     gu_gbps = gu_bytes / (gu_us / 1e6) / 1e9
-    log(f"kernels: prologue {k_us['decode_prologue']:.2f} us, gateup {gu_us:.2f} us "
+    log(f"kernels: gateup {gu_us:.2f} us "
         f"({gu_gbps:.0f} GB/s), down {dn_us:.2f} us ({dn_bytes / (dn_us / 1e6) / 1e9:.0f} GB/s)")
     traffic = counter_traffic("decode_gateup")
 

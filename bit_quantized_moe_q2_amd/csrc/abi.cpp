@@ -44,7 +44,6 @@ int max_tiles(int T, int E, int k) {
 struct Workspace {
   RouteBufs rb{};
   float *h = nullptr;      // decode: [T*k][F] f32
-  void *qbuf = nullptr;    // decode T == 1: quantised activations
   uint16_t *hb = nullptr;  // prefill: [T*k][F] bf16 (sorted order)
   float *o = nullptr;      // [T*k][D] f32
   uint16_t *xb = nullptr;  // prefill: [T][D] bf16
@@ -73,7 +72,6 @@ struct Workspace {
       // routing only
     } else if (mode == 0) {
       h = (float *)take(P * F * 4);
-      qbuf = take(qact_bytes(1, D));
       if (T > 1) o = (float *)take(P * D * 4);
     } else {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
@@ -237,15 +235,17 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
   const bool p_route = phases & DS4Q_PHASE_ROUTE, p_gu = phases & DS4Q_PHASE_GATEUP,
              p_down = phases & DS4Q_PHASE_DOWN;
   if (T == 1 && m.tg == DS4Q_TYPE_Q2_K && m.td == DS4Q_TYPE_Q2_K) {
-    if (p_route)
-      TIMED_TRY("decode_prologue", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 0, s));
-    if (p_gu)
-      TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 1, s));
+    // One token on int8 matrix cores: the gate/up launch routes the token
+    // itself, so the routing phase has nothing of its own to launch and the
+    // routing outputs follow the gate/up launch.
+    if (p_gu) {
+      TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 1, s));
+      // the grouping pass (expert order) runs only when asked for
+      if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+    }
     if (p_down)
-      TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, w.qbuf, y, acc, 2, s));
-    // the grouping pass (expert order) runs only when asked for
-    if (p_route && wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
-    return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
+      TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 2, s));
+    return p_gu ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
   if (p_route) {
     TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));

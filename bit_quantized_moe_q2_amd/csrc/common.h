@@ -125,32 +125,46 @@ __device__ __forceinline__ float float_from_ordered(uint32_t o) {
 // Top-k for E <= 256 logits (four per lane: expert lane + 64i): each round
 // takes the wave max of the order-preserving keys, then the smallest expert
 // index holding it (ties -> lower index).  Lane j < k returns slot j's expert
-// and softmax weight.
+// and softmax weight.  load() only issues the reads, so that a caller can
+// queue other loads behind them before select() waits.
+struct TopK256 {
+  float v[4];
+  __device__ __forceinline__ void load(const float *__restrict__ lg, int E, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? lg[e] : 0.f;
+    }
+  }
+  __device__ __forceinline__ void select(int E, int k, int lane, int *id, float *w) const {
+    uint32_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < E ? ordered_bits(v[i]) : 0u;
+    uint32_t my_id = 0, my_key = 0;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t gm = wave_umax(max(max(key[0], key[1]), max(key[2], key[3])));
+      uint32_t cand = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cand = key[i] == gm ? min(cand, (uint32_t)(lane + 64 * i)) : cand;
+      const uint32_t ew = wave_umin(cand);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(lane + 64 * i) == ew ? 0u : key[i];
+      if (lane == j) { my_id = ew; my_key = gm; }
+    }
+    const float top = float_from_ordered(readlane(my_key, 0));
+    const float ex = lane < k ? expf(float_from_ordered(my_key) - top) : 0.f;
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) den += __builtin_bit_cast(float, readlane(__builtin_bit_cast(uint32_t, ex), j));
+    *id = (int)my_id;
+    *w = ex / den;
+  }
+};
+
 __device__ __forceinline__ void wave_topk256(const float *__restrict__ lg, int E, int k, int lane,
                                              int *id, float *w) {
-  uint32_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? ordered_bits(lg[e]) : 0u;
-  }
-  uint32_t my_id = 0, my_key = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t gm = wave_umax(max(max(key[0], key[1]), max(key[2], key[3])));
-    uint32_t cand = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cand = key[i] == gm ? min(cand, (uint32_t)(lane + 64 * i)) : cand;
-    const uint32_t ew = wave_umin(cand);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(lane + 64 * i) == ew ? 0u : key[i];
-    if (lane == j) { my_id = ew; my_key = gm; }
-  }
-  const float top = float_from_ordered(readlane(my_key, 0));
-  const float ex = lane < k ? expf(float_from_ordered(my_key) - top) : 0.f;
-  float den = 0.f;
-  for (int j = 0; j < k; ++j) den += __builtin_bit_cast(float, readlane(__builtin_bit_cast(uint32_t, ex), j));
-  *id = (int)my_id;
-  *w = ex / den;
+  TopK256 t;
+  t.load(lg, E, lane);
+  t.select(E, k, lane, id, w);
 }
 
 // Top-k of E logits by (logit desc, index asc) for one token, computed by a

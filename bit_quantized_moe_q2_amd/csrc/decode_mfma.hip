@@ -22,14 +22,18 @@
 // byte k*4 + i of the 16-byte operand is value 128(g>>1) + 32k + 16(g&1) + 4j
 // + i, whose code sits in byte i of dword j at bit pair k and whose sub-block
 // 8(g>>1) + 2k + (g&1) is the same for all four i.  With a single token the
-// A rows are all the same vector, so every C row holds the result.
+// three limbs take A rows 0..2 (rows 3..15 are zero), so one MFMA per K tile
+// gives all three limb products of 16 weight rows: C[limb][row], held by
+// lanes 0..15.
 //
-// A step is three kernels: a one-workgroup prologue (routing + quantised
-// activations into the workspace), gate/up + SwiGLU, and down + weighted
-// combine (each of its waves quantises its slot's SwiGLU row into LDS).  The
-// gate/up waves do no routing or activation arithmetic of their own: each
-// reads its expert id, issues its weight loads, copies its quantised
-// activation fragments into LDS and runs the MFMA loop.
+// A step is two kernels.  Gate/up + SwiGLU: every wave routes the token
+// itself (top-k of the logits, a few hundred VALU instructions, cheaper than
+// a launch and a round trip through memory), issues its expert's weight loads,
+// quantises its own quarter of x into LDS meanwhile and runs the MFMA loop;
+// workgroup (0, 0) also stores the routing for the second kernel.  Down +
+// weighted combine: each wave quantises its share of its slot's SwiGLU row
+// into LDS while its weight loads are in flight.  The RMS norm of the input
+// is a per-token factor, applied to the gate and up sums in the epilogue.
 #include "common.h"
 #include "launch.h"
 
@@ -83,15 +87,6 @@ __device__ __forceinline__ uint32_t pack_i8(float a, float b, float c, float d) 
          (((uint32_t)(int)c & 0xFFu) << 16) | (((uint32_t)(int)d & 0xFFu) << 24);
 }
 
-// Quantised activations of one vector of NBV blocks (global workspace):
-// frag [NBV][3 limbs][4 j][4 g][4 k] dwords, sum [NBV][16] (sub-block sums),
-// sig [NBV] (block scales).
-struct QAct {
-  uint32_t *frag;
-  float *sum;
-  float *sig;
-};
-
 // One thread quantises the 16 activations of one sub-block s (values
 // 16s..16s+15 of a block) with the block scale inv = 127 / max|x| and writes
 // its 3 limbs x 4 dwords into the block's fragments frag[limb][j][g][k].
@@ -122,99 +117,36 @@ __device__ __forceinline__ float max16(float m) {
   return m;
 }
 
-// Thread `t` (of at least 16*NBV, groups of 16 consecutive threads inside one
-// wave per block) quantises sub-block t&15 of block t>>4 of `v` (global); the
-// block's sigma and sub-block sums are multiplied by `scale` (a positive
-// per-vector factor: limbs do not change with it).  `ld` selects coherent
-// loads for data written by other workgroups of the same kernel.
-template <bool COHERENT>
-__device__ __forceinline__ void quantize_one(const float *__restrict__ v, int t, float scale,
-                                             QAct q) {
-  const int b = t >> 4, s = t & 15;
-  float x[16];
-  const float *src = v + b * 256 + 16 * s;
-  if constexpr (COHERENT) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 f = reinterpret_cast<const float4 *>(src)[i];
-      x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
-    }
-  }
-  float m = 0.f, sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    m = fmaxf(m, fabsf(x[i]));
-    sum += x[i];
-  }
-  m = max16(m);
-  const float inv = m > 0.f ? 127.0f / m : 0.0f;
-  quantize_subblock(x, inv, s, q.frag + b * 192);
-  q.sum[b * 16 + s] = sum * scale;
-  if (s == 0) q.sig[b] = (m / 127.0f) * scale;
-}
-
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Quantised activations of NBW blocks (from block b0) held in registers on
-// their way from the workspace into a wave's LDS area.  Loaded before the
-// weight loads are issued and stored after, so that waiting for them does not
-// wait for the (in-order) weight loads.
-template <int NBW>
-struct QActStage {
-  static constexpr int NF = (NBW * 48 + 63) / 64, NS = (NBW * 16 + 63) / 64;
-  u32x4 f[NF];
-  float sm[NS];
-  float sg;
-  __device__ __forceinline__ void load(const QAct &q, int b0, int lane) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(q.frag + b0 * 192);
-#pragma unroll
-    for (int i = 0; i < NF; ++i)
-      if (lane + 64 * i < NBW * 48) f[i] = src[lane + 64 * i];
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      if (lane + 64 * i < NBW * 16) sm[i] = q.sum[b0 * 16 + lane + 64 * i];
-    if (lane < NBW) sg = q.sig[b0 + lane];
-  }
-  __device__ __forceinline__ void store(int lane, uint32_t *__restrict__ frag, float *__restrict__ sum,
-                                        float *__restrict__ sig) const {
-    u32x4 *dst = reinterpret_cast<u32x4 *>(frag);
-#pragma unroll
-    for (int i = 0; i < NF; ++i)
-      if (lane + 64 * i < NBW * 48) dst[lane + 64 * i] = f[i];
-#pragma unroll
-    for (int i = 0; i < NS; ++i)
-      if (lane + 64 * i < NBW * 16) sum[lane + 64 * i] = sm[i];
-    if (lane < NBW) sig[lane] = sg;
-    wave_lds_sync();
-  }
-};
-
-// The 12 A fragments (3 limbs x 4 K tiles) of one block for lane group g.
+// A operand of one block: row r < 3 of A is limb r of the activations, rows
+// 3..15 are zero, so one MFMA yields the three limb dot products of 16 weight
+// rows at once (C[limb][row]).  Lane (n, g) holds row n's 16 int8 of K group
+// g for each of the 4 K tiles j.
 struct AFrag {
-  i32x4 a[3][4];
-  __device__ __forceinline__ void load(const uint32_t *__restrict__ frag_blk, int g) {
+  i32x4 a[4];
+  __device__ __forceinline__ void load(const uint32_t *__restrict__ frag_blk, int n, int g) {
 #pragma unroll
-    for (int l = 0; l < 3; ++l)
+    for (int j = 0; j < 4; ++j) a[j] = (i32x4){0, 0, 0, 0};
+    if (n < 3) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a[l][j] = *reinterpret_cast<const i32x4 *>(frag_blk + l * 64 + (j * 4 + g) * 4);
+        a[j] = *reinterpret_cast<const i32x4 *>(frag_blk + n * 64 + (j * 4 + g) * 4);
+    }
   }
 };
 
-// Block epilogue: main (replicated over the four lane groups) and the lane
-// group's quarter of the min term.
-__device__ __forceinline__ void block_post(const Q2KRaw &r, const uint32_t sb[4], const i32x4 c[3],
+// Block epilogue: the main term (C rows 0..2 = limbs, held by lane group 0;
+// zero in the other groups) and the lane group's quarter of the min term.
+__device__ __forceinline__ void block_post(const Q2KRaw &r, const uint32_t sb[4], const i32x4 c,
                                            const float *__restrict__ xsum_blk, float sigma, int g,
                                            float &main_acc, float &min_acc) {
   const int p = g & 1, h = g >> 1;
-  const float f = fmaf((float)c[2].x, INV254SQ, fmaf((float)c[1].x, INV254, (float)c[0].x));
+  const float f = fmaf((float)c.z, INV254SQ, fmaf((float)c.y, INV254, (float)c.x));
   main_acc = fmaf(f16lo(r.dd) * sigma, f, main_acc);
   float mn = (float)(sb[0] >> 4) * xsum_blk[8 * h + p];
   mn = fmaf((float)(sb[1] >> 4), xsum_blk[8 * h + 2 + p], mn);
@@ -223,14 +155,14 @@ __device__ __forceinline__ void block_post(const Q2KRaw &r, const uint32_t sb[4]
   min_acc = fmaf(f16hi(r.dd), mn, min_acc);
 }
 
-// One block of NM weight rows (gate and up share the activations): all
-// twelve A fragments are read from LDS once, then 12*NM MFMAs.
+// One block of NM weight rows (gate and up share the activations): the four
+// A fragments are read from LDS once, then 4*NM MFMAs.
 template <int NM>
 __device__ __forceinline__ void block_dot(const Q2KRaw *const r[NM], const uint32_t *__restrict__ frag_blk,
-                                          const float *__restrict__ xsum_blk, float sigma, int g,
+                                          const float *__restrict__ xsum_blk, float sigma, int n, int g,
                                           float *main_acc, float *min_acc) {
   AFrag af;
-  af.load(frag_blk, g);
+  af.load(frag_blk, n, g);
   uint32_t sb[NM][4], tab[NM][4];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -238,128 +170,17 @@ __device__ __forceinline__ void block_dot(const Q2KRaw *const r[NM], const uint3
 #pragma unroll
     for (int q = 0; q < 4; ++q) tab[m][q] = qsc_table(sb[m][q]);
   }
-  i32x4 c[NM][3];
+  i32x4 c[NM];
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int l = 0; l < 3; ++l) c[m][l] = (i32x4){0, 0, 0, 0};
+  for (int m = 0; m < NM; ++m) c[m] = (i32x4){0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const i32x4 b = b_frag(*r[m], j, tab[m]);
-#pragma unroll
-      for (int l = 0; l < 3; ++l) c[m][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af.a[l][j], b, c[m][l], 0, 0, 0);
-    }
+    for (int m = 0; m < NM; ++m)
+      c[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af.a[j], b_frag(*r[m], j, tab[m]), c[m], 0, 0, 0);
   }
 #pragma unroll
   for (int m = 0; m < NM; ++m) block_post(*r[m], sb[m], c[m], xsum_blk, sigma, g, main_acc[m], min_acc[m]);
-}
-
-template <int MAXE>
-__device__ __forceinline__ void route_token(const float *__restrict__ lg, int E, int k, int lane,
-                                            int *id, float *w) {
-  if constexpr (MAXE == 256) wave_topk256(lg, E, k, lane, id, w);
-  else wave_topk<MAXE>(lg, E, k, lane, id, w);
-}
-
-// Prologue, one workgroup of 256 threads: routing of the token (wave 0:
-// ids, weights) and the
-// quantised activations of x (optionally RMS-normalised: only the block
-// scales and sub-block sums carry the factor).
-template <int D, int MAXE>
-__global__ __launch_bounds__(256) void prologue_t1_kernel(const float *__restrict__ x,
-                                                          const float *__restrict__ logits, int E,
-                                                          int k, int rmsnorm, float eps, QAct xq,
-                                                          int32_t *__restrict__ ids,
-                                                          float *__restrict__ wts) {
-  constexpr int NB = D / 256;
-  __shared__ float red[4];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (w == 0) {
-    int id;
-    float wt;
-    route_token<MAXE>(logits, E, k, lane, &id, &wt);
-    if (lane < k) {
-      ids[lane] = id;
-      wts[lane] = wt;
-    }
-  }
-  float scale = 1.0f;
-  if (rmsnorm) {
-    float ss = 0.f;
-    for (int i = 4 * tid; i < D; i += 1024) {
-      const float4 t = *reinterpret_cast<const float4 *>(x + i);
-      ss = fmaf(t.x, t.x, ss); ss = fmaf(t.y, t.y, ss);
-      ss = fmaf(t.z, t.z, ss); ss = fmaf(t.w, t.w, ss);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    if (lane == 0) red[w] = ss;
-    __syncthreads();
-    scale = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)D + eps);
-  }
-  if (tid < NB * 16) quantize_one<false>(x, tid, scale, xq);
-}
-
-// Gate/up + SwiGLU for one token.  Grid (F/16, k): 16 rows of one routed
-// expert per workgroup; its four waves split each row's NB blocks into
-// quarters and meet in LDS.
-template <int D>
-__global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
-    const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up, int F, QAct xq,
-    const int32_t *__restrict__ ids, float *__restrict__ h) {
-  constexpr int NB = D / 256;
-  constexpr int BPW = NB >= 4 ? NB / 4 : 1;
-  __shared__ __attribute__((aligned(16))) uint32_t frag[4][BPW][192];
-  __shared__ float xsum[4][BPW][16];
-  __shared__ float sig[4][BPW];
-  __shared__ float part[4][2][16];
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int slot = blockIdx.y;
-  const int row = blockIdx.x * 16 + n;
-  const int b0 = w * BPW;
-  const bool has = b0 < NB;
-  const int64_t rb = (int64_t)NB * BB_Q2K;
-  Q2KRaw rg[BPW], ru[BPW];
-  float main_g = 0.f, main_u = 0.f, min_g = 0.f, min_u = 0.f;
-  if (has) {
-    QActStage<BPW> st;
-    st.load(xq, b0, lane);
-    const int e = ids[slot];
-    const int64_t off = ((int64_t)e * F + row) * rb;
-#pragma unroll
-    for (int bl = 0; bl < BPW; ++bl) {
-      rg[bl].load(gate + off + (b0 + bl) * BB_Q2K, g);
-      ru[bl].load(up + off + (b0 + bl) * BB_Q2K, g);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    st.store(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
-    float mains[2] = {0.f, 0.f}, mins[2] = {0.f, 0.f};
-#pragma unroll
-    for (int bl = 0; bl < BPW; ++bl) {
-      const Q2KRaw *rr[2] = {&rg[bl], &ru[bl]};
-      block_dot<2>(rr, frag[w][bl], xsum[w][bl], sig[w][bl], g, mains, mins);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    main_g = mains[0]; main_u = mains[1];
-    min_g = mins[0] + __shfl_xor(mins[0], 16, 64);
-    min_g += __shfl_xor(min_g, 32, 64);
-    min_u = mins[1] + __shfl_xor(mins[1], 16, 64);
-    min_u += __shfl_xor(min_u, 32, 64);
-  }
-  if (g == 0) {
-    part[w][0][n] = main_g - min_g;
-    part[w][1][n] = main_u - min_u;
-  }
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    const float gs = (part[0][0][n] + part[1][0][n]) + (part[2][0][n] + part[3][0][n]);
-    const float us = (part[0][1][n] + part[1][1][n]) + (part[2][1][n] + part[3][1][n]);
-    h[(int64_t)slot * F + row] = silu(gs) * us;
-  }
 }
 
 // One lane's share of quantising NB blocks of a vector (global) into a wave's
@@ -382,6 +203,17 @@ struct QuantStage {
         }
       }
     }
+  }
+  // Sum of squares of the lane's values (0 for lanes without a sub-block).
+  __device__ __forceinline__ float sumsq(int lane) const {
+    float ss = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+      if (lane + 64 * it < NB * 16) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss = fmaf(x[it][i], x[it][i], ss);
+      }
+    return ss;
   }
   __device__ __forceinline__ void quantise(int lane, uint32_t *__restrict__ frag, float *__restrict__ sum,
                                            float *__restrict__ sig) const {
@@ -407,108 +239,188 @@ struct QuantStage {
   }
 };
 
-// Down projection + weighted combine for one token.  Grid D/16, one wave per
-// routing slot (blockDim = 64k): each wave quantises its slot's SwiGLU row
-// into LDS, streams its expert's 16 down rows, and the slots meet in LDS:
+// Routing of the one token by a whole wave: lane j < k gets slot j's expert
+// and weight.  The logit loads are issued by load(); select() waits for them.
+template <int MAXE>
+struct TokenRoute {
+  TopK256 t;
+  const float *lg;
+  __device__ __forceinline__ void load(const float *__restrict__ logits, int E, int lane) {
+    lg = logits;
+    if constexpr (MAXE == 256) t.load(logits, E, lane);
+  }
+  __device__ __forceinline__ void select(int E, int k, int lane, int *id, float *w) const {
+    if constexpr (MAXE == 256) t.select(E, k, lane, id, w);
+    else wave_topk<MAXE>(lg, E, k, lane, id, w);
+  }
+};
+
+// Gate/up + SwiGLU for one token.  Grid (F/16, k): 16 rows of one routed
+// expert per workgroup; its four waves split each row's NB blocks into
+// quarters and meet in LDS.  Every wave routes the token ("ds4.c 해독하기 1/8",
+// DS4_SHAPE_FLASH passage: 6 of 256 routed experts) and quantises its own
+// quarter of x; workgroup (0, 0) stores the routing for the down kernel.
+// With rmsnorm, the sums are multiplied by 1/sqrt(mean(x^2) + eps): the
+// quantised limbs do not depend on that factor.
+template <int D, int MAXE>
+__global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
+    const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up, int F, int E, int k,
+    const float *__restrict__ x, const float *__restrict__ logits, int rmsnorm, float eps,
+    int32_t *__restrict__ ids_out, float *__restrict__ w_out, float *__restrict__ h) {
+  constexpr int NB = D / 256;
+  constexpr int BPW = NB >= 4 ? NB / 4 : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t frag[4][BPW][192];
+  __shared__ float xsum[4][BPW][16];
+  __shared__ float sig[4][BPW];
+  __shared__ float part[4][2][16];
+  __shared__ float ssq[4];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int slot = blockIdx.y;
+  const int row = blockIdx.x * 16 + n;
+  const int b0 = w * BPW;
+  const bool has = b0 < NB;
+  TokenRoute<MAXE> rt;
+  rt.load(logits, E, lane);
+  QuantStage<BPW> xs;
+  if (has) xs.load(x + b0 * 256, lane);
+  int my_id;
+  float my_w;
+  rt.select(E, k, lane, &my_id, &my_w);
+  if (blockIdx.x == 0 && slot == 0 && w == 0 && lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = my_w;
+  }
+  const int e = (int)readlane((uint32_t)my_id, slot);
+  const int64_t rb = (int64_t)NB * BB_Q2K;
+  float main_g = 0.f, main_u = 0.f, min_g = 0.f, min_u = 0.f, ss = 0.f;
+  if (has) {
+    Q2KRaw rg[BPW], ru[BPW];
+    const int64_t off = ((int64_t)e * F + row) * rb;
+#pragma unroll
+    for (int bl = 0; bl < BPW; ++bl) {
+      rg[bl].load(gate + off + (b0 + bl) * BB_Q2K, g);
+      ru[bl].load(up + off + (b0 + bl) * BB_Q2K, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
+    if (rmsnorm) ss = xs.sumsq(lane);
+    float mains[2] = {0.f, 0.f}, mins[2] = {0.f, 0.f};
+#pragma unroll
+    for (int bl = 0; bl < BPW; ++bl) {
+      const Q2KRaw *rr[2] = {&rg[bl], &ru[bl]};
+      block_dot<2>(rr, frag[w][bl], xsum[w][bl], sig[w][bl], n, g, mains, mins);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    main_g = mains[0]; main_u = mains[1];
+    min_g = mins[0] + __shfl_xor(mins[0], 16, 64);
+    min_g += __shfl_xor(min_g, 32, 64);
+    min_u = mins[1] + __shfl_xor(mins[1], 16, 64);
+    min_u += __shfl_xor(min_u, 32, 64);
+  }
+  if (rmsnorm) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) ssq[w] = ss;
+  }
+  if (g == 0) {
+    part[w][0][n] = main_g - min_g;
+    part[w][1][n] = main_u - min_u;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const float scale = rmsnorm ? 1.0f / sqrtf(((ssq[0] + ssq[1]) + (ssq[2] + ssq[3])) / (float)D + eps) : 1.0f;
+    const float gs = ((part[0][0][n] + part[1][0][n]) + (part[2][0][n] + part[3][0][n])) * scale;
+    const float us = ((part[0][1][n] + part[1][1][n]) + (part[2][1][n] + part[3][1][n])) * scale;
+    h[(int64_t)slot * F + row] = silu(gs) * us;
+  }
+}
+
+// Down projection + weighted combine for one token.  Grid D/16; WPS waves per
+// routing slot (blockDim = 64 * k * WPS), each taking NB/WPS blocks of the
+// slot's rows: a wave quantises its part of the slot's SwiGLU row into LDS,
+// streams its expert's 16 down rows, and the waves meet in LDS:
 // y (+)= sum_j w_j * (W2[e_j] h_j), summed in slot order.
 template <int F>
-__global__ __launch_bounds__(512) void down_q2k_t1_kernel(
+__global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
     const uint8_t *__restrict__ down, int D, int k, const int32_t *__restrict__ ids,
     const float *__restrict__ wts, const float *__restrict__ h, float *__restrict__ y,
     int accumulate) {
   constexpr int NB = F / 256;
-  __shared__ __attribute__((aligned(16))) uint32_t frag[8][NB][192];
-  __shared__ float xsum[8][NB][16];
-  __shared__ float sig[8][NB];
-  __shared__ float part[8][16];
+  constexpr int WPS = NB >= 2 ? 2 : 1;
+  constexpr int BPW = NB / WPS;
+  __shared__ __attribute__((aligned(16))) uint32_t frag[8 * WPS][BPW][192];
+  __shared__ float xsum[8 * WPS][BPW][16];
+  __shared__ float sig[8 * WPS][BPW];
+  __shared__ float part[8 * WPS][16];
 
-  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int j = wv / WPS, b0 = (wv % WPS) * BPW;
   const int n = lane & 15, g = lane >> 4;
   const int row = blockIdx.x * 16 + n;
-  QuantStage<NB> qs;
-  qs.load(h + (int64_t)j * F, lane);
+  QuantStage<BPW> qs;
+  qs.load(h + (int64_t)j * F + b0 * 256, lane);
   const int e = ids[j];
 
   const int64_t rb = (int64_t)NB * BB_Q2K;
-  Q2KRaw rw[NB];
-  const uint8_t *rowp = down + ((int64_t)e * D + row) * rb;
+  Q2KRaw rw[BPW];
+  const uint8_t *rowp = down + ((int64_t)e * D + row) * rb + b0 * BB_Q2K;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
+  for (int b = 0; b < BPW; ++b) {
     rw[b].load(rowp + b * BB_Q2K, g);
     __builtin_amdgcn_sched_barrier(0);
   }
-  qs.quantise(lane, &frag[j][0][0], &xsum[j][0][0], &sig[j][0]);
+  qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
   float main_acc = 0.f, min_acc = 0.f;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
+  for (int b = 0; b < BPW; ++b) {
     const Q2KRaw *rr[1] = {&rw[b]};
-    block_dot<1>(rr, frag[j][b], xsum[j][b], sig[j][b], g, &main_acc, &min_acc);
+    block_dot<1>(rr, frag[wv][b], xsum[wv][b], sig[wv][b], n, g, &main_acc, &min_acc);
     __builtin_amdgcn_sched_barrier(0);
   }
   min_acc += __shfl_xor(min_acc, 16, 64);
   min_acc += __shfl_xor(min_acc, 32, 64);
-  if (g == 0) part[j][n] = main_acc - min_acc;
+  if (g == 0) part[wv][n] = main_acc - min_acc;
   __syncthreads();
   if (threadIdx.x < 16) {
     float acc = 0.f;
-    for (int s = 0; s < k; ++s) acc = fmaf(wts[s], part[s][n], acc);
+    for (int s = 0; s < k; ++s) {
+      float ps = part[s * WPS][n];
+#pragma unroll
+      for (int q = 1; q < WPS; ++q) ps += part[s * WPS + q][n];
+      acc = fmaf(wts[s], ps, acc);
+    }
     y[row] = accumulate ? y[row] + acc : acc;
   }
 }
 
 }  // namespace
 
-size_t qact_bytes(int n_vec, int len) {
-  const size_t nb = (size_t)len / 256;
-  return ((size_t)n_vec * nb * (192 * 4 + 16 * 4 + 4) + 255) & ~(size_t)255;
-}
-
-static QAct qact_view(void *base, int n_vec, int len) {
-  const size_t nb = (size_t)n_vec * (len / 256);
-  QAct q;
-  q.frag = static_cast<uint32_t *>(base);
-  q.sum = reinterpret_cast<float *>(q.frag + nb * 192);
-  q.sig = q.sum + nb * 16;
-  return q;
-}
-
 hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *logits,
-                                bool rmsnorm, float eps, const RouteBufs &rb, float *h, void *qbuf,
-                                float *y, bool accumulate, int phase, hipStream_t s) {
-  const QAct xq = qact_view(qbuf, 1, m.D);
-  if (phase == 0) {
-#define DS4Q_PRO(DD)                                                                            \
-  if (m.E <= 256)                                                                               \
-    hipLaunchKernelGGL((prologue_t1_kernel<DD, 256>), dim3(1), dim3(256), 0, s, x, logits, m.E,  \
-                       m.k, rmsnorm ? 1 : 0, eps, xq, rb.ids, rb.w);                             \
-  else                                                                                          \
-    hipLaunchKernelGGL((prologue_t1_kernel<DD, ROUTE_MAX_E>), dim3(1), dim3(256), 0, s, x,       \
-                       logits, m.E, m.k, rmsnorm ? 1 : 0, eps, xq, rb.ids, rb.w)
-    switch (m.D) {
-      case 256: DS4Q_PRO(256); break;
-      case 512: DS4Q_PRO(512); break;
-      case 1024: DS4Q_PRO(1024); break;
-      case 2048: DS4Q_PRO(2048); break;
-      case 4096: DS4Q_PRO(4096); break;
-      default: return hipErrorInvalidValue;
-    }
-#undef DS4Q_PRO
-  } else if (phase == 1) {
+                                bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
+                                bool accumulate, int phase, hipStream_t s) {
+  if (phase == 1) {
     const dim3 grid(m.F / 16, m.k);
-#define DS4Q_GU(DD)                                                                             \
-  hipLaunchKernelGGL((gateup_q2k_t1_kernel<DD>), grid, dim3(256), 0, s, m.gate, m.up, m.F, xq,   \
-                     rb.ids, h)
+#define DS4Q_GU(DD, ME)                                                                          \
+  hipLaunchKernelGGL((gateup_q2k_t1_kernel<DD, ME>), grid, dim3(256), 0, s, m.gate, m.up, m.F,     \
+                     m.E, m.k, x, logits, rmsnorm ? 1 : 0, eps, rb.ids, rb.w, h)
+#define DS4Q_GU_E(DD)                            \
+  if (m.E <= 256) DS4Q_GU(DD, 256);              \
+  else DS4Q_GU(DD, ROUTE_MAX_E)
     switch (m.D) {
-      case 256: DS4Q_GU(256); break;
-      case 512: DS4Q_GU(512); break;
-      case 1024: DS4Q_GU(1024); break;
-      case 2048: DS4Q_GU(2048); break;
-      case 4096: DS4Q_GU(4096); break;
+      case 256: DS4Q_GU_E(256); break;
+      case 512: DS4Q_GU_E(512); break;
+      case 1024: DS4Q_GU_E(1024); break;
+      case 2048: DS4Q_GU_E(2048); break;
+      case 4096: DS4Q_GU_E(4096); break;
       default: return hipErrorInvalidValue;
     }
+#undef DS4Q_GU_E
 #undef DS4Q_GU
-  } else {
-    const dim3 block(64 * m.k);
+  } else if (phase == 2) {
+    const int wps = m.F >= 512 ? 2 : 1;
+    const dim3 block(64 * m.k * wps);
 #define DS4Q_DN(FF)                                                                             \
   hipLaunchKernelGGL((down_q2k_t1_kernel<FF>), dim3(m.D / 16), block, 0, s, m.down, m.D, m.k,    \
                      rb.ids, rb.w, h, y, accumulate ? 1 : 0)
@@ -521,6 +433,8 @@ hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *l
       default: return hipErrorInvalidValue;
     }
 #undef DS4Q_DN
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -48,14 +48,12 @@ hipError_t launch_decode_gateup(const MoeDims &m, const float *x, const float *i
 // T > 1: o [T*k][D] f32 (pair-indexed), then launch_combine.
 hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const RouteBufs &rb,
                               float *o, float *y, bool accumulate, hipStream_t s);
-// Single-token Q2_K decode on int8 matrix cores, in three phases: 0 =
-// prologue (routing into rb.ids / rb.w, quantised x into qbuf), 1 = gate/up +
-// SwiGLU into h, 2 = down + weighted combine into y.  qbuf holds
-// qact_bytes(1, D) bytes.
-size_t qact_bytes(int n_vec, int len);
+// Single-token Q2_K decode on int8 matrix cores, in two phases: 1 = routing
+// (into rb.ids / rb.w) + gate/up + SwiGLU into h, 2 = down + weighted combine
+// into y.
 hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *logits,
-                                bool rmsnorm, float eps, const RouteBufs &rb, float *h, void *qbuf,
-                                float *y, bool accumulate, int phase, hipStream_t s);
+                                bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
+                                bool accumulate, int phase, hipStream_t s);
 // y[t] (+)= sum_j w[t][j] * o[row(t, j)]; row = pair index, or sorted
 // position (via pair_pos) when by_pos.
 hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,

@@ -143,7 +143,7 @@ int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits
                     void *stream);
 
 /* Phases of the decode launches, for ds4q_moe_decode_phases. */
-#define DS4Q_PHASE_ROUTE 0x1u  /* routing (and, for one Q2_K token, the quantised input) */
+#define DS4Q_PHASE_ROUTE 0x1u  /* routing (nothing of its own for one Q2_K token, see below) */
 #define DS4Q_PHASE_GATEUP 0x2u /* gate/up projections + SwiGLU into the workspace */
 #define DS4Q_PHASE_DOWN 0x4u   /* down projection + weighted combine into y */
 #define DS4Q_PHASE_ALL 0x7u
@@ -155,8 +155,9 @@ int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits
  * workspace that covers ROUTE, GATEUP and DOWN in that order computes
  * exactly what one ds4q_moe_decode call computes.  Repeating GATEUP or DOWN
  * alone is idempotent without DS4Q_F_ACCUMULATE; with it each DOWN adds
- * again.  Same argument rules and errors as ds4q_moe_decode; route is
- * written by the ROUTE phase only. */
+ * again.  Same argument rules and errors as ds4q_moe_decode.  route is
+ * written by the phase that routes: ROUTE, except for a single token with
+ * Q2_K gate/up and down, whose GATEUP launch routes the token itself. */
 int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float *logits,
                            int32_t n_tok, float *y, const ds4q_route_out *route, void *workspace,
                            size_t workspace_bytes, uint32_t phases, void *stream);
@@ -194,7 +195,7 @@ int ds4q_moe_stack(const ds4q_moe_layer *layers, int32_t n_layers, int32_t mode,
 int ds4q_timing_enable(int on);
 /* Waits for the recorded events, then returns one entry per launch site:
  * names (max_names x name_len chars, NUL-terminated: "topk", "group",
- * "decode_prologue", "decode_gateup", "decode_down", "prep_bf16",
+ * "decode_gateup", "decode_down", "prep_bf16",
  * "prefill_gateup", "prefill_down", "combine"), summed milliseconds and
  * launch counts (host arrays).  Clears the record. */
 int ds4q_timing_read(char *names, int name_len, double *total_ms, int64_t *count, int max_names,
