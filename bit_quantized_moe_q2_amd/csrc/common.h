@@ -101,20 +101,13 @@ __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
 
-// Wave-wide unsigned max / min; the result is uniform.
+// Wave-wide unsigned max; the result is uniform.
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   v = max(v, dpp<DPP_XOR1>(v));
   v = max(v, dpp<DPP_XOR2>(v));
   v = max(v, dpp<DPP_HALF_MIRROR>(v));
   v = max(v, dpp<DPP_MIRROR>(v));
   return max(max(readlane(v, 0), readlane(v, 16)), max(readlane(v, 32), readlane(v, 48)));
-}
-__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
-  v = min(v, dpp<DPP_XOR1>(v));
-  v = min(v, dpp<DPP_XOR2>(v));
-  v = min(v, dpp<DPP_HALF_MIRROR>(v));
-  v = min(v, dpp<DPP_MIRROR>(v));
-  return min(min(readlane(v, 0), readlane(v, 16)), min(readlane(v, 32), readlane(v, 48)));
 }
 
 __device__ __forceinline__ float float_from_ordered(uint32_t o) {
@@ -124,7 +117,7 @@ __device__ __forceinline__ float float_from_ordered(uint32_t o) {
 
 // Top-k for E <= 256 logits (four per lane: expert lane + 64i): each round
 // takes the wave max of the order-preserving keys, then the smallest expert
-// index holding it (ties -> lower index).  Lane j < k returns slot j's expert
+// index holding it (ties -> lower index) from ballots.  Lane j < k returns slot j's expert
 // and softmax weight.  load() only issues the reads, so that a caller can
 // queue other loads behind them before select() waits.
 struct TopK256 {
@@ -136,27 +129,41 @@ struct TopK256 {
       v[i] = e < E ? lg[e] : 0.f;
     }
   }
-  __device__ __forceinline__ void select(int E, int k, int lane, int *id, float *w) const {
+  // The first k_need slots (k_need <= k); with weights, the softmax over the
+  // k selected (then k_need must equal k).
+  __device__ __forceinline__ void select(int E, int k, int k_need, bool weights, int lane, int *id,
+                                         float *w) const {
     uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < E ? ordered_bits(v[i]) : 0u;
     uint32_t my_id = 0, my_key = 0;
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < k_need; ++j) {
       const uint32_t gm = wave_umax(max(max(key[0], key[1]), max(key[2], key[3])));
-      uint32_t cand = 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cand = key[i] == gm ? min(cand, (uint32_t)(lane + 64 * i)) : cand;
-      const uint32_t ew = wave_umin(cand);
+      // The smallest expert index holding gm: experts lane + 64i are in
+      // index order i-major, so the first non-empty ballot in i and its
+      // lowest set lane give it (scalar bit scans, no second reduction).
+      const uint64_t m0 = __builtin_amdgcn_ballot_w64(key[0] == gm);
+      const uint64_t m1 = __builtin_amdgcn_ballot_w64(key[1] == gm);
+      const uint64_t m2 = __builtin_amdgcn_ballot_w64(key[2] == gm);
+      const uint64_t m3 = __builtin_amdgcn_ballot_w64(key[3] == gm);
+      const uint32_t c0 = m0 ? (uint32_t)__builtin_ctzll(m0) : 256u;
+      const uint32_t c1 = m1 ? 64u + (uint32_t)__builtin_ctzll(m1) : 256u;
+      const uint32_t c2 = m2 ? 128u + (uint32_t)__builtin_ctzll(m2) : 256u;
+      const uint32_t c3 = m3 ? 192u + (uint32_t)__builtin_ctzll(m3) : 256u;
+      const uint32_t ew = min(min(c0, c1), min(c2, c3));
 #pragma unroll
       for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(lane + 64 * i) == ew ? 0u : key[i];
       if (lane == j) { my_id = ew; my_key = gm; }
     }
-    const float top = float_from_ordered(readlane(my_key, 0));
-    const float ex = lane < k ? expf(float_from_ordered(my_key) - top) : 0.f;
-    float den = 0.f;
-    for (int j = 0; j < k; ++j) den += __builtin_bit_cast(float, readlane(__builtin_bit_cast(uint32_t, ex), j));
     *id = (int)my_id;
-    *w = ex / den;
+    *w = 0.f;
+    if (weights) {
+      const float top = float_from_ordered(readlane(my_key, 0));
+      const float ex = lane < k ? expf(float_from_ordered(my_key) - top) : 0.f;
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += __builtin_bit_cast(float, readlane(__builtin_bit_cast(uint32_t, ex), j));
+      *w = ex / den;
+    }
   }
 };
 
@@ -164,7 +171,7 @@ __device__ __forceinline__ void wave_topk256(const float *__restrict__ lg, int E
                                              int *id, float *w) {
   TopK256 t;
   t.load(lg, E, lane);
-  t.select(E, k, lane, id, w);
+  t.select(E, k, k, true, lane, id, w);
 }
 
 // Top-k of E logits by (logit desc, index asc) for one token, computed by a

@@ -26,11 +26,12 @@
 // gives all three limb products of 16 weight rows: C[limb][row], held by
 // lanes 0..15.
 //
-// A step is two kernels.  Gate/up + SwiGLU: every wave routes the token
-// itself (top-k of the logits, a few hundred VALU instructions, cheaper than
-// a launch and a round trip through memory), issues its expert's weight loads,
-// quantises its own quarter of x into LDS meanwhile and runs the MFMA loop;
-// workgroup (0, 0) also stores the routing for the second kernel.  Down +
+// A step is two kernels.  Gate/up + SwiGLU: each workgroup routes the token
+// itself (top-k of the logits in one wave, a few hundred VALU instructions,
+// cheaper than a launch and a round trip through memory); every wave then
+// issues its expert's weight loads, quantises its own quarter of x into LDS
+// meanwhile and runs the MFMA loop; workgroup (0, 0) also stores the routing
+// for the second kernel.  Down +
 // weighted combine: each wave quantises its share of its slot's SwiGLU row
 // into LDS while its weight loads are in flight.  The RMS norm of the input
 // is a per-token factor, applied to the gate and up sums in the epilogue.
@@ -249,17 +250,20 @@ struct TokenRoute {
     lg = logits;
     if constexpr (MAXE == 256) t.load(logits, E, lane);
   }
-  __device__ __forceinline__ void select(int E, int k, int lane, int *id, float *w) const {
-    if constexpr (MAXE == 256) t.select(E, k, lane, id, w);
+  // The first k_need slots; the softmax weights only when asked for (then
+  // all k slots are selected).
+  __device__ __forceinline__ void select(int E, int k, int k_need, bool weights, int lane, int *id,
+                                         float *w) const {
+    if constexpr (MAXE == 256) t.select(E, k, weights ? k : k_need, weights, lane, id, w);
     else wave_topk<MAXE>(lg, E, k, lane, id, w);
   }
 };
 
 // Gate/up + SwiGLU for one token.  Grid (F/16, k): 16 rows of one routed
 // expert per workgroup; its four waves split each row's NB blocks into
-// quarters and meet in LDS.  Every wave routes the token ("ds4.c 해독하기 1/8",
-// DS4_SHAPE_FLASH passage: 6 of 256 routed experts) and quantises its own
-// quarter of x; workgroup (0, 0) stores the routing for the down kernel.
+// quarters and meet in LDS.  One wave routes the token ("ds4.c 해독하기 1/8",
+// DS4_SHAPE_FLASH passage: 6 of 256 routed experts), each wave quantises its
+// own quarter of x; workgroup (0, 0) stores the routing for the down kernel.
 // With rmsnorm, the sums are multiplied by 1/sqrt(mean(x^2) + eps): the
 // quantised limbs do not depend on that factor.
 template <int D, int MAXE>
@@ -274,6 +278,7 @@ __global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
   __shared__ float sig[4][BPW];
   __shared__ float part[4][2][16];
   __shared__ float ssq[4];
+  __shared__ int expert;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -281,18 +286,35 @@ __global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
   const int row = blockIdx.x * 16 + n;
   const int b0 = w * BPW;
   const bool has = b0 < NB;
+  // One wave per workgroup routes (which one rotates with the workgroup, so
+  // that the routing work spreads over the SIMDs); the others only queue
+  // their x loads before the barrier.
+  const bool router = w == ((blockIdx.x + blockIdx.y) & 3);
   TokenRoute<MAXE> rt;
-  rt.load(logits, E, lane);
+  if (router) rt.load(logits, E, lane);
   QuantStage<BPW> xs;
   if (has) xs.load(x + b0 * 256, lane);
-  int my_id;
-  float my_w;
-  rt.select(E, k, lane, &my_id, &my_w);
-  if (blockIdx.x == 0 && slot == 0 && w == 0 && lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = my_w;
+  if (router) {
+    int my_id;
+    float my_w;
+    // every wave of the workgroup waits for this: issue it ahead of the
+    // quantising waves that share its SIMD
+    // only workgroup (0, 0) stores the routing; the others need their slot
+    const bool store = blockIdx.x == 0 && slot == 0;
+    __builtin_amdgcn_s_setprio(3);
+    rt.select(E, k, slot + 1, store, lane, &my_id, &my_w);
+    __builtin_amdgcn_s_setprio(0);
+    if (store && lane < k) {
+      ids_out[lane] = my_id;
+      w_out[lane] = my_w;
+    }
+    if (lane == slot) expert = my_id;
+  } else if (has) {
+    // the other waves quantise their x while the routing wave selects
+    xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
   }
-  const int e = (int)readlane((uint32_t)my_id, slot);
+  __syncthreads();
+  const int e = expert;
   const int64_t rb = (int64_t)NB * BB_Q2K;
   float main_g = 0.f, main_u = 0.f, min_g = 0.f, min_u = 0.f, ss = 0.f;
   if (has) {
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
       ru[bl].load(up + off + (b0 + bl) * BB_Q2K, g);
       __builtin_amdgcn_sched_barrier(0);
     }
-    xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
+    if (router) xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
     if (rmsnorm) ss = xs.sumsq(lane);
     float mains[2] = {0.f, 0.f}, mins[2] = {0.f, 0.f};
 #pragma unroll
@@ -340,7 +362,7 @@ __global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
 // Down projection + weighted combine for one token.  Grid D/16; WPS waves per
 // routing slot (blockDim = 64 * k * WPS), each taking NB/WPS blocks of the
 // slot's rows: a wave quantises its part of the slot's SwiGLU row into LDS,
-// streams its expert's 16 down rows, and the waves meet in LDS:
+// then streams its expert's 16 down rows, and the waves meet in LDS:
 // y (+)= sum_j w_j * (W2[e_j] h_j), summed in slot order.
 template <int F>
 __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
@@ -362,6 +384,10 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
   QuantStage<BPW> qs;
   qs.load(h + (int64_t)j * F + b0 * 256, lane);
   const int e = ids[j];
+  // Quantise first: while this wave does, the other waves' weight loads keep
+  // the memory pipeline full, and this wave's blocks can be used as soon as
+  // they arrive.
+  qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
 
   const int64_t rb = (int64_t)NB * BB_Q2K;
   Q2KRaw rw[BPW];
@@ -371,7 +397,6 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
     rw[b].load(rowp + b * BB_Q2K, g);
     __builtin_amdgcn_sched_barrier(0);
   }
-  qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
   float main_acc = 0.f, min_acc = 0.f;
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {

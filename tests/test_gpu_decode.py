@@ -281,3 +281,26 @@ def test_decode_phases_compose(gpu, qt, T):
         ds4q.ds4q_moe_decode_phases(lay.L, x, lg, T, y, None, ws, ds4q.PHASE_DOWN)
     torch.cuda.synchronize()
     assert np.array_equal(a.view(np.uint32), y.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("E", [256, 200, 512])
+def test_decode_one_token_route_ties(gpu, E):
+    """The one-token Q2_K path routes inside its gate/up kernel: tied logits
+    (equal values, +0 against -0, a tie across the k boundary) must pick the
+    same experts in the same slot order as the oracle, for E up to 256 (four
+    logits per lane) and above (the general top-k)."""
+    ds4q = gpu
+    lay = SynthLayer(ds4q, DEV, 512, 256, E, 6, 10, seed=700 + E)
+    base = synth.logits_normal(synth.stream_key(25, E), 5, E)
+    base[0] = 0.0
+    base[1, [E - 1, 10, 99]] = 9.0
+    base[2, :] = -0.0
+    base[2, 3] = 0.0
+    base[3, [5, 6, 7, 8, 9, 10, 11]] = 3.5
+    base[4, [E - 2, E - 1, 0]] = 7.0
+    for t in range(5):
+        _log(f"one-token ties E={E} row {t}")
+        x = synth.x_f32(synth.stream_key(26, t), 1, 512)
+        y, ids = _decode(ds4q, lay, x, base[t:t + 1])
+        assert np.array_equal(ids, oracle.route(base[t:t + 1], 6)[0]), t
+        assert normwise_err(y, lay.oracle_moe(x, base[t:t + 1])) <= TOL_FP32
