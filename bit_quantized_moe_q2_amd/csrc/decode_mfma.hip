@@ -7,12 +7,15 @@
 // X_s being the sum of x over sub-block s.  The integer weights sc*q lie in
 // 0..45 and are fed to v_mfma_i32_16x16x64_i8 as they are; the block's
 // activations are split into three int8 limbs with a per-block scale
-// sigma = max|x| / 127:
-//   x ~= sigma * (a0 + a1/254 + a2/254^2),  |a_i| <= 127,
-// (residual below sigma/2/254^2, about 2^-22 of the block's largest value),
-// so each limb's product with the weights is accumulated exactly in int32 and
-// the block result is d*sigma*(C0 + C1/254 + C2/254^2) in fp32.  The min term
-// uses X_s summed in fp32 from the unquantised activations.
+// sigma = max|x| / 127: N = trunc(x * 127 * 65536 / max|x| + 32896) has the
+// balanced base-256 digits a0 = byte 2, a1 = byte 1 - 128, a2 = byte 0 - 128
+// (all within [-127, 127]), so that
+//   x ~= sigma * (a0 + a1/256 + a2/65536)
+// with a residual below 1.3 * sigma / 65536 (about 2^-23 of the block's
+// largest value).  Each limb's product with the weights is accumulated
+// exactly in int32 and the block result is d*sigma*(C0 + C1/256 + C2/65536)
+// in fp32.  The min term uses X_s summed in fp32 from the unquantised
+// activations.
 //
 // MFMA operand layout (v_mfma_i32_16x16x64_i8): lane l holds 16 int8 of A
 // row l%16 and 16 int8 of B column l%16 for the same 16 K slots (K group
@@ -44,8 +47,8 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float INV254 = 1.0f / 254.0f;
-constexpr float INV254SQ = 1.0f / (254.0f * 254.0f);
+constexpr float INV256 = 1.0f / 256.0f;
+constexpr float INV65536 = 1.0f / 65536.0f;
 
 // Raw bytes of one 256-value Q2_K block that lane group g uses.
 struct Q2KRaw {
@@ -65,10 +68,10 @@ __device__ __forceinline__ void sub_bytes(const Q2KRaw &r, int p, uint32_t sb[4]
   sb[0] = a0 & 0xFFu; sb[1] = (a0 >> 16) & 0xFFu; sb[2] = a1 & 0xFFu; sb[3] = (a1 >> 16) & 0xFFu;
 }
 
-// Byte table [0, sc, 2sc, 3sc] of a sub-block's integer weights.
+// Byte table [0, sc, 2sc, 3sc] of a sub-block's integer weights: sc * 0x030201
+// puts sc, 2sc, 3sc (at most 45) in bytes 0..2 without carries.
 __device__ __forceinline__ uint32_t qsc_table(uint32_t sb) {
-  const uint32_t sc = sb & 15u;
-  return __umul24(sc, 0x00020100u) + (__umul24(sc, 3u) << 24);
+  return ((sb & 15u) * 0x030201u) << 8;
 }
 
 // B operand of K tile j: dword k = the sub-block's table looked up with the
@@ -83,32 +86,29 @@ __device__ __forceinline__ i32x4 b_frag(const Q2KRaw &r, int j, const uint32_t t
   return b;
 }
 
-__device__ __forceinline__ uint32_t pack_i8(float a, float b, float c, float d) {
-  return ((uint32_t)(int)a & 0xFFu) | (((uint32_t)(int)b & 0xFFu) << 8) |
-         (((uint32_t)(int)c & 0xFFu) << 16) | (((uint32_t)(int)d & 0xFFu) << 24);
-}
 
 // One thread quantises the 16 activations of one sub-block s (values
 // 16s..16s+15 of a block) with the block scale inv = 127 / max|x| and writes
-// its 3 limbs x 4 dwords into the block's fragments frag[limb][j][g][k].
+// its 3 limbs x 4 dwords into the block's fragments frag[limb][j][g][k]: the
+// digits of N (see above) are gathered byte-wise with v_perm.
 __device__ __forceinline__ void quantize_subblock(const float v[16], float inv, int s,
                                                   uint32_t *__restrict__ frag_blk) {
   const int h = s >> 3, k = (s >> 1) & 3, p = s & 1, g = 2 * h + p;
+  const float scale = inv * 65536.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float a0[4], a1[4], a2[4];
+    uint32_t n[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float u = v[4 * j + i] * inv;
-      a0[i] = rintf(u);
-      const float r1 = (u - a0[i]) * 254.0f;
-      a1[i] = rintf(r1);
-      a2[i] = rintf((r1 - a1[i]) * 254.0f);
-    }
+    for (int i = 0; i < 4; ++i) n[i] = (uint32_t)(int)fmaf(v[4 * j + i], scale, 32896.0f);
+    // bytes 0 and 1 of values 0..3, and byte 2
+    const uint32_t p01 = __builtin_amdgcn_perm(n[1], n[0], 0x05010400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(n[3], n[2], 0x05010400u);
+    const uint32_t q01 = __builtin_amdgcn_perm(n[1], n[0], 0x0C0C0602u);
+    const uint32_t q23 = __builtin_amdgcn_perm(n[3], n[2], 0x0C0C0602u);
     const int off = (j * 4 + g) * 4 + k;
-    frag_blk[0 * 64 + off] = pack_i8(a0[0], a0[1], a0[2], a0[3]);
-    frag_blk[1 * 64 + off] = pack_i8(a1[0], a1[1], a1[2], a1[3]);
-    frag_blk[2 * 64 + off] = pack_i8(a2[0], a2[1], a2[2], a2[3]);
+    frag_blk[0 * 64 + off] = __builtin_amdgcn_perm(q23, q01, 0x05040100u);
+    frag_blk[1 * 64 + off] = __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u;
+    frag_blk[2 * 64 + off] = __builtin_amdgcn_perm(p23, p01, 0x05040100u) ^ 0x80808080u;
   }
 }
 
@@ -147,7 +147,7 @@ __device__ __forceinline__ void block_post(const Q2KRaw &r, const uint32_t sb[4]
                                            const float *__restrict__ xsum_blk, float sigma, int g,
                                            float &main_acc, float &min_acc) {
   const int p = g & 1, h = g >> 1;
-  const float f = fmaf((float)c.z, INV254SQ, fmaf((float)c.y, INV254, (float)c.x));
+  const float f = fmaf((float)c.z, INV65536, fmaf((float)c.y, INV256, (float)c.x));
   main_acc = fmaf(f16lo(r.dd) * sigma, f, main_acc);
   float mn = (float)(sb[0] >> 4) * xsum_blk[8 * h + p];
   mn = fmaf((float)(sb[1] >> 4), xsum_blk[8 * h + 2 + p], mn);
