@@ -260,23 +260,25 @@ struct TokenRoute {
 };
 
 // Gate/up + SwiGLU for one token.  Grid (F/16, k): 16 rows of one routed
-// expert per workgroup; its four waves split each row's NB blocks into
-// quarters and meet in LDS.  One wave routes the token ("ds4.c 해독하기 1/8",
-// DS4_SHAPE_FLASH passage: 6 of 256 routed experts), each wave quantises its
-// own quarter of x; workgroup (0, 0) stores the routing for the down kernel.
-// With rmsnorm, the sums are multiplied by 1/sqrt(mean(x^2) + eps): the
-// quantised limbs do not depend on that factor.
+// expert per workgroup of eight waves; waves 0..3 take the four quarters of
+// each gate row's NB blocks, waves 4..7 those of the up rows (one matrix per
+// wave streams faster than interleaving both), and the waves meet in LDS.
+// One wave routes the token ("ds4.c 해독하기 1/8", DS4_SHAPE_FLASH passage: 6
+// of 256 routed experts); each wave quantises its own quarter of x;
+// workgroup (0, 0) stores the routing for the down kernel.  With rmsnorm,
+// the sums are multiplied by 1/sqrt(mean(x^2) + eps): the quantised limbs do
+// not depend on that factor.
 template <int D, int MAXE>
-__global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
+__global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
     const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up, int F, int E, int k,
     const float *__restrict__ x, const float *__restrict__ logits, int rmsnorm, float eps,
     int32_t *__restrict__ ids_out, float *__restrict__ w_out, float *__restrict__ h) {
   constexpr int NB = D / 256;
   constexpr int BPW = NB >= 4 ? NB / 4 : 1;
-  __shared__ __attribute__((aligned(16))) uint32_t frag[4][BPW][192];
-  __shared__ float xsum[4][BPW][16];
-  __shared__ float sig[4][BPW];
-  __shared__ float part[4][2][16];
+  __shared__ __attribute__((aligned(16))) uint32_t frag[8][BPW][192];
+  __shared__ float xsum[8][BPW][16];
+  __shared__ float sig[8][BPW];
+  __shared__ float part[8][16];
   __shared__ float ssq[4];
   __shared__ int expert;
 
@@ -284,12 +286,14 @@ __global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
   const int n = lane & 15, g = lane >> 4;
   const int slot = blockIdx.y;
   const int row = blockIdx.x * 16 + n;
-  const int b0 = w * BPW;
+  const int quarter = w & 3;
+  const int b0 = quarter * BPW;
   const bool has = b0 < NB;
+  const uint8_t *__restrict__ mat = w < 4 ? gate : up;
   // One wave per workgroup routes (which one rotates with the workgroup, so
-  // that the routing work spreads over the SIMDs); the others only queue
-  // their x loads before the barrier.
-  const bool router = w == ((blockIdx.x + blockIdx.y) & 3);
+  // that the routing work spreads over the SIMDs); the others queue their x
+  // loads and quantise while it selects.
+  const bool router = w == ((blockIdx.x + blockIdx.y) & 7);
   TokenRoute<MAXE> rt;
   if (router) rt.load(logits, E, lane);
   QuantStage<BPW> xs;
@@ -297,9 +301,9 @@ __global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
   if (router) {
     int my_id;
     float my_w;
-    // every wave of the workgroup waits for this: issue it ahead of the
-    // quantising waves that share its SIMD
-    // only workgroup (0, 0) stores the routing; the others need their slot
+    // only workgroup (0, 0) stores the routing; the others need their slot.
+    // Every wave of the workgroup waits for this, so it is issued ahead of
+    // the quantising waves that share its SIMD.
     const bool store = blockIdx.x == 0 && slot == 0;
     __builtin_amdgcn_s_setprio(3);
     rt.select(E, k, slot + 1, store, lane, &my_id, &my_w);
@@ -310,51 +314,42 @@ __global__ __launch_bounds__(256) void gateup_q2k_t1_kernel(
     }
     if (lane == slot) expert = my_id;
   } else if (has) {
-    // the other waves quantise their x while the routing wave selects
     xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
   }
   __syncthreads();
   const int e = expert;
   const int64_t rb = (int64_t)NB * BB_Q2K;
-  float main_g = 0.f, main_u = 0.f, min_g = 0.f, min_u = 0.f, ss = 0.f;
+  float main_acc = 0.f, min_acc = 0.f, ss = 0.f;
   if (has) {
-    Q2KRaw rg[BPW], ru[BPW];
-    const int64_t off = ((int64_t)e * F + row) * rb;
+    Q2KRaw rw[BPW];
+    const uint8_t *rowp = mat + ((int64_t)e * F + row) * rb + b0 * BB_Q2K;
 #pragma unroll
     for (int bl = 0; bl < BPW; ++bl) {
-      rg[bl].load(gate + off + (b0 + bl) * BB_Q2K, g);
-      ru[bl].load(up + off + (b0 + bl) * BB_Q2K, g);
+      rw[bl].load(rowp + bl * BB_Q2K, g);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (router) xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
-    if (rmsnorm) ss = xs.sumsq(lane);
-    float mains[2] = {0.f, 0.f}, mins[2] = {0.f, 0.f};
+    if (rmsnorm && w < 4) ss = xs.sumsq(lane);
 #pragma unroll
     for (int bl = 0; bl < BPW; ++bl) {
-      const Q2KRaw *rr[2] = {&rg[bl], &ru[bl]};
-      block_dot<2>(rr, frag[w][bl], xsum[w][bl], sig[w][bl], n, g, mains, mins);
+      const Q2KRaw *rr[1] = {&rw[bl]};
+      block_dot<1>(rr, frag[w][bl], xsum[w][bl], sig[w][bl], n, g, &main_acc, &min_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    main_g = mains[0]; main_u = mains[1];
-    min_g = mins[0] + __shfl_xor(mins[0], 16, 64);
-    min_g += __shfl_xor(min_g, 32, 64);
-    min_u = mins[1] + __shfl_xor(mins[1], 16, 64);
-    min_u += __shfl_xor(min_u, 32, 64);
+    min_acc += __shfl_xor(min_acc, 16, 64);
+    min_acc += __shfl_xor(min_acc, 32, 64);
   }
-  if (rmsnorm) {
+  if (rmsnorm && w < 4) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
     if (lane == 0) ssq[w] = ss;
   }
-  if (g == 0) {
-    part[w][0][n] = main_g - min_g;
-    part[w][1][n] = main_u - min_u;
-  }
+  if (g == 0) part[w][n] = main_acc - min_acc;
   __syncthreads();
   if (threadIdx.x < 16) {
     const float scale = rmsnorm ? 1.0f / sqrtf(((ssq[0] + ssq[1]) + (ssq[2] + ssq[3])) / (float)D + eps) : 1.0f;
-    const float gs = ((part[0][0][n] + part[1][0][n]) + (part[2][0][n] + part[3][0][n])) * scale;
-    const float us = ((part[0][1][n] + part[1][1][n]) + (part[2][1][n] + part[3][1][n])) * scale;
+    const float gs = ((part[0][n] + part[1][n]) + (part[2][n] + part[3][n])) * scale;
+    const float us = ((part[4][n] + part[5][n]) + (part[6][n] + part[7][n])) * scale;
     h[(int64_t)slot * F + row] = silu(gs) * us;
   }
 }
@@ -428,7 +423,7 @@ hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *l
   if (phase == 1) {
     const dim3 grid(m.F / 16, m.k);
 #define DS4Q_GU(DD, ME)                                                                          \
-  hipLaunchKernelGGL((gateup_q2k_t1_kernel<DD, ME>), grid, dim3(256), 0, s, m.gate, m.up, m.F,     \
+  hipLaunchKernelGGL((gateup_q2k_t1_kernel<DD, ME>), grid, dim3(512), 0, s, m.gate, m.up, m.F,     \
                      m.E, m.k, x, logits, rmsnorm ? 1 : 0, eps, rb.ids, rb.w, h)
 #define DS4Q_GU_E(DD)                            \
   if (m.E <= 256) DS4Q_GU(DD, 256);              \
