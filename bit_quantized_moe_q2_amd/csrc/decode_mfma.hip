@@ -62,6 +62,12 @@ struct Q2KRaw {
   }
 };
 
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Scale/min bytes of the lane's four sub-blocks (k = 0..3).
 __device__ __forceinline__ void sub_bytes(const Q2KRaw &r, int p, uint32_t sb[4]) {
   const uint32_t a0 = r.s0 >> (8 * p), a1 = r.s1 >> (8 * p);
@@ -116,12 +122,6 @@ __device__ __forceinline__ float max16(float m) {
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   return m;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // A operand of one block: row r < 3 of A is limb r of the activations, rows
@@ -264,10 +264,11 @@ struct TokenRoute {
 // each gate row's NB blocks, waves 4..7 those of the up rows (one matrix per
 // wave streams faster than interleaving both), and the waves meet in LDS.
 // One wave routes the token ("ds4.c 해독하기 1/8", DS4_SHAPE_FLASH passage: 6
-// of 256 routed experts); each wave quantises its own quarter of x;
-// workgroup (0, 0) stores the routing for the down kernel.  With rmsnorm,
-// the sums are multiplied by 1/sqrt(mean(x^2) + eps): the quantised limbs do
-// not depend on that factor.
+// of 256 routed experts); the other wave of its quarter pair quantises that
+// quarter of x, gate and up waves share the fragments; workgroup (0, 0)
+// stores the routing for the down kernel.  With rmsnorm, the sums are
+// multiplied by 1/sqrt(mean(x^2) + eps): the quantised limbs do not depend on
+// that factor.
 template <int D, int MAXE>
 __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
     const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up, int F, int E, int k,
@@ -275,9 +276,9 @@ __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
     int32_t *__restrict__ ids_out, float *__restrict__ w_out, float *__restrict__ h) {
   constexpr int NB = D / 256;
   constexpr int BPW = NB >= 4 ? NB / 4 : 1;
-  __shared__ __attribute__((aligned(16))) uint32_t frag[8][BPW][192];
-  __shared__ float xsum[8][BPW][16];
-  __shared__ float sig[8][BPW];
+  __shared__ __attribute__((aligned(16))) uint32_t frag[4][BPW][192];
+  __shared__ float xsum[4][BPW][16];
+  __shared__ float sig[4][BPW];
   __shared__ float part[8][16];
   __shared__ float ssq[4];
   __shared__ int expert;
@@ -291,13 +292,16 @@ __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
   const bool has = b0 < NB;
   const uint8_t *__restrict__ mat = w < 4 ? gate : up;
   // One wave per workgroup routes (which one rotates with the workgroup, so
-  // that the routing work spreads over the SIMDs); the others queue their x
-  // loads and quantise while it selects.
-  const bool router = w == ((blockIdx.x + blockIdx.y) & 7);
+  // that the routing work spreads over the SIMDs); the other wave of its
+  // quarter pair quantises, and so does the gate wave of each other pair.
+  const int router_w = (blockIdx.x + blockIdx.y) & 7;
+  const bool router = w == router_w;
+  const bool quantiser = w == (quarter == (router_w & 3) ? (router_w ^ 4) : quarter);
   TokenRoute<MAXE> rt;
   if (router) rt.load(logits, E, lane);
   QuantStage<BPW> xs;
-  if (has) xs.load(x + b0 * 256, lane);
+  float ss = 0.f;
+  if (quantiser && has) xs.load(x + b0 * 256, lane);
   if (router) {
     int my_id;
     float my_w;
@@ -313,13 +317,19 @@ __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
       w_out[lane] = my_w;
     }
     if (lane == slot) expert = my_id;
-  } else if (has) {
-    xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
+  } else if (quantiser && has) {
+    xs.quantise(lane, &frag[quarter][0][0], &xsum[quarter][0][0], &sig[quarter][0]);
+    if (rmsnorm) ss = xs.sumsq(lane);
+  }
+  if (quantiser && rmsnorm) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) ssq[quarter] = ss;
   }
   __syncthreads();
   const int e = expert;
   const int64_t rb = (int64_t)NB * BB_Q2K;
-  float main_acc = 0.f, min_acc = 0.f, ss = 0.f;
+  float main_acc = 0.f, min_acc = 0.f;
   if (has) {
     Q2KRaw rw[BPW];
     const uint8_t *rowp = mat + ((int64_t)e * F + row) * rb + b0 * BB_Q2K;
@@ -328,21 +338,14 @@ __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
       rw[bl].load(rowp + bl * BB_Q2K, g);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (router) xs.quantise(lane, &frag[w][0][0], &xsum[w][0][0], &sig[w][0]);
-    if (rmsnorm && w < 4) ss = xs.sumsq(lane);
 #pragma unroll
     for (int bl = 0; bl < BPW; ++bl) {
       const Q2KRaw *rr[1] = {&rw[bl]};
-      block_dot<1>(rr, frag[w][bl], xsum[w][bl], sig[w][bl], n, g, &main_acc, &min_acc);
+      block_dot<1>(rr, frag[quarter][bl], xsum[quarter][bl], sig[quarter][bl], n, g, &main_acc, &min_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
     min_acc += __shfl_xor(min_acc, 16, 64);
     min_acc += __shfl_xor(min_acc, 32, 64);
-  }
-  if (rmsnorm && w < 4) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    if (lane == 0) ssq[w] = ss;
   }
   if (g == 0) part[w][n] = main_acc - min_acc;
   __syncthreads();
