@@ -67,6 +67,6 @@ hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, co
 hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, const RouteBufs &rb,
                                int max_tiles, float *o, hipStream_t s);
 
-constexpr int PREFILL_TILE_M = 128;
+constexpr int PREFILL_TILE_M = 96;
 
 }  // namespace ds4q

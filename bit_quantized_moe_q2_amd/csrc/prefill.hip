@@ -57,28 +57,46 @@ struct RowStep;
 
 template <>
 struct RowStep<TYPE_Q2_K> {
-  uint32_t qa0, qa1, qb0, qb1, sc[4], dd;
+  // Lane group g covers sub-blocks 4g..4g+3 (values 64g..64g+63) of the
+  // block; MFMA step J takes values 64g + 8P + i with P = (J>>1) + 4(J&1):
+  // code bytes 16 + 32(g>>1) + 8(P&3) + i at bit pair (2g + (P>>2)) & 3,
+  // sub-block 4g + (P>>1).  (This order retires each pair of code dwords
+  // after two steps and keeps two sub-block tables live.)  A sub-block has
+  // four possible weights: they are computed once (fp32 fma, one rounding,
+  // then bf16 round-to-nearest-even) into a byte table, and each pair of bf16
+  // outputs is two v_perm lookups.
+  uint32_t q[8], scm, dd;
   __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
-    qa0 = ld32(blk + 16 + 8 * g); qa1 = ld32(blk + 20 + 8 * g);
-    qb0 = ld32(blk + 48 + 8 * g); qb1 = ld32(blk + 52 + 8 * g);
-    sc[0] = ld32(blk); sc[1] = ld32(blk + 4); sc[2] = ld32(blk + 8); sc[3] = ld32(blk + 12);
+    const uint8_t *qs = blk + 16 + 32 * (g >> 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = ld32(qs + 4 * i);
+    scm = ld32(blk + 4 * g);
     dd = ld32(blk + 80);
   }
-  // B fragment of MFMA step j (K = 32j .. 32j+31 of the block): values
-  // 32j + 8g + i = codes of bytes 32(j>>2) + 8g + i at bit pair j&3, sub-block
-  // 2j + (g>>1).
-  template <int J>
-  __device__ __forceinline__ bf16x8 frag(int g) const {
-    const uint32_t w0 = ((J >> 2) ? qb0 : qa0) >> (2 * (J & 3));
-    const uint32_t w1 = ((J >> 2) ? qb1 : qa1) >> (2 * (J & 3));
-    const uint32_t t0 = w0 & 0x03030303u, t1 = w1 & 0x03030303u;
-    const uint32_t sb = (sc[J >> 1] >> (16 * (J & 1) + 8 * (g >> 1))) & 0xFFu;
+  // bf16 table [v0 v1 | v2 v3] (low dword, high dword) of sub-block 4g + c.
+  __device__ __forceinline__ void table(int c, uint32_t &t01, uint32_t &t23) const {
+    const uint32_t sb = (scm >> (8 * c)) & 0xFFu;
     const float ds = f16lo(dd) * (float)(sb & 15u);
     const float dm = -(f16hi(dd) * (float)(sb >> 4));
-    return to_frag(pack_bf16(fmaf(ds, ub0(t0), dm), fmaf(ds, ub1(t0), dm)),
-                   pack_bf16(fmaf(ds, ub2(t0), dm), fmaf(ds, ub3(t0), dm)),
-                   pack_bf16(fmaf(ds, ub0(t1), dm), fmaf(ds, ub1(t1), dm)),
-                   pack_bf16(fmaf(ds, ub2(t1), dm), fmaf(ds, ub3(t1), dm)));
+    t01 = pack_bf16(dm, fmaf(ds, 1.0f, dm));
+    t23 = pack_bf16(fmaf(ds, 2.0f, dm), fmaf(ds, 3.0f, dm));
+  }
+  // Two bf16 weights for codes in bytes b, b+1 of x (b = 0 or 2).
+  template <int B>
+  __device__ __forceinline__ static uint32_t look(uint32_t x, uint32_t t01, uint32_t t23) {
+    constexpr uint32_t spread = B == 0 ? 0x01010000u : 0x03030202u;
+    const uint32_t sel = (__builtin_amdgcn_perm(x, x, spread) << 1) + 0x01000100u;
+    return __builtin_amdgcn_perm(t23, t01, sel);
+  }
+  static constexpr int step_p(int J) { return (J >> 1) + 4 * (J & 1); }
+  template <int J>
+  __device__ __forceinline__ bf16x8 frag(int g, uint32_t t01, uint32_t t23) const {
+    constexpr int P = step_p(J);
+    const int sh = 2 * ((2 * g + (P >> 2)) & 3);
+    const uint32_t x0 = (q[2 * (P & 3)] >> sh) & 0x03030303u;
+    const uint32_t x1 = (q[2 * (P & 3) + 1] >> sh) & 0x03030303u;
+    return to_frag(look<0>(x0, t01, t23), look<2>(x0, t01, t23), look<0>(x1, t01, t23),
+                   look<2>(x1, t01, t23));
   }
 };
 
@@ -88,8 +106,9 @@ struct RowStep<TYPE_Q4_1> {
   __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int) { base = blk; }
   // MFMA step j = Q4_1 block j of the K step: values 8g + i, i.e. nibbles of
   // qs[8(g&1) + i], low for g < 2, high for g >= 2.
+  __device__ __forceinline__ void table(int, uint32_t &t01, uint32_t &t23) const { t01 = t23 = 0u; }
   template <int J>
-  __device__ __forceinline__ bf16x8 frag(int g) const {
+  __device__ __forceinline__ bf16x8 frag(int g, uint32_t, uint32_t) const {
     const uint8_t *blk = base + J * BB_Q41;
     const uint32_t dm = ld32(blk);
     const int sh = 4 * (g >> 1);
@@ -158,16 +177,25 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   const int step_bytes = (int)row_bytes(TYPE, KS);
   for (int kb = 0; kb < K / KS; ++kb) {
     __syncthreads();
-    // stage A: 128 rows x 256 bf16 = 32 chunks of 16 B per row
+    // stage A: 128 rows x 256 bf16 = 32 chunks of 16 B per row, four chunks
+    // per thread at a time (bounds the registers in flight)
 #pragma unroll
-    for (int i = 0; i < TM * (KS / 8) / 256; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 5, col8 = c & 31;
-      const int src = arow[row];
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (src >= 0)
-        v = *reinterpret_cast<const uint4 *>(A + (int64_t)src * K + kb * KS + col8 * 8);
-      *reinterpret_cast<uint4 *>(&As[row * LDA + col8 * 8]) = v;
+    for (int i0 = 0; i0 < TM * (KS / 8) / 256; i0 += 4) {
+      uint4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * (i0 + i);
+        const int src = arow[c >> 5];
+        v[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (src >= 0)
+          v[i] = *reinterpret_cast<const uint4 *>(A + (int64_t)src * K + kb * KS + (c & 31) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * (i0 + i);
+        *reinterpret_cast<uint4 *>(&As[(c >> 5) * LDA + (c & 31) * 8]) = v[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
@@ -175,13 +203,24 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t) rs[t].load(brow[t] + (int64_t)kb * step_bytes, g);
 
+    // K order inside the step: MFMA step J, lane group g takes the step's
+    // values A_KOFF(J, g) .. +7 (the same for A and B).
+    // (Q2_K: steps 4c..4c+3 use sub-block tables c and c + 2.)
+    uint32_t tab[4][2][2];
 #define DS4Q_STEP(J)                                                                   \
   {                                                                                    \
+    if ((J) % 4 == 0 && TYPE == TYPE_Q2_K)                                             \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                  \
+        rs[t].table((J) >> 2, tab[t][0][0], tab[t][0][1]);                             \
+        rs[t].table(((J) >> 2) + 2, tab[t][1][0], tab[t][1][1]);                       \
+      }                                                                                \
     bf16x8 b[4];                                                                       \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) b[t] = rs[t].template frag<J>(g);    \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                      \
+        b[t] = rs[t].template frag<J>(g, tab[t][(J) & 1][0], tab[t][(J) & 1][1]);       \
+    const int koff = TYPE == TYPE_Q2_K ? 64 * g + 8 * RowStep<TYPE_Q2_K>::step_p(J) : 32 * (J) + 8 * g; \
     _Pragma("unroll") for (int i = 0; i < MT; ++i) {                                   \
       if (i < n_mt) {                                                                  \
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[(16 * i + n) * LDA + 32 * (J) + 8 * g]); \
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[(16 * i + n) * LDA + koff]); \
         _Pragma("unroll") for (int t = 0; t < 4; ++t)                                  \
             acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[t], acc[i][t], 0, 0, 0); \
       }                                                                                \
