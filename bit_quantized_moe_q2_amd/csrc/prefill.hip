@@ -184,11 +184,11 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
       uint4 v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // rows of absent pairs read row 0 and store zeros (no branch)
         const int c = tid + 256 * (i0 + i);
         const int src = arow[c >> 5];
-        v[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (src >= 0)
-          v[i] = *reinterpret_cast<const uint4 *>(A + (int64_t)src * K + kb * KS + (c & 31) * 8);
+        const uint4 t = *reinterpret_cast<const uint4 *>(A + (int64_t)(src < 0 ? 0 : src) * K + kb * KS + (c & 31) * 8);
+        v[i] = src < 0 ? make_uint4(0u, 0u, 0u, 0u) : t;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -214,15 +214,19 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
         rs[t].table((J) >> 2, tab[t][0][0], tab[t][0][1]);                             \
         rs[t].table(((J) >> 2) + 2, tab[t][1][0], tab[t][1][1]);                       \
       }                                                                                \
+    /* A fragments first (rows of absent pairs hold zeros), so that their    */ \
+    /* LDS latency hides behind the weight dequantisation                    */ \
+    const int koff = TYPE == TYPE_Q2_K ? 64 * g + 8 * RowStep<TYPE_Q2_K>::step_p(J) : 32 * (J) + 8 * g; \
+    bf16x8 a[MT];                                                                      \
+    _Pragma("unroll") for (int i = 0; i < MT; ++i)                                     \
+        a[i] = *reinterpret_cast<const bf16x8 *>(&As[(16 * i + n) * LDA + koff]);      \
     bf16x8 b[4];                                                                       \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                      \
         b[t] = rs[t].template frag<J>(g, tab[t][(J) & 1][0], tab[t][(J) & 1][1]);       \
-    const int koff = TYPE == TYPE_Q2_K ? 64 * g + 8 * RowStep<TYPE_Q2_K>::step_p(J) : 32 * (J) + 8 * g; \
     _Pragma("unroll") for (int i = 0; i < MT; ++i) {                                   \
       if (i < n_mt) {                                                                  \
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[(16 * i + n) * LDA + koff]); \
         _Pragma("unroll") for (int t = 0; t < 4; ++t)                                  \
-            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[t], acc[i][t], 0, 0, 0); \
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[t], acc[i][t], 0, 0, 0); \
       }                                                                                \
     }                                                                                  \
   }
