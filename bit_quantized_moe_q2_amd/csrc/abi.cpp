@@ -47,9 +47,12 @@ struct Workspace {
   uint16_t *hb = nullptr;  // prefill: [T*k][F] bf16 (sorted order)
   float *o = nullptr;      // [T*k][D] f32
   uint16_t *xb = nullptr;  // prefill: [T][D] bf16
+  PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
   size_t bytes = 0;
 
-  Workspace(uint8_t *base, int D, int F, int E, int k, int T, int mode) {
+  // i8_in / i8_h: prefill with Q2_K gate/up resp. down (int8 matrix cores)
+  Workspace(uint8_t *base, int D, int F, int E, int k, int T, int mode, bool i8_in = false,
+            bool i8_h = false) {
     size_t off = 0;
     auto take = [&](size_t n) -> void * {
       void *p = base ? base + off : nullptr;
@@ -78,6 +81,14 @@ struct Workspace {
       hb = (uint16_t *)take(P * F * 2);
       o = (float *)take(P * D * 4);
       xb = (uint16_t *)take((size_t)T * D * 2);
+      if (i8_in) {
+        void *p = take(prep_i8_bytes(T, D));
+        if (base) xq = prep_i8_view(p, T, D);
+      }
+      if (i8_h) {
+        void *p = take(prep_i8_bytes(P, F));
+        if (base) hq = prep_i8_view(p, P, F);
+      }
     }
     bytes = off;
   }
@@ -98,6 +109,9 @@ int check_layer(const ds4q_moe_layer *L) {
   if (!(L->norm_eps >= 0.0f) || !isfinite(L->norm_eps)) return DS4Q_E_INVAL;
   return DS4Q_OK;
 }
+
+bool i8_gateup(const ds4q_moe_layer *L) { return L->type_gate == DS4Q_TYPE_Q2_K; }
+bool i8_down(const ds4q_moe_layer *L) { return L->type_down == DS4Q_TYPE_Q2_K; }
 
 MoeDims dims_of(const ds4q_moe_layer *L) {
   MoeDims m;
@@ -206,7 +220,8 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, ALIGN) ||
       route_misaligned(route))
     return DS4Q_E_ALIGN;
-  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode);
+  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode,
+                       i8_gateup(L), i8_down(L));
   if (ws_bytes < need.bytes) return DS4Q_E_WORKSPACE;
   const size_t xb = (size_t)T * L->n_embd * x_elem, yb = (size_t)T * L->n_embd * 4;
   const size_t lb = (size_t)T * L->n_expert * 4;
@@ -263,19 +278,31 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
                 int32_t T, float *y, const ds4q_route_out *route, void *ws, hipStream_t s,
                 uint32_t flags) {
   const MoeDims m = dims_of(L);
-  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1);
+  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, i8_gateup(L), i8_down(L));
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
   TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, false, s));
   TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
-  const uint16_t *xb = static_cast<const uint16_t *>(x);
-  if (xf) {
-    TIMED_TRY("prep_bf16", launch_prep_bf16(xf, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xb, s));
-    xb = w.xb;
-  }
   const int mt = max_tiles(T, m.E, m.k);
-  TIMED_TRY("prefill_gateup", launch_prefill_gateup(m, xb, T, w.rb, mt, w.hb, s));
-  TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.o, s));
+  if (i8_gateup(L)) {
+    TIMED_TRY("prep_i8", launch_prep_i8(x, xf != nullptr, norm && xf ? w.rb.inv_rms : nullptr, T, m.D,
+                                        w.xq, s));
+    TIMED_TRY("prefill_gateup", launch_prefill_i8_gateup(m, w.xq, T, w.rb, mt, w.hb, s));
+  } else {
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    if (xf) {
+      TIMED_TRY("prep_bf16", launch_prep_bf16(xf, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xb, s));
+      xb = w.xb;
+    }
+    TIMED_TRY("prefill_gateup", launch_prefill_gateup(m, xb, T, w.rb, mt, w.hb, s));
+  }
+  if (i8_down(L)) {
+    const int64_t P = (int64_t)T * m.k;
+    TIMED_TRY("prep_i8", launch_prep_i8(w.hb, false, nullptr, P, m.F, w.hq, s));
+    TIMED_TRY("prefill_down", launch_prefill_i8_down(m, w.hq, T, w.rb, mt, w.o, s));
+  } else {
+    TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.o, s));
+  }
   TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, s));
   return copy_route(route, w.rb, T, m.E, m.k, s);
 }
@@ -365,7 +392,7 @@ DS4Q_API int ds4q_route(const float *logits, int32_t n_tok, int32_t n_expert, in
 DS4Q_API size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t mode) {
   if (check_layer(L) || max_tok < 0 || (mode != 0 && mode != 1)) return 0;
   return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used,
-                   max_tok > 0 ? max_tok : 1, mode)
+                   max_tok > 0 ? max_tok : 1, mode, i8_gateup(L), i8_down(L))
       .bytes;
 }
 

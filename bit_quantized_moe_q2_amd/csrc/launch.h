@@ -67,6 +67,25 @@ hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, co
 hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, const RouteBufs &rb,
                                int max_tiles, float *o, hipStream_t s);
 
+// Prefill on Q2_K weights, int8 matrix cores: activation rows prepared as
+// two int8 digits per value (MFMA fragment order), hi/lo bf16 sub-block sums
+// and a per-row scale.
+struct PrepI8 {
+  uint8_t *q;    // [rows][K/256][2][256]
+  uint16_t *x;   // [rows][K/256][2][16] bf16
+  float *sig;    // [rows]
+};
+size_t prep_i8_bytes(int64_t rows, int K);
+PrepI8 prep_i8_view(void *base, int64_t rows, int K);
+// src: f32 (f32in; times inv_rms[row] when given, then rounded to bf16) or
+// bf16 rows [rows][K].
+hipError_t launch_prep_i8(const void *src, bool f32in, const float *inv_rms, int64_t rows, int K,
+                          const PrepI8 &p, hipStream_t s);
+hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                    int max_tiles, uint16_t *hb, hipStream_t s);
+hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                  int max_tiles, float *o, hipStream_t s);
+
 constexpr int PREFILL_TILE_M = 96;
 
 }  // namespace ds4q

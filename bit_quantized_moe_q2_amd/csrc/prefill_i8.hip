@@ -1,0 +1,466 @@
+// Prefill path on Q2_K weights with int8 matrix cores.
+//
+// Arithmetic.  For one 256-value block of a weight row ("【#2】ds4.c 해독하기",
+// Q2_K block-layout table) and an activation row a,
+//   sum_v w_v a_v = d * sum_v (sc*q)_v a_v  -  dmin * sum_s mn_s A_s,
+// A_s the sums of a over the 16 sub-blocks.  prep_i8_kernel prepares each
+// activation row once per call (layer-input token rows, or the bf16 SwiGLU
+// rows of the down projection): sigma = max|a| / 127 over the row,
+// N = round(a / sigma * 256) split into balanced base-256 digits a0 (high)
+// and a1 (low), both int8, so a = sigma * (a0 + a1/256) up to sigma/512;
+// the sub-block sums A_s / sigma (of the unquantised row) are kept as two
+// bf16 halves, hi + lo.
+//
+// prefill_i8_kernel: the integer part runs on v_mfma_i32_16x16x64_i8 with
+// the 16 A rows = 8 tokens x 2 digits (row 2*token + digit) and B = the
+// integer weights sc*q in 0..45 (v_perm of the byte table [0, sc, 2sc, 3sc]
+// with the 2-bit codes); per block the two digit rows of a token combine
+// exactly as 256*C0 + C1 and enter fp32 as d/256 * (256*C0 + C1).  The min
+// term runs on v_mfma_f32_16x16x32_bf16 over K = 16 sub-blocks x {hi, lo}
+// with B = bf16(-dmin * mn), accumulating straight into the same fp32
+// registers; its 16 A rows are 16 tokens ordered so that each lane's four
+// accumulator rows are the tokens of its integer results.  The epilogue
+// scales by sigma (then SwiGLU, or the plain store of the down rows).
+//
+// Data movement: the activation tiles reach LDS by direct global->LDS loads
+// (global_load_lds_dwordx4), double-buffered one 256-column block ahead;
+// each 256-byte digit row is stored with its 16-byte chunks XOR-swizzled by
+// the row index, so the 16 lanes that read one chunk column hit 16
+// different bank groups.  Weights go straight to registers, also one block
+// ahead.
+#include "common.h"
+#include "launch.h"
+
+namespace ds4q {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int TMI = PREFILL_TILE_M;  // tokens (sorted pairs) per m-tile
+constexpr int SUBT = TMI / 8;        // integer MFMA row groups of 8 tokens
+constexpr int NPAIR = SUBT / 2;      // min-term MFMA row groups of 16 tokens
+constexpr int QROW = 512;            // digit bytes of one row's 256-column block
+constexpr int XROW = 64;             // hi/lo sub-block sums (bf16) of one row's block
+constexpr int ASTAGE = TMI * QROW;   // LDS bytes of one stage of digit rows
+constexpr int XSTAGE = TMI * XROW;
+constexpr int NDMA_A = TMI / 16;     // 1-KiB A loads per wave per block (8 waves)
+constexpr int NDMA_X = TMI / 16;     // 1-KiB X loads per block (waves 0..NDMA_X-1)
+static_assert(TMI % 16 == 0 && NDMA_X <= 8, "m-tile must be a multiple of 16, at most 128");
+
+// 24-bit unsigned multiply (full-rate v_mul_u32_u24; both operands < 2^24).
+__device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// The bytes of one Q2_K block that lane group g uses: code quarter g
+// (16 bytes), the scale/min bytes of sub-blocks 8(g>>1)..8(g>>1)+7, d|dmin.
+struct Q2KPart {
+  u32x4 q;
+  uint32_t s0, s1, dd;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
+    q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
+    s0 = ld32(blk + 8 * (g >> 1));
+    s1 = ld32(blk + 8 * (g >> 1) + 4);
+    dd = ld32(blk + 80);
+  }
+};
+
+// Weight operands of one block for one 16-row n-subtile.  Code byte c of
+// dword j of quarter g holds, in bit pair k, value
+// 128(g>>1) + 32k + 16(g&1) + 4j + c, of sub-block 8(g>>1) + 2k + (g&1);
+// K-tile j, dword k of the B fragment is that bit pair looked up in the
+// sub-block's table [0, sc, 2sc, 3sc].
+struct WOps {
+  i32x4 b[4];    // integer B fragments of K-tiles 0..3
+  bf16x8 bmin;   // -dmin * mn of sub-blocks 8(g>>1)..8(g>>1)+7
+  float dsc;     // d / 256
+  __device__ __forceinline__ void build(const Q2KPart &r, int g) {
+    const int p = g & 1;
+    const uint32_t a0 = r.s0 >> (8 * p), a1 = r.s1 >> (8 * p);
+    uint32_t tab[4];
+    tab[0] = mul_u24(a0 & 15u, 0x03020100u >> 8) << 8;
+    tab[1] = mul_u24((a0 >> 16) & 15u, 0x03020100u >> 8) << 8;
+    tab[2] = mul_u24(a1 & 15u, 0x03020100u >> 8) << 8;
+    tab[3] = mul_u24((a1 >> 16) & 15u, 0x03020100u >> 8) << 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = r.q[j];
+      b[j].x = (int)__builtin_amdgcn_perm(0u, tab[0], w & 0x03030303u);
+      b[j].y = (int)__builtin_amdgcn_perm(0u, tab[1], (w >> 2) & 0x03030303u);
+      b[j].z = (int)__builtin_amdgcn_perm(0u, tab[2], (w >> 4) & 0x03030303u);
+      b[j].w = (int)__builtin_amdgcn_perm(0u, tab[3], (w >> 6) & 0x03030303u);
+    }
+    const float nd = -f16hi(r.dd);
+    const uint32_t m0 = (r.s0 >> 4) & 0x0F0F0F0Fu, m1 = (r.s1 >> 4) & 0x0F0F0F0Fu;
+    const u32x4 pk = {pack_bf16x2(nd * ub0(m0), nd * ub1(m0)), pack_bf16x2(nd * ub2(m0), nd * ub3(m0)),
+                      pack_bf16x2(nd * ub0(m1), nd * ub1(m1)), pack_bf16x2(nd * ub2(m1), nd * ub3(m1))};
+    bmin = __builtin_bit_cast(bf16x8, pk);
+    dsc = f16lo(r.dd) * (1.0f / 256.0f);
+  }
+};
+
+// One workgroup per activation row, one thread per 16-value sub-block.
+// F32IN: the row is x * inv_rms (or x) rounded to bf16 first, as on the
+// bf16 path; otherwise the row is bf16 bits.  Output per (row, block):
+// digits [digit][chunk c = 4j + g][dword k][byte] with byte i of dword k of
+// chunk 4j+g the value 128(g>>1) + 32k + 16(g&1) + 4j + i (the B order
+// above), hi/lo sums [2][16] bf16, and sigma per row.
+template <bool F32IN>
+__global__ __launch_bounds__(256) void prep_i8_kernel(const void *__restrict__ src,
+                                                      const float *__restrict__ inv_rms, int K,
+                                                      uint8_t *__restrict__ aq,
+                                                      uint16_t *__restrict__ ax,
+                                                      float *__restrict__ asig) {
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nsub = K >> 4, nb = K >> 8;
+  __shared__ float red[4];
+  float v[16];
+  float m = 0.f;
+  const bool act = t < nsub;
+  if (act) {
+    if constexpr (F32IN) {
+      const float s = inv_rms ? inv_rms[row] : 1.0f;
+      const float4 *x = reinterpret_cast<const float4 *>(static_cast<const float *>(src) + row * K + 16 * t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = x[i];
+        v[4 * i] = bf16_to_f32(bf16_rne_bits(f.x * s));
+        v[4 * i + 1] = bf16_to_f32(bf16_rne_bits(f.y * s));
+        v[4 * i + 2] = bf16_to_f32(bf16_rne_bits(f.z * s));
+        v[4 * i + 3] = bf16_to_f32(bf16_rne_bits(f.w * s));
+      }
+    } else {
+      const u32x4 *x = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(src) + row * K + 16 * t);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x4 u = x[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[8 * i + 2 * c] = bf16_to_f32(u[c] & 0xFFFFu);
+          v[8 * i + 2 * c + 1] = bf16_to_f32(u[c] >> 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = mx > 0.f ? 127.0f / mx : 0.0f;
+  if (t == 0) asig[row] = mx * (1.0f / 127.0f);
+  if (!act) return;
+  const int b = t >> 4, s = t & 15;
+  const int g = 2 * (s >> 3) + (s & 1), k = (s >> 1) & 3;
+  uint32_t *qb = reinterpret_cast<uint32_t *>(aq + (row * nb + b) * QROW);
+  const float scale = inv * 256.0f;
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // N + 32896 = 256 * (a0 + 128) + (a1 + 128), positive for |N| <= 32512
+    uint32_t n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sum += v[4 * j + i];
+      n[i] = (uint32_t)(int)fmaf(v[4 * j + i], scale, 32896.5f);
+    }
+    const uint32_t p01 = __builtin_amdgcn_perm(n[1], n[0], 0x05010400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(n[3], n[2], 0x05010400u);
+    const int off = (4 * j + g) * 4 + k;
+    qb[off] = __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u;       // a0
+    qb[64 + off] = __builtin_amdgcn_perm(p23, p01, 0x05040100u) ^ 0x80808080u;  // a1
+  }
+  const float xs = sum * inv;
+  const uint32_t hi = bf16_rne_bits(xs);
+  const uint32_t lo = bf16_rne_bits(xs - bf16_to_f32(hi));
+  uint16_t *xr = ax + (row * nb + b) * (XROW / 2);
+  xr[s] = (uint16_t)hi;
+  xr[16 + s] = (uint16_t)lo;
+}
+
+// Work item -> (m-tile, n-tile).  The live items (n_tiles * n_ntiles, known
+// on the device only) are cut into 8 contiguous ranges, one per XCD
+// (workgroup i runs on XCD i % 8), so every XCD gets work and the n-tiles of
+// one m-tile share that XCD's L2.  Returns false for an idle workgroup.
+__device__ __forceinline__ bool tile_of(int n_live_m, int n_ntiles, int *mtile, int *ntile) {
+  const int live = n_live_m * n_ntiles;
+  const int per = (live + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per + slot;
+  if (slot >= per || logical >= live) return false;
+  *mtile = logical / n_ntiles;
+  *ntile = logical % n_ntiles;
+  return true;
+}
+
+__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// Per-wave state of one work item (set up once, shared by every block).
+struct ItemCtx {
+  const uint8_t *abase;         // uniform: digit rows of the tile's first row (or row 0)
+  const uint8_t *xbase;         // uniform: sums of the same row
+  uint32_t aoffs[NDMA_A];       // lane's byte offsets from abase for the wave's A loads
+  uint32_t xoffs;               // lane's byte offset from xbase for the wave's X load
+  const uint8_t *brow[2];       // weight rows of the two n-subtiles (lane's row)
+  int aoff[4];                  // LDS offsets of the lane's A chunks, K-tiles 0..3
+  int xoff;                     // LDS offset of the lane's min-term chunk
+  int nb, w, g;                 // w wave-uniform
+};
+
+// The block loop for NP live 16-token groups (tokens >= 16*NP are absent):
+// acc[ip][t] += the products of blocks 0..nb-1, all branches uniform and
+// known at compile time inside a block.
+template <int NP>
+__device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint8_t *As1, uint8_t *Xs0,
+                                           uint8_t *Xs1, f32x4 (&acc)[NPAIR][2]) {
+  const int w = cx.w, g = cx.g, nb = cx.nb;
+  auto issue = [&](int kb, uint8_t *As, uint8_t *Xs) {
+    const uint8_t *ab = cx.abase + (int64_t)kb * QROW;
+#pragma unroll
+    for (int u = 0; u < NDMA_A; ++u)
+      if (NDMA_A * w + u < 8 * NP) dma16(ab + cx.aoffs[u], As + (NDMA_A * w + u) * 1024);
+    if (w < NP) dma16(cx.xbase + (int64_t)kb * XROW + cx.xoffs, Xs + w * 1024);
+  };
+  Q2KPart r[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t], g);
+  issue(0, As0, Xs0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  auto step = [&](int kb, const uint8_t *As, const uint8_t *Xs, uint8_t *An, uint8_t *Xn) {
+    WOps wo[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) wo[t].build(r[t], g);
+    if (kb + 1 < nb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t] + (int64_t)(kb + 1) * BB_Q2K, g);
+      issue(kb + 1, An, Xn);
+    }
+    // A fragments of row group i come from As + i*4096 + aoff[j]; the
+    // next group's reads are issued before this group's MFMAs
+    const uint8_t *ap[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ap[j] = As + cx.aoff[j];
+    const uint8_t *xp = Xs + cx.xoff;
+    i32x4 a[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const i32x4 *>(ap[j]);
+#pragma unroll
+    for (int ip = 0; ip < NP; ++ip) {
+      const bf16x8 xa = *reinterpret_cast<const bf16x8 *>(xp + ip * 16 * XROW);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = 2 * ip + h;
+        if (i + 1 < 2 * NP) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            a[(i + 1) & 1][j] = *reinterpret_cast<const i32x4 *>(ap[j] + (i + 1) * 4096);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][0], wo[t].b[0], (i32x4){0, 0, 0, 0}, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][1], wo[t].b[1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][2], wo[t].b[2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][3], wo[t].b[3], c, 0, 0, 0);
+          acc[ip][t][2 * h] = fmaf(wo[t].dsc, (float)((c.x << 8) + c.y), acc[ip][t][2 * h]);
+          acc[ip][t][2 * h + 1] = fmaf(wo[t].dsc, (float)((c.z << 8) + c.w), acc[ip][t][2 * h + 1]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[ip][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wo[t].bmin, acc[ip][t], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next block's weights and tiles landed
+    __syncthreads();
+  };
+
+  for (int kb = 0; kb < nb; kb += 2) {
+    step(kb, As0, Xs0, As1, Xs1);
+    if (kb + 1 < nb) step(kb + 1, As1, Xs1, As0, Xs0);
+  }
+}
+
+// SWIGLU: an n-tile is 128 rows of F; wave w owns rows 16w..16w+15 of both
+// gate (t = 0) and up (t = 1).  Otherwise an n-tile is 256 down rows, wave w
+// owning rows 32w + 16t .. +15.  Eight waves; m-tile = TMI sorted pairs of
+// one expert.
+template <bool SWIGLU>
+__global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
+    const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
+    const uint8_t *__restrict__ aq, const uint16_t *__restrict__ ax, const float *__restrict__ asig,
+    int gather_tokens, int kslots, RouteBufs rb, int n_ntiles, uint16_t *__restrict__ hb,
+    float *__restrict__ o) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[ASTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[ASTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t Xs0[XSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t Xs1[XSTAGE];
+  __shared__ int arow[TMI];
+
+  int mtile, ntile;
+  if (!tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];
+  const int end = rb.offsets[e + 1];
+  const int valid = end - start < TMI ? end - start : TMI;
+  const int np = (valid + 15) >> 4;  // live 16-token groups
+
+  if (tid < TMI) {
+    const int m = tid < valid ? tid : 0;  // absent rows repeat row 0; never stored
+    arow[tid] = gather_tokens ? rb.pairs[start + m] / kslots : start + m;
+  }
+  __syncthreads();
+
+  ItemCtx cx;
+  cx.nb = K >> 8;
+  cx.w = __builtin_amdgcn_readfirstlane(w);
+  cx.g = g;
+  // A load u of wave w covers digit rows 4I..4I+3 (tokens 2I, 2I+1),
+  // I = NDMA_A*w + u; lane -> row 4I + lane/16, stored chunk lane%16 = data
+  // chunk (lane%16) ^ (row%16).  X load of wave w: tokens 16w + lane/4.
+  // Offsets are relative to row 0 (gathered token rows: < 2^29 bytes) or to
+  // the tile's first sorted row.
+  const int64_t rowq = (int64_t)cx.nb * QROW, rowx = (int64_t)cx.nb * XROW;
+  const int rbase = gather_tokens ? 0 : start;
+  cx.abase = aq + rbase * rowq;
+  cx.xbase = reinterpret_cast<const uint8_t *>(ax) + rbase * rowx;
+#pragma unroll
+  for (int u = 0; u < NDMA_A; ++u) {
+    const int I = NDMA_A * w + u;
+    const int r = 4 * I + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    cx.aoffs[u] = (uint32_t)((arow[r >> 1] - rbase) * rowq) + (r & 1) * 256 + c * 16;
+  }
+  cx.xoffs = (uint32_t)((arow[(16 * w + (lane >> 2)) % TMI] - rbase) * rowx) + (lane & 3) * 16;
+  const int64_t rbytes = (int64_t)cx.nb * BB_Q2K;
+  int wrow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if constexpr (SWIGLU) {
+      wrow[t] = ntile * 128 + 16 * w + n;
+      cx.brow[t] = (t == 0 ? W0 : W1) + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
+    } else {
+      wrow[t] = ntile * 256 + 32 * w + 16 * t + n;
+      cx.brow[t] = W0 + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
+    }
+  }
+  // LDS read offsets: digit row 16i + n, data chunk 4j + g (stored at
+  // (4j + g) ^ n); min-term row n of group ip = token
+  // 16ip + 8((n&3)>>1) + 2(n>>2) + (n&1), chunk g = (half g&1, sub-blocks
+  // 8(g>>1)..+7)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cx.aoff[j] = n * 256 + (((4 * j + g) ^ n) << 4);
+  cx.xoff = (8 * ((n & 3) >> 1) + 2 * (n >> 2) + (n & 1)) * XROW + (g & 1) * 32 + (g >> 1) * 16;
+
+  f32x4 acc[NPAIR][2];
+#pragma unroll
+  for (int ip = 0; ip < NPAIR; ++ip)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[ip][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  static_assert(NPAIR == 6, "block_loop dispatch covers 1..6 groups");
+  switch (np) {
+    case 1: block_loop<1>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 2: block_loop<2>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 3: block_loop<3>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 4: block_loop<4>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 5: block_loop<5>(cx, As0, As1, Xs0, Xs1, acc); break;
+    default: block_loop<6>(cx, As0, As1, Xs0, Xs1, acc); break;
+  }
+
+  // epilogue: lane (g, n) holds, for group ip, rows q = 0..3 = tokens
+  // 16ip + 8(q>>1) + 2g + (q&1) of weight row n of each n-subtile t
+#pragma unroll
+  for (int ip = 0; ip < NPAIR; ++ip) {
+    if (ip >= np) break;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = 16 * ip + 8 * (q >> 1) + 2 * g + (q & 1);
+      if (m >= valid) continue;
+      const float sg = asig[arow[m]];
+      const int64_t pos = start + m;
+      const float v0 = acc[ip][0][q] * sg, v1 = acc[ip][1][q] * sg;
+      if constexpr (SWIGLU) {
+        hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
+      } else {
+        o[pos * rows_per_expert + wrow[0]] = v0;
+        o[pos * rows_per_expert + wrow[1]] = v1;
+      }
+    }
+  }
+}
+
+unsigned grid_of(int max_tiles, int n_ntiles) {
+  const int64_t total = (int64_t)max_tiles * n_ntiles;
+  return (unsigned)((total + 7) / 8 * 8);
+}
+
+}  // namespace
+
+size_t prep_i8_bytes(int64_t rows, int K) {
+  const size_t nb = (size_t)K / 256;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  return up((size_t)rows * nb * QROW) + up((size_t)rows * nb * XROW) + up((size_t)rows * 4);
+}
+
+PrepI8 prep_i8_view(void *base, int64_t rows, int K) {
+  const size_t nb = (size_t)K / 256;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  PrepI8 p;
+  uint8_t *b = static_cast<uint8_t *>(base);
+  p.q = b;
+  p.x = reinterpret_cast<uint16_t *>(b + up((size_t)rows * nb * QROW));
+  p.sig = reinterpret_cast<float *>(b + up((size_t)rows * nb * QROW) + up((size_t)rows * nb * XROW));
+  return p;
+}
+
+hipError_t launch_prep_i8(const void *src, bool f32in, const float *inv_rms, int64_t rows, int K,
+                          const PrepI8 &p, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (f32in)
+    hipLaunchKernelGGL((prep_i8_kernel<true>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms, K,
+                       p.q, p.x, p.sig);
+  else
+    hipLaunchKernelGGL((prep_i8_kernel<false>), dim3((unsigned)rows), dim3(256), 0, s, src, nullptr, K,
+                       p.q, p.x, p.sig);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                    int max_tiles, uint16_t *hb, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nn = m.F / 128;
+  hipLaunchKernelGGL((prefill_i8_kernel<true>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.gate,
+                     m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, hb, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                  int max_tiles, float *o, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nn = m.D / 256;
+  hipLaunchKernelGGL((prefill_i8_kernel<false>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.down,
+                     nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, o);
+  return hipGetLastError();
+}
+
+}  // namespace ds4q
