@@ -64,6 +64,22 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Grouped-GEMM work item -> (m-tile, n-tile).  The live items
+// (n_live_m * n_ntiles; the m-tile count is known on the device only) are
+// cut into 8 contiguous ranges, one per XCD (workgroup i runs on XCD i % 8),
+// so every XCD gets work and the n-tiles of one m-tile share that XCD's L2.
+// Returns false for a workgroup without work.
+__device__ __forceinline__ bool xcd_tile_of(int n_live_m, int n_ntiles, int *mtile, int *ntile) {
+  const int live = n_live_m * n_ntiles;
+  const int per = (live + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per + slot;
+  if (slot >= per || logical >= live) return false;
+  *mtile = logical / n_ntiles;
+  *ntile = logical % n_ntiles;
+  return true;
+}
+
 // ---------------------------------------------------------------- routing
 
 // Order-preserving uint32 of an fp32 value, with -0.0 folded onto +0.0 so

@@ -132,12 +132,8 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t As[TM * LDA];
   __shared__ int arow[TM];
 
-  // XCD-aware order: consecutive logical work items (the n-tiles of one
-  // m-tile) land on the same XCD, whose L2 then serves the shared A rows.
-  const int total = gridDim.x;
-  const int logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int mtile = logical / n_ntiles, ntile = logical % n_ntiles;
-  if (mtile >= *rb.n_tiles) return;
+  int mtile, ntile;
+  if (!xcd_tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g = lane >> 4;

@@ -48,10 +48,8 @@ constexpr int NPAIR = SUBT / 2;      // min-term MFMA row groups of 16 tokens
 constexpr int QROW = 512;            // digit bytes of one row's 256-column block
 constexpr int XROW = 64;             // hi/lo sub-block sums (bf16) of one row's block
 constexpr int ASTAGE = TMI * QROW;   // LDS bytes of one stage of digit rows
-constexpr int XSTAGE = TMI * XROW;
-constexpr int NDMA_A = TMI / 16;     // 1-KiB A loads per wave per block (8 waves)
-constexpr int NDMA_X = TMI / 16;     // 1-KiB X loads per block (waves 0..NDMA_X-1)
-static_assert(TMI % 16 == 0 && NDMA_X <= 8, "m-tile must be a multiple of 16, at most 128");
+constexpr int XSTAGE = 8 * 1024;       // one 1-KiB sum-row load per wave (16 tokens)
+static_assert(TMI % 16 == 0 && TMI <= 128, "m-tile must be a multiple of 16, at most 128");
 
 // 24-bit unsigned multiply (full-rate v_mul_u32_u24; both operands < 2^24).
 __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
@@ -193,20 +191,9 @@ __global__ __launch_bounds__(256) void prep_i8_kernel(const void *__restrict__ s
   xr[16 + s] = (uint16_t)lo;
 }
 
-// Work item -> (m-tile, n-tile).  The live items (n_tiles * n_ntiles, known
-// on the device only) are cut into 8 contiguous ranges, one per XCD
-// (workgroup i runs on XCD i % 8), so every XCD gets work and the n-tiles of
-// one m-tile share that XCD's L2.  Returns false for an idle workgroup.
-__device__ __forceinline__ bool tile_of(int n_live_m, int n_ntiles, int *mtile, int *ntile) {
-  const int live = n_live_m * n_ntiles;
-  const int per = (live + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
-  const int logical = (blockIdx.x & 7) * per + slot;
-  if (slot >= per || logical >= live) return false;
-  *mtile = logical / n_ntiles;
-  *ntile = logical % n_ntiles;
-  return true;
-}
+// sched_barrier mask: ALU, MFMA and LDS instructions may be scheduled
+// across, global memory instructions may not.
+constexpr int SCHED_NOVMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200;
 
 __device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
@@ -214,46 +201,80 @@ __device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
 
 // Per-wave state of one work item (set up once, shared by every block).
 struct ItemCtx {
-  const uint8_t *abase;         // uniform: digit rows of the tile's first row (or row 0)
-  const uint8_t *xbase;         // uniform: sums of the same row
-  uint32_t aoffs[NDMA_A];       // lane's byte offsets from abase for the wave's A loads
-  uint32_t xoffs;               // lane's byte offset from xbase for the wave's X load
+  const uint8_t *abase;         // uniform: digit rows of row rbase
+  const uint8_t *xbase;         // uniform: sub-block sums of row rbase
+  const int *arow;              // LDS: source row of each of the tile's TMI tokens
+  int rbase;                    // 0 (gathered token rows) or the tile's first sorted row
   const uint8_t *brow[2];       // weight rows of the two n-subtiles (lane's row)
   int aoff[4];                  // LDS offsets of the lane's A chunks, K-tiles 0..3
   int xoff;                     // LDS offset of the lane's min-term chunk
-  int nb, w, g;                 // w wave-uniform
+  int nb, w, g, lane;           // w wave-uniform
 };
 
 // The block loop for NP live 16-token groups (tokens >= 16*NP are absent):
-// acc[ip][t] += the products of blocks 0..nb-1, all branches uniform and
-// known at compile time inside a block.
+// acc[ip][t] += the products of blocks 0..nb-1.
 template <int NP>
 __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint8_t *As1, uint8_t *Xs0,
                                            uint8_t *Xs1, f32x4 (&acc)[NPAIR][2]) {
-  const int w = cx.w, g = cx.g, nb = cx.nb;
-  auto issue = [&](int kb, uint8_t *As, uint8_t *Xs) {
-    const uint8_t *ab = cx.abase + (int64_t)kb * QROW;
+  const int w = cx.w, g = cx.g, nb = cx.nb, lane = cx.lane;
+  // Every wave issues the same requests per block, so the wait counts below
+  // are exact: NP digit-row loads (load I = 8u + w covers digit rows
+  // 4I..4I+3 = tokens 2I, 2I+1; lane -> row 4I + lane/16, stored chunk
+  // lane%16 = data chunk (lane%16) ^ (row%16)), one sum-row load (tokens
+  // 16(w % NP) + lane/4 into the wave's 1-KiB slot, so slot t/16 holds token
+  // t at byte 64t; slots >= NP hold copies nobody reads), and the raw weight
+  // bytes of its two n-subtiles.  Request offsets are relative to row rbase (gathered token
+  // rows: < 2^29 bytes).  Blocks past the end are requested again as the
+  // last block, so the loop has no branches.
+  const int64_t rowq = (int64_t)nb * QROW, rowx = (int64_t)nb * XROW;
+  uint32_t aoffs[NP];
 #pragma unroll
-    for (int u = 0; u < NDMA_A; ++u)
-      if (NDMA_A * w + u < 8 * NP) dma16(ab + cx.aoffs[u], As + (NDMA_A * w + u) * 1024);
-    if (w < NP) dma16(cx.xbase + (int64_t)kb * XROW + cx.xoffs, Xs + w * 1024);
+  for (int u = 0; u < NP; ++u) {
+    const int I = 8 * u + w;
+    const int r = 4 * I + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    aoffs[u] = (uint32_t)((cx.arow[r >> 1] - cx.rbase) * rowq) + (r & 1) * 256 + c * 16;
+  }
+  const int xtok = 16 * (w % NP) + (lane >> 2);
+  const uint32_t xoffs = (uint32_t)((cx.arow[xtok] - cx.rbase) * rowx) + (lane & 3) * 16;
+
+  auto issue_a = [&](int u, int kb, uint8_t *As) {
+    dma16(cx.abase + (int64_t)kb * QROW + aoffs[u], As + (8 * u + w) * 1024);
   };
-  Q2KPart r[2];
+  auto issue_x = [&](int kb, uint8_t *Xs) { dma16(cx.xbase + (int64_t)kb * XROW + xoffs, Xs + w * 1024); };
+  auto issue_tile = [&](int kb, uint8_t *As, uint8_t *Xs) {
+    issue_x(kb, Xs);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t], g);
-  issue(0, As0, Xs0);
+    for (int u = 0; u < NP; ++u) issue_a(u, kb, As);
+  };
+  auto issue_w = [&](int kb, Q2KPart (&r)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t] + (int64_t)kb * BB_Q2K, g);
+  };
+
+  // Weights run two blocks ahead (raw bytes of blocks kb+1 and kb+2 in
+  // flight or landed during block kb, alternating between rw[0] and rw[1]);
+  // the tile of kb+1 is requested before the weights of kb+2, so waiting
+  // until only the last NWLD requests are outstanding means the tile landed.
+  constexpr int NWLD = 6;  // weight load instructions per block: 2 x (16 + 8 + 4 bytes)
+  Q2KPart rw[2][2];
+  issue_tile(0, As0, Xs0);
+  issue_w(0, rw[0]);
+  issue_w(nb > 1 ? 1 : 0, rw[1]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  auto step = [&](int kb, const uint8_t *As, const uint8_t *Xs, uint8_t *An, uint8_t *Xn) {
+  auto step = [&](int kb, Q2KPart (&r)[2], const uint8_t *As, const uint8_t *Xs, uint8_t *An,
+                  uint8_t *Xn) {
     WOps wo[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) wo[t].build(r[t], g);
-    if (kb + 1 < nb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t] + (int64_t)(kb + 1) * BB_Q2K, g);
-      issue(kb + 1, An, Xn);
-    }
+    // requests for later blocks, in this order: the sum rows and digit-row
+    // load 0 before row group 0, digit-row load u before group u, and the
+    // weights right after the last one.  SCHED_NOVMEM lets computation and
+    // LDS accesses move across these points but no global request.
+    const int kn = kb + 1 < nb ? kb + 1 : nb - 1, kw = kb + 2 < nb ? kb + 2 : nb - 1;
+    issue_x(kn, Xn);
     // A fragments of row group i come from As + i*4096 + aoff[j]; the
     // next group's reads are issued before this group's MFMAs
     const uint8_t *ap[4];
@@ -265,6 +286,13 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
     for (int j = 0; j < 4; ++j) a[0][j] = *reinterpret_cast<const i32x4 *>(ap[j]);
 #pragma unroll
     for (int ip = 0; ip < NP; ++ip) {
+      __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);
+      issue_a(ip, kn, An);
+      if (ip == NP - 1) {
+        __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);
+        issue_w(kw, r);
+      }
+      __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);
       const bf16x8 xa = *reinterpret_cast<const bf16x8 *>(xp + ip * 16 * XROW);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -288,14 +316,30 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
       for (int t = 0; t < 2; ++t)
         acc[ip][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wo[t].bmin, acc[ip][t], 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next block's weights and tiles landed
-    __syncthreads();
+    // Each wave waits for its own tile requests and LDS reads; then the
+    // barrier alone publishes the tile (a workgroup fence would also wait
+    // for the weight requests still in flight).  The scheduling barriers
+    // keep the next block's operand build (which needs those weights) below
+    // this point; the empty asm statements keep memory accesses in place.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | NWLD);  // vmcnt(NWLD) lgkmcnt(0): tile of kb+1 landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  for (int kb = 0; kb < nb; kb += 2) {
-    step(kb, As0, Xs0, As1, Xs1);
-    if (kb + 1 < nb) step(kb + 1, As1, Xs1, As0, Xs0);
+  // nb is a power of two; the loop body is exactly two blocks, so every path
+  // into a block leaves the same requests outstanding
+  if (nb == 1) {
+    step(0, rw[0], As0, Xs0, As1, Xs1);
+  } else {
+    for (int kb = 0; kb < nb; kb += 2) {
+      step(kb, rw[0], As0, Xs0, As1, Xs1);
+      step(kb + 1, rw[1], As1, Xs1, As0, Xs0);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no request outlives the loop
 }
 
 // SWIGLU: an n-tile is 128 rows of F; wave w owns rows 16w..16w+15 of both
@@ -315,7 +359,7 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
   __shared__ int arow[TMI];
 
   int mtile, ntile;
-  if (!tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;
+  if (!xcd_tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -334,23 +378,11 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
   cx.nb = K >> 8;
   cx.w = __builtin_amdgcn_readfirstlane(w);
   cx.g = g;
-  // A load u of wave w covers digit rows 4I..4I+3 (tokens 2I, 2I+1),
-  // I = NDMA_A*w + u; lane -> row 4I + lane/16, stored chunk lane%16 = data
-  // chunk (lane%16) ^ (row%16).  X load of wave w: tokens 16w + lane/4.
-  // Offsets are relative to row 0 (gathered token rows: < 2^29 bytes) or to
-  // the tile's first sorted row.
-  const int64_t rowq = (int64_t)cx.nb * QROW, rowx = (int64_t)cx.nb * XROW;
-  const int rbase = gather_tokens ? 0 : start;
-  cx.abase = aq + rbase * rowq;
-  cx.xbase = reinterpret_cast<const uint8_t *>(ax) + rbase * rowx;
-#pragma unroll
-  for (int u = 0; u < NDMA_A; ++u) {
-    const int I = NDMA_A * w + u;
-    const int r = 4 * I + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    cx.aoffs[u] = (uint32_t)((arow[r >> 1] - rbase) * rowq) + (r & 1) * 256 + c * 16;
-  }
-  cx.xoffs = (uint32_t)((arow[(16 * w + (lane >> 2)) % TMI] - rbase) * rowx) + (lane & 3) * 16;
+  cx.lane = lane;
+  cx.arow = arow;
+  cx.rbase = gather_tokens ? 0 : start;
+  cx.abase = aq + (int64_t)cx.rbase * cx.nb * QROW;
+  cx.xbase = reinterpret_cast<const uint8_t *>(ax) + (int64_t)cx.rbase * cx.nb * XROW;
   const int64_t rbytes = (int64_t)cx.nb * BB_Q2K;
   int wrow[2];
 #pragma unroll
