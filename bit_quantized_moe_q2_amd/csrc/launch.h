@@ -59,7 +59,7 @@ hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *l
 hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
                           float *y, bool accumulate, hipStream_t s);
 
-// Prefill path.
+// Prefill path on Q4_1 weights (bf16 matrix cores).
 hipError_t launch_prep_bf16(const float *x, const float *inv_rms, int T, int D, uint16_t *xb,
                             hipStream_t s);
 hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, const RouteBufs &rb,

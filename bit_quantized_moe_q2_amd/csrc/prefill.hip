@@ -1,8 +1,9 @@
-// Prefill path: grouped GEMMs over experts on gfx950 bf16 matrix cores.
+// Prefill path on Q4_1 weights: grouped GEMMs over experts on gfx950 bf16
+// matrix cores.  (Q2_K weights take the int8 path in prefill_i8.hip.)
 //
 // The pairs (token, slot) are grouped by expert (route.hip); the m-tile list
-// holds up to 128 consecutive sorted pairs of one expert.  For one work item
-// (m-tile, n-tile):
+// holds up to PREFILL_TILE_M consecutive sorted pairs of one expert.  For one
+// work item (m-tile, n-tile):
 //   GEMM-1: A = the tile's token rows of x (bf16, gathered), B = gate and up
 //           rows of the expert, C = A * B^T in fp32; epilogue h = silu(g) * u
 //           rounded to bf16, stored per sorted pair position.
@@ -12,14 +13,12 @@
 // ("【#2】ds4.c 해독하기": w1 = gate, w3 = up, w2 = down, SwiGLU, and the
 // routing weight multiplies the routed SwiGLU row before the down projection.)
 //
-// Data movement.  The A tile (128 rows x 256 K, bf16) is staged in LDS once per
-// K step and read by all four waves.  B never touches LDS: each lane
-// dequantises exactly the 8 weights its MFMA B operand holds — 8 consecutive K
-// of one weight row, which in a Q2_K block are 8 consecutive code bytes at one
-// bit pair, sharing one scale/min byte; in a Q4_1 block 8 nibbles of one half
-// — straight from global memory into registers (fp32 fma, one rounding, then
-// round-to-nearest-even bf16).  Each weight of the expert's n-tile is
-// dequantised once per m-tile.
+// Data movement.  The A tile (m-tile rows x 256 K, bf16) is staged in LDS once
+// per K step and read by all four waves.  B never touches LDS: each lane
+// dequantises exactly the 8 weights its MFMA B operand holds — 8 nibbles of
+// one half of a Q4_1 block — straight from global memory into registers (fp32
+// fma, one rounding, then round-to-nearest-even bf16).  Each weight of the
+// expert's n-tile is dequantised once per m-tile.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8*(l/16) .. +7],
 // B lane l holds B[8*(l/16) .. +7][l%16] (the same K slots as A),
@@ -50,65 +49,14 @@ __device__ __forceinline__ bf16x8 to_frag(uint32_t a, uint32_t b, uint32_t c, ui
   return __builtin_bit_cast(bf16x8, (u32x4){a, b, c, d});
 }
 
-// Raw bytes of one weight row's K step (one Q2_K block, or eight Q4_1 blocks)
-// that lane group g needs.
-template <int TYPE>
-struct RowStep;
-
-template <>
-struct RowStep<TYPE_Q2_K> {
-  // Lane group g covers sub-blocks 4g..4g+3 (values 64g..64g+63) of the
-  // block; MFMA step J takes values 64g + 8P + i with P = (J>>1) + 4(J&1):
-  // code bytes 16 + 32(g>>1) + 8(P&3) + i at bit pair (2g + (P>>2)) & 3,
-  // sub-block 4g + (P>>1).  (This order retires each pair of code dwords
-  // after two steps and keeps two sub-block tables live.)  A sub-block has
-  // four possible weights: they are computed once (fp32 fma, one rounding,
-  // then bf16 round-to-nearest-even) into a byte table, and each pair of bf16
-  // outputs is two v_perm lookups.
-  uint32_t q[8], scm, dd;
-  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
-    const uint8_t *qs = blk + 16 + 32 * (g >> 1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = ld32(qs + 4 * i);
-    scm = ld32(blk + 4 * g);
-    dd = ld32(blk + 80);
-  }
-  // bf16 table [v0 v1 | v2 v3] (low dword, high dword) of sub-block 4g + c.
-  __device__ __forceinline__ void table(int c, uint32_t &t01, uint32_t &t23) const {
-    const uint32_t sb = (scm >> (8 * c)) & 0xFFu;
-    const float ds = f16lo(dd) * (float)(sb & 15u);
-    const float dm = -(f16hi(dd) * (float)(sb >> 4));
-    t01 = pack_bf16(dm, fmaf(ds, 1.0f, dm));
-    t23 = pack_bf16(fmaf(ds, 2.0f, dm), fmaf(ds, 3.0f, dm));
-  }
-  // Two bf16 weights for codes in bytes b, b+1 of x (b = 0 or 2).
-  template <int B>
-  __device__ __forceinline__ static uint32_t look(uint32_t x, uint32_t t01, uint32_t t23) {
-    constexpr uint32_t spread = B == 0 ? 0x01010000u : 0x03030202u;
-    const uint32_t sel = (__builtin_amdgcn_perm(x, x, spread) << 1) + 0x01000100u;
-    return __builtin_amdgcn_perm(t23, t01, sel);
-  }
-  static constexpr int step_p(int J) { return (J >> 1) + 4 * (J & 1); }
-  template <int J>
-  __device__ __forceinline__ bf16x8 frag(int g, uint32_t t01, uint32_t t23) const {
-    constexpr int P = step_p(J);
-    const int sh = 2 * ((2 * g + (P >> 2)) & 3);
-    const uint32_t x0 = (q[2 * (P & 3)] >> sh) & 0x03030303u;
-    const uint32_t x1 = (q[2 * (P & 3) + 1] >> sh) & 0x03030303u;
-    return to_frag(look<0>(x0, t01, t23), look<2>(x0, t01, t23), look<0>(x1, t01, t23),
-                   look<2>(x1, t01, t23));
-  }
-};
-
-template <>
-struct RowStep<TYPE_Q4_1> {
+// Raw bytes of one weight row's K step (eight Q4_1 blocks) that lane group g
+// needs: MFMA step j = Q4_1 block j of the K step, values 8g + i, i.e.
+// nibbles of qs[8(g&1) + i], low for g < 2, high for g >= 2.
+struct Q41Step {
   const uint8_t *base;
-  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int) { base = blk; }
-  // MFMA step j = Q4_1 block j of the K step: values 8g + i, i.e. nibbles of
-  // qs[8(g&1) + i], low for g < 2, high for g >= 2.
-  __device__ __forceinline__ void table(int, uint32_t &t01, uint32_t &t23) const { t01 = t23 = 0u; }
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk) { base = blk; }
   template <int J>
-  __device__ __forceinline__ bf16x8 frag(int g, uint32_t, uint32_t) const {
+  __device__ __forceinline__ bf16x8 frag(int g) const {
     const uint8_t *blk = base + J * BB_Q41;
     const uint32_t dm = ld32(blk);
     const int sh = 4 * (g >> 1);
@@ -124,7 +72,7 @@ struct RowStep<TYPE_Q4_1> {
 
 // SWIGLU: n-tile = 128 rows of F for gate and up (wave w: rows 32w..32w+31 of
 // both); otherwise n-tile = 256 down rows (wave w: rows 64w..64w+63).
-template <int TYPE, bool SWIGLU>
+template <bool SWIGLU>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint16_t *__restrict__ A, int gather_tokens, int kslots, RouteBufs rb, int n_ntiles,
@@ -148,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     arow[tid] = src;
   }
 
-  const int64_t rbytes = row_bytes(TYPE, K);
+  const int64_t rbytes = row_bytes(TYPE_Q4_1, K);
   const uint8_t *brow[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -170,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int step_bytes = (int)row_bytes(TYPE, KS);
+  const int step_bytes = (int)row_bytes(TYPE_Q4_1, KS);
   for (int kb = 0; kb < K / KS; ++kb) {
     __syncthreads();
     // stage A: 128 rows x 256 bf16 = 32 chunks of 16 B per row, four chunks
@@ -195,30 +143,22 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     }
     __syncthreads();
 
-    RowStep<TYPE> rs[4];
+    Q41Step rs[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) rs[t].load(brow[t] + (int64_t)kb * step_bytes, g);
+    for (int t = 0; t < 4; ++t) rs[t].load(brow[t] + (int64_t)kb * step_bytes);
 
     // K order inside the step: MFMA step J, lane group g takes the step's
-    // values A_KOFF(J, g) .. +7 (the same for A and B).
-    // (Q2_K: steps 4c..4c+3 use sub-block tables c and c + 2.)
-    uint32_t tab[4][2][2];
+    // values 32J + 8g .. +7 (the same for A and B).
 #define DS4Q_STEP(J)                                                                   \
   {                                                                                    \
-    if ((J) % 4 == 0 && TYPE == TYPE_Q2_K)                                             \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                  \
-        rs[t].table((J) >> 2, tab[t][0][0], tab[t][0][1]);                             \
-        rs[t].table(((J) >> 2) + 2, tab[t][1][0], tab[t][1][1]);                       \
-      }                                                                                \
     /* A fragments first (rows of absent pairs hold zeros), so that their    */ \
     /* LDS latency hides behind the weight dequantisation                    */ \
-    const int koff = TYPE == TYPE_Q2_K ? 64 * g + 8 * RowStep<TYPE_Q2_K>::step_p(J) : 32 * (J) + 8 * g; \
+    const int koff = 32 * (J) + 8 * g;                                                 \
     bf16x8 a[MT];                                                                      \
     _Pragma("unroll") for (int i = 0; i < MT; ++i)                                     \
         a[i] = *reinterpret_cast<const bf16x8 *>(&As[(16 * i + n) * LDA + koff]);      \
     bf16x8 b[4];                                                                       \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                      \
-        b[t] = rs[t].template frag<J>(g, tab[t][(J) & 1][0], tab[t][(J) & 1][1]);       \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) b[t] = rs[t].template frag<J>(g);    \
     _Pragma("unroll") for (int i = 0; i < MT; ++i) {                                   \
       if (i < n_mt) {                                                                  \
         _Pragma("unroll") for (int t = 0; t < 4; ++t)                                  \
@@ -292,12 +232,8 @@ hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, co
   if (T == 0) return hipSuccess;
   const int nn = m.F / 128;
   const dim3 grid(grid_for(max_tiles, nn));
-  if (m.tg == TYPE_Q2_K)
-    hipLaunchKernelGGL((prefill_gemm_kernel<TYPE_Q2_K, true>), grid, dim3(256), 0, s, m.gate, m.up,
-                       m.D, m.F, xb, 1, m.k, rb, nn, hb, nullptr);
-  else
-    hipLaunchKernelGGL((prefill_gemm_kernel<TYPE_Q4_1, true>), grid, dim3(256), 0, s, m.gate, m.up,
-                       m.D, m.F, xb, 1, m.k, rb, nn, hb, nullptr);
+  hipLaunchKernelGGL((prefill_gemm_kernel<true>), grid, dim3(256), 0, s, m.gate, m.up, m.D, m.F, xb,
+                     1, m.k, rb, nn, hb, nullptr);
   return hipGetLastError();
 }
 
@@ -306,12 +242,8 @@ hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, cons
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
   const dim3 grid(grid_for(max_tiles, nn));
-  if (m.td == TYPE_Q2_K)
-    hipLaunchKernelGGL((prefill_gemm_kernel<TYPE_Q2_K, false>), grid, dim3(256), 0, s, m.down,
-                       nullptr, m.F, m.D, hb, 0, m.k, rb, nn, nullptr, o);
-  else
-    hipLaunchKernelGGL((prefill_gemm_kernel<TYPE_Q4_1, false>), grid, dim3(256), 0, s, m.down,
-                       nullptr, m.F, m.D, hb, 0, m.k, rb, nn, nullptr, o);
+  hipLaunchKernelGGL((prefill_gemm_kernel<false>), grid, dim3(256), 0, s, m.down, nullptr, m.F, m.D,
+                     hb, 0, m.k, rb, nn, nullptr, o);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-"""GPU parity of the prefill path (bf16 MFMA grouped GEMMs) through the C ABI
-against the oracle: max relative error <= 1e-2 — per token row (max |err| /
+"""GPU parity of the prefill path (grouped GEMMs: int8 MFMA on Q2_K weights,
+bf16 MFMA on Q4_1 weights) through the C ABI against the oracle: max relative error <= 1e-2 — per token row (max |err| /
 max |ref| of the row) at the DeepSeek-V4-Flash expert shape, tensor-wide at
 the smaller test shapes (see helpers.normwise_err_tensor); routing ids and
 grouping bit-exact."""
@@ -58,7 +58,7 @@ def _check_route(lg, k, E, got):
     assert np.array_equal(cnt, rc) and np.array_equal(off, ro) and np.array_equal(pairs, rp)
 
 
-@pytest.mark.parametrize("qt,qtd", [(10, 10), (3, 3), (10, 3)])
+@pytest.mark.parametrize("qt,qtd", [(10, 10), (3, 3), (10, 3), (3, 10)])
 @pytest.mark.parametrize("T", [1, 5, 100, 300])
 def test_prefill_small(gpu, qt, qtd, T):
     ds4q = gpu
@@ -85,11 +85,13 @@ def test_prefill_skewed_multi_tile(gpu):
     assert normwise_err_tensor(y[sample], lay.oracle_moe(xf[sample], lg[sample], n_threads=16)) <= TOL_BF16
 
 
+@pytest.mark.parametrize("qt", [10, 3])
 @pytest.mark.parametrize("D,F", [(256, 4096), (4096, 256), (1024, 512)])
-def test_prefill_shapes(gpu, D, F):
+def test_prefill_shapes(gpu, qt, D, F):
+    """Edge widths: a 256-wide K is a single Q2_K block per row."""
     ds4q = gpu
-    _log(f"prefill shapes D={D} F={F}")
-    lay = SynthLayer(ds4q, DEV, D, F, 8, 2, 3, seed=620 + D)
+    _log(f"prefill shapes qt={qt} D={D} F={F}")
+    lay = SynthLayer(ds4q, DEV, D, F, 8, 2, qt, seed=620 + D)
     bits, xf = _bf16_input(synth.stream_key(34, D), 40, D)
     lg = synth.logits_normal(synth.stream_key(35, D), 40, 8)
     y, _ = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg, route=False)
