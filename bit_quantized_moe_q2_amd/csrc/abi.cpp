@@ -46,7 +46,7 @@ struct Workspace {
   float *h = nullptr;      // decode: [T*k][F] f32
   uint16_t *hb = nullptr;  // prefill: [T*k][F] bf16 (sorted order)
   float *o = nullptr;      // [T*k][D] f32
-  uint16_t *xb = nullptr;  // prefill: [T][D] bf16
+  uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
   PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
   size_t bytes = 0;
 
@@ -80,7 +80,7 @@ struct Workspace {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
       hb = (uint16_t *)take(P * F * 2);
       o = (float *)take(P * D * 4);
-      xb = (uint16_t *)take((size_t)T * D * 2);
+      if (!i8_in) xb = (uint16_t *)take((size_t)T * D * 2);
       if (i8_in) {
         void *p = take(prep_i8_bytes(T, D));
         if (base) xq = prep_i8_view(p, T, D);
