@@ -1,7 +1,9 @@
 """GPU parity of the 43-layer routed-expert stack (DeepSeek-V4-Flash depth:
 43 layers x 256 experts, top-6, 4096/2048) held resident in HBM: Q2_K
-(90.9 GB) and Q4_1 (173.1 GB), decode of one token and a 4096-token prefill
-chunk.  x <- x + MoE_l(rmsnorm(x)) per layer.
+(90.9 GB), Q4_1 (173.1 GB) and mixed (Q2_K layers 0-36, Q4_1 layers 37-42,
+the placement of the pages' mixed GGUF with the two block types built here:
+102.4 GB), decode of one token and a 4096-token prefill chunk.
+x <- x + MoE_l(rmsnorm(x)) per layer.
 
 Checks:
 * ds4q_moe_stack equals the layer-by-layer composition through
@@ -30,8 +32,17 @@ def _log(msg):
     print(msg, flush=True)
 
 
+MIXED_FIRST_Q41 = 37  # mixed stack: layers 37..42 are Q4_1
+
+
+def _qtype(qt, l):
+    if qt == "mixed":
+        return 3 if l >= MIXED_FIRST_Q41 else 10
+    return qt
+
+
 def _layers(ds4q, qt, seed):
-    return [SynthLayer(ds4q, DEV, D, F, E, K, qt, seed=seed, layer=l) for l in range(L_FLASH)]
+    return [SynthLayer(ds4q, DEV, D, F, E, K, _qtype(qt, l), seed=seed, layer=l) for l in range(L_FLASH)]
 
 
 def _free():
@@ -47,7 +58,9 @@ def _stack_case(ds4q, qt, mode, T, check_layers, seed):
     x0 = synth.x_f32(synth.stream_key(seed, 1), T, D)
     lg = np.stack([synth.logits_normal(synth.stream_key(seed, 2, l), T, E) for l in range(L_FLASH)])
     lg_d = torch.from_numpy(lg).to(DEV)
-    ws = torch.empty(ds4q.ds4q_moe_workspace_size(lays[0].L, T, mode), dtype=torch.uint8, device=DEV)
+    # the stack needs the largest of its layers' workspaces (the types differ in a mixed stack)
+    wsb = max(ds4q.ds4q_moe_workspace_size(l.L, T, mode) for l in lays)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
 
     # 1. the stack entry point
     xs = torch.from_numpy(x0).to(DEV)
@@ -83,10 +96,14 @@ def _stack_case(ds4q, qt, mode, T, check_layers, seed):
     return lays, x0, lg, x_stack, x_lbl, errs
 
 
-@pytest.mark.parametrize("qt", [10, 3])
+def _seed(base, qt):
+    return base + (qt if isinstance(qt, int) else 20)
+
+
+@pytest.mark.parametrize("qt", [10, 3, "mixed"])
 def test_stack_decode_one_token(gpu, qt):
     ds4q = gpu
-    lays, x0, lg, x_stack, x_lbl, errs = _stack_case(ds4q, qt, 0, 1, set(range(L_FLASH)), 700 + qt)
+    lays, x0, lg, x_stack, x_lbl, errs = _stack_case(ds4q, qt, 0, 1, set(range(L_FLASH)), _seed(700, qt))
     assert np.array_equal(x_stack.view(np.uint32), x_lbl.view(np.uint32))
     for l, e in errs:
         assert e <= 2e-3, (l, e)
@@ -99,10 +116,11 @@ def test_stack_decode_one_token(gpu, qt):
     _free()
 
 
-@pytest.mark.parametrize("qt", [10, 3])
+@pytest.mark.parametrize("qt", [10, 3, "mixed"])
 def test_stack_prefill_chunk(gpu, qt):
     ds4q = gpu
-    lays, x0, lg, x_stack, x_lbl, errs = _stack_case(ds4q, qt, 1, 4096, {0, 21, 42}, 800 + qt)
+    check = {0, 21, 42} if qt != "mixed" else {0, 21, MIXED_FIRST_Q41 - 1, MIXED_FIRST_Q41, 42}
+    lays, x0, lg, x_stack, x_lbl, errs = _stack_case(ds4q, qt, 1, 4096, check, _seed(800, qt))
     assert np.array_equal(x_stack.view(np.uint32), x_lbl.view(np.uint32))
     for l, e in errs:
         assert e <= 1e-2, (l, e)
