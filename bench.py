@@ -11,7 +11,8 @@ each with its own seeded router logits and activations, so weight bytes come
 from HBM.  Steps are replayed from a HIP graph that holds one step per layer.
 
 Also measured in the same run: the 4096-token prefill chunk (bf16, uniform
-routing) as a secondary figure, the dominant kernels' durations from HIP
+routing) and one token through the 43-layer stack (Q2_K, and mixed: Q2_K
+layers 0-36 with Q4_1 layers 37-42) as secondary figures, the dominant kernels' durations from HIP
 events the library records around its own launches, and the CPU oracle on a
 bounded sample of the same decode workload.
 
@@ -95,6 +96,9 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--stack-tokens", type=int, default=50,
+                    help="tokens timed through each 43-layer stack")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="decode tokens the oracle runs (about 15 s on 16 host threads)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -299,6 +303,55 @@ def main():
                          "int8_ops_per_algorithmic_op": 2},
             "kernels_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in pt.items()},
         }
+
+    # ------------------------------------------------------------ stack (secondary)
+    if not args.no_stack and NL == 43:
+        # mixed stack: the first 37 Q2_K layers above plus 6 Q4_1 layers
+        log("generating 6 layers of Q4_1 experts for the mixed stack ...")
+        q41 = []
+        for l in range(37, 43):
+            t = {}
+            for name, rows, cols in (("gate", F, D), ("up", F, D), ("down", D, F)):
+                buf = torch.empty(E * rows * cols // 32 * 20, dtype=torch.uint8, device=dev)
+                keep.append(synth.device_fill("q4_1", buf, [synth.layer_key(seed + 1, l, name, e)
+                                                             for e in range(E)], rows * cols // 32))
+                t[name] = buf
+            q41.append(ds4q.MoeLayer.from_tensors(t["gate"], t["up"], t["down"], D, F, E, K,
+                                                  ds4q.TYPE_Q4_1))
+        torch.cuda.synchronize()
+        lgs_st = torch.from_numpy(np.stack([synth.logits_normal(synth.stream_key(seed, 5, l), 1, E)
+                                            for l in range(NL)])).to(dev)
+        x_st = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 6), 1, D)).to(dev)
+        x_run = torch.empty_like(x_st)
+        result["stack_decode"] = {}
+        for name, lays in (("q2_k", layers), ("mixed", layers[:37] + q41)):
+            ws_st = torch.empty(max(ds4q.ds4q_moe_workspace_size(L, 1, 0) for L in lays),
+                                dtype=torch.uint8, device=dev)
+
+            def stack_token():
+                x_run.copy_(x_st)
+                ds4q.ds4q_moe_stack(lays, 0, x_run, lgs_st, 1, ws_st)
+
+            stack_token()
+            torch.cuda.synchronize()
+            gs = capture(stack_token)
+            gs.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(args.stack_tokens):
+                gs.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            t_ms = ev0.elapsed_time(ev1) / args.stack_tokens
+            wbytes = sum(K * (2 * F * ds4q.row_bytes(L.type_gate, D) + D * ds4q.row_bytes(L.type_down, F))
+                         for L in lays)
+            log(f"stack {name}: {t_ms * 1e3:.1f} us/token through {len(lays)} layers, "
+                f"{wbytes / (t_ms / 1e3) / 1e9:.0f} GB/s")
+            result["stack_decode"][name] = {
+                "workload": f"stack43_decode_1tok_{name}", "us_per_token": round(t_ms * 1e3, 2),
+                "tokens_per_s": round(1e3 / t_ms, 1), "weight_bytes_per_token": wbytes,
+                "hbm_gbps": round(wbytes / (t_ms / 1e3) / 1e9, 1)}
+            del gs, ws_st
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
