@@ -50,7 +50,8 @@ struct Workspace {
   PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
   size_t bytes = 0;
 
-  // i8_in / i8_h: prefill with Q2_K gate/up resp. down (int8 matrix cores)
+  // mode 1 (prefill): i8_in / i8_h = Q2_K gate/up resp. down (int8 matrix
+  // cores); mode 0 (decode): i8_in = the grouped int8 path (see i8_flags)
   Workspace(uint8_t *base, int D, int F, int E, int k, int T, int mode, bool i8_in = false,
             bool i8_h = false) {
     size_t off = 0;
@@ -76,6 +77,13 @@ struct Workspace {
     } else if (mode == 0) {
       h = (float *)take(P * F * 4);
       if (T > 1) o = (float *)take(P * D * 4);
+      if (i8_in) {  // decode of 2..64 tokens on Q2_K: the grouped int8 kernels
+        rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
+        void *p = take(prep_i8_bytes(T, D));
+        if (base) xq = prep_i8_view(p, T, D);
+        p = take(prep_i8_bytes(P, F));
+        if (base) hq = prep_i8_view(p, P, F);
+      }
     } else {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
       hb = (uint16_t *)take(P * F * 2);
@@ -112,6 +120,18 @@ int check_layer(const ds4q_moe_layer *L) {
 
 bool i8_gateup(const ds4q_moe_layer *L) { return L->type_gate == DS4Q_TYPE_Q2_K; }
 bool i8_down(const ds4q_moe_layer *L) { return L->type_down == DS4Q_TYPE_Q2_K; }
+// Decode of 2..64 tokens with Q2_K weights throughout runs on the grouped
+// int8 kernels (one token has its own kernels).
+bool i8_decode(const ds4q_moe_layer *L, int T) { return T > 1 && i8_gateup(L) && i8_down(L); }
+
+// Workspace flags of a call (see Workspace).
+struct WsFlags {
+  bool a, b;
+};
+WsFlags i8_flags(const ds4q_moe_layer *L, int T, int mode) {
+  if (mode == 1) return {i8_gateup(L), i8_down(L)};
+  return {i8_decode(L, T), false};
+}
 
 MoeDims dims_of(const ds4q_moe_layer *L) {
   MoeDims m;
@@ -220,8 +240,8 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, ALIGN) ||
       route_misaligned(route))
     return DS4Q_E_ALIGN;
-  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode,
-                       i8_gateup(L), i8_down(L));
+  const WsFlags f = i8_flags(L, T, mode);
+  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b);
   if (ws_bytes < need.bytes) return DS4Q_E_WORKSPACE;
   const size_t xb = (size_t)T * L->n_embd * x_elem, yb = (size_t)T * L->n_embd * 4;
   const size_t lb = (size_t)T * L->n_expert * 4;
@@ -245,7 +265,8 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
                const ds4q_route_out *route, void *ws, hipStream_t s, uint32_t flags,
                uint32_t phases = DS4Q_PHASE_ALL) {
   const MoeDims m = dims_of(L);
-  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0);
+  const WsFlags f = i8_flags(L, T, 0);
+  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0, f.a, f.b);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const bool p_route = phases & DS4Q_PHASE_ROUTE, p_gu = phases & DS4Q_PHASE_GATEUP,
              p_down = phases & DS4Q_PHASE_DOWN;
@@ -261,6 +282,25 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     if (p_down)
       TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 2, s));
     return p_gu ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
+  }
+  if (f.a) {
+    // 2..64 tokens on Q2_K: expert-grouped m-tiles on int8 matrix cores;
+    // h and o in sorted-pair order
+    const int mt = max_tiles(T, m.E, m.k);
+    if (p_route) {
+      TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, false, s));
+      TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
+    }
+    if (p_gu) {
+      TIMED_TRY("prep_i8", launch_prep_i8(x, true, false, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xq, s));
+      TIMED_TRY("decode_gateup", launch_decode_i8_gateup(m, w.xq, T, w.rb, mt, w.h, s));
+    }
+    if (p_down) {
+      TIMED_TRY("prep_i8", launch_prep_i8(w.h, true, false, nullptr, (int64_t)T * m.k, m.F, w.hq, s));
+      TIMED_TRY("decode_down", launch_decode_i8_down(m, w.hq, T, w.rb, mt, w.o, s));
+      TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, s));
+    }
+    return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
   if (p_route) {
     TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));
@@ -278,15 +318,16 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
                 int32_t T, float *y, const ds4q_route_out *route, void *ws, hipStream_t s,
                 uint32_t flags) {
   const MoeDims m = dims_of(L);
-  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, i8_gateup(L), i8_down(L));
+  const WsFlags f = i8_flags(L, T, 1);
+  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, f.a, f.b);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
   TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, false, s));
   TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
   const int mt = max_tiles(T, m.E, m.k);
   if (i8_gateup(L)) {
-    TIMED_TRY("prep_i8", launch_prep_i8(x, xf != nullptr, norm && xf ? w.rb.inv_rms : nullptr, T, m.D,
-                                        w.xq, s));
+    TIMED_TRY("prep_i8", launch_prep_i8(x, xf != nullptr, true, norm && xf ? w.rb.inv_rms : nullptr, T,
+                                        m.D, w.xq, s));
     TIMED_TRY("prefill_gateup", launch_prefill_i8_gateup(m, w.xq, T, w.rb, mt, w.hb, s));
   } else {
     const uint16_t *xb = static_cast<const uint16_t *>(x);
@@ -298,7 +339,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   }
   if (i8_down(L)) {
     const int64_t P = (int64_t)T * m.k;
-    TIMED_TRY("prep_i8", launch_prep_i8(w.hb, false, nullptr, P, m.F, w.hq, s));
+    TIMED_TRY("prep_i8", launch_prep_i8(w.hb, false, false, nullptr, P, m.F, w.hq, s));
     TIMED_TRY("prefill_down", launch_prefill_i8_down(m, w.hq, T, w.rb, mt, w.o, s));
   } else {
     TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.o, s));
@@ -391,9 +432,9 @@ DS4Q_API int ds4q_route(const float *logits, int32_t n_tok, int32_t n_expert, in
 
 DS4Q_API size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t mode) {
   if (check_layer(L) || max_tok < 0 || (mode != 0 && mode != 1)) return 0;
-  return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used,
-                   max_tok > 0 ? max_tok : 1, mode, i8_gateup(L), i8_down(L))
-      .bytes;
+  const int T = max_tok > 0 ? max_tok : 1;
+  const WsFlags f = i8_flags(L, T, mode);
+  return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b).bytes;
 }
 
 DS4Q_API int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits,

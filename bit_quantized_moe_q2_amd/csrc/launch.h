@@ -77,14 +77,20 @@ struct PrepI8 {
 };
 size_t prep_i8_bytes(int64_t rows, int K);
 PrepI8 prep_i8_view(void *base, int64_t rows, int K);
-// src: f32 (f32in; times inv_rms[row] when given, then rounded to bf16) or
-// bf16 rows [rows][K].
-hipError_t launch_prep_i8(const void *src, bool f32in, const float *inv_rms, int64_t rows, int K,
-                          const PrepI8 &p, hipStream_t s);
+// src: f32 (f32in; times inv_rms[row] when given, then rounded to bf16 when
+// round_bf16) or bf16 rows [rows][K].
+hipError_t launch_prep_i8(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
+                          int64_t rows, int K, const PrepI8 &p, hipStream_t s);
 hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                     int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                   int max_tiles, float *o, hipStream_t s);
+// The same grouped kernels under the decode contract (2..64 tokens, Q2_K):
+// fp32 SwiGLU rows h [T*k][F] in sorted order, min term to about 16 bits.
+hipError_t launch_decode_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                   int max_tiles, float *h, hipStream_t s);
+hipError_t launch_decode_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                 int max_tiles, float *o, hipStream_t s);
 
 constexpr int PREFILL_TILE_M = 96;
 

@@ -41,6 +41,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TMI = PREFILL_TILE_M;  // tokens (sorted pairs) per m-tile
 constexpr int SUBT = TMI / 8;        // integer MFMA row groups of 8 tokens
@@ -80,9 +81,11 @@ struct Q2KPart {
 // 128(g>>1) + 32k + 16(g&1) + 4j + c, of sub-block 8(g>>1) + 2k + (g&1);
 // K-tile j, dword k of the B fragment is that bit pair looked up in the
 // sub-block's table [0, sc, 2sc, 3sc].
+template <bool EXACT_MIN>
 struct WOps {
   i32x4 b[4];    // integer B fragments of K-tiles 0..3
-  bf16x8 bmin;   // -dmin * mn of sub-blocks 8(g>>1)..8(g>>1)+7
+  bf16x8 bmin;   // -dmin * mn of sub-blocks 8(g>>1)..8(g>>1)+7, rounded to bf16
+  s16x4 bminlo;  // EXACT_MIN: the rounding residues of sub-blocks 4g..4g+3 (bf16)
   float dsc;     // d / 256
   __device__ __forceinline__ void build(const Q2KPart &r, int g) {
     const int p = g & 1;
@@ -102,20 +105,31 @@ struct WOps {
     }
     const float nd = -f16hi(r.dd);
     const uint32_t m0 = (r.s0 >> 4) & 0x0F0F0F0Fu, m1 = (r.s1 >> 4) & 0x0F0F0F0Fu;
-    const u32x4 pk = {pack_bf16x2(nd * ub0(m0), nd * ub1(m0)), pack_bf16x2(nd * ub2(m0), nd * ub3(m0)),
-                      pack_bf16x2(nd * ub0(m1), nd * ub1(m1)), pack_bf16x2(nd * ub2(m1), nd * ub3(m1))};
+    const float v[8] = {nd * ub0(m0), nd * ub1(m0), nd * ub2(m0), nd * ub3(m0),
+                        nd * ub0(m1), nd * ub1(m1), nd * ub2(m1), nd * ub3(m1)};
+    const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
     bmin = __builtin_bit_cast(bf16x8, pk);
+    if constexpr (EXACT_MIN) {
+      // residues of the lane's sub-blocks 4g..4g+3 (= 8(g>>1) + 4(g&1) + i)
+      const int o = 4 * (g & 1);
+      const uint32_t h01 = (g & 1) ? pk.z : pk.x, h23 = (g & 1) ? pk.w : pk.y;
+      const uint32_t l01 = pack_bf16x2(v[o] - bf16_to_f32(h01 & 0xFFFFu), v[o + 1] - bf16_to_f32(h01 >> 16));
+      const uint32_t l23 = pack_bf16x2(v[o + 2] - bf16_to_f32(h23 & 0xFFFFu), v[o + 3] - bf16_to_f32(h23 >> 16));
+      bminlo = __builtin_bit_cast(s16x4, ((unsigned long long)l23 << 32) | l01);
+    }
     dsc = f16lo(r.dd) * (1.0f / 256.0f);
   }
 };
 
 // One workgroup per activation row, one thread per 16-value sub-block.
-// F32IN: the row is x * inv_rms (or x) rounded to bf16 first, as on the
-// bf16 path; otherwise the row is bf16 bits.  Output per (row, block):
+// F32IN: the row is x * inv_rms (or x), rounded to bf16 first when ROUND
+// (the prefill input contract), else taken as it is (decode: fp32 rows);
+// otherwise the row is bf16 bits.  Output per (row, block):
 // digits [digit][chunk c = 4j + g][dword k][byte] with byte i of dword k of
 // chunk 4j+g the value 128(g>>1) + 32k + 16(g&1) + 4j + i (the B order
 // above), hi/lo sums [2][16] bf16, and sigma per row.
-template <bool F32IN>
+template <bool F32IN, bool ROUND>
 __global__ __launch_bounds__(256) void prep_i8_kernel(const void *__restrict__ src,
                                                       const float *__restrict__ inv_rms, int K,
                                                       uint8_t *__restrict__ aq,
@@ -135,10 +149,10 @@ __global__ __launch_bounds__(256) void prep_i8_kernel(const void *__restrict__ s
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 f = x[i];
-        v[4 * i] = bf16_to_f32(bf16_rne_bits(f.x * s));
-        v[4 * i + 1] = bf16_to_f32(bf16_rne_bits(f.y * s));
-        v[4 * i + 2] = bf16_to_f32(bf16_rne_bits(f.z * s));
-        v[4 * i + 3] = bf16_to_f32(bf16_rne_bits(f.w * s));
+        v[4 * i] = ROUND ? bf16_to_f32(bf16_rne_bits(f.x * s)) : f.x * s;
+        v[4 * i + 1] = ROUND ? bf16_to_f32(bf16_rne_bits(f.y * s)) : f.y * s;
+        v[4 * i + 2] = ROUND ? bf16_to_f32(bf16_rne_bits(f.z * s)) : f.z * s;
+        v[4 * i + 3] = ROUND ? bf16_to_f32(bf16_rne_bits(f.w * s)) : f.w * s;
       }
     } else {
       const u32x4 *x = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(src) + row * K + 16 * t);
@@ -208,14 +222,17 @@ struct ItemCtx {
   const uint8_t *brow[2];       // weight rows of the two n-subtiles (lane's row)
   int aoff[4];                  // LDS offsets of the lane's A chunks, K-tiles 0..3
   int xoff;                     // LDS offset of the lane's min-term chunk
+  int xoff4;                    // LDS offset of the lane's hi sums of sub-blocks 4g..4g+3
   int nb, w, g, lane;           // w wave-uniform
 };
 
 // The block loop for NP live 16-token groups (tokens >= 16*NP are absent):
-// acc[ip][t] += the products of blocks 0..nb-1.
-template <int NP>
+// acc[ip][t] += the products of blocks 0..nb-1.  EXACT_MIN adds the bf16
+// residues of -dmin*mn times the hi sums (one 16x16x16 bf16 MFMA), so that
+// the min term carries about 16 bits instead of 8.
+template <int NP, int NPMAX, bool EXACT_MIN>
 __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint8_t *As1, uint8_t *Xs0,
-                                           uint8_t *Xs1, f32x4 (&acc)[NPAIR][2]) {
+                                           uint8_t *Xs1, f32x4 (&acc)[NPMAX][2]) {
   const int w = cx.w, g = cx.g, nb = cx.nb, lane = cx.lane;
   // Every wave issues the same requests per block, so the wait counts below
   // are exact: NP digit-row loads (load I = 8u + w covers digit rows
@@ -266,7 +283,7 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
 
   auto step = [&](int kb, Q2KPart (&r)[2], const uint8_t *As, const uint8_t *Xs, uint8_t *An,
                   uint8_t *Xn) {
-    WOps wo[2];
+    WOps<EXACT_MIN> wo[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) wo[t].build(r[t], g);
     // requests for later blocks, in this order: the sum rows and digit-row
@@ -315,6 +332,12 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         acc[ip][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wo[t].bmin, acc[ip][t], 0, 0, 0);
+      if constexpr (EXACT_MIN) {
+        const s16x4 xh = *reinterpret_cast<const s16x4 *>(Xs + cx.xoff4 + ip * 16 * XROW);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[ip][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, wo[t].bminlo, acc[ip][t], 0, 0, 0);
+      }
     }
     // Each wave waits for its own tile requests and LDS reads; then the
     // barrier alone publishes the tile (a workgroup fence would also wait
@@ -344,14 +367,16 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
 
 // SWIGLU: an n-tile is 128 rows of F; wave w owns rows 16w..16w+15 of both
 // gate (t = 0) and up (t = 1).  Otherwise an n-tile is 256 down rows, wave w
-// owning rows 32w + 16t .. +15.  Eight waves; m-tile = TMI sorted pairs of
-// one expert.
-template <bool SWIGLU>
+// owning rows 32w + 16t .. +15.  Eight waves; m-tile = up to TMI sorted pairs
+// of one expert, of which at most 16*NPMAX are present (the caller's bound).
+// DEC (the decode contract, at most 64 tokens): fp32 SwiGLU rows hf and the
+// exact min term; otherwise bf16 SwiGLU rows hb.
+template <bool SWIGLU, int NPMAX, bool DEC>
 __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint8_t *__restrict__ aq, const uint16_t *__restrict__ ax, const float *__restrict__ asig,
     int gather_tokens, int kslots, RouteBufs rb, int n_ntiles, uint16_t *__restrict__ hb,
-    float *__restrict__ o) {
+    float *__restrict__ hf, float *__restrict__ o) {
   __shared__ __attribute__((aligned(1024))) uint8_t As0[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t Xs0[XSTAGE];
@@ -365,7 +390,8 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
   const int n = lane & 15, g = lane >> 4;
   const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];
   const int end = rb.offsets[e + 1];
-  const int valid = end - start < TMI ? end - start : TMI;
+  const int cap = 16 * NPMAX < TMI ? 16 * NPMAX : TMI;
+  const int valid = end - start < cap ? end - start : cap;
   const int np = (valid + 15) >> 4;  // live 16-token groups
 
   if (tid < TMI) {
@@ -402,27 +428,28 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) cx.aoff[j] = n * 256 + (((4 * j + g) ^ n) << 4);
   cx.xoff = (8 * ((n & 3) >> 1) + 2 * (n >> 2) + (n & 1)) * XROW + (g & 1) * 32 + (g >> 1) * 16;
+  cx.xoff4 = (8 * ((n & 3) >> 1) + 2 * (n >> 2) + (n & 1)) * XROW + 8 * g;
 
-  f32x4 acc[NPAIR][2];
+  f32x4 acc[NPMAX][2];
 #pragma unroll
-  for (int ip = 0; ip < NPAIR; ++ip)
+  for (int ip = 0; ip < NPMAX; ++ip)
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[ip][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  static_assert(NPAIR == 6, "block_loop dispatch covers 1..6 groups");
+  static_assert(NPMAX >= 1 && NPMAX <= NPAIR, "1..6 groups of 16 tokens");
   switch (np) {
-    case 1: block_loop<1>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 2: block_loop<2>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 3: block_loop<3>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 4: block_loop<4>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 5: block_loop<5>(cx, As0, As1, Xs0, Xs1, acc); break;
-    default: block_loop<6>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 1: block_loop<1, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 2: if constexpr (NPMAX >= 2) block_loop<2, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 3: if constexpr (NPMAX >= 3) block_loop<3, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 4: if constexpr (NPMAX >= 4) block_loop<4, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 5: if constexpr (NPMAX >= 5) block_loop<5, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
+    default: if constexpr (NPMAX >= 6) block_loop<6, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
   }
 
   // epilogue: lane (g, n) holds, for group ip, rows q = 0..3 = tokens
   // 16ip + 8(q>>1) + 2g + (q&1) of weight row n of each n-subtile t
 #pragma unroll
-  for (int ip = 0; ip < NPAIR; ++ip) {
+  for (int ip = 0; ip < NPMAX; ++ip) {
     if (ip >= np) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -432,7 +459,10 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
       const int64_t pos = start + m;
       const float v0 = acc[ip][0][q] * sg, v1 = acc[ip][1][q] * sg;
       if constexpr (SWIGLU) {
-        hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
+        if constexpr (DEC)
+          hf[pos * rows_per_expert + wrow[0]] = silu(v0) * v1;
+        else
+          hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
       } else {
         o[pos * rows_per_expert + wrow[0]] = v0;
         o[pos * rows_per_expert + wrow[1]] = v1;
@@ -465,15 +495,18 @@ PrepI8 prep_i8_view(void *base, int64_t rows, int K) {
   return p;
 }
 
-hipError_t launch_prep_i8(const void *src, bool f32in, const float *inv_rms, int64_t rows, int K,
-                          const PrepI8 &p, hipStream_t s) {
+hipError_t launch_prep_i8(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
+                          int64_t rows, int K, const PrepI8 &p, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (f32in)
-    hipLaunchKernelGGL((prep_i8_kernel<true>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms, K,
-                       p.q, p.x, p.sig);
+  if (f32in && round_bf16)
+    hipLaunchKernelGGL((prep_i8_kernel<true, true>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms,
+                       K, p.q, p.x, p.sig);
+  else if (f32in)
+    hipLaunchKernelGGL((prep_i8_kernel<true, false>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms,
+                       K, p.q, p.x, p.sig);
   else
-    hipLaunchKernelGGL((prep_i8_kernel<false>), dim3((unsigned)rows), dim3(256), 0, s, src, nullptr, K,
-                       p.q, p.x, p.sig);
+    hipLaunchKernelGGL((prep_i8_kernel<false, false>), dim3((unsigned)rows), dim3(256), 0, s, src,
+                       nullptr, K, p.q, p.x, p.sig);
   return hipGetLastError();
 }
 
@@ -481,8 +514,8 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
                                     int max_tiles, uint16_t *hb, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.F / 128;
-  hipLaunchKernelGGL((prefill_i8_kernel<true>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.gate,
-                     m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, hb, nullptr);
+  hipLaunchKernelGGL((prefill_i8_kernel<true, NPAIR, false>), dim3(grid_of(max_tiles, nn)), dim3(512), 0,
+                     s, m.gate, m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, hb, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -490,8 +523,29 @@ hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, cons
                                   int max_tiles, float *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
-  hipLaunchKernelGGL((prefill_i8_kernel<false>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.down,
-                     nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, o);
+  hipLaunchKernelGGL((prefill_i8_kernel<false, NPAIR, false>), dim3(grid_of(max_tiles, nn)), dim3(512), 0,
+                     s, m.down, nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, nullptr, o);
+  return hipGetLastError();
+}
+
+// Decode of 2..64 tokens: an expert holds at most 64 pairs, i.e. 4 groups.
+hipError_t launch_decode_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                   int max_tiles, float *h, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (T > 64) return hipErrorInvalidValue;
+  const int nn = m.F / 128;
+  hipLaunchKernelGGL((prefill_i8_kernel<true, 4, true>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s,
+                     m.gate, m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, nullptr, h, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                 int max_tiles, float *o, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (T > 64) return hipErrorInvalidValue;
+  const int nn = m.D / 256;
+  hipLaunchKernelGGL((prefill_i8_kernel<false, 4, true>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s,
+                     m.down, nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, nullptr, o);
   return hipGetLastError();
 }
 
