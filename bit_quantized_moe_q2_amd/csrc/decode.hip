@@ -24,6 +24,10 @@ namespace {
 
 constexpr int WAVES = 4;
 
+// Block fields are 4-byte aligned only: wide loads of 4-byte-aligned data.
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+
 // ---------------------------------------------------------------- x slices
 
 template <int TYPE>
@@ -89,10 +93,11 @@ struct Chunk<TYPE_Q2_K> {
     const uint8_t *blk = row + (c >> 2) * BB_Q2K;
     const int g = c & 3, h = g >> 1;
     p = g & 1;
-    const uint8_t *qs = blk + 16 + 16 * g;
-    q[0] = ld32(qs); q[1] = ld32(qs + 4); q[2] = ld32(qs + 8); q[3] = ld32(qs + 12);
-    s0 = ld32(blk + 8 * h);
-    s1 = ld32(blk + 8 * h + 4);
+    const u32x4a qv = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
+    q[0] = qv.x; q[1] = qv.y; q[2] = qv.z; q[3] = qv.w;
+    const u32x2a sv = *reinterpret_cast<const u32x2a *>(blk + 8 * h);
+    s0 = sv.x;
+    s1 = sv.y;
     dd = ld32(blk + 80);
   }
   __device__ __forceinline__ float dot(const XSlice<TYPE_Q2_K> &x) const {
@@ -128,9 +133,14 @@ template <>
 struct Chunk<TYPE_Q4_1> {
   uint32_t w[10];
   __device__ __forceinline__ void load(const uint8_t *__restrict__ row, int c) {
+    // the chunk's 40 bytes (two blocks, 8-byte aligned) in three loads
     const uint8_t *p = row + c * (2 * BB_Q41);
-#pragma unroll
-    for (int i = 0; i < 10; ++i) w[i] = ld32(p + 4 * i);
+    const u32x4a a = *reinterpret_cast<const u32x4a *>(p);
+    const u32x4a b = *reinterpret_cast<const u32x4a *>(p + 16);
+    const u32x2a e = *reinterpret_cast<const u32x2a *>(p + 32);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    w[8] = e.x; w[9] = e.y;
   }
   __device__ __forceinline__ float dot(const XSlice<TYPE_Q4_1> &x) const {
     float r = 0.f;
