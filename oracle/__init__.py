@@ -63,6 +63,13 @@ def lib():
         L.orc_moe.argtypes = [P, P, P, i32, P, ctypes.c_int]
         L.orc_rmsnorm.argtypes = [P, i32, ctypes.c_double, P]
         L.orc_stack.argtypes = [P, i32, ctypes.c_int, P, P, i32, ctypes.c_double, ctypes.c_int]
+        L.orc_steer.argtypes = [P, ctypes.c_double, P, i32, i32, P, P]
+        L.orc_f16_rne.restype = ctypes.c_uint16
+        L.orc_f16_rne.argtypes = [ctypes.c_float]
+        L.orc_e4m3_rne.restype = ctypes.c_uint8
+        L.orc_e4m3_rne.argtypes = [ctypes.c_float]
+        L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
         _lib = L
     return _lib
 
@@ -234,3 +241,33 @@ def stack(layers, x: np.ndarray, logits: np.ndarray, prefill_bf16: bool,
     if rc:
         raise ValueError("bad layer types")
     return x
+
+
+def steer(dir_: np.ndarray, scale: float, y: np.ndarray, residual: np.ndarray | None = None) -> np.ndarray:
+    """[P3] out_r (+)= y_r - scale * dir * (dir . y_r), fp64, one rounding."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    dir_ = np.ascontiguousarray(dir_, dtype=np.float32)
+    rows, n = y.reshape(-1, y.shape[-1]).shape
+    out = np.empty_like(y)
+    res = None if residual is None else np.ascontiguousarray(residual, dtype=np.float32)
+    lib().orc_steer(_p(dir_), float(scale), _p(y), rows, n, None if res is None else _p(res), _p(out))
+    return out
+
+
+def f16_rne(x: np.ndarray) -> np.ndarray:
+    """[P4] f32 -> binary16 bits (see ds4q_oracle.h for the rounding reading)."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    L = lib()
+    return np.array([L.orc_f16_rne(float(v)) for v in x], dtype=np.uint16)
+
+
+def e4m3_rne(x: np.ndarray) -> np.ndarray:
+    """[P4] f32 -> OCP E4M3 bits, round to nearest even, saturating."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    L = lib()
+    return np.array([L.orc_e4m3_rne(float(v)) for v in x], dtype=np.uint8)
+
+
+def e4m3_value(bits) -> np.ndarray:
+    L = lib()
+    return np.array([L.orc_e4m3_value(int(b)) for b in np.asarray(bits).ravel()], dtype=np.float64)

@@ -312,3 +312,80 @@ int orc_stack(const orc_layer *layers, int32_t n_layers, int prefill_bf16, float
   free(y);
   return rc;
 }
+
+/* ---------------------------------------------------------------- steering
+ * [P3] directional-steering section: the projection of the layer's direction
+ * is subtracted from the FFN output, y - scale * dir * (dir . y). */
+void orc_steer(const float *dir, double scale, const float *y, int32_t n_rows, int32_t n,
+               const float *residual, float *out) {
+  for (int32_t r = 0; r < n_rows; ++r) {
+    const float *yr = y + (int64_t)r * n;
+    double d = 0.0;
+    for (int32_t i = 0; i < n; ++i) d += (double)dir[i] * (double)yr[i];
+    for (int32_t i = 0; i < n; ++i) {
+      double v = (double)yr[i] - scale * (double)dir[i] * d;
+      if (residual) v += (double)residual[(int64_t)r * n + i];
+      out[(int64_t)r * n + i] = (float)v;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------- codec
+ * [P4] distributed-transport passage: 32-bit floats, or 16 bits (f16) or
+ * 8 bits (E4M3) on the wire, decoded back to float by the receiver.
+ *
+ * Both encoders take the value of the fp32 input exactly (as a double) and
+ * pick the representable neighbour by comparing distances: a plain
+ * statement of round-to-nearest-even over the target grid. */
+
+/* Round |v| (finite, >= 0) to the grid m * 2^e, m integer, ties to even m. */
+static double round_grid(double v, int e) {
+  const double m = ldexp(v, -e);
+  double f = floor(m);
+  const double r = m - f;
+  if (r > 0.5 || (r == 0.5 && fmod(f, 2.0) != 0.0)) f += 1.0;
+  return ldexp(f, e);
+}
+
+uint16_t orc_f16_rne(float f) {
+  const double v = (double)f;
+  const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+  if (isnan(f)) return (uint16_t)(sign | 0x7E00u);
+  const double a = fabs(v);
+  if (isinf(f)) return (uint16_t)(sign | 0x7C00u);
+  /* binary16: normals (1 + m/1024) 2^(e-15), e = 1..30; subnormals m 2^-24 */
+  int e2 = a > 0.0 ? ilogb(a) : -25;
+  if (e2 < -14) e2 = -14;                 /* subnormal spacing 2^-24 */
+  double q = round_grid(a, e2 - 10);      /* 10 fraction bits */
+  if (q >= 65520.0 || q > 65504.0) return (uint16_t)(sign | 0x7C00u);
+  if (q == 0.0) return sign;
+  int eq = ilogb(q);
+  if (eq < -14) return (uint16_t)(sign | (uint16_t)ldexp(q, 24));  /* subnormal */
+  const uint16_t mant = (uint16_t)(ldexp(q, 10 - eq) - 1024.0);
+  return (uint16_t)(sign | (uint16_t)((eq + 15) << 10) | mant);
+}
+
+double orc_e4m3_value(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) v = NAN;
+  else if (e == 0) v = ldexp((double)m, -9);         /* subnormal: m/8 * 2^-6 */
+  else v = ldexp((double)(8 + m), e - 10);           /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+uint8_t orc_e4m3_rne(float f) {
+  const uint8_t sign = signbit(f) ? 0x80u : 0u;
+  if (isnan(f)) return (uint8_t)(sign | 0x7Fu);
+  const double a = fabs((double)f);
+  if (isinf(f) || a >= 464.0) return (uint8_t)(sign | 0x7Eu); /* 464 = midpoint 448|480: even -> 480 out of range */
+  int e2 = a > 0.0 ? ilogb(a) : -10;
+  if (e2 < -6) e2 = -6;                   /* subnormal spacing 2^-9 */
+  double q = round_grid(a, e2 - 3);       /* 3 fraction bits */
+  if (q > 448.0) return (uint8_t)(sign | 0x7Eu);
+  if (q == 0.0) return sign;
+  int eq = ilogb(q);
+  if (eq < -6) return (uint8_t)(sign | (uint8_t)ldexp(q, 9));    /* subnormal */
+  const uint8_t mant = (uint8_t)(ldexp(q, 3 - eq) - 8.0);
+  return (uint8_t)(sign | (uint8_t)((eq + 7) << 3) | mant);
+}

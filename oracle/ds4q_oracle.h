@@ -12,6 +12,12 @@
  *       after the routing weight.
  *  [P2] "ds4.c 해독하기 1/8" (molayo1419.me) — DS4_SHAPE_FLASH passage:
  *       256 routed experts, 6 used per token.
+ *  [P3] "【#8】ds4.c 해독하기" (molayo1419.me) — directional steering: per
+ *       layer a direction dir, applied to the FFN output as
+ *       y - scale * dir * (dir . y).
+ *  [P4] "【#6】ds4.c 분석하기" (molayo1419.me) — distributed transport: the
+ *       activations between graph slices travel as 32-bit floats or are
+ *       packed to 16 bits (f16) or 8 bits (E4M3) and decoded back to float.
  *  [P5] "자체 저비트 포맷을 llama.cpp로 옮기기: 복원값이 비트까지 같은 GGUF Q4_1
  *       재부호화" (ThakiCloud) — section on the Q4_1 block (struct, nibble
  *       order, y = d*q + m), section on the two lossless conditions, the
@@ -27,6 +33,13 @@
  *  - SwiGLU h = silu(gate) * up; expert output down*h; token output is the
  *    routing-weighted sum over slots in slot order.
  *  - stack: x_{l+1} = x_l + MoE_l(rmsnorm(x_l)), parameter-free RMS norm.
+ *  - steering: the dot product and the update in fp64, one rounding to f32
+ *    (optionally after adding to a residual row); dir used as given.
+ *  - activation codec: f16 = IEEE binary16 with round-to-nearest-even,
+ *    overflow to +-inf, NaN to the quiet NaN sign|0x7E00; E4M3 = the OCP
+ *    8-bit E4M3 ("FN") encoding: bias 7, subnormals, no infinities, NaN =
+ *    sign|0x7F, largest finite 448; round to nearest even, magnitudes that
+ *    round beyond 448 (and +-inf) saturate to +-448, NaN to sign|0x7F.
  */
 #ifndef DS4Q_ORACLE_H
 #define DS4Q_ORACLE_H
@@ -73,6 +86,16 @@ int orc_moe(const orc_layer *L, const float *x, const float *logits, int32_t n_t
 void orc_rmsnorm(const float *x, int32_t n, double eps, double *out);
 int orc_stack(const orc_layer *layers, int32_t n_layers, int prefill_bf16, float *x,
               const float *logits, int32_t n_tok, double eps, int n_threads);
+
+/* [P3] directional steering: out_r (+)= y_r - scale * dir * (dir . y_r)
+ * for each row r of y [n_rows][n]; residual (nullable) is added first. */
+void orc_steer(const float *dir, double scale, const float *y, int32_t n_rows, int32_t n,
+               const float *residual, float *out);
+
+/* [P4] activation wire formats. */
+uint16_t orc_f16_rne(float f);
+uint8_t orc_e4m3_rne(float f);
+double orc_e4m3_value(uint8_t b);
 
 #ifdef __cplusplus
 }
