@@ -11,8 +11,9 @@ each with its own seeded router logits and activations, so weight bytes come
 from HBM.  Steps are replayed from a HIP graph that holds one step per layer.
 
 Also measured in the same run: the 4096-token prefill chunk (bf16, uniform
-routing) and one token through the 43-layer stack (Q2_K, and mixed: Q2_K
-layers 0-36 with Q4_1 layers 37-42) as secondary figures, the dominant kernels' durations from HIP
+routing), one token through the 43-layer stack (Q2_K, and mixed: Q2_K
+layers 0-36 with Q4_1 layers 37-42), and the activation-hop codec and
+directional steering on 4096 x 4096 f32 as secondary figures, the dominant kernels' durations from HIP
 events the library records around its own launches, and the CPU oracle on a
 bounded sample of the same decode workload.
 
@@ -97,6 +98,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-aux", action="store_true", help="skip the codec and steering figures")
     ap.add_argument("--stack-tokens", type=int, default=50,
                     help="tokens timed through each 43-layer stack")
     ap.add_argument("--cpu-sample", type=int, default=1024,
@@ -352,6 +354,48 @@ def main():
                 "tokens_per_s": round(1e3 / t_ms, 1), "weight_bytes_per_token": wbytes,
                 "hbm_gbps": round(wbytes / (t_ms / 1e3) / 1e9, 1)}
             del gs, ws_st
+
+    # ------------------------------------------------------------ codec and steering (secondary)
+    if not args.no_aux:
+        T_h = 4096
+        n = T_h * D
+        xh = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 7), T_h, D)).to(dev)
+        wire = torch.empty(n * 2, dtype=torch.uint8, device=dev)
+        back = torch.empty(T_h, D, dtype=torch.float32, device=dev)
+        res_h = torch.empty(T_h, D, dtype=torch.float32, device=dev)
+        dvec = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 8), 1, D)).to(dev)
+        dvec /= torch.linalg.vector_norm(dvec)
+
+        def timed(fn, reps=20):
+            fn()
+            torch.cuda.synchronize()
+            gx = capture(fn)
+            gx.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(reps):
+                gx.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / reps * 1e3  # us
+
+        aux = {}
+        for bits in (16, 8):
+            us = timed(lambda b=bits: ds4q.ds4q_act_encode(xh, n, b, wire))
+            nb = n * 4 + n * bits // 8
+            aux[f"encode_f32_to_{'f16' if bits == 16 else 'e4m3'}"] = {
+                "us": round(us, 2), "gbps": round(nb / (us / 1e6) / 1e9, 1)}
+            us = timed(lambda b=bits: ds4q.ds4q_act_decode(wire, n, b, back))
+            aux[f"decode_{'f16' if bits == 16 else 'e4m3'}_to_f32"] = {
+                "us": round(us, 2), "gbps": round(nb / (us / 1e6) / 1e9, 1)}
+        us = timed(lambda: ds4q.ds4q_steer(dvec, 0.5, back, T_h, D, res_h, ds4q.F_ACCUMULATE))
+        nb = n * 4 * 3 + D * 4
+        aux["steer_accumulate"] = {"us": round(us, 2), "gbps": round(nb / (us / 1e6) / 1e9, 1)}
+        log("aux (4096 x 4096 f32 hop / rows): " + ", ".join(f"{k} {v['us']} us {v['gbps']} GB/s"
+                                                             for k, v in aux.items()))
+        result["aux_4096x4096"] = {"workload": "activation hop codec and steering, 4096 x 4096 f32",
+                                   "peak_gbps": HBM_PEAK_GBPS, **aux}
+        del xh, wire, back, res_h
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4

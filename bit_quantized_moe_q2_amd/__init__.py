@@ -19,7 +19,8 @@ __all__ = [
     "ds4q_abi_version", "ds4q_strerror", "ds4q_dequant", "ds4q_matvec", "ds4q_route",
     "ds4q_route_workspace_size", "ds4q_moe_workspace_size", "ds4q_moe_decode",
     "ds4q_moe_decode_phases", "PHASE_ROUTE", "PHASE_GATEUP", "PHASE_DOWN", "PHASE_ALL",
-    "ds4q_moe_prefill", "ds4q_moe_stack", "ds4q_timing_enable", "ds4q_timing_read",
+    "ds4q_moe_prefill", "ds4q_moe_stack", "ds4q_steer", "ds4q_act_encode", "ds4q_act_decode",
+    "ds4q_timing_enable", "ds4q_timing_read",
     "QK", "BLOCK_BYTES", "row_bytes",
 ]
 
@@ -103,6 +104,9 @@ def load():
         "ds4q_moe_decode_phases": (ctypes.c_int, [LP, P, P, i32, P, RP, P, sz, ctypes.c_uint32, P]),
         "ds4q_moe_prefill": (ctypes.c_int, [LP, P, i32, P, i32, P, RP, P, sz, P]),
         "ds4q_moe_stack": (ctypes.c_int, [LP, i32, i32, P, P, i32, P, sz, P]),
+        "ds4q_steer": (ctypes.c_int, [P, ctypes.c_float, P, i32, i32, P, ctypes.c_uint32, P]),
+        "ds4q_act_encode": (ctypes.c_int, [P, i64, i32, P, P]),
+        "ds4q_act_decode": (ctypes.c_int, [P, i64, i32, P, P]),
         "ds4q_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "ds4q_timing_read": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int,
                                             ctypes.POINTER(ctypes.c_int)]),
@@ -202,6 +206,19 @@ def ds4q_moe_stack(layers, mode, x, logits, n_tok, workspace, workspace_bytes=No
     _check("ds4q_moe_stack", load().ds4q_moe_stack(
         arr, len(layers), mode, _ptr(x), _ptr(logits), n_tok, _ptr(workspace),
         _ws_bytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def ds4q_steer(dir_, scale, y, n_rows, n_embd, out, flags=0, stream=None):
+    _check("ds4q_steer", load().ds4q_steer(_ptr(dir_), float(scale), _ptr(y), n_rows, n_embd,
+                                           _ptr(out), flags, _stream(stream)))
+
+
+def ds4q_act_encode(src, n, bits, dst, stream=None):
+    _check("ds4q_act_encode", load().ds4q_act_encode(_ptr(src), n, bits, _ptr(dst), _stream(stream)))
+
+
+def ds4q_act_decode(src, n, bits, dst, stream=None):
+    _check("ds4q_act_decode", load().ds4q_act_decode(_ptr(src), n, bits, _ptr(dst), _stream(stream)))
 
 
 def ds4q_timing_enable(on: bool):

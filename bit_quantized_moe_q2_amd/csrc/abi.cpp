@@ -473,6 +473,45 @@ DS4Q_API int ds4q_moe_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_
                      static_cast<hipStream_t>(stream), L->flags);
 }
 
+DS4Q_API int ds4q_steer(const float *dir, float scale, const float *y, int32_t n_rows, int32_t n_embd,
+                        float *out, uint32_t flags, void *stream) {
+  if (flags & ~DS4Q_F_ACCUMULATE) return DS4Q_E_INVAL;
+  if (n_rows < 0 || n_embd < 4 || n_embd > 65536 || n_embd % 4) return DS4Q_E_SHAPE;
+  if (n_rows == 0) return DS4Q_OK;
+  if (!dir || !y || !out || !isfinite(scale)) return DS4Q_E_INVAL;
+  if (!aligned(dir, 16) || !aligned(y, 16) || !aligned(out, 16)) return DS4Q_E_ALIGN;
+  const size_t rb = (size_t)n_rows * n_embd * 4;
+  if (overlap(dir, (size_t)n_embd * 4, out, rb)) return DS4Q_E_ALIAS;
+  if ((const void *)y != out && overlap(y, rb, out, rb)) return DS4Q_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TIMED_TRY("steer", launch_steer(dir, scale, y, n_rows, n_embd, out, flags & DS4Q_F_ACCUMULATE, s));
+  return DS4Q_OK;
+}
+
+DS4Q_API int ds4q_act_encode(const float *src, int64_t n, int32_t bits, void *dst, void *stream) {
+  if (bits != 32 && bits != 16 && bits != 8) return DS4Q_E_INVAL;
+  if (n < 0) return DS4Q_E_SHAPE;
+  if (n == 0) return DS4Q_OK;
+  if (!src || !dst) return DS4Q_E_INVAL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return DS4Q_E_ALIGN;
+  if (overlap(src, (size_t)n * 4, dst, (size_t)n * bits / 8)) return DS4Q_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TIMED_TRY("act_encode", launch_act_encode(src, n, bits, dst, s));
+  return DS4Q_OK;
+}
+
+DS4Q_API int ds4q_act_decode(const void *src, int64_t n, int32_t bits, float *dst, void *stream) {
+  if (bits != 32 && bits != 16 && bits != 8) return DS4Q_E_INVAL;
+  if (n < 0) return DS4Q_E_SHAPE;
+  if (n == 0) return DS4Q_OK;
+  if (!src || !dst) return DS4Q_E_INVAL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return DS4Q_E_ALIGN;
+  if (overlap(src, (size_t)n * bits / 8, dst, (size_t)n * 4)) return DS4Q_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TIMED_TRY("act_decode", launch_act_decode(src, n, bits, dst, s));
+  return DS4Q_OK;
+}
+
 DS4Q_API int ds4q_moe_stack(const ds4q_moe_layer *layers, int32_t n_layers, int32_t mode, float *x,
                             const float *logits, int32_t n_tok, void *workspace,
                             size_t workspace_bytes, void *stream) {

@@ -92,6 +92,14 @@ hipError_t launch_decode_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, con
 hipError_t launch_decode_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                  int max_tiles, float *o, hipStream_t s);
 
+// Directional steering: out_r (+)= y_r - scale * dir * (dir . y_r), rows of n
+// floats (n % 4 == 0, 16-byte aligned); out may be y.
+hipError_t launch_steer(const float *dir, float scale, const float *y, int64_t n_rows, int n,
+                        float *out, bool accumulate, hipStream_t s);
+// Activation wire formats: bits 32 (copy), 16 (f16) or 8 (E4M3).
+hipError_t launch_act_encode(const float *src, int64_t n, int bits, void *dst, hipStream_t s);
+hipError_t launch_act_decode(const void *src, int64_t n, int bits, float *dst, hipStream_t s);
+
 constexpr int PREFILL_TILE_M = 96;
 
 }  // namespace ds4q

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DS4Q_ABI_VERSION 2
+#define DS4Q_ABI_VERSION 3
 
 /* Tensor types.  Numeric values follow the public GGML/GGUF type ids. */
 typedef enum {
@@ -198,6 +198,30 @@ int ds4q_moe_stack(const ds4q_moe_layer *layers, int32_t n_layers, int32_t mode,
                    const float *logits, int32_t n_tok, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* Directional steering ("【#8】ds4.c 해독하기", directional-steering section:
+ * the layer's direction is projected out of its FFN output): for each row r
+ * of y [n_rows][n_embd] f32,
+ *   out_r (+)= y_r - scale * dir * (dir . y_r)
+ * (+= with DS4Q_F_ACCUMULATE, e.g. onto the residual stream; the only flag).
+ * dir: device f32 [n_embd], used as given (a unit vector makes this a
+ * projection).  fp32 arithmetic: the dot product reduced in fp32, one fma per
+ * value.  n_embd: multiple of 4, 4..65536; n_rows >= 0.  dir, y, out: device,
+ * 16-byte aligned; out may be y (in place), dir may not overlap out. */
+int ds4q_steer(const float *dir, float scale, const float *y, int32_t n_rows, int32_t n_embd,
+               float *out, uint32_t flags, void *stream);
+
+/* Activation wire formats ("【#6】ds4.c 분석하기", distributed-transport
+ * passage: activations between pipeline stages travel as 32-bit floats or
+ * packed to 16 or 8 bits and are decoded back to float).  bits = 32: plain
+ * copy; 16: IEEE binary16, round to nearest even, overflow to +-inf, NaN to
+ * sign|0x7E00; 8: OCP E4M3 (bias 7, subnormals, largest finite 448, NaN
+ * sign|0x7F, no infinities), round to nearest even, magnitudes beyond 448
+ * and +-inf saturate to +-448.  Decoding is exact.  n >= 0 values; src and dst
+ * device, 16-byte aligned, not overlapping; dst holds n * bits / 8 bytes
+ * (encode) or n floats (decode).  Other bit widths: DS4Q_E_INVAL. */
+int ds4q_act_encode(const float *src, int64_t n, int32_t bits, void *dst, void *stream);
+int ds4q_act_decode(const void *src, int64_t n, int32_t bits, float *dst, void *stream);
+
 /* Per-kernel timing for profiling harnesses (not thread-safe; intended for a
  * single benchmarking thread).  While enabled, every kernel launch made by
  * the calls above is bracketed by two HIP events recorded on the call's
@@ -207,7 +231,8 @@ int ds4q_timing_enable(int on);
 /* Waits for the recorded events, then returns one entry per launch site:
  * names (max_names x name_len chars, NUL-terminated: "topk", "group",
  * "decode_gateup", "decode_down", "prep_bf16",
- * "prep_i8", "prefill_gateup", "prefill_down", "combine"), summed milliseconds and
+ * "prep_i8", "prefill_gateup", "prefill_down", "combine", "steer", "act_encode",
+ * "act_decode"), summed milliseconds and
  * launch counts (host arrays).  Clears the record. */
 int ds4q_timing_read(char *names, int name_len, double *total_ms, int64_t *count, int max_names,
                      int *n_names);

@@ -148,3 +148,31 @@ def test_prefill_and_stack_validation(lib):
 
 def test_timing_read_empty(lib):
     assert ds4q.ds4q_timing_read() == {}
+
+
+def test_steer_validation(lib):
+    f = lib.ds4q_steer
+    d, y, o = BASE, BASE + (1 << 30), BASE + (2 << 30)
+    assert f(d, 1.0, y, 4, 4096, o, 0x2, None) == E_INVAL          # RMSNORM is not a steering flag
+    assert f(d, 1.0, y, -1, 4096, o, 0, None) == E_SHAPE
+    assert f(d, 1.0, y, 4, 4098, o, 0, None) == E_SHAPE            # n_embd % 4
+    assert f(d, 1.0, y, 4, 0, o, 0, None) == E_SHAPE
+    assert f(d, 1.0, y, 0, 4096, o, 0, None) == OK                 # nothing to do
+    assert f(None, 1.0, y, 4, 4096, o, 0, None) == E_INVAL
+    assert f(d, float("nan"), y, 4, 4096, o, 0, None) == E_INVAL
+    assert f(d + 4, 1.0, y, 4, 4096, o, 0, None) == E_ALIGN
+    assert f(d, 1.0, y, 4, 4096, d, 0, None) == E_ALIAS            # out over dir
+    assert f(d, 1.0, y, 4, 4096, y + 16, 0, None) == E_ALIAS       # out partly over y
+
+
+def test_codec_validation(lib):
+    enc, dec = lib.ds4q_act_encode, lib.ds4q_act_decode
+    s, t = BASE, BASE + (1 << 30)
+    for f in (enc, dec):
+        assert f(s, 1024, 12, t, None) == E_INVAL
+        assert f(s, -1, 16, t, None) == E_SHAPE
+        assert f(s, 0, 16, t, None) == OK
+        assert f(None, 1024, 16, t, None) == E_INVAL
+        assert f(s + 8, 1024, 16, t, None) == E_ALIGN
+    assert enc(s, 1024, 16, s + 1024, None) == E_ALIAS             # dst inside src
+    assert dec(s, 1024, 8, s + 512, None) == E_ALIAS
