@@ -62,7 +62,9 @@ def lib():
         L.orc_expert_ffn.argtypes = [P, i32, P, P]
         L.orc_moe.argtypes = [P, P, P, i32, P, ctypes.c_int]
         L.orc_rmsnorm.argtypes = [P, i32, ctypes.c_double, P]
-        L.orc_stack.argtypes = [P, i32, ctypes.c_int, P, P, i32, ctypes.c_double, ctypes.c_int]
+        L.orc_stack.argtypes = [P, i32, ctypes.c_int, P, P, i32, ctypes.c_double, ctypes.c_int,
+                                P, ctypes.c_double]
+        L.orc_steer_f64.argtypes = [P, ctypes.c_double, P, i32, i32]
         L.orc_steer.argtypes = [P, ctypes.c_double, P, i32, i32, P, P]
         L.orc_f16_rne.restype = ctypes.c_uint16
         L.orc_f16_rne.argtypes = [ctypes.c_float]
@@ -231,13 +233,18 @@ def rmsnorm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 
 
 def stack(layers, x: np.ndarray, logits: np.ndarray, prefill_bf16: bool,
-          eps: float = 1e-6, n_threads: int = 0) -> np.ndarray:
-    """x: [T][D] fp32 residual stream; logits: [L][T][E].  Returns the new x."""
+          eps: float = 1e-6, n_threads: int = 0, dirs: np.ndarray | None = None,
+          steer_scale: float = 0.0) -> np.ndarray:
+    """x: [T][D] fp32 residual stream; logits: [L][T][E]; dirs (optional):
+    layer-major steering directions [L][D] ([P3]).  Returns the new x."""
     arr = (_Layer * len(layers))(*[l.s for l in layers])
     x = np.array(x, dtype=np.float32, copy=True, order="C")
     logits = np.ascontiguousarray(logits, dtype=np.float32)
+    if dirs is not None:
+        dirs = np.ascontiguousarray(dirs, dtype=np.float32)
+        assert dirs.shape == (len(layers), x.shape[1])
     rc = lib().orc_stack(arr, len(layers), int(prefill_bf16), _p(x), _p(logits), x.shape[0],
-                         eps, n_threads)
+                         eps, n_threads, None if dirs is None else _p(dirs), float(steer_scale))
     if rc:
         raise ValueError("bad layer types")
     return x
@@ -252,6 +259,15 @@ def steer(dir_: np.ndarray, scale: float, y: np.ndarray, residual: np.ndarray | 
     res = None if residual is None else np.ascontiguousarray(residual, dtype=np.float32)
     lib().orc_steer(_p(dir_), float(scale), _p(y), rows, n, None if res is None else _p(res), _p(out))
     return out
+
+
+def steer_f64(dir_: np.ndarray, scale: float, y: np.ndarray) -> np.ndarray:
+    """[P3] y_r - scale * dir * (dir . y_r) on fp64 rows, no rounding."""
+    y = np.array(y, dtype=np.float64, copy=True, order="C")
+    dir_ = np.ascontiguousarray(dir_, dtype=np.float32)
+    rows, n = y.reshape(-1, y.shape[-1]).shape
+    lib().orc_steer_f64(_p(dir_), float(scale), _p(y), rows, n)
+    return y
 
 
 def f16_rne(x: np.ndarray) -> np.ndarray:

@@ -286,7 +286,8 @@ void orc_rmsnorm(const float *x, int32_t n, double eps, double *out) {
  * before the experts see it.  x is the fp32 residual stream, updated in place
  * (the sum x + y is rounded to fp32 after each layer). */
 int orc_stack(const orc_layer *layers, int32_t n_layers, int prefill_bf16, float *x,
-              const float *logits, int32_t n_tok, double eps, int n_threads) {
+              const float *logits, int32_t n_tok, double eps, int n_threads,
+              const float *dirs, double steer_scale) {
   int32_t D = layers[0].n_embd, E = layers[0].n_expert;
   float *n32 = (float *)malloc((size_t)n_tok * D * sizeof(float));
   double *nd = (double *)malloc((size_t)D * sizeof(double));
@@ -305,6 +306,9 @@ int orc_stack(const orc_layer *layers, int32_t n_layers, int prefill_bf16, float
       }
     }
     rc = orc_moe(&layers[l], n32, logits + (int64_t)l * n_tok * E, n_tok, y, n_threads);
+    /* [P3]: the layer's own direction (row l of the layer-major table) is
+     * projected out of its FFN output before the residual add */
+    if (dirs) orc_steer_f64(dirs + (int64_t)l * D, steer_scale, y, n_tok, D);
     for (int64_t i = 0; i < (int64_t)n_tok * D; ++i) x[i] = (float)((double)x[i] + y[i]);
   }
   free(n32);
@@ -327,6 +331,15 @@ void orc_steer(const float *dir, double scale, const float *y, int32_t n_rows, i
       if (residual) v += (double)residual[(int64_t)r * n + i];
       out[(int64_t)r * n + i] = (float)v;
     }
+  }
+}
+
+void orc_steer_f64(const float *dir, double scale, double *y, int32_t n_rows, int32_t n) {
+  for (int32_t r = 0; r < n_rows; ++r) {
+    double *yr = y + (int64_t)r * n;
+    double d = 0.0;
+    for (int32_t i = 0; i < n; ++i) d += (double)dir[i] * yr[i];
+    for (int32_t i = 0; i < n; ++i) yr[i] -= scale * (double)dir[i] * d;
   }
 }
 

@@ -84,13 +84,19 @@ int orc_expert_ffn(const orc_layer *L, int32_t e, const double *x, double *o);
 int orc_moe(const orc_layer *L, const float *x, const float *logits, int32_t n_tok,
             double *y, int n_threads);
 void orc_rmsnorm(const float *x, int32_t n, double eps, double *out);
+/* dirs (nullable): layer-major steering directions [n_layers][n_embd]; when
+ * given, layer l's MoE output is steered with dirs + l*n_embd and
+ * steer_scale (fp64, before the residual add). */
 int orc_stack(const orc_layer *layers, int32_t n_layers, int prefill_bf16, float *x,
-              const float *logits, int32_t n_tok, double eps, int n_threads);
+              const float *logits, int32_t n_tok, double eps, int n_threads,
+              const float *dirs, double steer_scale);
 
 /* [P3] directional steering: out_r (+)= y_r - scale * dir * (dir . y_r)
  * for each row r of y [n_rows][n]; residual (nullable) is added first. */
 void orc_steer(const float *dir, double scale, const float *y, int32_t n_rows, int32_t n,
                const float *residual, float *out);
+/* The same on fp64 rows, in place, without rounding. */
+void orc_steer_f64(const float *dir, double scale, double *y, int32_t n_rows, int32_t n);
 
 /* [P4] activation wire formats. */
 uint16_t orc_f16_rne(float f);

@@ -6,6 +6,7 @@ brute-force search over the E4M3 code table (CPU only)."""
 import numpy as np
 
 import oracle
+import synth
 
 
 # ---------------------------------------------------------------- steering
