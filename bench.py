@@ -11,9 +11,11 @@ each with its own seeded router logits and activations, so weight bytes come
 from HBM.  Steps are replayed from a HIP graph that holds one step per layer.
 
 Also measured in the same run: the 4096-token prefill chunk (bf16, uniform
-routing), one token through the 43-layer stack (Q2_K, and mixed: Q2_K
-layers 0-36 with Q4_1 layers 37-42), and the activation-hop codec and
-directional steering on 4096 x 4096 f32 as secondary figures, the dominant kernels' durations from HIP
+routing), one token through the 43-layer stack (Q2_K; mixed: Q2_K
+layers 0-36 with Q4_1 layers 37-42; and Q2_K with every layer's MoE output
+steered by its own row of a [43][4096] direction table), and the
+activation-hop codec and standalone directional steering on 4096 x 4096 f32
+as secondary figures, the dominant kernels' durations from HIP
 events the library records around its own launches, and the CPU oracle on a
 bounded sample of the same decode workload.
 
@@ -325,8 +327,18 @@ def main():
                                             for l in range(NL)])).to(dev)
         x_st = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 6), 1, D)).to(dev)
         x_run = torch.empty_like(x_st)
+        # steered Q2_K stack: layer l's MoE output loses row l of a layer-major
+        # [43][4096] table of unit directions (scale 1)
+        dirs = torch.from_numpy(np.stack([synth.x_f32(synth.stream_key(seed, 9, l), 1, D)[0]
+                                          for l in range(NL)])).to(dev)
+        dirs /= torch.linalg.vector_norm(dirs, dim=1, keepdim=True)
+        steered = []
+        for l, L in enumerate(layers):
+            Ls = ds4q.MoeLayer.from_buffer_copy(L)
+            Ls.steer_dir, Ls.steer_scale = dirs[l].data_ptr(), 1.0
+            steered.append(Ls)
         result["stack_decode"] = {}
-        for name, lays in (("q2_k", layers), ("mixed", layers[:37] + q41)):
+        for name, lays in (("q2_k", layers), ("mixed", layers[:37] + q41), ("q2_k_steered", steered)):
             ws_st = torch.empty(max(ds4q.ds4q_moe_workspace_size(L, 1, 0) for L in lays),
                                 dtype=torch.uint8, device=dev)
 
@@ -353,6 +365,9 @@ def main():
                 "workload": f"stack43_decode_1tok_{name}", "us_per_token": round(t_ms * 1e3, 2),
                 "tokens_per_s": round(1e3 / t_ms, 1), "weight_bytes_per_token": wbytes,
                 "hbm_gbps": round(wbytes / (t_ms / 1e3) / 1e9, 1)}
+            if name == "q2_k_steered":
+                base_us = result["stack_decode"]["q2_k"]["us_per_token"]
+                result["stack_decode"][name]["steer_us_per_layer"] = round((t_ms * 1e3 - base_us) / NL, 3)
             del gs, ws_st
 
     # ------------------------------------------------------------ codec and steering (secondary)

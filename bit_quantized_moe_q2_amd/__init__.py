@@ -51,17 +51,26 @@ class MoeLayer(ctypes.Structure):
                 ("type_gate", ctypes.c_int32), ("type_up", ctypes.c_int32),
                 ("type_down", ctypes.c_int32),
                 ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
-                ("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float)]
+                ("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float),
+                ("steer_dir", ctypes.c_void_p), ("steer_scale", ctypes.c_float)]
 
     @classmethod
     def from_tensors(cls, gate, up, down, n_embd, n_ff, n_expert, k, type_gate,
-                     type_up=None, type_down=None, flags=0, norm_eps=1e-6):
+                     type_up=None, type_down=None, flags=0, norm_eps=1e-6,
+                     steer_dir=None, steer_scale=0.0):
         L = cls(n_embd, n_ff, n_expert, k, type_gate,
                 type_gate if type_up is None else type_up,
                 type_gate if type_down is None else type_down,
-                _ptr(gate), _ptr(up), _ptr(down), flags, norm_eps)
-        L._keep = (gate, up, down)          # keep the tensors alive with the struct
+                _ptr(gate), _ptr(up), _ptr(down), flags, norm_eps, _ptr(steer_dir), steer_scale)
+        L._keep = (gate, up, down, steer_dir)  # keep the tensors alive with the struct
         return L
+
+    def set_steering(self, steer_dir, steer_scale):
+        """Steer this layer's MoE output with a device f32 [n_embd] direction
+        (None switches steering off)."""
+        self.steer_dir = _ptr(steer_dir)
+        self.steer_scale = steer_scale
+        self._keep = self._keep[:3] + (steer_dir,)
 
 
 class RouteOut(ctypes.Structure):

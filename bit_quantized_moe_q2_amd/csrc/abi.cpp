@@ -46,6 +46,7 @@ struct Workspace {
   float *h = nullptr;      // decode: [T*k][F] f32
   uint16_t *hb = nullptr;  // prefill: [T*k][F] bf16 (sorted order)
   float *o = nullptr;      // [T*k][D] f32
+  float *stage = nullptr;  // decode of one token: [D] f32, the unsteered output before steering
   uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
   PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
   size_t bytes = 0;
@@ -77,6 +78,7 @@ struct Workspace {
     } else if (mode == 0) {
       h = (float *)take(P * F * 4);
       if (T > 1) o = (float *)take(P * D * 4);
+      else stage = (float *)take((size_t)D * 4);
       if (i8_in) {  // decode of 2..64 tokens on Q2_K: the grouped int8 kernels
         rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
         void *p = take(prep_i8_bytes(T, D));
@@ -115,7 +117,21 @@ int check_layer(const ds4q_moe_layer *L) {
   if (!aligned(L->gate, 16) || !aligned(L->up, 16) || !aligned(L->down, 16)) return DS4Q_E_ALIGN;
   if (L->flags & ~(DS4Q_F_ACCUMULATE | DS4Q_F_RMSNORM_INPUT)) return DS4Q_E_INVAL;
   if (!(L->norm_eps >= 0.0f) || !isfinite(L->norm_eps)) return DS4Q_E_INVAL;
+  if (L->steer_dir) {
+    if (!aligned(L->steer_dir, 16)) return DS4Q_E_ALIGN;
+    if (!isfinite(L->steer_scale)) return DS4Q_E_INVAL;
+  }
   return DS4Q_OK;
+}
+
+SteerArgs steer_of(const ds4q_moe_layer *L, float *stage) {
+  SteerArgs st;
+  if (L->steer_dir) {
+    st.dir = L->steer_dir;
+    st.scale = L->steer_scale;
+    st.stage = stage;
+  }
+  return st;
 }
 
 bool i8_gateup(const ds4q_moe_layer *L) { return L->type_gate == DS4Q_TYPE_Q2_K; }
@@ -249,6 +265,11 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
       overlap(ws, need.bytes, logits, lb))
     return DS4Q_E_ALIAS;
   if ((const void *)y != x && overlap(y, yb, x, xb)) return DS4Q_E_ALIAS;
+  if (L->steer_dir) {
+    const size_t db = (size_t)L->n_embd * 4;
+    if (overlap(L->steer_dir, db, y, yb) || overlap(L->steer_dir, db, ws, need.bytes))
+      return DS4Q_E_ALIAS;
+  }
   if (overlap(y, yb, logits, lb)) return DS4Q_E_ALIAS;
   if (route_overlaps(route, T, L->n_expert, L->n_expert_used, ws, need.bytes) ||
       route_overlaps(route, T, L->n_expert, L->n_expert_used, y, yb) ||
@@ -268,6 +289,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
   const WsFlags f = i8_flags(L, T, 0);
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0, f.a, f.b);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
+  const SteerArgs st = steer_of(L, w.stage);
   const bool p_route = phases & DS4Q_PHASE_ROUTE, p_gu = phases & DS4Q_PHASE_GATEUP,
              p_down = phases & DS4Q_PHASE_DOWN;
   if (T == 1 && m.tg == DS4Q_TYPE_Q2_K && m.td == DS4Q_TYPE_Q2_K) {
@@ -275,12 +297,12 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     // itself, so the routing phase has nothing of its own to launch and the
     // routing outputs follow the gate/up launch.
     if (p_gu) {
-      TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 1, s));
+      TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 1, st, s));
       // the grouping pass (expert order) runs only when asked for
       if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
     }
     if (p_down)
-      TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 2, s));
+      TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 2, st, s));
     return p_gu ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
   if (f.a) {
@@ -298,7 +320,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     if (p_down) {
       TIMED_TRY("prep_i8", launch_prep_i8(w.h, true, false, nullptr, (int64_t)T * m.k, m.F, w.hq, s));
       TIMED_TRY("decode_down", launch_decode_i8_down(m, w.hq, T, w.rb, mt, w.o, s));
-      TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, s));
+      TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, st, s));
     }
     return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
@@ -310,7 +332,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
   }
   if (p_gu)
     TIMED_TRY("decode_gateup", launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
-  if (p_down) TIMED_TRY("decode_down", launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, s));
+  if (p_down) TIMED_TRY("decode_down", launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, st, s));
   return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
 }
 
@@ -344,7 +366,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   } else {
     TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.o, s));
   }
-  TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, s));
+  TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, steer_of(L, nullptr), s));
   return copy_route(route, w.rb, T, m.E, m.k, s);
 }
 

@@ -245,7 +245,7 @@ template <int TYPE, int L, int RS>
 __global__ __launch_bounds__(512) void down_slots_kernel(const uint8_t *__restrict__ down, int D,
                                                          int k, const float *__restrict__ h,
                                                          RouteBufs rb, float *__restrict__ y,
-                                                         int accumulate) {
+                                                         int accumulate, float *__restrict__ stage) {
   constexpr int RPW = 64 / L;
   constexpr int ROWS = RS * RPW;
   __shared__ float part[8][ROWS];
@@ -271,7 +271,8 @@ __global__ __launch_bounds__(512) void down_slots_kernel(const uint8_t *__restri
     const int r = row0 + threadIdx.x;
     float acc = 0.f;
     for (int s = 0; s < k; ++s) acc = fmaf(rb.w[s], part[s][threadIdx.x], acc);
-    y[r] = accumulate ? y[r] + acc : acc;
+    if (stage) stage[r] = acc;  // steered by the launch that follows
+    else y[r] = accumulate ? y[r] + acc : acc;
   }
 }
 
@@ -331,6 +332,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   *yp = acc;
 }
 
+// Combine with directional steering: one workgroup per token row (D <= 4096,
+// four float4 per thread), the row's weighted sum kept in registers while its
+// dot product with the direction is reduced, then y (+)= v - scale*dir*(dir.v).
+__global__ __launch_bounds__(256) void combine_steer_kernel(const float *__restrict__ o, RouteBufs rb,
+                                                            int k, int D, int by_pos,
+                                                            const float *__restrict__ dir, float scale,
+                                                            float *__restrict__ y, int accumulate) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  float4 v[4];
+  float p = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = 4 * (threadIdx.x + 256 * c);
+    v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < D) {
+      for (int j = 0; j < k; ++j) {
+        const int pp = t * k + j;
+        const int64_t row = by_pos ? rb.pair_pos[pp] : pp;
+        const float4 a = *reinterpret_cast<const float4 *>(o + row * D + i);
+        const float w = rb.w[pp];
+        v[c].x = fmaf(w, a.x, v[c].x); v[c].y = fmaf(w, a.y, v[c].y);
+        v[c].z = fmaf(w, a.z, v[c].z); v[c].w = fmaf(w, a.w, v[c].w);
+      }
+      const float4 d = *reinterpret_cast<const float4 *>(dir + i);
+      p = fmaf(d.x, v[c].x, p); p = fmaf(d.y, v[c].y, p);
+      p = fmaf(d.z, v[c].z, p); p = fmaf(d.w, v[c].w, p);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = p;
+  __syncthreads();
+  const float sd = -scale * ((red[0] + red[1]) + (red[2] + red[3]));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = 4 * (threadIdx.x + 256 * c);
+    if (i < D) {
+      const float4 d = *reinterpret_cast<const float4 *>(dir + i);
+      float4 r = make_float4(fmaf(sd, d.x, v[c].x), fmaf(sd, d.y, v[c].y), fmaf(sd, d.z, v[c].z),
+                             fmaf(sd, d.w, v[c].w));
+      float4 *yp = reinterpret_cast<float4 *>(y + (int64_t)t * D + i);
+      if (accumulate) {
+        const float4 old = *yp;
+        r.x += old.x; r.y += old.y; r.z += old.z; r.w += old.w;
+      }
+      *yp = r;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 #define DS4Q_DISPATCH_L(L_VAL, ...)                     \
@@ -385,7 +437,8 @@ hipError_t launch_decode_gateup(const MoeDims &m, const float *x, const float *i
 }
 
 hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const RouteBufs &rb,
-                              float *o, float *y, bool accumulate, hipStream_t s) {
+                              float *o, float *y, bool accumulate, const SteerArgs &st,
+                              hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int L = m.F / 64;
   if (T == 1) {
@@ -394,11 +447,13 @@ hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const Rou
       const int per_wg = RS * (64 / LL);
       const dim3 grid(m.D / per_wg);
       if (m.td == TYPE_Q2_K)
-        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0);
+        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0, st.dir ? st.stage : nullptr);
       else
-        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0);
+        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0, st.dir ? st.stage : nullptr);
     });
-    return hipGetLastError();
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !st.dir) return err;
+    return launch_steer(st.dir, st.scale, st.stage, 1, m.D, y, accumulate, s);
   }
   const int max_active = T * m.k < m.E ? T * m.k : m.E;
   DS4Q_DISPATCH_L(L, {
@@ -412,13 +467,18 @@ hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const Rou
   });
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_combine(o, rb, T, m.k, m.D, false, y, accumulate, s);
+  return launch_combine(o, rb, T, m.k, m.D, false, y, accumulate, st, s);
 }
 
 hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
-                          float *y, bool accumulate, hipStream_t s) {
+                          float *y, bool accumulate, const SteerArgs &st, hipStream_t s) {
   const int64_t n4 = (int64_t)T * (D / 4);
   if (n4 == 0) return hipSuccess;
+  if (st.dir) {
+    hipLaunchKernelGGL(combine_steer_kernel, dim3((unsigned)T), dim3(256), 0, s, o, rb, k, D,
+                       by_pos ? 1 : 0, st.dir, st.scale, y, accumulate ? 1 : 0);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, o, rb, T,
                      k, D, by_pos ? 1 : 0, y, accumulate ? 1 : 0);
   return hipGetLastError();

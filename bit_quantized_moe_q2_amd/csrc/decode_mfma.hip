@@ -366,7 +366,7 @@ template <int F>
 __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
     const uint8_t *__restrict__ down, int D, int k, const int32_t *__restrict__ ids,
     const float *__restrict__ wts, const float *__restrict__ h, float *__restrict__ y,
-    int accumulate) {
+    int accumulate, float *__restrict__ stage) {
   constexpr int NB = F / 256;
   constexpr int WPS = NB >= 2 ? 2 : 1;
   constexpr int BPW = NB / WPS;
@@ -414,7 +414,8 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
       for (int q = 1; q < WPS; ++q) ps += part[s * WPS + q][n];
       acc = fmaf(wts[s], ps, acc);
     }
-    y[row] = accumulate ? y[row] + acc : acc;
+    if (stage) stage[row] = acc;  // steered by the launch that follows
+    else y[row] = accumulate ? y[row] + acc : acc;
   }
 }
 
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
 
 hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *logits,
                                 bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
-                                bool accumulate, int phase, hipStream_t s) {
+                                bool accumulate, int phase, const SteerArgs &st, hipStream_t s) {
   if (phase == 1) {
     const dim3 grid(m.F / 16, m.k);
 #define DS4Q_GU(DD, ME)                                                                          \
@@ -446,7 +447,7 @@ hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *l
     const dim3 block(64 * m.k * wps);
 #define DS4Q_DN(FF)                                                                             \
   hipLaunchKernelGGL((down_q2k_t1_kernel<FF>), dim3(m.D / 16), block, 0, s, m.down, m.D, m.k,    \
-                     rb.ids, rb.w, h, y, accumulate ? 1 : 0)
+                     rb.ids, rb.w, h, y, accumulate ? 1 : 0, st.dir ? st.stage : nullptr)
     switch (m.F) {
       case 256: DS4Q_DN(256); break;
       case 512: DS4Q_DN(512); break;
@@ -456,6 +457,11 @@ hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *l
       default: return hipErrorInvalidValue;
     }
 #undef DS4Q_DN
+    if (st.dir) {
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      return launch_steer(st.dir, st.scale, st.stage, 1, m.D, y, accumulate, s);
+    }
   } else {
     return hipErrorInvalidValue;
   }

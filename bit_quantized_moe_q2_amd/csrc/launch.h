@@ -35,6 +35,15 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, const float *x,
 // Counting-sort grouping of the T*k pairs; tile_m > 0 also builds m-tiles.
 hipError_t launch_group(int T, int E, int k, int tile_m, const RouteBufs &rb, hipStream_t s);
 
+// Directional steering of a layer's MoE output (dir == nullptr: none).
+// stage ([D] f32) is one-token decode workspace: the down kernel writes the
+// unsteered row there and launch_steer writes y from it.
+struct SteerArgs {
+  const float *dir = nullptr;
+  float scale = 0.f;
+  float *stage = nullptr;
+};
+
 struct MoeDims {
   int D, F, E, k;
   int tg, tu, td;  // block types of gate, up, down
@@ -46,18 +55,23 @@ hipError_t launch_decode_gateup(const MoeDims &m, const float *x, const float *i
                                 const RouteBufs &rb, float *h, hipStream_t s);
 // Decode path: down projection.  T == 1: fused weighted combine into y.
 // T > 1: o [T*k][D] f32 (pair-indexed), then launch_combine.
+// With st.dir set the output is steered (one token: the down kernel writes
+// st.stage and launch_steer follows; several: in the combine).
 hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const RouteBufs &rb,
-                              float *o, float *y, bool accumulate, hipStream_t s);
+                              float *o, float *y, bool accumulate, const SteerArgs &st,
+                              hipStream_t s);
 // Single-token Q2_K decode on int8 matrix cores, in two phases: 1 = routing
 // (into rb.ids / rb.w) + gate/up + SwiGLU into h, 2 = down + weighted combine
 // into y.
 hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *logits,
                                 bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
-                                bool accumulate, int phase, hipStream_t s);
+                                bool accumulate, int phase, const SteerArgs &st, hipStream_t s);
 // y[t] (+)= sum_j w[t][j] * o[row(t, j)]; row = pair index, or sorted
 // position (via pair_pos) when by_pos.
+// With st.dir set, each token row is steered before it is written (one
+// workgroup per row).
 hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
-                          float *y, bool accumulate, hipStream_t s);
+                          float *y, bool accumulate, const SteerArgs &st, hipStream_t s);
 
 // Prefill path on Q4_1 weights (bf16 matrix cores).
 hipError_t launch_prep_bf16(const float *x, const float *inv_rms, int T, int D, uint16_t *xb,

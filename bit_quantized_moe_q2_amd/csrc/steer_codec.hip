@@ -3,7 +3,8 @@
 // Directional steering ("【#8】ds4.c 해독하기", directional-steering section):
 // per row, out (+)= y - scale * dir * (dir . y), the layer's direction
 // projected out of its FFN output.  One workgroup per row: a block reduction
-// of dir . y in fp32, then one fma per value.
+// of dir . y in fp32, then one fma per value.  The one-token decode path runs
+// this on the row the down kernel staged.
 //
 // Activation wire formats ("【#6】ds4.c 분석하기", distributed-transport
 // passage): the activations between pipeline stages travel as 32-bit floats
@@ -20,6 +21,10 @@ namespace {
 
 // ---------------------------------------------------------------- steering
 
+// One workgroup per row.  Up to 4096 values the row stays in registers (CH
+// float4 per thread, all loads issued before the first use): one memory round
+// trip, the block reduction, then the writes.  Longer rows loop twice.
+template <int CH>
 __global__ __launch_bounds__(256) void steer_kernel(const float *__restrict__ dir, float scale,
                                                     const float *y, int n, float *out, int accumulate) {
   const int64_t row = blockIdx.x;
@@ -28,28 +33,57 @@ __global__ __launch_bounds__(256) void steer_kernel(const float *__restrict__ di
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   __shared__ float red[4];
   float p = 0.f;
-  for (int i = 4 * t; i < n; i += 1024) {
-    const float4 a = *reinterpret_cast<const float4 *>(dir + i);
-    const float4 b = *reinterpret_cast<const float4 *>(yr + i);
-    p = fmaf(a.x, b.x, p);
-    p = fmaf(a.y, b.y, p);
-    p = fmaf(a.z, b.z, p);
-    p = fmaf(a.w, b.w, p);
+  float4 a[CH > 0 ? CH : 1], b[CH > 0 ? CH : 1];
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int i = 4 * (t + 256 * c);
+      if (i < n) {
+        a[c] = *reinterpret_cast<const float4 *>(dir + i);
+        b[c] = *reinterpret_cast<const float4 *>(yr + i);
+      } else {
+        a[c] = b[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      p = fmaf(a[c].x, b[c].x, p);
+      p = fmaf(a[c].y, b[c].y, p);
+      p = fmaf(a[c].z, b[c].z, p);
+      p = fmaf(a[c].w, b[c].w, p);
+    }
+  } else {
+    for (int i = 4 * t; i < n; i += 1024) {
+      const float4 u = *reinterpret_cast<const float4 *>(dir + i);
+      const float4 v = *reinterpret_cast<const float4 *>(yr + i);
+      p = fmaf(u.x, v.x, p);
+      p = fmaf(u.y, v.y, p);
+      p = fmaf(u.z, v.z, p);
+      p = fmaf(u.w, v.w, p);
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
   if (lane == 0) red[w] = p;
   __syncthreads();  // also orders every read of the row before any write (out may be y)
   const float sd = -scale * ((red[0] + red[1]) + (red[2] + red[3]));
-  for (int i = 4 * t; i < n; i += 1024) {
-    const float4 a = *reinterpret_cast<const float4 *>(dir + i);
-    const float4 b = *reinterpret_cast<const float4 *>(yr + i);
-    float4 v = make_float4(fmaf(sd, a.x, b.x), fmaf(sd, a.y, b.y), fmaf(sd, a.z, b.z), fmaf(sd, a.w, b.w));
+  auto emit = [&](int i, float4 u, float4 v) {
+    float4 r = make_float4(fmaf(sd, u.x, v.x), fmaf(sd, u.y, v.y), fmaf(sd, u.z, v.z), fmaf(sd, u.w, v.w));
     if (accumulate) {
       const float4 o = *reinterpret_cast<const float4 *>(orow + i);
-      v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+      r = make_float4(o.x + r.x, o.y + r.y, o.z + r.z, o.w + r.w);
     }
-    *reinterpret_cast<float4 *>(orow + i) = v;
+    *reinterpret_cast<float4 *>(orow + i) = r;
+  };
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int i = 4 * (t + 256 * c);
+      if (i < n) emit(i, a[c], b[c]);
+    }
+  } else {
+    for (int i = 4 * t; i < n; i += 1024)
+      emit(i, *reinterpret_cast<const float4 *>(dir + i), *reinterpret_cast<const float4 *>(yr + i));
   }
 }
 
@@ -167,8 +201,16 @@ unsigned blocks_of(int64_t n, int groups) {
 hipError_t launch_steer(const float *dir, float scale, const float *y, int64_t n_rows, int n,
                         float *out, bool accumulate, hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(steer_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, dir, scale, y, n, out,
-                     accumulate ? 1 : 0);
+  const dim3 grid((unsigned)n_rows);
+  const int acc = accumulate ? 1 : 0;
+  if (n <= 1024)
+    hipLaunchKernelGGL(steer_kernel<1>, grid, dim3(256), 0, s, dir, scale, y, n, out, acc);
+  else if (n <= 2048)
+    hipLaunchKernelGGL(steer_kernel<2>, grid, dim3(256), 0, s, dir, scale, y, n, out, acc);
+  else if (n <= 4096)
+    hipLaunchKernelGGL(steer_kernel<4>, grid, dim3(256), 0, s, dir, scale, y, n, out, acc);
+  else
+    hipLaunchKernelGGL(steer_kernel<0>, grid, dim3(256), 0, s, dir, scale, y, n, out, acc);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DS4Q_ABI_VERSION 3
+#define DS4Q_ABI_VERSION 4
 
 /* Tensor types.  Numeric values follow the public GGML/GGUF type ids. */
 typedef enum {
@@ -77,13 +77,26 @@ enum {
  * and up must share a type, down may differ.  Device pointers, 16-byte
  * aligned.  n_embd and n_ff each one of 256, 512, 1024, 2048, 4096
  * (DS4_SHAPE_FLASH: 4096 and 2048); n_expert 1..1024; n_expert_used 1..8 and
- * <= n_expert; norm_eps finite and >= 0. */
+ * <= n_expert; norm_eps finite and >= 0.
+ *
+ * Directional steering of the layer's FFN output ("【#8】ds4.c 해독하기",
+ * directional-steering section: each layer projects its own direction out of
+ * its FFN output): with steer_dir non-NULL, every token's MoE output v is
+ * replaced by v - steer_scale * dir * (dir . v) before it is written or
+ * accumulated (fp32; the dot product reduced in fp32 in a fixed order).
+ * steer_dir: device f32 [n_embd], 16-byte aligned, used as given (a unit
+ * vector makes this a projection), must not overlap y or the workspace;
+ * steer_scale finite (> 0 suppresses the direction, < 0 amplifies it).  For a
+ * layer-major table dirs [n_layers][n_embd], layer l takes dirs + l*n_embd.
+ * NULL = no steering (steer_scale ignored). */
 typedef struct {
   int32_t n_embd, n_ff, n_expert, n_expert_used;
   int32_t type_gate, type_up, type_down; /* ds4q_type */
   const void *gate, *up, *down;
   uint32_t flags;
   float norm_eps;
+  const float *steer_dir;
+  float steer_scale;
 } ds4q_moe_layer;
 
 /* Optional routing outputs (device pointers; any may be NULL). */
@@ -187,7 +200,7 @@ int ds4q_moe_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, con
                      size_t workspace_bytes, void *stream);
 
 /* Layer stack ([P2]: 43 layers in the Flash shape): for l in 0..n_layers-1,
- *   x <- x + MoE_l(rmsnorm(x))
+ *   x <- x + MoE_l(rmsnorm(x))   (MoE_l steered when layers[l].steer_dir is set)
  * with layer l's descriptor layers[l] (its flags are ignored: RMSNORM_INPUT
  * and ACCUMULATE are implied) and router logits logits + l*n_tok*n_expert.
  * mode 0 = decode path (n_tok <= 64), 1 = prefill path.  x: device f32

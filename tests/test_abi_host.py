@@ -150,6 +150,31 @@ def test_timing_read_empty(lib):
     assert ds4q.ds4q_timing_read() == {}
 
 
+def test_layer_steering_validation(lib):
+    """Steering fields of the layer descriptor (directional-steering section
+    of the steering page): alignment, a finite scale, no overlap of the
+    direction with the output or the workspace.  NULL switches it off."""
+    x, lg, y, w = BASE + (8 << 32), BASE + (9 << 32), BASE + (10 << 32), BASE + (11 << 32)
+    dvec = BASE + (12 << 32)
+
+    def dec(L, T=4, y=y):
+        need = lib.ds4q_moe_workspace_size(ctypes.byref(L), T, 0)
+        return lib.ds4q_moe_decode(ctypes.byref(L), x, lg, T, y, None, w, need, None)
+
+    assert dec(_layer(steer_dir=dvec + 4, steer_scale=1.0)) == E_ALIGN
+    assert dec(_layer(steer_dir=dvec, steer_scale=float("nan"))) == E_INVAL
+    assert dec(_layer(steer_dir=dvec, steer_scale=float("inf"))) == E_INVAL
+    assert dec(_layer(steer_dir=y + 1024, steer_scale=1.0)) == E_ALIAS   # inside y
+    assert dec(_layer(steer_dir=w + 256, steer_scale=1.0)) == E_ALIAS    # inside the workspace
+    assert dec(_layer(steer_dir=dvec, steer_scale=1.0), T=0) == OK
+    assert lib.ds4q_moe_workspace_size(ctypes.byref(_layer(steer_dir=dvec + 4, steer_scale=1.0)), 1, 0) == 0
+    bad = (ds4q.MoeLayer * 2)(_layer(), _layer(steer_dir=dvec + 8, steer_scale=1.0))
+    assert lib.ds4q_moe_stack(bad, 2, 0, x, lg, 1, w, 1 << 30, None) == E_ALIGN
+    # the one-token workspace holds the staged row of the steering tail
+    assert (lib.ds4q_moe_workspace_size(ctypes.byref(_layer()), 1, 0)
+            >= 4096 * 4 + 6 * 2048 * 4)
+
+
 def test_steer_validation(lib):
     f = lib.ds4q_steer
     d, y, o = BASE, BASE + (1 << 30), BASE + (2 << 30)
