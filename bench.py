@@ -292,6 +292,19 @@ def main():
         ds4q.ds4q_timing_enable(False)
         g1_ms = pt["prefill_gateup"][0] / pt["prefill_gateup"][1]
         g1_tf = T * K * 2 * 2 * D * F / (g1_ms / 1e3) / 1e12
+        # the same chunk with the layer's output steered (fused into the combine)
+        dp = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 9, 0), 1, D)[0]).to(dev)
+        dp /= torch.linalg.vector_norm(dp)
+        Lsp = ds4q.MoeLayer.from_buffer_copy(layers[0])
+        Lsp.steer_dir, Lsp.steer_scale = dp.data_ptr(), 1.0
+        ds4q.ds4q_timing_enable(True)
+        for _ in range(5):
+            ds4q.ds4q_moe_prefill(Lsp, xb, ds4q.TYPE_BF16, lgp, T, yp, None, ws_p)
+        torch.cuda.synchronize()
+        pts = ds4q.ds4q_timing_read()
+        ds4q.ds4q_timing_enable(False)
+        comb_us = pt["combine"][0] / pt["combine"][1] * 1e3
+        comb_steer_us = pts["combine"][0] / pts["combine"][1] * 1e3
         log(f"prefill: {p_ms:.3f} ms/chunk, {flops / (p_ms / 1e3) / 1e12:.1f} TFLOP/s; "
             f"gateup {g1_ms:.3f} ms ({g1_tf:.1f} TFLOP/s)")
         result["prefill"] = {
@@ -306,7 +319,11 @@ def main():
                          "frac": round(g1_tf / MFMA_INT8_PEAK_TOPS, 4), "traffic": None,
                          "int8_ops_per_algorithmic_op": 2},
             "kernels_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in pt.items()},
+            # combine of the 4096 x 6 expert rows, plain and with the steering
+            # epilogue (row dot product + projection in the same launch)
+            "combine_us": round(comb_us, 2), "combine_steered_us": round(comb_steer_us, 2),
         }
+        log(f"prefill combine: {comb_us:.1f} us, steered {comb_steer_us:.1f} us")
 
     # ------------------------------------------------------------ stack (secondary)
     if not args.no_stack and NL == 43:
