@@ -65,6 +65,8 @@ def lib():
         L.orc_stack.argtypes = [P, i32, ctypes.c_int, P, P, i32, ctypes.c_double, ctypes.c_int,
                                 P, ctypes.c_double]
         L.orc_steer_f64.argtypes = [P, ctypes.c_double, P, i32, i32]
+        L.orc_moe_imatrix.argtypes = [P, P, P, i32, P, P, ctypes.c_int]
+        L.orc_expert_swiglu.argtypes = [P, i32, P, P]
         L.orc_steer.argtypes = [P, ctypes.c_double, P, i32, i32, P, P]
         L.orc_f16_rne.restype = ctypes.c_uint16
         L.orc_f16_rne.argtypes = [ctypes.c_float]
@@ -223,6 +225,29 @@ def moe(layer: Layer, x: np.ndarray, logits: np.ndarray, n_threads: int = 0) -> 
     if rc:
         raise ValueError("bad layer types")
     return y
+
+
+def expert_swiglu(layer: Layer, e: int, x: np.ndarray) -> np.ndarray:
+    """The expert's SwiGLU row silu(W1 x) * (W3 x), fp64 [n_ff]."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    h = np.empty(layer.s.n_ff, dtype=np.float64)
+    if lib().orc_expert_swiglu(ctypes.byref(layer.s), e, _p(x), _p(h)):
+        raise ValueError("bad layer types")
+    return h
+
+
+def moe_imatrix(layer: Layer, x: np.ndarray, logits: np.ndarray, n_threads: int = 0):
+    """[P1] imatrix statistics of one layer call on MoE input rows x:
+    (imat_in [E][n_embd], imat_down [E][n_ff]), fp64, expert-major."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    E = layer.s.n_expert
+    a = np.zeros((E, layer.s.n_embd), dtype=np.float64)
+    b = np.zeros((E, layer.s.n_ff), dtype=np.float64)
+    if lib().orc_moe_imatrix(ctypes.byref(layer.s), _p(x), _p(logits), x.shape[0], _p(a), _p(b),
+                             n_threads):
+        raise ValueError("bad layer types")
+    return a, b
 
 
 def rmsnorm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:

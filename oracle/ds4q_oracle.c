@@ -223,21 +223,31 @@ static double dot_row(int type, const uint8_t *row, int64_t cols, const double *
 
 /* One routed expert on one token, all fp64: g = W1 x, u = W3 x,
  * h = silu(g) * u, o = W2 h  ([P1]: w1 = gate, w3 = up, w2 = down). */
-int orc_expert_ffn(const orc_layer *L, int32_t e, const double *x, double *o) {
+/* The expert's SwiGLU row h = silu(W1 x) * (W3 x), [n_ff]. */
+int orc_expert_swiglu(const orc_layer *L, int32_t e, const double *x, double *h) {
   int64_t D = L->n_embd, F = L->n_ff;
   int64_t gb = tensor_bytes(L->type_gate, F, D), ub = tensor_bytes(L->type_up, F, D);
-  int64_t db = tensor_bytes(L->type_down, D, F);
-  if (gb < 0 || ub < 0 || db < 0) return -1;
-  const uint8_t *G = L->gate + e * gb, *U = L->up + e * ub, *W2 = L->down + e * db;
-  double *h = (double *)malloc((size_t)F * sizeof(double));
+  if (gb < 0 || ub < 0) return -1;
+  const uint8_t *G = L->gate + e * gb, *U = L->up + e * ub;
   for (int64_t r = 0; r < F; ++r) {
     double g = dot_row(L->type_gate, G + r * (gb / F), D, x);
     double u = dot_row(L->type_up, U + r * (ub / F), D, x);
     h[r] = g / (1.0 + exp(-g)) * u;
   }
-  for (int64_t i = 0; i < D; ++i) o[i] = dot_row(L->type_down, W2 + i * (db / D), F, h);
-  free(h);
   return 0;
+}
+
+int orc_expert_ffn(const orc_layer *L, int32_t e, const double *x, double *o) {
+  int64_t D = L->n_embd, F = L->n_ff;
+  int64_t db = tensor_bytes(L->type_down, D, F);
+  if (db < 0) return -1;
+  const uint8_t *W2 = L->down + e * db;
+  double *h = (double *)malloc((size_t)F * sizeof(double));
+  int rc = orc_expert_swiglu(L, e, x, h);
+  if (!rc)
+    for (int64_t i = 0; i < D; ++i) o[i] = dot_row(L->type_down, W2 + i * (db / D), F, h);
+  free(h);
+  return rc;
 }
 
 /* y_t = sum over slots j (in slot order) of p_j * expert_{id_j}(x_t). */
@@ -270,6 +280,51 @@ int orc_moe(const orc_layer *L, const float *x, const float *logits, int32_t n_t
   free(ids);
   free(w);
   return rc;
+}
+
+/* [P1] imatrix passage: the activation statistics collected on the routed
+ * experts, per expert and input column, expert-major:
+ *   imat_in   [n_expert][n_embd] += sum over the tokens routed to the expert
+ *             of x[col]^2, x the MoE input row (one vector serves the gate and
+ *             the up tensor, which read the same input);
+ *   imat_down [n_expert][n_ff]   += sum over the same (token, slot) pairs of
+ *             (p * h[col])^2, h the expert's SwiGLU row and p the pair's
+ *             routing weight (the down projection's input).
+ * fp64, tokens then slots in order; experts are independent (one thread
+ * each). */
+int orc_moe_imatrix(const orc_layer *L, const float *x, const float *logits, int32_t n_tok,
+                    double *imat_in, double *imat_down, int n_threads) {
+  int32_t k = L->n_expert_used, E = L->n_expert, D = L->n_embd, F = L->n_ff;
+  if (tensor_bytes(L->type_gate, F, D) < 0 || tensor_bytes(L->type_up, F, D) < 0) return -1;
+  int32_t *ids = (int32_t *)malloc((size_t)n_tok * k * sizeof(int32_t));
+  double *w = (double *)malloc((size_t)n_tok * k * sizeof(double));
+  orc_route(logits, n_tok, E, k, ids, w);
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int32_t e = 0; e < E; ++e) {
+    double *xt = (double *)malloc((size_t)D * sizeof(double));
+    double *h = (double *)malloc((size_t)F * sizeof(double));
+    for (int32_t t = 0; t < n_tok; ++t)
+      for (int32_t j = 0; j < k; ++j) {
+        if (ids[t * k + j] != e) continue;
+        for (int32_t i = 0; i < D; ++i) {
+          xt[i] = x[(int64_t)t * D + i];
+          imat_in[(int64_t)e * D + i] += xt[i] * xt[i];
+        }
+        orc_expert_swiglu(L, e, xt, h);
+        for (int32_t i = 0; i < F; ++i) {
+          const double v = w[t * k + j] * h[i];
+          imat_down[(int64_t)e * F + i] += v * v;
+        }
+      }
+    free(xt);
+    free(h);
+  }
+  free(ids);
+  free(w);
+  return 0;
 }
 
 /* Parameter-free RMS norm: n = x / sqrt(mean(x^2) + eps). */

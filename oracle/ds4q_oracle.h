@@ -80,7 +80,11 @@ typedef struct {
   const uint8_t *gate, *up, *down;   /* [n_expert][rows][blocks] */
 } orc_layer;
 
+int orc_expert_swiglu(const orc_layer *L, int32_t e, const double *x, double *h);
 int orc_expert_ffn(const orc_layer *L, int32_t e, const double *x, double *o);
+/* [P1] imatrix statistics of one layer call on MoE input rows x (see the .c). */
+int orc_moe_imatrix(const orc_layer *L, const float *x, const float *logits, int32_t n_tok,
+                    double *imat_in, double *imat_down, int n_threads);
 int orc_moe(const orc_layer *L, const float *x, const float *logits, int32_t n_tok,
             double *y, int n_threads);
 void orc_rmsnorm(const float *x, int32_t n, double eps, double *out);

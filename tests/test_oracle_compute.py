@@ -237,6 +237,73 @@ def test_moe_token_separability_and_dominant_expert():
         assert np.allclose(y2[t], oracle.expert_ffn(L, 4, x[t].astype(np.float64)), rtol=1e-12, atol=1e-9)
 
 
+# ---------------------------------------------------------------- imatrix
+# "【#2】ds4.c 해독하기", imatrix passage: per routed expert and input column,
+# sum of squares of the gate/up input (the MoE input row) and of the down
+# input (the routed SwiGLU row after the routing weight), expert-major.
+
+def test_imatrix_constant_experts_closed_form():
+    """gate = a_e, up = b_e constants: h = silu(a_e S) * b_e S in every row,
+    so imat_down[e][j] = sum over e's pairs of (p * h)^2 for every j, and
+    imat_in[e] = sum over e's tokens of x^2.  Distinct a_e, b_e per expert pin
+    the expert-major layout; p inside the square pins where the weight goes."""
+    D, F, E, k, T = 256, 256, 16, 6, 7
+    rng = np.random.default_rng(31)
+    gate_c = [float(np.float16(v)) for v in rng.uniform(-0.5, 0.5, E)]
+    up_c = [float(np.float16(v)) for v in rng.uniform(-0.5, 0.5, E)]
+    L = tiny_layer(Q2, D, F, E, k, gate_c, up_c, [[0.0] * D for _ in range(E)])
+    x = synth.x_f32(synth.stream_key(32), T, D) * 0.05
+    lg = synth.logits_normal(synth.stream_key(33), T, E)
+    ids, w = _brute_route(lg, k)
+    a, b = oracle.moe_imatrix(L, x, lg)
+    ref_a = np.zeros((E, D))
+    ref_b = np.zeros((E, F))
+    for t in range(T):
+        S = x[t].astype(np.float64).sum()
+        for j in range(k):
+            e = ids[t, j]
+            ref_a[e] += x[t].astype(np.float64) ** 2
+            ref_b[e] += (w[t, j] * _silu(gate_c[e] * S) * up_c[e] * S) ** 2
+    assert np.allclose(a, ref_a, rtol=1e-13, atol=0)
+    assert np.allclose(b, ref_b, rtol=1e-11, atol=1e-300)
+    assert np.all(b[np.setdiff1d(np.arange(E), ids)] == 0)
+
+
+@pytest.mark.parametrize("qname", ["q2_k", "q4_1"])
+def test_imatrix_brute_force_dequant_numpy(qname):
+    """A random layer: the SwiGLU rows recomputed with numpy from the
+    dequantised matrices, the statistics summed by hand; every token lands in
+    exactly k experts, so the input statistic summed over experts is k times
+    the column energy of x."""
+    D, F, E, k, T = 256, 256, 8, 3, 5
+    L, (g, u, d) = _random_layer(qname, D, F, E, k, 34)
+    qt = Q2 if qname == "q2_k" else Q4
+    x = synth.x_f32(synth.stream_key(35), T, D)
+    lg = synth.logits_normal(synth.stream_key(36), T, E)
+    ids, w = _brute_route(lg, k)
+    a, b = oracle.moe_imatrix(L, x, lg)
+    ref_a = np.zeros((E, D))
+    ref_b = np.zeros((E, F))
+    for t in range(T):
+        xt = x[t].astype(np.float64)
+        for j in range(k):
+            e = ids[t, j]
+            G = oracle.dequant_f32(qt, g[e], F, D).astype(np.float64)
+            U = oracle.dequant_f32(qt, u[e], F, D).astype(np.float64)
+            gv, uv = G @ xt, U @ xt
+            ref_a[e] += xt ** 2
+            ref_b[e] += (w[t, j] * gv / (1.0 + np.exp(-gv)) * uv) ** 2
+    assert np.allclose(a, ref_a, rtol=1e-13)
+    assert np.allclose(b, ref_b, rtol=1e-9, atol=1e-12 * ref_b.max())
+    assert np.allclose(a.sum(axis=0), k * (x.astype(np.float64) ** 2).sum(axis=0), rtol=1e-13)
+    # the SwiGLU row helper itself against numpy
+    h = oracle.expert_swiglu(L, int(ids[0, 0]), x[0])
+    G = oracle.dequant_f32(qt, g[ids[0, 0]], F, D).astype(np.float64)
+    U = oracle.dequant_f32(qt, u[ids[0, 0]], F, D).astype(np.float64)
+    gv, uv = G @ x[0].astype(np.float64), U @ x[0].astype(np.float64)
+    assert np.allclose(h, gv / (1.0 + np.exp(-gv)) * uv, rtol=1e-12, atol=1e-15)
+
+
 # ---------------------------------------------------------------- stack
 
 def test_rmsnorm_closed_form():
