@@ -305,6 +305,27 @@ def main():
         ds4q.ds4q_timing_enable(False)
         comb_us = pt["combine"][0] / pt["combine"][1] * 1e3
         comb_steer_us = pts["combine"][0] / pts["combine"][1] * 1e3
+        # the same chunk collecting the imatrix statistics (input and down)
+        st_in = torch.zeros(E, D, device=dev)
+        st_dn = torch.zeros(E, F, device=dev)
+        Lim = ds4q.MoeLayer.from_buffer_copy(layers[0])
+        Lim.imatrix_in, Lim.imatrix_down = st_in.data_ptr(), st_dn.data_ptr()
+        ws_im = torch.empty(ds4q.ds4q_moe_workspace_size(Lim, T, 1), dtype=torch.uint8, device=dev)
+        ds4q.ds4q_moe_prefill(Lim, xb, ds4q.TYPE_BF16, lgp, T, yp, None, ws_im)
+        torch.cuda.synchronize()
+        ds4q.ds4q_timing_enable(True)
+        for _ in range(5):
+            ds4q.ds4q_moe_prefill(Lim, xb, ds4q.TYPE_BF16, lgp, T, yp, None, ws_im)
+        torch.cuda.synchronize()
+        pti = ds4q.ds4q_timing_read()
+        ds4q.ds4q_timing_enable(False)
+        im_us = pti["imatrix"][0] / pti["imatrix"][1] * 1e3
+        P = T * K
+        n_tiles = E + P // 96 + 1
+        # bf16 input rows and SwiGLU rows read once per pair, partial rows
+        # written and read back, the statistics read and written
+        im_bytes = P * (D + F) * 2 + n_tiles * (D + F) * 4 * 2 + E * (D + F) * 4 * 2
+        del ws_im
         log(f"prefill: {p_ms:.3f} ms/chunk, {flops / (p_ms / 1e3) / 1e12:.1f} TFLOP/s; "
             f"gateup {g1_ms:.3f} ms ({g1_tf:.1f} TFLOP/s)")
         result["prefill"] = {
@@ -322,7 +343,12 @@ def main():
             # combine of the 4096 x 6 expert rows, plain and with the steering
             # epilogue (row dot product + projection in the same launch)
             "combine_us": round(comb_us, 2), "combine_steered_us": round(comb_steer_us, 2),
+            # imatrix statistics hook on the same chunk (bytes are an upper
+            # bound: the partial rows of live tiles only are written)
+            "imatrix_us": round(im_us, 2), "imatrix_bytes": im_bytes,
+            "imatrix_gbps": round(im_bytes / (im_us / 1e6) / 1e9, 1),
         }
+        log(f"prefill imatrix hook: {im_us:.1f} us, {im_bytes / (im_us / 1e6) / 1e9:.0f} GB/s")
         log(f"prefill combine: {comb_us:.1f} us, steered {comb_steer_us:.1f} us")
 
     # ------------------------------------------------------------ stack (secondary)

@@ -52,7 +52,8 @@ class MoeLayer(ctypes.Structure):
                 ("type_down", ctypes.c_int32),
                 ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float),
-                ("steer_dir", ctypes.c_void_p), ("steer_scale", ctypes.c_float)]
+                ("steer_dir", ctypes.c_void_p), ("steer_scale", ctypes.c_float),
+                ("imatrix_in", ctypes.c_void_p), ("imatrix_down", ctypes.c_void_p)]
 
     @classmethod
     def from_tensors(cls, gate, up, down, n_embd, n_ff, n_expert, k, type_gate,
@@ -64,6 +65,13 @@ class MoeLayer(ctypes.Structure):
                 _ptr(gate), _ptr(up), _ptr(down), flags, norm_eps, _ptr(steer_dir), steer_scale)
         L._keep = (gate, up, down, steer_dir)  # keep the tensors alive with the struct
         return L
+
+    def set_imatrix(self, imatrix_in, imatrix_down):
+        """Accumulate the layer's imatrix statistics into device f32 tensors
+        [n_expert][n_embd] and [n_expert][n_ff] (None: not collected)."""
+        self.imatrix_in = _ptr(imatrix_in)
+        self.imatrix_down = _ptr(imatrix_down)
+        self._keep_stats = (imatrix_in, imatrix_down)
 
     def set_steering(self, steer_dir, steer_scale):
         """Steer this layer's MoE output with a device f32 [n_embd] direction

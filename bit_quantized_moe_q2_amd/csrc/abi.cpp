@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <utility>
+
 #include "../../include/ds4q.h"
 #include "launch.h"
 
@@ -47,6 +49,7 @@ struct Workspace {
   uint16_t *hb = nullptr;  // prefill: [T*k][F] bf16 (sorted order)
   float *o = nullptr;      // [T*k][D] f32
   float *stage = nullptr;  // decode of one token: [D] f32, the unsteered output before steering
+  float *imat_part = nullptr;  // imatrix on m-tiles: [max_tiles][max(D, F)] f32 partial rows
   uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
   PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
   size_t bytes = 0;
@@ -54,7 +57,7 @@ struct Workspace {
   // mode 1 (prefill): i8_in / i8_h = Q2_K gate/up resp. down (int8 matrix
   // cores); mode 0 (decode): i8_in = the grouped int8 path (see i8_flags)
   Workspace(uint8_t *base, int D, int F, int E, int k, int T, int mode, bool i8_in = false,
-            bool i8_h = false) {
+            bool i8_h = false, bool stats = false) {
     size_t off = 0;
     auto take = [&](size_t n) -> void * {
       void *p = base ? base + off : nullptr;
@@ -85,6 +88,7 @@ struct Workspace {
         if (base) xq = prep_i8_view(p, T, D);
         p = take(prep_i8_bytes(P, F));
         if (base) hq = prep_i8_view(p, P, F);
+        if (stats) imat_part = (float *)take((size_t)max_tiles(T, E, k) * (D > F ? D : F) * 4);
       }
     } else {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
@@ -99,6 +103,7 @@ struct Workspace {
         void *p = take(prep_i8_bytes(P, F));
         if (base) hq = prep_i8_view(p, P, F);
       }
+      if (stats) imat_part = (float *)take((size_t)max_tiles(T, E, k) * (D > F ? D : F) * 4);
     }
     bytes = off;
   }
@@ -121,6 +126,11 @@ int check_layer(const ds4q_moe_layer *L) {
     if (!aligned(L->steer_dir, 16)) return DS4Q_E_ALIGN;
     if (!isfinite(L->steer_scale)) return DS4Q_E_INVAL;
   }
+  if (!aligned(L->imatrix_in, 16) || !aligned(L->imatrix_down, 16)) return DS4Q_E_ALIGN;
+  if (L->imatrix_in && L->imatrix_down &&
+      overlap(L->imatrix_in, (size_t)L->n_expert * L->n_embd * 4, L->imatrix_down,
+              (size_t)L->n_expert * L->n_ff * 4))
+    return DS4Q_E_ALIAS;
   return DS4Q_OK;
 }
 
@@ -142,11 +152,12 @@ bool i8_decode(const ds4q_moe_layer *L, int T) { return T > 1 && i8_gateup(L) &&
 
 // Workspace flags of a call (see Workspace).
 struct WsFlags {
-  bool a, b;
+  bool a, b, stats;
 };
+bool wants_stats(const ds4q_moe_layer *L) { return L->imatrix_in || L->imatrix_down; }
 WsFlags i8_flags(const ds4q_moe_layer *L, int T, int mode) {
-  if (mode == 1) return {i8_gateup(L), i8_down(L)};
-  return {i8_decode(L, T), false};
+  if (mode == 1) return {i8_gateup(L), i8_down(L), wants_stats(L)};
+  return {i8_decode(L, T), false, wants_stats(L)};
 }
 
 MoeDims dims_of(const ds4q_moe_layer *L) {
@@ -257,7 +268,8 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
       route_misaligned(route))
     return DS4Q_E_ALIGN;
   const WsFlags f = i8_flags(L, T, mode);
-  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b);
+  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b,
+                       f.stats);
   if (ws_bytes < need.bytes) return DS4Q_E_WORKSPACE;
   const size_t xb = (size_t)T * L->n_embd * x_elem, yb = (size_t)T * L->n_embd * 4;
   const size_t lb = (size_t)T * L->n_expert * 4;
@@ -270,6 +282,21 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
     if (overlap(L->steer_dir, db, y, yb) || overlap(L->steer_dir, db, ws, need.bytes))
       return DS4Q_E_ALIAS;
   }
+  // the statistics are written: they overlap no input, output or workspace
+  const std::pair<const void *, size_t> stats[2] = {
+      {L->imatrix_in, (size_t)L->n_expert * L->n_embd * 4},
+      {L->imatrix_down, (size_t)L->n_expert * L->n_ff * 4}};
+  for (const auto &st : stats) {
+    if (!st.first) continue;
+    if (overlap(st.first, st.second, x, xb) || overlap(st.first, st.second, y, yb) ||
+        overlap(st.first, st.second, logits, lb) || overlap(st.first, st.second, ws, need.bytes) ||
+        (L->steer_dir && overlap(st.first, st.second, L->steer_dir, (size_t)L->n_embd * 4)) ||
+        overlap(st.first, st.second, L->gate, (size_t)L->n_expert * L->n_ff * row_bytes(L->type_gate, L->n_embd)) ||
+        overlap(st.first, st.second, L->up, (size_t)L->n_expert * L->n_ff * row_bytes(L->type_up, L->n_embd)) ||
+        overlap(st.first, st.second, L->down, (size_t)L->n_expert * L->n_embd * row_bytes(L->type_down, L->n_ff)) ||
+        route_overlaps(route, T, L->n_expert, L->n_expert_used, st.first, st.second))
+      return DS4Q_E_ALIAS;
+  }
   if (overlap(y, yb, logits, lb)) return DS4Q_E_ALIAS;
   if (route_overlaps(route, T, L->n_expert, L->n_expert_used, ws, need.bytes) ||
       route_overlaps(route, T, L->n_expert, L->n_expert_used, y, yb) ||
@@ -277,6 +304,24 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
       route_overlaps(route, T, L->n_expert, L->n_expert_used, logits, lb))
     return DS4Q_E_ALIAS;
   return DS4Q_OK;
+}
+
+// imatrix statistics of a call, launched once the routing and the SwiGLU
+// rows exist and before anything writes y (which may be x).
+hipError_t launch_stats(const ds4q_moe_layer *L, const MoeDims &m, const Workspace &w, int seg_mode,
+                        int max_seg, const ImatRows &in, const ImatRows &h, hipStream_t s) {
+  if (!wants_stats(L)) return hipSuccess;
+  return launch_imatrix(m, w.rb, seg_mode, max_seg, in, L->imatrix_in, h, L->imatrix_down,
+                        w.imat_part, s);
+}
+
+ImatRows rows_of(const void *p, bool bf16, const float *inv_rms, bool by_sorted) {
+  ImatRows r;
+  r.rows = p;
+  r.bf16 = bf16;
+  r.inv_rms = inv_rms;
+  r.by_sorted = by_sorted;
+  return r;
 }
 
 // The decode launches in three phases (DS4Q_PHASE_*): routing and input
@@ -287,7 +332,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
                uint32_t phases = DS4Q_PHASE_ALL) {
   const MoeDims m = dims_of(L);
   const WsFlags f = i8_flags(L, T, 0);
-  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0, f.a, f.b);
+  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0, f.a, f.b, f.stats);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const SteerArgs st = steer_of(L, w.stage);
   const bool p_route = phases & DS4Q_PHASE_ROUTE, p_gu = phases & DS4Q_PHASE_GATEUP,
@@ -300,6 +345,10 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
       TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 1, st, s));
       // the grouping pass (expert order) runs only when asked for
       if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+      ImatRows in = rows_of(x, false, nullptr, false);
+      in.norm_self = norm;  // the gate/up launch keeps the inverse RMS to itself
+      in.eps = L->norm_eps;
+      TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_SLOTS, m.k, in, rows_of(w.h, false, nullptr, false), s));
     }
     if (p_down)
       TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 2, st, s));
@@ -316,6 +365,8 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     if (p_gu) {
       TIMED_TRY("prep_i8", launch_prep_i8(x, true, false, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xq, s));
       TIMED_TRY("decode_gateup", launch_decode_i8_gateup(m, w.xq, T, w.rb, mt, w.h, s));
+      TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
+                                        rows_of(w.h, false, nullptr, true), s));
     }
     if (p_down) {
       TIMED_TRY("prep_i8", launch_prep_i8(w.h, true, false, nullptr, (int64_t)T * m.k, m.F, w.hq, s));
@@ -330,8 +381,13 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     // order); the grouping pass (expert order) runs only when asked for.
     if (T > 1 || wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
   }
-  if (p_gu)
+  if (p_gu) {
     TIMED_TRY("decode_gateup", launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
+    const int na = T * m.k < m.E ? T * m.k : m.E;
+    TIMED_TRY("imatrix", launch_stats(L, m, w, T == 1 ? IMAT_SEG_SLOTS : IMAT_SEG_ACTIVE, T == 1 ? m.k : na,
+                                      rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
+                                      rows_of(w.h, false, nullptr, false), s));
+  }
   if (p_down) TIMED_TRY("decode_down", launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, st, s));
   return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
 }
@@ -341,7 +397,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
                 uint32_t flags) {
   const MoeDims m = dims_of(L);
   const WsFlags f = i8_flags(L, T, 1);
-  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, f.a, f.b);
+  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, f.a, f.b, f.stats);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
   TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, false, s));
@@ -358,6 +414,11 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
       xb = w.xb;
     }
     TIMED_TRY("prefill_gateup", launch_prefill_gateup(m, xb, T, w.rb, mt, w.hb, s));
+  }
+  {
+    ImatRows in = rows_of(x, xf == nullptr, norm && xf ? w.rb.inv_rms : nullptr, false);
+    in.round_bf16 = xf != nullptr;  // the expert GEMMs read the bf16 rounding of the f32 input
+    TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, in, rows_of(w.hb, true, nullptr, true), s));
   }
   if (i8_down(L)) {
     const int64_t P = (int64_t)T * m.k;
@@ -456,7 +517,8 @@ DS4Q_API size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok
   if (check_layer(L) || max_tok < 0 || (mode != 0 && mode != 1)) return 0;
   const int T = max_tok > 0 ? max_tok : 1;
   const WsFlags f = i8_flags(L, T, mode);
-  return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b).bytes;
+  return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b,
+                   f.stats).bytes;
 }
 
 DS4Q_API int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits,

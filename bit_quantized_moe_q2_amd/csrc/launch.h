@@ -116,4 +116,28 @@ hipError_t launch_act_decode(const void *src, int64_t n, int bits, float *dst, h
 
 constexpr int PREFILL_TILE_M = 96;
 
+// imatrix statistics of one layer call (imatrix.hip).  Segments of an
+// expert's pairs: the k slots of one token, the active experts (pairs grouped
+// without m-tiles), or the m-tiles.
+enum { IMAT_SEG_SLOTS = 0, IMAT_SEG_ACTIVE = 1, IMAT_SEG_TILES = 2 };
+// Where a statistic reads its rows.  Input statistic: rows of x by token
+// (f32 or bf16), times inv_rms[token] when given (or the row's own inverse
+// RMS computed in place when norm_self: one token), rounded to bf16 when
+// round_bf16.  Down statistic: SwiGLU rows (f32 or bf16) at the sorted
+// position (by_sorted) or the pair index, times the pair's routing weight.
+struct ImatRows {
+  const void *rows = nullptr;
+  bool bf16 = false;
+  const float *inv_rms = nullptr;
+  bool norm_self = false;
+  float eps = 0.f;
+  bool round_bf16 = false;
+  bool by_sorted = false;
+};
+// stat_in [E][D] and stat_down [E][F] (either may be null) += the statistics;
+// partial: [max_seg][max(D, F)] f32 workspace for IMAT_SEG_TILES.
+hipError_t launch_imatrix(const MoeDims &m, const RouteBufs &rb, int seg_mode, int max_seg,
+                          const ImatRows &in, float *stat_in, const ImatRows &h, float *stat_down,
+                          float *partial, hipStream_t s);
+
 }  // namespace ds4q

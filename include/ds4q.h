@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DS4Q_ABI_VERSION 4
+#define DS4Q_ABI_VERSION 5
 
 /* Tensor types.  Numeric values follow the public GGML/GGUF type ids. */
 typedef enum {
@@ -88,7 +88,26 @@ enum {
  * vector makes this a projection), must not overlap y or the workspace;
  * steer_scale finite (> 0 suppresses the direction, < 0 amplifies it).  For a
  * layer-major table dirs [n_layers][n_embd], layer l takes dirs + l*n_embd.
- * NULL = no steering (steer_scale ignored). */
+ * NULL = no steering (steer_scale ignored).
+ *
+ * imatrix statistics ([P1] imatrix passage: per routed expert and input
+ * column, the sum of squares of the activations the expert's projections
+ * read; one entry per tensor of n_expert * n_columns values, expert-major):
+ * with imatrix_in non-NULL, every call adds, for each (token, slot) pair
+ * routed to expert e, n[c]^2 to imatrix_in[e][c] (device f32
+ * [n_expert][n_embd]), n the MoE input row as the path feeds it to the
+ * gate/up projections (decode: fp32, RMS-normalised with
+ * DS4Q_F_RMSNORM_INPUT; prefill: the bf16 row).  The one vector serves both
+ * the gate and the up tensor.  With imatrix_down non-NULL it adds
+ * (p * h[c])^2 to imatrix_down[e][c] (device f32 [n_expert][n_ff]), h the
+ * SwiGLU row as the path feeds it to the down projection (decode fp32,
+ * prefill bf16) and p the pair's routing weight.  Sums are fp32, over an
+ * expert's pairs in sorted order, then added to the arrays (deterministic, no
+ * atomics; accumulate over calls, the caller zeroes them).  16-byte aligned,
+ * overlapping nothing else.  When either is set the workspace of the prefill
+ * and of 2..64-token Q2_K decode grows by (min(P, n_expert) + P/96 + 1) *
+ * max(n_embd, n_ff) * 4 bytes, P = n_tok * n_expert_used
+ * (ds4q_moe_workspace_size reads the descriptor). */
 typedef struct {
   int32_t n_embd, n_ff, n_expert, n_expert_used;
   int32_t type_gate, type_up, type_down; /* ds4q_type */
@@ -97,6 +116,8 @@ typedef struct {
   float norm_eps;
   const float *steer_dir;
   float steer_scale;
+  float *imatrix_in;
+  float *imatrix_down;
 } ds4q_moe_layer;
 
 /* Optional routing outputs (device pointers; any may be NULL). */
@@ -174,7 +195,7 @@ int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits
  * workspace that covers ROUTE, GATEUP and DOWN in that order computes
  * exactly what one ds4q_moe_decode call computes.  Repeating GATEUP or DOWN
  * alone is idempotent without DS4Q_F_ACCUMULATE; with it each DOWN adds
- * again.  Same argument rules and errors as ds4q_moe_decode.  route is
+ * again (and each GATEUP adds the imatrix statistics again).  Same argument rules and errors as ds4q_moe_decode.  route is
  * written by the phase that routes: ROUTE, except for a single token with
  * Q2_K gate/up and down, whose GATEUP launch routes the token itself. */
 int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float *logits,

@@ -175,6 +175,31 @@ def test_layer_steering_validation(lib):
             >= 4096 * 4 + 6 * 2048 * 4)
 
 
+def test_layer_imatrix_validation(lib):
+    """imatrix accumulators of the layer descriptor: 16-byte alignment, no
+    overlap with each other, the output, the workspace or the weights; the
+    m-tile paths reserve partial rows in the workspace only when asked."""
+    x, lg, y, w = BASE + (8 << 32), BASE + (9 << 32), BASE + (10 << 32), BASE + (11 << 32)
+    sa, sb = BASE + (12 << 32), BASE + (13 << 32)
+
+    def pre(L, T=64):
+        need = lib.ds4q_moe_workspace_size(ctypes.byref(L), T, 1)
+        return lib.ds4q_moe_prefill(ctypes.byref(L), x, ds4q.TYPE_F32, lg, T, y, None, w, need, None)
+
+    assert pre(_layer(imatrix_in=sa + 4)) == E_ALIGN
+    assert pre(_layer(imatrix_down=sb + 8)) == E_ALIGN
+    assert pre(_layer(imatrix_in=sa, imatrix_down=sa + 4096)) == E_ALIAS     # the two overlap
+    assert pre(_layer(imatrix_in=y)) == E_ALIAS                                # over the output
+    assert pre(_layer(imatrix_down=w + 1024)) == E_ALIAS                       # inside the workspace
+    assert pre(_layer(imatrix_in=BASE + 256)) == E_ALIAS                       # inside the gate tensor
+    assert pre(_layer(imatrix_in=sa, imatrix_down=sb), T=0) == OK
+    plain = lib.ds4q_moe_workspace_size(ctypes.byref(_layer()), 4096, 1)
+    stats = lib.ds4q_moe_workspace_size(ctypes.byref(_layer(imatrix_in=sa)), 4096, 1)
+    assert stats - plain >= (256 + 4096 * 6 // 96 + 1) * 4096 * 4
+    assert (lib.ds4q_moe_workspace_size(ctypes.byref(_layer(imatrix_in=sa)), 1, 0)
+            == lib.ds4q_moe_workspace_size(ctypes.byref(_layer()), 1, 0))
+
+
 def test_steer_validation(lib):
     f = lib.ds4q_steer
     d, y, o = BASE, BASE + (1 << 30), BASE + (2 << 30)
