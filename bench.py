@@ -52,6 +52,7 @@ def log(*a):
 GATEUP_BYTES = K * 2 * F * Q2K_ROW_D + D * 4 + K * F * 4
 COUNTER_FILE = os.path.join(ROOT, "profiles", "decode_q2k_1tok_hbm_counters.txt")
 KERNEL_SOURCES = ("bit_quantized_moe_q2_amd/csrc/decode_mfma.hip",
+                  "bit_quantized_moe_q2_amd/csrc/mfma_t1.h",
                   "bit_quantized_moe_q2_amd/csrc/common.h")
 
 

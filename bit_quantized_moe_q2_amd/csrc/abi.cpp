@@ -337,21 +337,27 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
   const SteerArgs st = steer_of(L, w.stage);
   const bool p_route = phases & DS4Q_PHASE_ROUTE, p_gu = phases & DS4Q_PHASE_GATEUP,
              p_down = phases & DS4Q_PHASE_DOWN;
-  if (T == 1 && m.tg == DS4Q_TYPE_Q2_K && m.td == DS4Q_TYPE_Q2_K) {
-    // One token on int8 matrix cores: the gate/up launch routes the token
-    // itself, so the routing phase has nothing of its own to launch and the
-    // routing outputs follow the gate/up launch.
+  if (T == 1) {
+    // One token on int8 matrix cores (either block format, chosen per
+    // tensor): the gate/up launch routes the token itself, so the routing
+    // phase has nothing of its own to launch and the routing outputs follow
+    // the gate/up launch.
+    auto t1 = [&](int phase) {
+      const int type = phase == 1 ? m.tg : m.td;
+      return type == DS4Q_TYPE_Q2_K
+                 ? launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, phase, st, s)
+                 : launch_decode_q41_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, phase, st, s);
+    };
     if (p_gu) {
-      TIMED_TRY("decode_gateup", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 1, st, s));
+      TIMED_TRY("decode_gateup", t1(1));
       // the grouping pass (expert order) runs only when asked for
       if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
       ImatRows in = rows_of(x, false, nullptr, false);
       in.norm_self = norm;  // the gate/up launch keeps the inverse RMS to itself
       in.eps = L->norm_eps;
-      TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_SLOTS, m.k, in, rows_of(w.h, false, nullptr, false), s));
+      if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_SLOTS, m.k, in, rows_of(w.h, false, nullptr, false), s));
     }
-    if (p_down)
-      TIMED_TRY("decode_down", launch_decode_q2k_t1(m, x, logits, norm, L->norm_eps, w.rb, w.h, y, acc, 2, st, s));
+    if (p_down) TIMED_TRY("decode_down", t1(2));
     return p_gu ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
   if (f.a) {
@@ -359,13 +365,13 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     // h and o in sorted-pair order
     const int mt = max_tiles(T, m.E, m.k);
     if (p_route) {
-      TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, false, s));
+      TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, s));
       TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
     }
     if (p_gu) {
       TIMED_TRY("prep_i8", launch_prep_i8(x, true, false, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xq, s));
       TIMED_TRY("decode_gateup", launch_decode_i8_gateup(m, w.xq, T, w.rb, mt, w.h, s));
-      TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
+      if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
                                         rows_of(w.h, false, nullptr, true), s));
     }
     if (p_down) {
@@ -376,15 +382,13 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
   if (p_route) {
-    TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, T == 1, s));
-    // For T == 1 the top-k kernel already wrote the active-expert lists (slot
-    // order); the grouping pass (expert order) runs only when asked for.
-    if (T > 1 || wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+    TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, s));
+    TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
   }
   if (p_gu) {
     TIMED_TRY("decode_gateup", launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
     const int na = T * m.k < m.E ? T * m.k : m.E;
-    TIMED_TRY("imatrix", launch_stats(L, m, w, T == 1 ? IMAT_SEG_SLOTS : IMAT_SEG_ACTIVE, T == 1 ? m.k : na,
+    if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_ACTIVE, na,
                                       rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
                                       rows_of(w.h, false, nullptr, false), s));
   }
@@ -400,7 +404,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, f.a, f.b, f.stats);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
-  TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, false, s));
+  TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, s));
   TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
   const int mt = max_tiles(T, m.E, m.k);
   if (i8_gateup(L)) {
@@ -418,7 +422,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   {
     ImatRows in = rows_of(x, xf == nullptr, norm && xf ? w.rb.inv_rms : nullptr, false);
     in.round_bf16 = xf != nullptr;  // the expert GEMMs read the bf16 rounding of the f32 input
-    TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, in, rows_of(w.hb, true, nullptr, true), s));
+    if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, in, rows_of(w.hb, true, nullptr, true), s));
   }
   if (i8_down(L)) {
     const int64_t P = (int64_t)T * m.k;
@@ -508,7 +512,7 @@ DS4Q_API int ds4q_route(const float *logits, int32_t n_tok, int32_t n_expert, in
     return DS4Q_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace w(static_cast<uint8_t *>(workspace), 0, 0, n_expert, k, n_tok, 2);
-  HIP_TRY(launch_topk(logits, n_tok, n_expert, k, nullptr, 0, 0.f, w.rb, false, s));
+  HIP_TRY(launch_topk(logits, n_tok, n_expert, k, nullptr, 0, 0.f, w.rb, s));
   if (wants_grouping(out)) HIP_TRY(launch_group(n_tok, n_expert, k, 0, w.rb, s));
   return copy_route(out, w.rb, n_tok, n_expert, k, s);
 }

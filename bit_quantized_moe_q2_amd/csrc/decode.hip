@@ -239,43 +239,6 @@ __global__ __launch_bounds__(256) void gateup_kernel(const uint8_t *__restrict__
 
 // ---------------------------------------------------------------- decode down
 
-// Single token: one wave per routing slot (blockDim = 64*k); slot partials
-// meet in LDS and are summed in slot order: y (+)= sum_j w_j * (W2[e_j] h_j).
-template <int TYPE, int L, int RS>
-__global__ __launch_bounds__(512) void down_slots_kernel(const uint8_t *__restrict__ down, int D,
-                                                         int k, const float *__restrict__ h,
-                                                         RouteBufs rb, float *__restrict__ y,
-                                                         int accumulate, float *__restrict__ stage) {
-  constexpr int RPW = 64 / L;
-  constexpr int ROWS = RS * RPW;
-  __shared__ float part[8][ROWS];
-  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
-  const int c = lane % L, rs = lane / L;
-  const int F = 64 * L;
-  const int64_t rbytes = row_bytes(TYPE, F);
-  const int row0 = blockIdx.x * ROWS;
-  const int e = rb.ids[j];
-  const uint8_t *W2 = down + (int64_t)e * D * rbytes;
-  XSlice<TYPE> hs;
-  hs.load(h + (int64_t)j * F, c, 1.0f);
-  Chunk<TYPE> ch[RS];
-#pragma unroll
-  for (int i = 0; i < RS; ++i) ch[i].load(W2 + (int64_t)(row0 + i * RPW + rs) * rbytes, c);
-#pragma unroll
-  for (int i = 0; i < RS; ++i) {
-    const float v = group_sum<L>(ch[i].dot(hs));
-    if (c == 0) part[j][i * RPW + rs] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < ROWS) {
-    const int r = row0 + threadIdx.x;
-    float acc = 0.f;
-    for (int s = 0; s < k; ++s) acc = fmaf(rb.w[s], part[s][threadIdx.x], acc);
-    if (stage) stage[r] = acc;  // steered by the launch that follows
-    else y[r] = accumulate ? y[r] + acc : acc;
-  }
-}
-
 // Several tokens: grid x = row blocks of D, y = active experts; every pair of
 // the expert writes o[p][row] (unweighted); launch_combine sums the slots.
 template <int TYPE, int L, int RS>
@@ -441,20 +404,6 @@ hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const Rou
                               hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int L = m.F / 64;
-  if (T == 1) {
-    DS4Q_DISPATCH_L(L, {
-      constexpr int RS = LL == 64 ? 2 : 4;
-      const int per_wg = RS * (64 / LL);
-      const dim3 grid(m.D / per_wg);
-      if (m.td == TYPE_Q2_K)
-        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0, st.dir ? st.stage : nullptr);
-      else
-        hipLaunchKernelGGL((down_slots_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(64 * m.k), 0, s, m.down, m.D, m.k, h, rb, y, accumulate ? 1 : 0, st.dir ? st.stage : nullptr);
-    });
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess || !st.dir) return err;
-    return launch_steer(st.dir, st.scale, st.stage, 1, m.D, y, accumulate, s);
-  }
   const int max_active = T * m.k < m.E ? T * m.k : m.E;
   DS4Q_DISPATCH_L(L, {
     constexpr int RS = row_slots<LL>();

@@ -31,7 +31,7 @@ struct RouteBufs {
 
 // Top-k + softmax per token; with x != NULL also the per-token inverse RMS.
 hipError_t launch_topk(const float *logits, int T, int E, int k, const float *x, int D, float eps,
-                       const RouteBufs &rb, bool single_token_lists, hipStream_t s);
+                       const RouteBufs &rb, hipStream_t s);
 // Counting-sort grouping of the T*k pairs; tile_m > 0 also builds m-tiles.
 hipError_t launch_group(int T, int E, int k, int tile_m, const RouteBufs &rb, hipStream_t s);
 
@@ -64,6 +64,12 @@ hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const Rou
 // (into rb.ids / rb.w) + gate/up + SwiGLU into h, 2 = down + weighted combine
 // into y.
 hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *logits,
+                                bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
+                                bool accumulate, int phase, const SteerArgs &st, hipStream_t s);
+// The same two phases on Q4_1 tensors (decode_q41.hip).  The gate/up and down
+// kernels of the two formats share the workspace contract, so a layer may mix
+// them (phase 1 by the gate/up type, phase 2 by the down type).
+hipError_t launch_decode_q41_t1(const MoeDims &m, const float *x, const float *logits,
                                 bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
                                 bool accumulate, int phase, const SteerArgs &st, hipStream_t s);
 // y[t] (+)= sum_j w[t][j] * o[row(t, j)]; row = pair index, or sorted

@@ -18,7 +18,7 @@ constexpr int MAX_E = ROUTE_MAX_E;
 // One wave per token.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, const float *__restrict__ x, int D,
-                                                   float eps, RouteBufs rb, int single) {
+                                                   float eps, RouteBufs rb) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -29,15 +29,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   if (lane < k) {
     rb.ids[t * k + lane] = my_id;
     rb.w[t * k + lane] = my_w;
-    if (single) {
-      rb.act_expert[lane] = my_id;
-      rb.act_begin[lane] = lane;
-      rb.pairs[lane] = lane;
-    }
-  }
-  if (single && lane == 0) {
-    rb.act_begin[k] = k;
-    *rb.n_active = k;
   }
   if (x) {
     const float *xr = x + (int64_t)t * D;
@@ -116,10 +107,10 @@ __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int ti
 }  // namespace
 
 hipError_t launch_topk(const float *logits, int T, int E, int k, const float *x, int D, float eps,
-                       const RouteBufs &rb, bool single_token_lists, hipStream_t s) {
+                       const RouteBufs &rb, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, x, D, eps,
-                     rb, single_token_lists ? 1 : 0);
+                     rb);
   return hipGetLastError();
 }
 

@@ -166,12 +166,14 @@ size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t
  * down input; [P2] top-k routing): for each token t,
  *   y_t (+)= sum_j p_tj * W2[e_tj] (silu(W1[e_tj] n_t) * (W3[e_tj] n_t)),
  * n_t = x_t (or its RMS norm with DS4Q_F_RMSNORM_INPUT), fp32 in and out.
- * With Q2_K weights the products run on int8 matrix cores against the exact
- * integers sc*q: the input and SwiGLU vectors enter as int8 digits times a
- * scale (three digits per 256-value block for one token, two per row for
- * 2..64 tokens: residual below 2^-15 of the row maximum), the min term in
- * fp32 (one token) or bf16 hi + lo (2..64 tokens), the SwiGLU rows stay
- * fp32; Q4_1 runs on fp32 vector arithmetic.
+ * One token runs on int8 matrix cores for either format (chosen per tensor):
+ * the input and SwiGLU vectors enter as three int8 digits per value times a
+ * scale per 256 values (residual below 2^-23 of the chunk maximum) against
+ * the exact integers sc*q (Q2_K) or q (Q4_1), with the min / offset term in
+ * fp32.  2..64 tokens on Q2_K weights throughout run on the grouped int8
+ * kernels (two digits per row: residual below 2^-15 of the row maximum, min
+ * term with bf16 hi + lo weights); with Q4_1 or mixed types they run on fp32
+ * vector arithmetic.  The SwiGLU rows stay fp32.
  * x: device f32 [n_tok][n_embd]; logits: device f32 [n_tok][n_expert];
  * y: device f32 [n_tok][n_embd] — may be the same pointer as x (in-place
  * residual with DS4Q_F_ACCUMULATE), must not partially overlap it.
