@@ -13,12 +13,20 @@
 // ("【#2】ds4.c 해독하기": w1 = gate, w3 = up, w2 = down, SwiGLU, and the
 // routing weight multiplies the routed SwiGLU row before the down projection.)
 //
-// Data movement.  The A tile (m-tile rows x 256 K, bf16) is staged in LDS once
-// per K step and read by all four waves.  B never touches LDS: each lane
-// dequantises exactly the 8 weights its MFMA B operand holds — 8 nibbles of
-// one half of a Q4_1 block — straight from global memory into registers (fp32
-// fma, one rounding, then round-to-nearest-even bf16).  Each weight of the
-// expert's n-tile is dequantised once per m-tile.
+// Data movement (eight waves; wave w owns 16 gate + 16 up rows, or 32 down
+// rows, and all the tile's rows of A).  K advances in steps of 256 values
+// (eight Q4_1 blocks).  The next step's A tile (96 rows x 512 B of bf16) goes
+// to the other of two LDS buffers by global_load_lds_dwordx4 (one 1-KiB
+// instruction = 2 rows x 32 chunks; chunk c of row r is stored at chunk
+// position c ^ (r & 15), so the 16 lanes reading one chunk column touch 16
+// distinct bank groups), and the raw bytes of the next step's weights go to
+// registers, while the current step computes.  One wait and one barrier per
+// step.  B never touches LDS: each lane dequantises exactly the 8 weights its
+// MFMA B operand holds -- 8 nibbles of one half of a Q4_1 block -- from those
+// registers (fp32 fma, one rounding, then round-to-nearest-even bf16); each
+// weight of the n-tile is dequantised once per m-tile.  The step loop is
+// instantiated per count of live 16-row subtiles, so it has no branches;
+// rows of absent pairs repeat row 0 and are never stored.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8*(l/16) .. +7],
 // B lane l holds B[8*(l/16) .. +7][l%16] (the same K slots as A),
@@ -34,10 +42,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int TM = PREFILL_TILE_M;  // pairs per m-tile
-constexpr int KS = 256;             // K per LDS stage
-constexpr int LDA = KS + 8;         // padded LDS row (bf16 elements)
-constexpr int MT = TM / 16;         // 16-row MFMA tiles along M
+constexpr int TM = PREFILL_TILE_M;        // pairs per m-tile
+constexpr int MT = TM / 16;               // 16-row MFMA subtiles along M
+constexpr int KS = 256;                   // K per step (eight Q4_1 blocks)
+constexpr int NJ = KS / 64;               // Q4_1 block pairs per step (two MFMAs each)
+constexpr int AROWB = KS * 2;             // bytes of one A row per step
+constexpr int ASTAGE = TM * AROWB;        // one LDS buffer (48 KiB)
+constexpr int STEP_BYTES = KS / 32 * BB_Q41;  // bytes of one weight row per step
+
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
@@ -49,150 +61,221 @@ __device__ __forceinline__ bf16x8 to_frag(uint32_t a, uint32_t b, uint32_t c, ui
   return __builtin_bit_cast(bf16x8, (u32x4){a, b, c, d});
 }
 
-// Raw bytes of one weight row's K step (eight Q4_1 blocks) that lane group g
-// needs: MFMA step j = Q4_1 block j of the K step, values 8g + i, i.e.
-// nibbles of qs[8(g&1) + i], low for g < 2, high for g >= 2.
-struct Q41Step {
-  const uint8_t *base;
-  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk) { base = blk; }
-  template <int J>
-  __device__ __forceinline__ bf16x8 frag(int g) const {
-    const uint8_t *blk = base + J * BB_Q41;
-    const uint32_t dm = ld32(blk);
-    const int sh = 4 * (g >> 1);
-    const uint32_t t0 = (ld32(blk + 4 + 8 * (g & 1)) >> sh) & 0x0F0F0F0Fu;
-    const uint32_t t1 = (ld32(blk + 8 + 8 * (g & 1)) >> sh) & 0x0F0F0F0Fu;
+__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+// Raw bytes of a pair of Q4_1 blocks (2jp, 2jp+1) for lane group g: block
+// b = 2jp + (g >> 1), half p = g & 1 -- 12 bytes from offset 8p, i.e. (d, m)
+// and code bytes 0..7 for p = 0, code bytes 4..15 for p = 1; the lane's code
+// bytes 8p..8p+7 are dwords 1 and 2 either way.  Their low nibbles are values
+// 8p..8p+7 of block b (the lane's B operand of the pair's "low" MFMA), their
+// high nibbles values 16+8p..16+8p+7 (of the "high" MFMA); so the pair's two
+// MFMAs cover its 64 values with one load per lane.  Lanes of half 1 take
+// (d, m) from their half-0 partner 16 lanes below (v_permlane16_swap).
+typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+struct Q41Raw {
+  uint32_t x, c0, c1;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ pair, int g) {
+    const u32x3a v = *reinterpret_cast<const u32x3a *>(pair + (g >> 1) * BB_Q41 + 8 * (g & 1));
+    x = v.x;
+    c0 = v.y;
+    c1 = v.z;
+  }
+  // B operands of the low and the high MFMA
+  __device__ __forceinline__ void frags(bf16x8 &lo, bf16x8 &hi) const {
+    // the even 16-lane row of each pair (p = 0) holds (d, m); both rows get it
+    const uint32_t dm = __builtin_amdgcn_permlane16_swap(x, x, false, false)[0];
+    uint32_t l0 = c0 & 0x0F0F0F0Fu, l1 = c1 & 0x0F0F0F0Fu;
+    uint32_t h0 = (c0 >> 4) & 0x0F0F0F0Fu, h1 = (c1 >> 4) & 0x0F0F0F0Fu;
+    // opaque to the combiner, so that each byte converts with one
+    // v_cvt_f32_ubyteN instead of a bit-field extract and a convert
+    asm("" : "+v"(l0), "+v"(l1), "+v"(h0), "+v"(h1));
     const float d = f16lo(dm), m = f16hi(dm);
-    return to_frag(pack_bf16(fmaf(d, ub0(t0), m), fmaf(d, ub1(t0), m)),
-                   pack_bf16(fmaf(d, ub2(t0), m), fmaf(d, ub3(t0), m)),
-                   pack_bf16(fmaf(d, ub0(t1), m), fmaf(d, ub1(t1), m)),
-                   pack_bf16(fmaf(d, ub2(t1), m), fmaf(d, ub3(t1), m)));
+    lo = to_frag(pack_bf16(fmaf(d, ub0(l0), m), fmaf(d, ub1(l0), m)),
+                 pack_bf16(fmaf(d, ub2(l0), m), fmaf(d, ub3(l0), m)),
+                 pack_bf16(fmaf(d, ub0(l1), m), fmaf(d, ub1(l1), m)),
+                 pack_bf16(fmaf(d, ub2(l1), m), fmaf(d, ub3(l1), m)));
+    hi = to_frag(pack_bf16(fmaf(d, ub0(h0), m), fmaf(d, ub1(h0), m)),
+                 pack_bf16(fmaf(d, ub2(h0), m), fmaf(d, ub3(h0), m)),
+                 pack_bf16(fmaf(d, ub0(h1), m), fmaf(d, ub1(h1), m)),
+                 pack_bf16(fmaf(d, ub2(h1), m), fmaf(d, ub3(h1), m)));
   }
 };
 
-// SWIGLU: n-tile = 128 rows of F for gate and up (wave w: rows 32w..32w+31 of
-// both); otherwise n-tile = 256 down rows (wave w: rows 64w..64w+63).
+struct StepCtx {
+  const uint8_t *abase;     // A rows (bytes)
+  int64_t aoff[MT];         // byte offsets of the lane's DMA chunks (row part + chunk)
+  int aoffj[2 * NJ];        // LDS offsets of the lane's A chunks, low and high MFMA of pair jp
+  const uint8_t *brow[2];   // the lane's two weight rows
+  int w, g;
+};
+
+// Wait for every request of this wave, then a bare workgroup barrier (a
+// workgroup fence would add nothing: the wait already covers the DMA).
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The step loop for NMT live subtiles: acc[i][t] += A(subtile i) * B(t)^T.
+// Every wave issues the same requests every step (the A rows of NU DMA
+// loads, rows >= 16*NMT repeating row 0 and never read, and its weights);
+// the step past the end requests the last step again, so the loop has no
+// branches and the only wait is the one at the step's end.
+template <int NMT>
+__device__ __forceinline__ void q41_loop(const StepCtx &cx, int ns, uint8_t *As0, uint8_t *As1,
+                                         f32x4 (&acc)[MT][2]) {
+  constexpr int NU = NMT;  // DMA loads per wave (2 rows each): rows 0 .. 16*NU-1
+  const int w = cx.w, g = cx.g;
+  auto issue_a = [&](int s, uint8_t *As) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      dma16(cx.abase + (int64_t)s * AROWB + cx.aoff[u], As + (8 * u + w) * 1024);
+  };
+  auto issue_w = [&](int s, Q41Raw (&r)[2][NJ]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) r[t][j].load(cx.brow[t] + (int64_t)s * STEP_BYTES + 2 * j * BB_Q41, g);
+  };
+  auto compute = [&](const uint8_t *As, const Q41Raw (&r)[2][NJ]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      bf16x8 b[2][2];  // [t][low/high]
+      r[0][j].frags(b[0][0], b[0][1]);
+      r[1][j].frags(b[1][0], b[1][1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 a[NMT];
+#pragma unroll
+        for (int i = 0; i < NMT; ++i)
+          a[i] = *reinterpret_cast<const bf16x8 *>(As + i * (16 * AROWB) + cx.aoffj[2 * j + h]);
+#pragma unroll
+        for (int i = 0; i < NMT; ++i) {
+          acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[0][h], acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[1][h], acc[i][1], 0, 0, 0);
+        }
+      }
+    }
+  };
+  Q41Raw rw0[2][NJ], rw1[2][NJ];
+  issue_a(0, As0);
+  issue_w(0, rw0);
+  step_barrier();
+  for (int s = 0; s + 1 < ns; s += 2) {
+    // nothing is outstanding here (the last step ended with a full wait);
+    // saying so at the loop head keeps the compiler from adding a wait for
+    // the loads issued below before this step's computation
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(s + 1, As1);
+    issue_w(s + 1, rw1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As0, rw0);
+    __builtin_amdgcn_sched_barrier(0);
+    step_barrier();  // step s+1 landed; every wave is done with As0
+    const int s2 = s + 2 < ns ? s + 2 : ns - 1;
+    issue_a(s2, As0);
+    issue_w(s2, rw0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As1, rw1);
+    __builtin_amdgcn_sched_barrier(0);
+    step_barrier();
+  }
+  if (ns & 1) compute(As0, rw0);  // a single step (K = 256)
+}
+
+// SWIGLU: n-tile = 128 rows of F for gate and up (wave w: row 16w + n of
+// both); otherwise n-tile = 256 down rows (wave w: rows 32w + 16t + n).
 template <bool SWIGLU>
-__global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
+__global__ __launch_bounds__(512) void prefill_q41_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint16_t *__restrict__ A, int gather_tokens, int kslots, RouteBufs rb, int n_ntiles,
     uint16_t *__restrict__ hb, float *__restrict__ o) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[TM * LDA];
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[ASTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[ASTAGE];
   __shared__ int arow[TM];
 
   int mtile, ntile;
   if (!xcd_tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];
   const int end = rb.offsets[e + 1];
   const int valid = end - start < TM ? end - start : TM;
-  const int n_mt = (valid + 15) >> 4;
+  const int nmt = (valid + 15) >> 4;
 
   if (tid < TM) {
-    int src = -1;
-    if (tid < valid) src = gather_tokens ? rb.pairs[start + tid] / kslots : start + tid;
-    arow[tid] = src;
+    const int m = tid < valid ? tid : 0;  // absent rows repeat row 0; never stored
+    arow[tid] = gather_tokens ? rb.pairs[start + m] / kslots : start + m;
   }
+  __syncthreads();
 
+  StepCtx cx;
+  cx.w = w;
+  cx.g = g;
+  cx.abase = reinterpret_cast<const uint8_t *>(A);
+  // DMA load I = 8u + w covers rows 2I, 2I+1: lane l takes row 2I + l/32 and
+  // stores it at chunk position l%32, which holds data chunk (l%32) ^ (row%16)
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int r = 2 * (8 * u + w) + (lane >> 5);
+    const int c = (lane & 31) ^ (r & 15);
+    cx.aoff[u] = (int64_t)arow[r] * (2 * K) + c * 16;
+  }
+  // pair jp: block b = 2jp + (g >> 1); the low MFMA reads chunk 4b + (g & 1)
+  // (values 8p..8p+7), the high one chunk 4b + 2 + (g & 1)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = 4 * (2 * j + (g >> 1)) + (g & 1);
+    cx.aoffj[2 * j] = n * AROWB + ((c ^ n) * 16);
+    cx.aoffj[2 * j + 1] = n * AROWB + (((c + 2) ^ n) * 16);
+  }
   const int64_t rbytes = row_bytes(TYPE_Q4_1, K);
-  const uint8_t *brow[4];
+  int wrow[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    int r;
-    const uint8_t *Wt;
+  for (int t = 0; t < 2; ++t) {
     if constexpr (SWIGLU) {
-      r = ntile * 128 + 32 * w + 16 * (t & 1) + n;
-      Wt = (t < 2) ? W0 : W1;
+      wrow[t] = ntile * 128 + 16 * w + n;
+      cx.brow[t] = (t == 0 ? W0 : W1) + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
     } else {
-      r = ntile * 256 + 64 * w + 16 * t + n;
-      Wt = W0;
+      wrow[t] = ntile * 256 + 32 * w + 16 * t + n;
+      cx.brow[t] = W0 + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
     }
-    brow[t] = Wt + ((int64_t)e * rows_per_expert + r) * rbytes;
   }
 
-  f32x4 acc[MT][4];
+  f32x4 acc[MT][2];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  const int step_bytes = (int)row_bytes(TYPE_Q4_1, KS);
-  for (int kb = 0; kb < K / KS; ++kb) {
-    __syncthreads();
-    // stage A: 128 rows x 256 bf16 = 32 chunks of 16 B per row, four chunks
-    // per thread at a time (bounds the registers in flight)
-#pragma unroll
-    for (int i0 = 0; i0 < TM * (KS / 8) / 256; i0 += 4) {
-      uint4 v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // rows of absent pairs read row 0 and store zeros (no branch)
-        const int c = tid + 256 * (i0 + i);
-        const int src = arow[c >> 5];
-        const uint4 t = *reinterpret_cast<const uint4 *>(A + (int64_t)(src < 0 ? 0 : src) * K + kb * KS + (c & 31) * 8);
-        v[i] = src < 0 ? make_uint4(0u, 0u, 0u, 0u) : t;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * (i0 + i);
-        *reinterpret_cast<uint4 *>(&As[(c >> 5) * LDA + (c & 31) * 8]) = v[i];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-
-    Q41Step rs[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) rs[t].load(brow[t] + (int64_t)kb * step_bytes);
-
-    // K order inside the step: MFMA step J, lane group g takes the step's
-    // values 32J + 8g .. +7 (the same for A and B).
-#define DS4Q_STEP(J)                                                                   \
-  {                                                                                    \
-    /* A fragments first (rows of absent pairs hold zeros), so that their    */ \
-    /* LDS latency hides behind the weight dequantisation                    */ \
-    const int koff = 32 * (J) + 8 * g;                                                 \
-    bf16x8 a[MT];                                                                      \
-    _Pragma("unroll") for (int i = 0; i < MT; ++i)                                     \
-        a[i] = *reinterpret_cast<const bf16x8 *>(&As[(16 * i + n) * LDA + koff]);      \
-    bf16x8 b[4];                                                                       \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) b[t] = rs[t].template frag<J>(g);    \
-    _Pragma("unroll") for (int i = 0; i < MT; ++i) {                                   \
-      if (i < n_mt) {                                                                  \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t)                                  \
-            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[t], acc[i][t], 0, 0, 0); \
-      }                                                                                \
-    }                                                                                  \
-  }
-    DS4Q_STEP(0) DS4Q_STEP(1) DS4Q_STEP(2) DS4Q_STEP(3)
-    DS4Q_STEP(4) DS4Q_STEP(5) DS4Q_STEP(6) DS4Q_STEP(7)
-#undef DS4Q_STEP
+  for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int ns = K / KS;
+  switch (nmt) {
+    case 1: q41_loop<1>(cx, ns, As0, As1, acc); break;
+    case 2: q41_loop<2>(cx, ns, As0, As1, acc); break;
+    case 3: q41_loop<3>(cx, ns, As0, As1, acc); break;
+    case 4: q41_loop<4>(cx, ns, As0, As1, acc); break;
+    case 5: q41_loop<5>(cx, ns, As0, As1, acc); break;
+    default: q41_loop<6>(cx, ns, As0, As1, acc); break;
   }
 
-  // epilogue
+  // epilogue: rows of live pairs only
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    if (i >= n_mt) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m = 16 * i + 4 * g + q;
       if (m >= valid) continue;
       const int64_t pos = start + m;
       if constexpr (SWIGLU) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = ntile * 128 + 32 * w + 16 * t + n;
-          const float hv = silu(acc[i][t][q]) * acc[i][t + 2][q];
-          hb[pos * rows_per_expert + r] = (uint16_t)bf16_rne_bits(hv);
-        }
+        const float hv = silu(acc[i][0][q]) * acc[i][1][q];
+        hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(hv);
       } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = ntile * 256 + 64 * w + 16 * t + n;
-          o[pos * rows_per_expert + r] = acc[i][t][q];
-        }
+        for (int t = 0; t < 2; ++t) o[pos * rows_per_expert + wrow[t]] = acc[i][t][q];
       }
     }
   }
@@ -232,7 +315,7 @@ hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, co
   if (T == 0) return hipSuccess;
   const int nn = m.F / 128;
   const dim3 grid(grid_for(max_tiles, nn));
-  hipLaunchKernelGGL((prefill_gemm_kernel<true>), grid, dim3(256), 0, s, m.gate, m.up, m.D, m.F, xb,
+  hipLaunchKernelGGL((prefill_q41_kernel<true>), grid, dim3(512), 0, s, m.gate, m.up, m.D, m.F, xb,
                      1, m.k, rb, nn, hb, nullptr);
   return hipGetLastError();
 }
@@ -242,7 +325,7 @@ hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, cons
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
   const dim3 grid(grid_for(max_tiles, nn));
-  hipLaunchKernelGGL((prefill_gemm_kernel<false>), grid, dim3(256), 0, s, m.down, nullptr, m.F, m.D,
+  hipLaunchKernelGGL((prefill_q41_kernel<false>), grid, dim3(512), 0, s, m.down, nullptr, m.F, m.D,
                      hb, 0, m.k, rb, nn, nullptr, o);
   return hipGetLastError();
 }
