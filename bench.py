@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-aux", action="store_true", help="skip the codec and steering figures")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (matvec/dequant, 64-token decode, Zipf and Q4_1 "
+                         "prefill, 43-layer prefill)")
     ap.add_argument("--stack-tokens", type=int, default=50,
                     help="tokens timed through each 43-layer stack")
     ap.add_argument("--cpu-sample", type=int, default=1024,
@@ -353,10 +356,10 @@ def main():
         log(f"prefill combine: {comb_us:.1f} us, steered {comb_steer_us:.1f} us")
 
     # ------------------------------------------------------------ stack (secondary)
+    q41 = []
     if not args.no_stack and NL == 43:
         # mixed stack: the first 37 Q2_K layers above plus 6 Q4_1 layers
         log("generating 6 layers of Q4_1 experts for the mixed stack ...")
-        q41 = []
         for l in range(37, 43):
             t = {}
             for name, rows, cols in (("gate", F, D), ("up", F, D), ("down", D, F)):
@@ -413,6 +416,116 @@ def main():
                 base_us = result["stack_decode"]["q2_k"]["us_per_token"]
                 result["stack_decode"][name]["steer_us_per_layer"] = round((t_ms * 1e3 - base_us) / NL, 3)
             del gs, ws_st
+
+    # ------------------------------------------------------------ other workloads (secondary)
+    if not args.no_configs and NL == 43:
+        cf = {}
+        evs = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def graph_time(fn, reps):
+            """ms per replay of a graph of fn (after one eager call)."""
+            fn()
+            torch.cuda.synchronize()
+            gr = capture(fn)
+            gr.replay()
+            torch.cuda.synchronize()
+            evs[0].record()
+            for _ in range(reps):
+                gr.replay()
+            evs[1].record()
+            torch.cuda.synchronize()
+            return evs[0].elapsed_time(evs[1]) / reps
+
+        # single matrices (2048 x 4096): each expert's gate tensor is one, so
+        # 128 distinct ones rotate through the graphs (352 MB of Q2_K, beyond
+        # the 256 MB MALL; outputs of the dequant rotate over 268 MB)
+        NM = 128
+        mats = {"q2_k": (ds4q.TYPE_Q2_K, layers[0].gate, 2048 * 4096 // 256 * 84)}
+        if q41:
+            mats["q4_1"] = (ds4q.TYPE_Q4_1, q41[0].gate, 2048 * 4096 // 32 * 20)
+        xv = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 10), 1, D)).to(dev)
+        yv = torch.empty(NM, F, device=dev)
+        deq = [torch.empty(F * D, device=dev) for _ in range(8)]
+        for qn, (qt, base, mb) in mats.items():
+            ms = graph_time(lambda: [ds4q.ds4q_matvec(qt, base + i * mb, F, D, xv, 1, yv[i]) for i in range(NM)], 20) / NM
+            b = mb + D * 4 + F * 4
+            cf[f"matvec_{qn}_2048x4096"] = {"us": round(ms * 1e3, 3), "bytes": b,
+                                            "gbps": round(b / (ms / 1e3) / 1e9, 1)}
+            ms = graph_time(lambda: [ds4q.ds4q_dequant(qt, base + i * mb, F, D, ds4q.TYPE_F32, deq[i % 8])
+                                     for i in range(NM)], 10) / NM
+            b = mb + F * D * 4
+            cf[f"dequant_{qn}_f32_2048x4096"] = {"us": round(ms * 1e3, 3), "bytes": b,
+                                                 "gbps": round(b / (ms / 1e3) / 1e9, 1)}
+        del deq, yv
+
+        # one layer decode of 64 tokens, cycling over the 43 layers
+        T64 = 64
+        x64 = torch.from_numpy(np.stack([synth.x_f32(synth.stream_key(seed, 11, l), T64, D) for l in range(NL)])).to(dev)
+        lg64n = np.stack([synth.logits_normal(synth.stream_key(seed, 12, l), T64, E) for l in range(NL)])
+        lg64 = torch.from_numpy(lg64n).to(dev)
+        y64 = torch.empty(NL, T64, D, device=dev)
+        wsb64 = ds4q.ds4q_moe_workspace_size(layers[0], T64, 0)
+        ws64 = [torch.empty(wsb64, dtype=torch.uint8, device=dev) for _ in range(NL)]
+        ms = graph_time(lambda: [ds4q.ds4q_moe_decode(layers[l], x64[l], lg64[l], T64, y64[l], None, ws64[l])
+                                 for l in range(NL)], 5) / NL
+        touched = np.mean([len(np.unique(np.argsort(-lg64n[l], axis=1, kind="stable")[:, :K])) for l in range(NL)])
+        b = touched * 3 * 2048 * 4096 // 256 * 84
+        cf["decode_64tok_q2_k"] = {"us_per_layer": round(ms * 1e3, 2), "tokens_per_s": round(T64 / (ms / 1e3), 1),
+                                   "experts_touched": round(float(touched), 1), "weight_bytes": int(b),
+                                   "gbps": round(b / (ms / 1e3) / 1e9, 1)}
+        del x64, lg64, y64, ws64
+
+        # 4096-token prefill chunks: Zipf(1.1) routing, and Q4_1 weights
+        if not args.no_prefill:
+            Tp = 4096
+            xbz = torch.from_numpy(synth.x_bf16(synth.stream_key(seed, 3), Tp, D).view(np.int16)).to(dev)
+            lgz = torch.from_numpy(synth.logits_zipf(synth.stream_key(seed, 13), Tp, E)).to(dev)
+            ypz = torch.empty(Tp, D, device=dev)
+            wsz = torch.empty(ds4q.ds4q_moe_workspace_size(layers[0], Tp, 1), dtype=torch.uint8, device=dev)
+            ms = graph_time(lambda: ds4q.ds4q_moe_prefill(layers[0], xbz, ds4q.TYPE_BF16, lgz, Tp, ypz, None, wsz), 10)
+            cf["prefill_4096tok_q2_k_zipf"] = {"ms": round(ms, 4), "tflops": round(Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
+            if q41:
+                lgu = torch.from_numpy(synth.logits_normal(synth.stream_key(seed, 4), Tp, E)).to(dev)
+                wsq = torch.empty(ds4q.ds4q_moe_workspace_size(q41[0], Tp, 1), dtype=torch.uint8, device=dev)
+                ms = graph_time(lambda: ds4q.ds4q_moe_prefill(q41[0], xbz, ds4q.TYPE_BF16, lgu, Tp, ypz, None, wsq), 10)
+                cf["prefill_4096tok_q4_1_uniform"] = {"ms": round(ms, 4),
+                                                      "tflops": round(Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
+                del wsq, lgu
+            del wsz, lgz
+
+            # one 4096-token chunk through the 43-layer stack (RMS norm, bf16
+            # layer inputs, residual), Q2_K and mixed
+            lgs_p = torch.from_numpy(np.stack([synth.logits_normal(synth.stream_key(seed, 14, l), Tp, E)
+                                               for l in range(NL)])).to(dev)
+            x0p = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 15), Tp, D)).to(dev)
+            xrun = torch.empty_like(x0p)
+            for name, lays in (("q2_k", layers), ("mixed", layers[:37] + q41)):
+                if len(lays) != NL:
+                    continue
+                wsp = torch.empty(max(ds4q.ds4q_moe_workspace_size(L, Tp, 1) for L in lays), dtype=torch.uint8,
+                                  device=dev)
+
+                def run_stack():
+                    xrun.copy_(x0p)
+                    ds4q.ds4q_moe_stack(lays, 1, xrun, lgs_p, Tp, wsp)
+
+                run_stack()
+                torch.cuda.synchronize()
+                evs[0].record()
+                for _ in range(2):
+                    run_stack()
+                evs[1].record()
+                torch.cuda.synchronize()
+                ms = evs[0].elapsed_time(evs[1]) / 2
+                cf[f"stack43_prefill_4096tok_{name}"] = {
+                    "ms_per_chunk": round(ms, 2), "tokens_per_s": round(Tp / (ms / 1e3), 1),
+                    "tflops": round(NL * Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
+                del wsp
+            del lgs_p, x0p, xrun, xbz, ypz
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["configs"] = cf
+        log("other workloads: " + json.dumps(cf))
 
     # ------------------------------------------------------------ codec and steering (secondary)
     if not args.no_aux:
