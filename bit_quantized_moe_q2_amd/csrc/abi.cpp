@@ -385,14 +385,19 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, s));
     TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
   }
+  // 2..64 tokens with Q4_1 or mixed types: grouped by expert on int8 matrix
+  // cores, h and o per pair index
   if (p_gu) {
-    TIMED_TRY("decode_gateup", launch_decode_gateup(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, s));
+    TIMED_TRY("decode_gateup", launch_decode_tn(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, w.o, 1, s));
     const int na = T * m.k < m.E ? T * m.k : m.E;
     if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_ACTIVE, na,
                                       rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
                                       rows_of(w.h, false, nullptr, false), s));
   }
-  if (p_down) TIMED_TRY("decode_down", launch_decode_down(m, w.h, T, w.rb, w.o, y, acc, st, s));
+  if (p_down) {
+    TIMED_TRY("decode_down", launch_decode_tn(m, x, nullptr, T, w.rb, w.h, w.o, 2, s));
+    TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, false, y, acc, st, s));
+  }
   return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
 }
 

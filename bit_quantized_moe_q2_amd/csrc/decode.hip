@@ -1,5 +1,6 @@
-// Memory-bound decode path (fp32 VALU): quantised matvec, routed gate/up +
-// SwiGLU, down projection and the routing-weighted combine.
+// The single quantised matvec on fp32 vector arithmetic, and the
+// routing-weighted combine of the experts' outputs (with the steering
+// epilogue) shared by the decode and prefill paths.
 //
 // Work layout.  A row of C = 64*L values is split into L "chunks" of 64 values,
 // one per lane; L consecutive lanes of a wave64 share a row, so a wave covers
@@ -13,9 +14,9 @@
 // (the min term hoisted out of the row loop); Q4_1: d*(sum q x) + m*(sum x).
 // Partial sums are combined with an xor-butterfly over the row's L lanes.
 //
-// Expert FFN ("【#2】ds4.c 해독하기": routed experts w1 = gate, w3 = up,
-// w2 = down; SwiGLU; the down input is the routed SwiGLU row, weighted):
-//   h = silu(W1 x) * (W3 x),  y += sum_j p_j * W2[e_j] h_j.
+// Combine ("【#2】ds4.c 해독하기": the routing weight multiplies the routed
+// SwiGLU row; the down projection is linear, so it is applied to each
+// expert's output instead): y_t (+)= sum_j p_j * o_j.
 #include "common.h"
 #include "launch.h"
 
@@ -195,82 +196,9 @@ __global__ __launch_bounds__(256) void matvec_kernel(const uint8_t *__restrict__
   }
 }
 
-// ---------------------------------------------------------------- decode gate/up
+// ---------------------------------------------------------------- combine
 
-// Grid: x = row blocks of F (WAVES * RS * RPW rows each), y = active experts.
-template <int TYPE, int L, int RS>
-__global__ __launch_bounds__(256) void gateup_kernel(const uint8_t *__restrict__ gate,
-                                                     const uint8_t *__restrict__ up, int F, int k,
-                                                     const float *__restrict__ x,
-                                                     const float *__restrict__ inv_rms,
-                                                     RouteBufs rb, float *__restrict__ h) {
-  constexpr int RPW = 64 / L;
-  const int j = blockIdx.y;
-  if (j >= *rb.n_active) return;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int c = lane % L, rs = lane / L;
-  const int64_t rbytes = row_bytes(TYPE, 64 * L);
-  const int e = rb.act_expert[j];
-  const uint8_t *W1 = gate + (int64_t)e * F * rbytes;
-  const uint8_t *W3 = up + (int64_t)e * F * rbytes;
-  const int row0 = (blockIdx.x * WAVES + wv) * RS * RPW;
-  const int pb = rb.act_begin[j], pe = rb.act_begin[j + 1];
-  for (int pi = pb; pi < pe; ++pi) {
-    const int p = rb.pairs[pi];
-    const int t = p / k;
-    XSlice<TYPE> xs;
-    xs.load(x + (int64_t)t * 64 * L, c, inv_rms ? inv_rms[t] : 1.0f);
-    Chunk<TYPE> cg[RS], cu[RS];
-#pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      const int r = row0 + i * RPW + rs;
-      cg[i].load(W1 + r * rbytes, c);
-      cu[i].load(W3 + r * rbytes, c);
-    }
-#pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      const int r = row0 + i * RPW + rs;
-      const float g = group_sum<L>(cg[i].dot(xs));
-      const float u = group_sum<L>(cu[i].dot(xs));
-      if (c == 0) h[(int64_t)p * F + r] = silu(g) * u;
-    }
-  }
-}
-
-// ---------------------------------------------------------------- decode down
-
-// Several tokens: grid x = row blocks of D, y = active experts; every pair of
-// the expert writes o[p][row] (unweighted); launch_combine sums the slots.
-template <int TYPE, int L, int RS>
-__global__ __launch_bounds__(256) void down_grouped_kernel(const uint8_t *__restrict__ down, int D,
-                                                           const float *__restrict__ h, RouteBufs rb,
-                                                           float *__restrict__ o) {
-  constexpr int RPW = 64 / L;
-  const int j = blockIdx.y;
-  if (j >= *rb.n_active) return;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int c = lane % L, rs = lane / L;
-  const int F = 64 * L;
-  const int64_t rbytes = row_bytes(TYPE, F);
-  const int e = rb.act_expert[j];
-  const uint8_t *W2 = down + (int64_t)e * D * rbytes;
-  const int row0 = (blockIdx.x * WAVES + wv) * RS * RPW;
-  const int pb = rb.act_begin[j], pe = rb.act_begin[j + 1];
-  for (int pi = pb; pi < pe; ++pi) {
-    const int p = rb.pairs[pi];
-    XSlice<TYPE> hs;
-    hs.load(h + (int64_t)p * F, c, 1.0f);
-    Chunk<TYPE> ch[RS];
-#pragma unroll
-    for (int i = 0; i < RS; ++i) ch[i].load(W2 + (int64_t)(row0 + i * RPW + rs) * rbytes, c);
-#pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      const float v = group_sum<L>(ch[i].dot(hs));
-      if (c == 0) o[(int64_t)p * D + row0 + i * RPW + rs] = v;
-    }
-  }
-}
-
+// y[t] (+)= sum_j w[t][j] * o[row(t, j)] in slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o, RouteBufs rb,
                                                       int T, int k, int D, int by_pos,
                                                       float *__restrict__ y, int accumulate) {
@@ -380,43 +308,6 @@ hipError_t launch_matvec(int w_type, const void *w, int64_t rows, int64_t cols, 
       hipLaunchKernelGGL((matvec_kernel<TYPE_Q4_1, LL, RS>), dim3(grid), dim3(256), 0, s, W, rows, x, n_tok, y);
   });
   return hipGetLastError();
-}
-
-hipError_t launch_decode_gateup(const MoeDims &m, const float *x, const float *inv_rms, int T,
-                                const RouteBufs &rb, float *h, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const int L = m.D / 64;
-  const int max_active = T * m.k < m.E ? T * m.k : m.E;
-  DS4Q_DISPATCH_L(L, {
-    constexpr int RS = row_slots<LL>();
-    const int per_wg = WAVES * RS * (64 / LL);
-    const dim3 grid(m.F / per_wg, max_active);
-    if (m.tg == TYPE_Q2_K)
-      hipLaunchKernelGGL((gateup_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(256), 0, s, m.gate, m.up, m.F, m.k, x, inv_rms, rb, h);
-    else
-      hipLaunchKernelGGL((gateup_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(256), 0, s, m.gate, m.up, m.F, m.k, x, inv_rms, rb, h);
-  });
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const RouteBufs &rb,
-                              float *o, float *y, bool accumulate, const SteerArgs &st,
-                              hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const int L = m.F / 64;
-  const int max_active = T * m.k < m.E ? T * m.k : m.E;
-  DS4Q_DISPATCH_L(L, {
-    constexpr int RS = row_slots<LL>();
-    const int per_wg = WAVES * RS * (64 / LL);
-    const dim3 grid(m.D / per_wg, max_active);
-    if (m.td == TYPE_Q2_K)
-      hipLaunchKernelGGL((down_grouped_kernel<TYPE_Q2_K, LL, RS>), grid, dim3(256), 0, s, m.down, m.D, h, rb, o);
-    else
-      hipLaunchKernelGGL((down_grouped_kernel<TYPE_Q4_1, LL, RS>), grid, dim3(256), 0, s, m.down, m.D, h, rb, o);
-  });
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return launch_combine(o, rb, T, m.k, m.D, false, y, accumulate, st, s);
 }
 
 hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,

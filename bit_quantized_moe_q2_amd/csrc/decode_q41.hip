@@ -32,48 +32,6 @@
 namespace ds4q {
 namespace {
 
-typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
-
-constexpr int CHUNK_BYTES = 8 * BB_Q41;  // 256 values
-
-// The 12 bytes lane (n, g) reads of K tile j of a chunk: block 2j + (g >> 1)
-// from offset 8 * (g & 1) (dm is the block's (d, m) in the lanes of half 0).
-struct Q41Raw {
-  uint32_t q0, q1, dm;
-  __device__ __forceinline__ void load(const uint8_t *__restrict__ chunk, int j, int g) {
-    const u32x3a v = *reinterpret_cast<const u32x3a *>(chunk + (2 * j + (g >> 1)) * BB_Q41 + 8 * (g & 1));
-    dm = v.x;
-    q0 = v.y;
-    q1 = v.z;
-  }
-};
-
-// One chunk (four K tiles, eight blocks) of 16 weight rows.
-__device__ __forceinline__ void chunk_dot_q41(const Q41Raw r[4], const uint32_t *__restrict__ frag_blk,
-                                              const float *__restrict__ xsum_blk, float sigma, int n, int g,
-                                              float &acc) {
-  const int limb = g < 2 ? n : n - 8;
-  const bool arow = limb >= 0 && limb < 3;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    i32x4 a = (i32x4){0, 0, 0, 0};
-    if (arow) a = *reinterpret_cast<const i32x4 *>(frag_blk + limb * 64 + (j * 4 + g) * 4);
-    i32x4 b;
-    b.x = (int)(r[j].q0 & 0x0F0F0F0Fu);
-    b.y = (int)(r[j].q1 & 0x0F0F0F0Fu);
-    b.z = (int)((r[j].q0 >> 4) & 0x0F0F0F0Fu);
-    b.w = (int)((r[j].q1 >> 4) & 0x0F0F0F0Fu);
-    const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, (i32x4){0, 0, 0, 0}, 0, 0, 0);
-    if ((g & 1) == 0) {
-      const int blk = 2 * j + (g >> 1);
-      const float f = fmaf((float)c.z, INV65536, fmaf((float)c.y, INV256, (float)c.x));
-      const float X = xsum_blk[2 * blk] + xsum_blk[2 * blk + 1];
-      acc = fmaf(f16lo(r[j].dm) * sigma, f, acc);
-      acc = fmaf(f16hi(r[j].dm), X, acc);
-    }
-  }
-}
-
 // Gate/up + SwiGLU for one token on Q4_1 (same grid, waves, routing and
 // epilogue as gateup_q2k_t1_kernel).
 template <int D, int MAXE>

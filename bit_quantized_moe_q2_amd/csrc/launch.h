@@ -50,22 +50,19 @@ struct MoeDims {
   const uint8_t *gate, *up, *down;
 };
 
-// Decode path (T <= 64): gate/up + SwiGLU -> h [T*k][F] f32 (pair-indexed).
-hipError_t launch_decode_gateup(const MoeDims &m, const float *x, const float *inv_rms, int T,
-                                const RouteBufs &rb, float *h, hipStream_t s);
-// Decode path: down projection.  T == 1: fused weighted combine into y.
-// T > 1: o [T*k][D] f32 (pair-indexed), then launch_combine.
-// With st.dir set the output is steered (one token: the down kernel writes
-// st.stage and launch_steer follows; several: in the combine).
-hipError_t launch_decode_down(const MoeDims &m, const float *h, int T, const RouteBufs &rb,
-                              float *o, float *y, bool accumulate, const SteerArgs &st,
-                              hipStream_t s);
 // Single-token Q2_K decode on int8 matrix cores, in two phases: 1 = routing
 // (into rb.ids / rb.w) + gate/up + SwiGLU into h, 2 = down + weighted combine
 // into y.
 hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *logits,
                                 bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
                                 bool accumulate, int phase, const SteerArgs &st, hipStream_t s);
+// Decode of 2..64 tokens grouped by expert on int8 matrix cores, either
+// format (decode_tn.hip): phase 1 = gate/up + SwiGLU into h [T*k][F] (pair
+// index), phase 2 = down into o [T*k][D] (pair index, unweighted); then
+// launch_combine(by_pos = false).  Needs the routing and the grouping
+// without m-tiles (act_expert / act_begin / pairs).
+hipError_t launch_decode_tn(const MoeDims &m, const float *x, const float *inv_rms, int T,
+                            const RouteBufs &rb, float *h, float *o, int phase, hipStream_t s);
 // The same two phases on Q4_1 tensors (decode_q41.hip).  The gate/up and down
 // kernels of the two formats share the workspace contract, so a layer may mix
 // them (phase 1 by the gate/up type, phase 2 by the down type).

@@ -1,8 +1,9 @@
-// Shared parts of the single-token decode kernels on int8 matrix cores
-// (Q2_K in decode_mfma.hip, Q4_1 in decode_q41.hip): operand types, the
-// quantisation of an activation vector into three int8 limbs per value in a
-// wave's LDS area (in the fragment order of either block format), and the
-// routing of the one token by a wave.
+// Shared parts of the decode kernels on int8 matrix cores (one token: Q2_K in
+// decode_mfma.hip, Q4_1 in decode_q41.hip; 2..64 tokens: decode_tn.hip):
+// operand types, the quantisation of an activation vector into three int8
+// limbs per value in a wave's LDS area (in the fragment order of either block
+// format), the routing of one token by a wave, and the weight operands and
+// per-block arithmetic of both formats.
 //
 // Limbs: per 256-value chunk sigma = max|x| / 127 and
 // N = trunc(x * 127 * 65536 / max|x| + 32896), whose balanced base-256 digits
@@ -161,6 +162,149 @@ struct TokenRoute {
     else wave_topk<MAXE>(lg, E, k, lane, id, w);
   }
 };
+
+// ---------------------------------------------------------------- Q2_K operands
+
+// Raw bytes of one 256-value Q2_K block that lane group g uses.
+struct Q2KRaw {
+  uint32_t q[4], s0, s1, dd;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
+    const uint8_t *qs = blk + 16 + 16 * g;
+    q[0] = ld32(qs); q[1] = ld32(qs + 4); q[2] = ld32(qs + 8); q[3] = ld32(qs + 12);
+    s0 = ld32(blk + 8 * (g >> 1));
+    s1 = ld32(blk + 8 * (g >> 1) + 4);
+    dd = ld32(blk + 80);
+  }
+};
+
+// Scale/min bytes of the lane's four sub-blocks (k = 0..3).
+__device__ __forceinline__ void sub_bytes(const Q2KRaw &r, int p, uint32_t sb[4]) {
+  const uint32_t a0 = r.s0 >> (8 * p), a1 = r.s1 >> (8 * p);
+  sb[0] = a0 & 0xFFu; sb[1] = (a0 >> 16) & 0xFFu; sb[2] = a1 & 0xFFu; sb[3] = (a1 >> 16) & 0xFFu;
+}
+
+// Byte table [0, sc, 2sc, 3sc] of a sub-block's integer weights: sc * 0x030201
+// puts sc, 2sc, 3sc (at most 45) in bytes 0..2 without carries.
+__device__ __forceinline__ uint32_t qsc_table(uint32_t sb) {
+  return ((sb & 15u) * 0x030201u) << 8;
+}
+
+// B operand of K tile j: dword k = the sub-block's table looked up with the
+// four 2-bit codes of bit pair k as byte selectors (v_perm_b32).
+__device__ __forceinline__ i32x4 b_frag(const Q2KRaw &r, int j, const uint32_t tab[4]) {
+  const uint32_t w = r.q[j];
+  i32x4 b;
+  b.x = (int)__builtin_amdgcn_perm(tab[0], tab[0], w & 0x03030303u);
+  b.y = (int)__builtin_amdgcn_perm(tab[1], tab[1], (w >> 2) & 0x03030303u);
+  b.z = (int)__builtin_amdgcn_perm(tab[2], tab[2], (w >> 4) & 0x03030303u);
+  b.w = (int)__builtin_amdgcn_perm(tab[3], tab[3], (w >> 6) & 0x03030303u);
+  return b;
+}
+
+
+// A operand of one block: row r < 3 of A is limb r of the activations, rows
+// 3..15 are zero, so one MFMA yields the three limb dot products of 16 weight
+// rows at once (C[limb][row]).  Lane (n, g) holds row n's 16 int8 of K group
+// g for each of the 4 K tiles j.
+struct AFrag {
+  i32x4 a[4];
+  __device__ __forceinline__ void load(const uint32_t *__restrict__ frag_blk, int n, int g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = (i32x4){0, 0, 0, 0};
+    if (n < 3) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a[j] = *reinterpret_cast<const i32x4 *>(frag_blk + n * 64 + (j * 4 + g) * 4);
+    }
+  }
+};
+
+// Block epilogue: the main term (C rows 0..2 = limbs, held by lane group 0;
+// zero in the other groups) and the lane group's quarter of the min term.
+__device__ __forceinline__ void block_post(const Q2KRaw &r, const uint32_t sb[4], const i32x4 c,
+                                           const float *__restrict__ xsum_blk, float sigma, int g,
+                                           float &main_acc, float &min_acc) {
+  const int p = g & 1, h = g >> 1;
+  const float f = fmaf((float)c.z, INV65536, fmaf((float)c.y, INV256, (float)c.x));
+  main_acc = fmaf(f16lo(r.dd) * sigma, f, main_acc);
+  float mn = (float)(sb[0] >> 4) * xsum_blk[8 * h + p];
+  mn = fmaf((float)(sb[1] >> 4), xsum_blk[8 * h + 2 + p], mn);
+  mn = fmaf((float)(sb[2] >> 4), xsum_blk[8 * h + 4 + p], mn);
+  mn = fmaf((float)(sb[3] >> 4), xsum_blk[8 * h + 6 + p], mn);
+  min_acc = fmaf(f16hi(r.dd), mn, min_acc);
+}
+
+// One block of NM weight rows (gate and up share the activations): the four
+// A fragments are read from LDS once, then 4*NM MFMAs.
+template <int NM>
+__device__ __forceinline__ void block_dot(const Q2KRaw *const r[NM], const uint32_t *__restrict__ frag_blk,
+                                          const float *__restrict__ xsum_blk, float sigma, int n, int g,
+                                          float *main_acc, float *min_acc) {
+  AFrag af;
+  af.load(frag_blk, n, g);
+  uint32_t sb[NM][4], tab[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    sub_bytes(*r[m], g & 1, sb[m]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tab[m][q] = qsc_table(sb[m][q]);
+  }
+  i32x4 c[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) c[m] = (i32x4){0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      c[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af.a[j], b_frag(*r[m], j, tab[m]), c[m], 0, 0, 0);
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m) block_post(*r[m], sb[m], c[m], xsum_blk, sigma, g, main_acc[m], min_acc[m]);
+}
+
+// ---------------------------------------------------------------- Q4_1 operands
+
+typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+
+constexpr int CHUNK_BYTES = 8 * BB_Q41;  // 256 values
+
+// The 12 bytes lane (n, g) reads of K tile j of a chunk: block 2j + (g >> 1)
+// from offset 8 * (g & 1) (dm is the block's (d, m) in the lanes of half 0).
+struct Q41Raw {
+  uint32_t q0, q1, dm;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ chunk, int j, int g) {
+    const u32x3a v = *reinterpret_cast<const u32x3a *>(chunk + (2 * j + (g >> 1)) * BB_Q41 + 8 * (g & 1));
+    dm = v.x;
+    q0 = v.y;
+    q1 = v.z;
+  }
+};
+
+// One chunk (four K tiles, eight blocks) of 16 weight rows.
+__device__ __forceinline__ void chunk_dot_q41(const Q41Raw r[4], const uint32_t *__restrict__ frag_blk,
+                                              const float *__restrict__ xsum_blk, float sigma, int n, int g,
+                                              float &acc) {
+  const int limb = g < 2 ? n : n - 8;
+  const bool arow = limb >= 0 && limb < 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    i32x4 a = (i32x4){0, 0, 0, 0};
+    if (arow) a = *reinterpret_cast<const i32x4 *>(frag_blk + limb * 64 + (j * 4 + g) * 4);
+    i32x4 b;
+    b.x = (int)(r[j].q0 & 0x0F0F0F0Fu);
+    b.y = (int)(r[j].q1 & 0x0F0F0F0Fu);
+    b.z = (int)((r[j].q0 >> 4) & 0x0F0F0F0Fu);
+    b.w = (int)((r[j].q1 >> 4) & 0x0F0F0F0Fu);
+    const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+    if ((g & 1) == 0) {
+      const int blk = 2 * j + (g >> 1);
+      const float f = fmaf((float)c.z, INV65536, fmaf((float)c.y, INV256, (float)c.x));
+      const float X = xsum_blk[2 * blk] + xsum_blk[2 * blk + 1];
+      acc = fmaf(f16lo(r[j].dm) * sigma, f, acc);
+      acc = fmaf(f16hi(r[j].dm), X, acc);
+    }
+  }
+}
 
 }  // namespace
 }  // namespace ds4q

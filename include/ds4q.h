@@ -172,8 +172,9 @@ size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t
  * the exact integers sc*q (Q2_K) or q (Q4_1), with the min / offset term in
  * fp32.  2..64 tokens on Q2_K weights throughout run on the grouped int8
  * kernels (two digits per row: residual below 2^-15 of the row maximum, min
- * term with bf16 hi + lo weights); with Q4_1 or mixed types they run on fp32
- * vector arithmetic.  The SwiGLU rows stay fp32.
+ * term with bf16 hi + lo weights); with Q4_1 or mixed types, on per-expert
+ * int8 kernels with the three-digit activations of the one-token path.  The
+ * SwiGLU rows stay fp32.
  * x: device f32 [n_tok][n_embd]; logits: device f32 [n_tok][n_expert];
  * y: device f32 [n_tok][n_embd] — may be the same pointer as x (in-place
  * residual with DS4Q_F_ACCUMULATE), must not partially overlap it.
