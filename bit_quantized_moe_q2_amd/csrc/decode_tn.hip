@@ -131,16 +131,16 @@ __global__ __launch_bounds__(512) void gateup_tn_kernel(const uint8_t *__restric
   const bool quantiser = w < 4 && has;  // the gate waves quantise the shared activations
   const uint8_t *__restrict__ mat = w < 4 ? gate : up;
 
+  // the first token's activations are requested before the weights, so that
+  // quantising them waits only for them (requests complete in order)
+  QuantStage<BPW, Q41> xs;
+  if (quantiser) xs.load(x + (int64_t)(rb.pairs[pb] / k) * D + b0 * 256, lane);
   WaveRows<Q41, BPW> wr;
   if (has) {
     const int64_t rb_bytes = row_bytes(Q41 ? TYPE_Q4_1 : TYPE_Q2_K, D);
     wr.load(mat + ((int64_t)e * F + row) * rb_bytes + (int64_t)b0 * (Q41 ? 8 * BB_Q41 : BB_Q2K), g);
   }
-  QuantStage<BPW, Q41> xs;
-  if (quantiser) {
-    xs.load(x + (int64_t)(rb.pairs[pb] / k) * D + b0 * 256, lane);
-    xs.quantise(lane, &frag[0][quarter][0][0], &xsum[0][quarter][0][0], &sig[0][quarter][0]);
-  }
+  if (quantiser) xs.quantise(lane, &frag[0][quarter][0][0], &xsum[0][quarter][0][0], &sig[0][quarter][0]);
   if (has) wr.build(g);
   __syncthreads();
   for (int i = 0; i < np; ++i) {
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(512) void down_tn_kernel(const uint8_t *__restrict_
   QuantStage<BPW, Q41> hs;
   if (has) {
     const int64_t rb_bytes = row_bytes(Q41 ? TYPE_Q4_1 : TYPE_Q2_K, F);
+    hs.load(h + (int64_t)rb.pairs[pb] * F + b0 * 256, lane);  // before the weights (see above)
     wr.load(down + ((int64_t)e * D + row) * rb_bytes + (int64_t)b0 * (Q41 ? 8 * BB_Q41 : BB_Q2K), g);
-    hs.load(h + (int64_t)rb.pairs[pb] * F + b0 * 256, lane);
     hs.quantise(lane, &frag[0][w][0][0], &xsum[0][w][0][0], &sig[0][w][0]);
     wr.build(g);
   }
