@@ -37,9 +37,11 @@ bool path_dim(int32_t d) { return d == 256 || d == 512 || d == 1024 || d == 2048
 constexpr size_t ALIGN = 256;
 size_t up(size_t v) { return (v + ALIGN - 1) & ~(ALIGN - 1); }
 
-int max_tiles(int T, int E, int k) {
+// Upper bound of the m-tiles of tile_m pairs: every active expert's last
+// tile may be partial.
+int max_tiles(int T, int E, int k, int tile_m) {
   const int P = T * k;
-  return (P < E ? P : E) + P / PREFILL_TILE_M + 1;
+  return (P < E ? P : E) + P / tile_m + 1;
 }
 
 // Workspace carving; with base == nullptr only the size is computed.
@@ -83,15 +85,14 @@ struct Workspace {
       if (T > 1) o = (float *)take(P * D * 4);
       else stage = (float *)take((size_t)D * 4);
       if (i8_in) {  // decode of 2..64 tokens on Q2_K: the grouped int8 kernels
-        rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
+        rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k, DECODE_TILE_M) * 8);
         void *p = take(prep_i8_bytes(T, D));
         if (base) xq = prep_i8_view(p, T, D);
         p = take(prep_i8_bytes(P, F));
         if (base) hq = prep_i8_view(p, P, F);
-        if (stats) imat_part = (float *)take((size_t)max_tiles(T, E, k) * (D > F ? D : F) * 4);
       }
     } else {
-      rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k) * 8);
+      rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * 8);
       hb = (uint16_t *)take(P * F * 2);
       o = (float *)take(P * D * 4);
       if (!i8_in) xb = (uint16_t *)take((size_t)T * D * 2);
@@ -103,7 +104,7 @@ struct Workspace {
         void *p = take(prep_i8_bytes(P, F));
         if (base) hq = prep_i8_view(p, P, F);
       }
-      if (stats) imat_part = (float *)take((size_t)max_tiles(T, E, k) * (D > F ? D : F) * 4);
+      if (stats) imat_part = (float *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * (D > F ? D : F) * 4);
     }
     bytes = off;
   }
@@ -361,22 +362,23 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     return p_gu ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
   if (f.a) {
-    // 2..64 tokens on Q2_K: expert-grouped m-tiles on int8 matrix cores;
-    // h and o in sorted-pair order
-    const int mt = max_tiles(T, m.E, m.k);
+    // 2..64 tokens on Q2_K: expert-grouped m-tiles of at most DECODE_TILE_M
+    // pairs on int8 matrix cores; h and o in sorted-pair order
+    const int mt = max_tiles(T, m.E, m.k, DECODE_TILE_M);
     if (p_route) {
       TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, s));
-      TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
+      TIMED_TRY("group", launch_group(T, m.E, m.k, DECODE_TILE_M, w.rb, s));
     }
     if (p_gu) {
       TIMED_TRY("prep_i8", launch_prep_i8(x, true, false, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xq, s));
-      TIMED_TRY("decode_gateup", launch_decode_i8_gateup(m, w.xq, T, w.rb, mt, w.h, s));
-      if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
+      TIMED_TRY("decode_gateup", launch_decode_grouped(m, w.xq, T, w.rb, mt, w.h, 1, s));
+      const int na = T * m.k < m.E ? T * m.k : m.E;
+      if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_ACTIVE, na, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
                                         rows_of(w.h, false, nullptr, true), s));
     }
     if (p_down) {
       TIMED_TRY("prep_i8", launch_prep_i8(w.h, true, false, nullptr, (int64_t)T * m.k, m.F, w.hq, s));
-      TIMED_TRY("decode_down", launch_decode_i8_down(m, w.hq, T, w.rb, mt, w.o, s));
+      TIMED_TRY("decode_down", launch_decode_grouped(m, w.hq, T, w.rb, mt, w.o, 2, s));
       TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, st, s));
     }
     return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
@@ -411,7 +413,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
   TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, s));
   TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
-  const int mt = max_tiles(T, m.E, m.k);
+  const int mt = max_tiles(T, m.E, m.k, PREFILL_TILE_M);
   if (i8_gateup(L)) {
     TIMED_TRY("prep_i8", launch_prep_i8(x, xf != nullptr, true, norm && xf ? w.rb.inv_rms : nullptr, T,
                                         m.D, w.xq, s));

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
 #pragma unroll
     for (int bl = 0; bl < BPW; ++bl) {
       const Q2KRaw *rr[1] = {&rw[bl]};
-      block_dot<1>(rr, frag[quarter][bl], xsum[quarter][bl], sig[quarter][bl], n, g, &main_acc, &min_acc);
+      block_dot<1, 1>(rr, frag[quarter][bl], xsum[quarter][bl], sig[quarter][bl], n, g, &main_acc, &min_acc);
       __builtin_amdgcn_sched_barrier(0);
     }
     min_acc += __shfl_xor(min_acc, 16, 64);
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {
     const Q2KRaw *rr[1] = {&rw[b]};
-    block_dot<1>(rr, frag[wv][b], xsum[wv][b], sig[wv][b], n, g, &main_acc, &min_acc);
+    block_dot<1, 4>(rr, frag[wv][b], xsum[wv][b], sig[wv][b], n, g, &main_acc, &min_acc);
     __builtin_amdgcn_sched_barrier(0);
   }
   min_acc += __shfl_xor(min_acc, 16, 64);

@@ -51,7 +51,11 @@ struct Q2KOps {
     af.load(frag_blk, n, g);
     i32x4 c = (i32x4){0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(af.a[j], b[j], c, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      if (j == 0) mfma_group_begin();
+      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(af.a[j], b[j], c, 0, 0, 0);
+    }
+    mfma_fence();
     const int p = g & 1, h = g >> 1;
     const float f = fmaf((float)c.z, INV65536, fmaf((float)c.y, INV256, (float)c.x));
     main_acc = fmaf(f16lo(dd) * sigma, f, main_acc);

@@ -1,0 +1,133 @@
+// Int8 matrix-core operands of Q2_K weights and of the two-digit activation
+// rows, shared by the prefill GEMMs (prefill_i8.hip) and the expert-grouped
+// decode (decode_grouped.hip).
+//
+// Arithmetic (block layout of "【#2】ds4.c 해독하기", Q2_K table): one
+// 256-value block of a weight row dotted with an activation row a is
+//   d * sum_v (sc*q)_v a_v  -  dmin * sum_s mn_s A_s,
+// A_s the sums of a over the 16 sub-blocks.  An activation row is prepared
+// once (prep_i8_kernel): sigma = max|a| / 127 over the row, N = round(a /
+// sigma * 256) as balanced base-256 digits a0 (high) and a1 (low), both int8,
+// and A_s / sigma as two bf16 halves hi + lo.  Per (row, block) the prepared
+// row holds QROW digit bytes [digit][chunk c = 4j + g][16 bytes] and XROW
+// bytes of sums [hi | lo][16 sub-blocks].
+#pragma once
+#include "common.h"
+
+namespace ds4q {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int QROW = 512;  // digit bytes of one row's 256-column block
+constexpr int XROW = 64;   // hi/lo sub-block sums (bf16) of one row's block
+
+// 24-bit unsigned multiply (full-rate v_mul_u32_u24; both operands < 2^24).
+__device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// The bytes of one Q2_K block that lane group g uses: code quarter g
+// (16 bytes), the scale/min bytes of sub-blocks 8(g>>1)..8(g>>1)+7, d|dmin.
+struct Q2KPart {
+  u32x4 q;
+  uint32_t s0, s1, dd;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
+    q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
+    s0 = ld32(blk + 8 * (g >> 1));
+    s1 = ld32(blk + 8 * (g >> 1) + 4);
+    dd = ld32(blk + 80);
+  }
+};
+
+// Weight operands of one block for one 16-row n-subtile.  Code byte c of
+// dword j of quarter g holds, in bit pair k, value
+// 128(g>>1) + 32k + 16(g&1) + 4j + c, of sub-block 8(g>>1) + 2k + (g&1);
+// K-tile j, dword k of the B fragment is that bit pair looked up in the
+// sub-block's table [0, sc, 2sc, 3sc].
+
+// The four sub-block tables of the lane (bit pair k -> table k).
+struct WTab {
+  uint32_t tab[4];
+  __device__ __forceinline__ void build(const Q2KPart &r, int g) {
+    const int p = g & 1;
+    const uint32_t a0 = r.s0 >> (8 * p), a1 = r.s1 >> (8 * p);
+    tab[0] = mul_u24(a0 & 15u, 0x03020100u >> 8) << 8;
+    tab[1] = mul_u24((a0 >> 16) & 15u, 0x03020100u >> 8) << 8;
+    tab[2] = mul_u24(a1 & 15u, 0x03020100u >> 8) << 8;
+    tab[3] = mul_u24((a1 >> 16) & 15u, 0x03020100u >> 8) << 8;
+  }
+  // integer B fragment of K-tile j
+  __device__ __forceinline__ i32x4 bfrag(const Q2KPart &r, int j) const {
+    const uint32_t w = r.q[j];
+    i32x4 b;
+    b.x = (int)__builtin_amdgcn_perm(0u, tab[0], w & 0x03030303u);
+    b.y = (int)__builtin_amdgcn_perm(0u, tab[1], (w >> 2) & 0x03030303u);
+    b.z = (int)__builtin_amdgcn_perm(0u, tab[2], (w >> 4) & 0x03030303u);
+    b.w = (int)__builtin_amdgcn_perm(0u, tab[3], (w >> 6) & 0x03030303u);
+    return b;
+  }
+};
+
+// Min-term and scale operands of the block.
+template <bool EXACT_MIN>
+struct WMin {
+  bf16x8 bmin;   // -dmin * mn of sub-blocks 8(g>>1)..8(g>>1)+7, rounded to bf16
+  s16x4 bminlo;  // EXACT_MIN: the rounding residues of sub-blocks 4g..4g+3 (bf16)
+  float dsc;     // d / 256
+  __device__ __forceinline__ void build(const Q2KPart &r, int g) {
+    const float nd = -f16hi(r.dd);
+    const uint32_t m0 = (r.s0 >> 4) & 0x0F0F0F0Fu, m1 = (r.s1 >> 4) & 0x0F0F0F0Fu;
+    const float v[8] = {nd * ub0(m0), nd * ub1(m0), nd * ub2(m0), nd * ub3(m0),
+                        nd * ub0(m1), nd * ub1(m1), nd * ub2(m1), nd * ub3(m1)};
+    const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
+    bmin = __builtin_bit_cast(bf16x8, pk);
+    if constexpr (EXACT_MIN) {
+      // residues of the lane's sub-blocks 4g..4g+3 (= 8(g>>1) + 4(g&1) + i)
+      const int o = 4 * (g & 1);
+      const uint32_t h01 = (g & 1) ? pk.z : pk.x, h23 = (g & 1) ? pk.w : pk.y;
+      const uint32_t l01 = pack_bf16x2(v[o] - bf16_to_f32(h01 & 0xFFFFu), v[o + 1] - bf16_to_f32(h01 >> 16));
+      const uint32_t l23 = pack_bf16x2(v[o + 2] - bf16_to_f32(h23 & 0xFFFFu), v[o + 3] - bf16_to_f32(h23 >> 16));
+      bminlo = __builtin_bit_cast(s16x4, ((unsigned long long)l23 << 32) | l01);
+    }
+    dsc = f16lo(r.dd) * (1.0f / 256.0f);
+  }
+};
+
+// All operands of the block at once.
+template <bool EXACT_MIN>
+struct WOps : WMin<EXACT_MIN> {
+  i32x4 b[4];  // integer B fragments of K-tiles 0..3
+  __device__ __forceinline__ void build(const Q2KPart &r, int g) {
+    WTab t;
+    t.build(r, g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = t.bfrag(r, j);
+    WMin<EXACT_MIN>::build(r, g);
+  }
+};
+
+// sched_barrier mask: ALU, MFMA and LDS instructions may be scheduled
+// across, global memory instructions may not.
+constexpr int SCHED_NOVMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200;
+
+__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+}  // namespace
+}  // namespace ds4q

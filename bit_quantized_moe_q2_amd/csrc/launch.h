@@ -102,12 +102,12 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
                                     int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                   int max_tiles, float *o, hipStream_t s);
-// The same grouped kernels under the decode contract (2..64 tokens, Q2_K):
-// fp32 SwiGLU rows h [T*k][F] in sorted order, min term to about 16 bits.
-hipError_t launch_decode_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                   int max_tiles, float *h, hipStream_t s);
-hipError_t launch_decode_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                 int max_tiles, float *o, hipStream_t s);
+// Decode of 2..64 tokens on Q2_K (decode_grouped.hip): m-tiles of at most
+// DECODE_TILE_M sorted pairs; phase 1 writes the fp32 SwiGLU rows [T*k][F]
+// from the prepared token rows, phase 2 the down rows [T*k][D] from the
+// prepared SwiGLU rows, both in sorted-pair order.
+hipError_t launch_decode_grouped(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+                                 int max_tiles, float *out, int phase, hipStream_t s);
 
 // Directional steering: out_r (+)= y_r - scale * dir * (dir . y_r), rows of n
 // floats (n % 4 == 0, 16-byte aligned); out may be y.
@@ -118,6 +118,7 @@ hipError_t launch_act_encode(const float *src, int64_t n, int bits, void *dst, h
 hipError_t launch_act_decode(const void *src, int64_t n, int bits, float *dst, hipStream_t s);
 
 constexpr int PREFILL_TILE_M = 96;
+constexpr int DECODE_TILE_M = 8;
 
 // imatrix statistics of one layer call (imatrix.hip).  Segments of an
 // expert's pairs: the k slots of one token, the active experts (pairs grouped

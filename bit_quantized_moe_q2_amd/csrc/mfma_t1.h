@@ -236,7 +236,7 @@ __device__ __forceinline__ void block_post(const Q2KRaw &r, const uint32_t sb[4]
 
 // One block of NM weight rows (gate and up share the activations): the four
 // A fragments are read from LDS once, then 4*NM MFMAs.
-template <int NM>
+template <int NM, int KG>
 __device__ __forceinline__ void block_dot(const Q2KRaw *const r[NM], const uint32_t *__restrict__ frag_blk,
                                           const float *__restrict__ xsum_blk, float sigma, int n, int g,
                                           float *main_acc, float *min_acc) {
@@ -252,11 +252,23 @@ __device__ __forceinline__ void block_dot(const Q2KRaw *const r[NM], const uint3
   i32x4 c[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) c[m] = (i32x4){0, 0, 0, 0};
+  // Fenced MFMA groups of KG K tiles (1, 2 or 4).  Larger groups fence less
+  // often but hold the B fragments of the whole group, which costs the
+  // gate/up kernel registers and a resident workgroup per CU, so it uses
+  // KG = 1 and the down kernel (one workgroup per CU) KG = 4.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j0 = 0; j0 < 4; j0 += KG) {
+    i32x4 bj[KG][NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-      c[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af.a[j], b_frag(*r[m], j, tab[m]), c[m], 0, 0, 0);
+    for (int j = 0; j < KG; ++j)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) bj[j][m] = b_frag(*r[m], j0 + j, tab[m]);
+    mfma_group_begin();
+#pragma unroll
+    for (int j = 0; j < KG; ++j)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) c[m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af.a[j0 + j], bj[j][m], c[m], 0, 0, 0);
+    mfma_fence();
   }
 #pragma unroll
   for (int m = 0; m < NM; ++m) block_post(*r[m], sb[m], c[m], xsum_blk, sigma, g, main_acc[m], min_acc[m]);

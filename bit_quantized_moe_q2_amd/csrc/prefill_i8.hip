@@ -29,98 +29,18 @@
 // different bank groups.  Weights go straight to registers, also one block
 // ahead.
 #include "common.h"
+#include "i8_ops.h"
 #include "launch.h"
 
 namespace ds4q {
 namespace {
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 constexpr int TMI = PREFILL_TILE_M;  // tokens (sorted pairs) per m-tile
 constexpr int SUBT = TMI / 8;        // integer MFMA row groups of 8 tokens
 constexpr int NPAIR = SUBT / 2;      // min-term MFMA row groups of 16 tokens
-constexpr int QROW = 512;            // digit bytes of one row's 256-column block
-constexpr int XROW = 64;             // hi/lo sub-block sums (bf16) of one row's block
 constexpr int ASTAGE = TMI * QROW;   // LDS bytes of one stage of digit rows
 constexpr int XSTAGE = 8 * 1024;       // one 1-KiB sum-row load per wave (16 tokens)
 static_assert(TMI % 16 == 0 && TMI <= 128, "m-tile must be a multiple of 16, at most 128");
-
-// 24-bit unsigned multiply (full-rate v_mul_u32_u24; both operands < 2^24).
-__device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
-}
-
-// The bytes of one Q2_K block that lane group g uses: code quarter g
-// (16 bytes), the scale/min bytes of sub-blocks 8(g>>1)..8(g>>1)+7, d|dmin.
-struct Q2KPart {
-  u32x4 q;
-  uint32_t s0, s1, dd;
-  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
-    q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
-    s0 = ld32(blk + 8 * (g >> 1));
-    s1 = ld32(blk + 8 * (g >> 1) + 4);
-    dd = ld32(blk + 80);
-  }
-};
-
-// Weight operands of one block for one 16-row n-subtile.  Code byte c of
-// dword j of quarter g holds, in bit pair k, value
-// 128(g>>1) + 32k + 16(g&1) + 4j + c, of sub-block 8(g>>1) + 2k + (g&1);
-// K-tile j, dword k of the B fragment is that bit pair looked up in the
-// sub-block's table [0, sc, 2sc, 3sc].
-template <bool EXACT_MIN>
-struct WOps {
-  i32x4 b[4];    // integer B fragments of K-tiles 0..3
-  bf16x8 bmin;   // -dmin * mn of sub-blocks 8(g>>1)..8(g>>1)+7, rounded to bf16
-  s16x4 bminlo;  // EXACT_MIN: the rounding residues of sub-blocks 4g..4g+3 (bf16)
-  float dsc;     // d / 256
-  __device__ __forceinline__ void build(const Q2KPart &r, int g) {
-    const int p = g & 1;
-    const uint32_t a0 = r.s0 >> (8 * p), a1 = r.s1 >> (8 * p);
-    uint32_t tab[4];
-    tab[0] = mul_u24(a0 & 15u, 0x03020100u >> 8) << 8;
-    tab[1] = mul_u24((a0 >> 16) & 15u, 0x03020100u >> 8) << 8;
-    tab[2] = mul_u24(a1 & 15u, 0x03020100u >> 8) << 8;
-    tab[3] = mul_u24((a1 >> 16) & 15u, 0x03020100u >> 8) << 8;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = r.q[j];
-      b[j].x = (int)__builtin_amdgcn_perm(0u, tab[0], w & 0x03030303u);
-      b[j].y = (int)__builtin_amdgcn_perm(0u, tab[1], (w >> 2) & 0x03030303u);
-      b[j].z = (int)__builtin_amdgcn_perm(0u, tab[2], (w >> 4) & 0x03030303u);
-      b[j].w = (int)__builtin_amdgcn_perm(0u, tab[3], (w >> 6) & 0x03030303u);
-    }
-    const float nd = -f16hi(r.dd);
-    const uint32_t m0 = (r.s0 >> 4) & 0x0F0F0F0Fu, m1 = (r.s1 >> 4) & 0x0F0F0F0Fu;
-    const float v[8] = {nd * ub0(m0), nd * ub1(m0), nd * ub2(m0), nd * ub3(m0),
-                        nd * ub0(m1), nd * ub1(m1), nd * ub2(m1), nd * ub3(m1)};
-    const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7])};
-    bmin = __builtin_bit_cast(bf16x8, pk);
-    if constexpr (EXACT_MIN) {
-      // residues of the lane's sub-blocks 4g..4g+3 (= 8(g>>1) + 4(g&1) + i)
-      const int o = 4 * (g & 1);
-      const uint32_t h01 = (g & 1) ? pk.z : pk.x, h23 = (g & 1) ? pk.w : pk.y;
-      const uint32_t l01 = pack_bf16x2(v[o] - bf16_to_f32(h01 & 0xFFFFu), v[o + 1] - bf16_to_f32(h01 >> 16));
-      const uint32_t l23 = pack_bf16x2(v[o + 2] - bf16_to_f32(h23 & 0xFFFFu), v[o + 3] - bf16_to_f32(h23 >> 16));
-      bminlo = __builtin_bit_cast(s16x4, ((unsigned long long)l23 << 32) | l01);
-    }
-    dsc = f16lo(r.dd) * (1.0f / 256.0f);
-  }
-};
 
 // One workgroup per activation row, one thread per 16-value sub-block.
 // F32IN: the row is x * inv_rms (or x), rounded to bf16 first when ROUND
@@ -205,14 +125,6 @@ __global__ __launch_bounds__(256) void prep_i8_kernel(const void *__restrict__ s
   xr[16 + s] = (uint16_t)lo;
 }
 
-// sched_barrier mask: ALU, MFMA and LDS instructions may be scheduled
-// across, global memory instructions may not.
-constexpr int SCHED_NOVMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200;
-
-__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-
 // Per-wave state of one work item (set up once, shared by every block).
 struct ItemCtx {
   const uint8_t *abase;         // uniform: digit rows of row rbase
@@ -222,15 +134,12 @@ struct ItemCtx {
   const uint8_t *brow[2];       // weight rows of the two n-subtiles (lane's row)
   int aoff[4];                  // LDS offsets of the lane's A chunks, K-tiles 0..3
   int xoff;                     // LDS offset of the lane's min-term chunk
-  int xoff4;                    // LDS offset of the lane's hi sums of sub-blocks 4g..4g+3
   int nb, w, g, lane;           // w wave-uniform
 };
 
 // The block loop for NP live 16-token groups (tokens >= 16*NP are absent):
-// acc[ip][t] += the products of blocks 0..nb-1.  EXACT_MIN adds the bf16
-// residues of -dmin*mn times the hi sums (one 16x16x16 bf16 MFMA), so that
-// the min term carries about 16 bits instead of 8.
-template <int NP, int NPMAX, bool EXACT_MIN>
+// acc[ip][t] += the products of blocks 0..nb-1.
+template <int NP, int NPMAX>
 __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint8_t *As1, uint8_t *Xs0,
                                            uint8_t *Xs1, f32x4 (&acc)[NPMAX][2]) {
   const int w = cx.w, g = cx.g, nb = cx.nb, lane = cx.lane;
@@ -283,7 +192,7 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
 
   auto step = [&](int kb, Q2KPart (&r)[2], const uint8_t *As, const uint8_t *Xs, uint8_t *An,
                   uint8_t *Xn) {
-    WOps<EXACT_MIN> wo[2];
+    WOps<false> wo[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) wo[t].build(r[t], g);
     // requests for later blocks, in this order: the sum rows and digit-row
@@ -319,25 +228,26 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
           for (int j = 0; j < 4; ++j)
             a[(i + 1) & 1][j] = *reinterpret_cast<const i32x4 *>(ap[j] + (i + 1) * 4096);
         }
+        // the two n-subtiles' chains, interleaved, as one fenced MFMA group
+        i32x4 c[2];
+        mfma_group_begin();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            c[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][j], wo[t].b[j], j ? c[t] : (i32x4){0, 0, 0, 0}, 0, 0, 0);
+        mfma_fence();
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][0], wo[t].b[0], (i32x4){0, 0, 0, 0}, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][1], wo[t].b[1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][2], wo[t].b[2], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 1][3], wo[t].b[3], c, 0, 0, 0);
-          acc[ip][t][2 * h] = fmaf(wo[t].dsc, (float)((c.x << 8) + c.y), acc[ip][t][2 * h]);
-          acc[ip][t][2 * h + 1] = fmaf(wo[t].dsc, (float)((c.z << 8) + c.w), acc[ip][t][2 * h + 1]);
+          acc[ip][t][2 * h] = fmaf(wo[t].dsc, (float)((c[t].x << 8) + c[t].y), acc[ip][t][2 * h]);
+          acc[ip][t][2 * h + 1] = fmaf(wo[t].dsc, (float)((c[t].z << 8) + c[t].w), acc[ip][t][2 * h + 1]);
         }
       }
+      mfma_group_begin();
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         acc[ip][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wo[t].bmin, acc[ip][t], 0, 0, 0);
-      if constexpr (EXACT_MIN) {
-        const s16x4 xh = *reinterpret_cast<const s16x4 *>(Xs + cx.xoff4 + ip * 16 * XROW);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[ip][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, wo[t].bminlo, acc[ip][t], 0, 0, 0);
-      }
+      mfma_fence();
     }
     // Each wave waits for its own tile requests and LDS reads; then the
     // barrier alone publishes the tile (a workgroup fence would also wait
@@ -369,14 +279,13 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
 // gate (t = 0) and up (t = 1).  Otherwise an n-tile is 256 down rows, wave w
 // owning rows 32w + 16t .. +15.  Eight waves; m-tile = up to TMI sorted pairs
 // of one expert, of which at most 16*NPMAX are present (the caller's bound).
-// DEC (the decode contract, at most 64 tokens): fp32 SwiGLU rows hf and the
-// exact min term; otherwise bf16 SwiGLU rows hb.
-template <bool SWIGLU, int NPMAX, bool DEC>
+// SwiGLU rows are written as bf16 (hb), down rows as fp32 (o).
+template <bool SWIGLU, int NPMAX>
 __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint8_t *__restrict__ aq, const uint16_t *__restrict__ ax, const float *__restrict__ asig,
     int gather_tokens, int kslots, RouteBufs rb, int n_ntiles, uint16_t *__restrict__ hb,
-    float *__restrict__ hf, float *__restrict__ o) {
+    float *__restrict__ o) {
   __shared__ __attribute__((aligned(1024))) uint8_t As0[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t Xs0[XSTAGE];
@@ -428,7 +337,6 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) cx.aoff[j] = n * 256 + (((4 * j + g) ^ n) << 4);
   cx.xoff = (8 * ((n & 3) >> 1) + 2 * (n >> 2) + (n & 1)) * XROW + (g & 1) * 32 + (g >> 1) * 16;
-  cx.xoff4 = (8 * ((n & 3) >> 1) + 2 * (n >> 2) + (n & 1)) * XROW + 8 * g;
 
   f32x4 acc[NPMAX][2];
 #pragma unroll
@@ -438,12 +346,12 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
 
   static_assert(NPMAX >= 1 && NPMAX <= NPAIR, "1..6 groups of 16 tokens");
   switch (np) {
-    case 1: block_loop<1, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 2: if constexpr (NPMAX >= 2) block_loop<2, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 3: if constexpr (NPMAX >= 3) block_loop<3, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 4: if constexpr (NPMAX >= 4) block_loop<4, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
-    case 5: if constexpr (NPMAX >= 5) block_loop<5, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
-    default: if constexpr (NPMAX >= 6) block_loop<6, NPMAX, DEC>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 1: block_loop<1, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 2: if constexpr (NPMAX >= 2) block_loop<2, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 3: if constexpr (NPMAX >= 3) block_loop<3, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 4: if constexpr (NPMAX >= 4) block_loop<4, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 5: if constexpr (NPMAX >= 5) block_loop<5, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    default: if constexpr (NPMAX >= 6) block_loop<6, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
   }
 
   // epilogue: lane (g, n) holds, for group ip, rows q = 0..3 = tokens
@@ -459,10 +367,7 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
       const int64_t pos = start + m;
       const float v0 = acc[ip][0][q] * sg, v1 = acc[ip][1][q] * sg;
       if constexpr (SWIGLU) {
-        if constexpr (DEC)
-          hf[pos * rows_per_expert + wrow[0]] = silu(v0) * v1;
-        else
-          hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
+        hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
       } else {
         o[pos * rows_per_expert + wrow[0]] = v0;
         o[pos * rows_per_expert + wrow[1]] = v1;
@@ -514,8 +419,8 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
                                     int max_tiles, uint16_t *hb, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.F / 128;
-  hipLaunchKernelGGL((prefill_i8_kernel<true, NPAIR, false>), dim3(grid_of(max_tiles, nn)), dim3(512), 0,
-                     s, m.gate, m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, hb, nullptr, nullptr);
+  hipLaunchKernelGGL((prefill_i8_kernel<true, NPAIR>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.gate,
+                     m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, hb, nullptr);
   return hipGetLastError();
 }
 
@@ -523,29 +428,8 @@ hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, cons
                                   int max_tiles, float *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
-  hipLaunchKernelGGL((prefill_i8_kernel<false, NPAIR, false>), dim3(grid_of(max_tiles, nn)), dim3(512), 0,
-                     s, m.down, nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, nullptr, o);
-  return hipGetLastError();
-}
-
-// Decode of 2..64 tokens: an expert holds at most 64 pairs, i.e. 4 groups.
-hipError_t launch_decode_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                   int max_tiles, float *h, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  if (T > 64) return hipErrorInvalidValue;
-  const int nn = m.F / 128;
-  hipLaunchKernelGGL((prefill_i8_kernel<true, 4, true>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s,
-                     m.gate, m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, nullptr, h, nullptr);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                 int max_tiles, float *o, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  if (T > 64) return hipErrorInvalidValue;
-  const int nn = m.D / 256;
-  hipLaunchKernelGGL((prefill_i8_kernel<false, 4, true>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s,
-                     m.down, nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, nullptr, o);
+  hipLaunchKernelGGL((prefill_i8_kernel<false, NPAIR>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.down,
+                     nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, o);
   return hipGetLastError();
 }
 

@@ -105,9 +105,8 @@ enum {
  * expert's pairs in sorted order, then added to the arrays (deterministic, no
  * atomics; accumulate over calls, the caller zeroes them).  16-byte aligned,
  * overlapping nothing else.  When either is set the workspace of the prefill
- * and of 2..64-token Q2_K decode grows by (min(P, n_expert) + P/96 + 1) *
- * max(n_embd, n_ff) * 4 bytes, P = n_tok * n_expert_used
- * (ds4q_moe_workspace_size reads the descriptor). */
+ * grows by (min(P, n_expert) + P/96 + 1) * max(n_embd, n_ff) * 4 bytes,
+ * P = n_tok * n_expert_used (ds4q_moe_workspace_size reads the descriptor). */
 typedef struct {
   int32_t n_embd, n_ff, n_expert, n_expert_used;
   int32_t type_gate, type_up, type_down; /* ds4q_type */
@@ -170,11 +169,12 @@ size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t
  * the input and SwiGLU vectors enter as three int8 digits per value times a
  * scale per 256 values (residual below 2^-23 of the chunk maximum) against
  * the exact integers sc*q (Q2_K) or q (Q4_1), with the min / offset term in
- * fp32.  2..64 tokens on Q2_K weights throughout run on the grouped int8
- * kernels (two digits per row: residual below 2^-15 of the row maximum, min
- * term with bf16 hi + lo weights); with Q4_1 or mixed types, on per-expert
- * int8 kernels with the three-digit activations of the one-token path.  The
- * SwiGLU rows stay fp32.
+ * fp32.  2..64 tokens on Q2_K weights throughout run on int8 matrix cores
+ * grouped by expert in tiles of at most 8 token-expert pairs (two digits per
+ * row: residual below 2^-15 of the row maximum; min term with bf16 weights
+ * and their bf16 residues, about 16 bits); with Q4_1 or mixed types, on
+ * per-expert int8 kernels with the three-digit activations of the one-token
+ * path.  The SwiGLU rows stay fp32.
  * x: device f32 [n_tok][n_embd]; logits: device f32 [n_tok][n_expert];
  * y: device f32 [n_tok][n_embd] — may be the same pointer as x (in-place
  * residual with DS4Q_F_ACCUMULATE), must not partially overlap it.
