@@ -62,15 +62,20 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
   constexpr int ROWS = RG * 32;  // weight rows per work item
   static_assert(NMAT * KS * RG == 8 && ROWS == rows_per_item(SWIGLU, NB), "eight waves");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
-  __shared__ int arow_s[GT];
+  __shared__ float sig_s[GT];
 
-  int mtile, ntile;
-  if (!xcd_tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;  // uniform
+  // Work item: m-tile blockIdx.x / n_ntiles, n-tile blockIdx.x % n_ntiles
+  // (a tile's activation rows are small, so keeping its n-tiles on one XCD
+  // buys little; this mapping lets the tile and the live tile count be read
+  // together).  Items past the live m-tiles exit at once.
+  const int mtile = blockIdx.x / n_ntiles, ntile = blockIdx.x % n_ntiles;
+  const int n_live = *rb.n_tiles;
+  const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];  // in the array (grid bound)
+  if (mtile >= n_live || e < 0) return;  // uniform; testing e keeps both loads ahead of the branch
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int kq = w % KS, rg = (w / KS) % RG, mat = w / (KS * RG);
-  const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];
 
   // the pair list entries of the tile (clamped into the list; entries past
   // the tile's end are never used)
@@ -109,7 +114,9 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
   const int lane_pair = NB >= 2 ? w : 2 * w + (lane >> 5);
   const int row_dig = arow(lane_pair);
   const int row_sum = arow((lane >> 2) & (GT - 1));
-  if (tid < GT) arow_s[tid] = arow(tid);
+  // the row scales of the tile's pairs, requested with the activation rows
+  // and kept in registers until the K parts meet
+  const float sig_r = tid < GT ? asig[arow(tid)] : 0.f;
   {
     const int d = (lane >> 4) & 1, c = (lane & 15) ^ ((2 * lane_pair + d) & 15);
     const uint8_t *src = aq + (int64_t)row_dig * NB * QROW + (NB >= 2 ? (lane >> 5) * QROW : 0) + d * 256 + c * 16;
@@ -187,6 +194,7 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
   // K parts: part[w][pair][32 rows] over the (no longer needed) digit rows
   __syncthreads();
   float *part = reinterpret_cast<float *>(lds);
+  if (tid < GT) sig_s[tid] = sig_r;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     part[(w * GT + 2 * g) * 32 + 16 * t + n] = acc[t][0];
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
       v0 += part[(((0 * RG + rgi) * KS + q) * GT + m) * 32 + rr];
       if constexpr (SWIGLU) v1 += part[(((1 * RG + rgi) * KS + q) * GT + m) * 32 + rr];
     }
-    const float sg = asig[arow_s[m]];
+    const float sg = sig_s[m];
     const int64_t pos = start + m;
     const int row = ntile * ROWS + r;
     if constexpr (SWIGLU) out[pos * rows_per_expert + row] = silu(v0 * sg) * (v1 * sg);
@@ -211,16 +219,12 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
   }
 }
 
-unsigned grid_of(int max_tiles, int n_ntiles) {
-  const int64_t total = (int64_t)max_tiles * n_ntiles;
-  return (unsigned)((total + 7) / 8 * 8);
-}
 
 template <bool SWIGLU>
 hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, const PrepI8 &a, int k,
                      int P, const RouteBufs &rb, int max_tiles, float *out, hipStream_t s) {
   const int nn = rows / rows_per_item(SWIGLU, nb);
-  const dim3 grid(grid_of(max_tiles, nn));
+  const dim3 grid((unsigned)max_tiles * nn);  // exactly: every item's m-tile is in the tile array
   const uint8_t *ax = reinterpret_cast<const uint8_t *>(a.x);
 #define DS4Q_DG(NBV)                                                                                 \
   hipLaunchKernelGGL((decode_grouped_kernel<SWIGLU, NBV>), grid, dim3(512), 0, s, W0, W1, rows, a.q, \

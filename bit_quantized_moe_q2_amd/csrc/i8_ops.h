@@ -97,11 +97,13 @@ struct WMin {
                       pack_bf16x2(v[6], v[7])};
     bmin = __builtin_bit_cast(bf16x8, pk);
     if constexpr (EXACT_MIN) {
-      // residues of the lane's sub-blocks 4g..4g+3 (= 8(g>>1) + 4(g&1) + i)
-      const int o = 4 * (g & 1);
-      const uint32_t h01 = (g & 1) ? pk.z : pk.x, h23 = (g & 1) ? pk.w : pk.y;
-      const uint32_t l01 = pack_bf16x2(v[o] - bf16_to_f32(h01 & 0xFFFFu), v[o + 1] - bf16_to_f32(h01 >> 16));
-      const uint32_t l23 = pack_bf16x2(v[o + 2] - bf16_to_f32(h23 & 0xFFFFu), v[o + 3] - bf16_to_f32(h23 >> 16));
+      // residues of the lane's sub-blocks 4g..4g+3 (= 8(g>>1) + 4(g&1) + i);
+      // one select per value (an index into v[] would become select chains)
+      const bool hi = g & 1;
+      const float q0 = hi ? v[4] : v[0], q1 = hi ? v[5] : v[1], q2 = hi ? v[6] : v[2], q3 = hi ? v[7] : v[3];
+      const uint32_t h01 = hi ? pk.z : pk.x, h23 = hi ? pk.w : pk.y;
+      const uint32_t l01 = pack_bf16x2(q0 - bf16_to_f32(h01 & 0xFFFFu), q1 - bf16_to_f32(h01 >> 16));
+      const uint32_t l23 = pack_bf16x2(q2 - bf16_to_f32(h23 & 0xFFFFu), q3 - bf16_to_f32(h23 >> 16));
       bminlo = __builtin_bit_cast(s16x4, ((unsigned long long)l23 << 32) | l01);
     }
     dsc = f16lo(r.dd) * (1.0f / 256.0f);
