@@ -256,6 +256,37 @@ def test_decode_full_layer_64_tokens(gpu, qt):
     assert normwise_err(y[sample], ref) <= TOL_FP32
 
 
+@pytest.mark.parametrize("T", [9, 64])
+def test_decode_experts_over_several_tiles(gpu, T):
+    """Every expert routed every token (E = k = 8): experts hold T pairs, i.e.
+    several m-tiles of the grouped decode (8 pairs each, the last one partial)."""
+    ds4q = gpu
+    _log(f"decode several tiles per expert T={T}")
+    lay = SynthLayer(ds4q, DEV, 512, 256, 8, 8, 10, seed=700 + T)
+    x = synth.x_f32(synth.stream_key(40, T), T, 512)
+    lg = synth.logits_normal(synth.stream_key(41, T), T, 8)
+    y, ids = _decode(ds4q, lay, x, lg)
+    assert np.array_equal(ids, oracle.route(lg, 8)[0])
+    assert normwise_err(y, lay.oracle_moe(x, lg)) <= TOL_FP32
+
+
+def test_decode_64_tokens_zipf(gpu):
+    """64 tokens with Zipf(1.1)-skewed routing, full shape: the popular experts
+    hold tens of pairs (several tiles each); 8 sampled tokens vs the oracle."""
+    ds4q = gpu
+    _log("decode full T=64 zipf")
+    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, 10, seed=710)
+    x = synth.x_f32(synth.stream_key(42), 64, 4096)
+    lg = synth.logits_zipf(synth.stream_key(43), 64, 256)
+    y, ids = _decode(ds4q, lay, x, lg)
+    assert np.array_equal(ids, oracle.route(lg, 6)[0])
+    counts = np.bincount(ids.ravel(), minlength=256)
+    assert counts.max() > 8  # the case this test is for
+    sample = np.array([0, 7, 19, 28, 36, 47, 55, 63])
+    ref = lay.oracle_moe(x[sample], lg[sample], n_threads=16)
+    assert normwise_err(y[sample], ref) <= TOL_FP32
+
+
 @pytest.mark.parametrize("qt,T", [(10, 1), (10, 3), (3, 1)])
 def test_decode_phases_compose(gpu, qt, T):
     """ROUTE, GATEUP and DOWN run as separate calls on one workspace give the
