@@ -25,18 +25,52 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const float *lg = logits + (int64_t)t * E;
   int my_id;
   float my_w;
-  wave_topk<MAX_E>(lg, E, k, lane, &my_id, &my_w);
+  if (E <= 256) {  // four logits per lane, DPP reductions (the one-token path's selection)
+    TopK256 tk;
+    tk.load(lg, E, lane);
+    tk.select(E, k, k, true, lane, &my_id, &my_w);
+  } else {
+    wave_topk<MAX_E>(lg, E, k, lane, &my_id, &my_w);
+  }
   if (lane < k) {
     rb.ids[t * k + lane] = my_id;
     rb.w[t * k + lane] = my_w;
   }
-  if (x) {
-    const float *xr = x + (int64_t)t * D;
+  if (x) {  // D is a multiple of 256 (path sizes)
+    const float4 *xr = reinterpret_cast<const float4 *>(x + (int64_t)t * D);
     float ss = 0.f;
-    for (int i = lane; i < D; i += 64) ss = fmaf(xr[i], xr[i], ss);
+    for (int i = lane; i < D / 4; i += 64) {
+      const float4 v = xr[i];
+      ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss); ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+    }
     ss = group_sum<64>(ss);
     if (lane == 0) rb.inv_rms[t] = 1.0f / sqrtf(ss / (float)D + eps);
   }
+}
+
+// Exclusive prefix sum over a 1024-thread workgroup (every thread calls it);
+// scratch holds 16 ints.  Returns the sum of v over threads < threadIdx.x and
+// sets *total to the sum over all threads.
+__device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) scratch[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = scratch[i];
+    before += i < wv ? c : 0;
+    all += c;
+  }
+  __syncthreads();  // scratch may be reused by the next scan
+  *total = all;
+  return before + incl - v;
 }
 
 // One workgroup per expert: histogram of all pair experts (for its offset),
@@ -52,32 +86,33 @@ __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int ti
   __syncthreads();
   for (int p = tid; p < P; p += 1024) atomicAdd(&hist[rb.ids[p]], 1);
   __syncthreads();
-  if (tid == 0) {
-    int off = 0;
-    for (int i = 0; i < e; ++i) off += hist[i];
-    s_off = off;
-    if (e == 0) {
-      int acc = 0, na = 0, nt = 0;
-      for (int i = 0; i < E; ++i) {
-        rb.counts[i] = hist[i];
-        rb.offsets[i] = acc;
-        if (hist[i] > 0) {
-          rb.act_expert[na] = i;
-          rb.act_begin[na] = acc;
-          ++na;
-          if (tile_m > 0)
-            for (int m0 = 0; m0 < hist[i]; m0 += tile_m) {
-              rb.tiles[2 * nt] = i;
-              rb.tiles[2 * nt + 1] = acc + m0;
-              ++nt;
-            }
-        }
-        acc += hist[i];
+  // thread i < E takes expert i: its offset, its place among the active
+  // experts and its first m-tile, by exclusive scans over the workgroup
+  const int c = tid < E ? hist[tid] : 0;
+  int n_pairs, n_act, n_til;
+  const int off = block_excl_scan(c, wave_tot, &n_pairs);
+  const int apos = block_excl_scan(c > 0 ? 1 : 0, wave_tot, &n_act);
+  const int ntile_mine = tile_m > 0 ? (c + tile_m - 1) / tile_m : 0;
+  const int tpos = block_excl_scan(ntile_mine, wave_tot, &n_til);
+  if (tid == e) s_off = off;
+  if (e == 0) {
+    if (tid < E) {
+      rb.counts[tid] = c;
+      rb.offsets[tid] = off;
+      if (c > 0) {
+        rb.act_expert[apos] = tid;
+        rb.act_begin[apos] = off;
       }
-      rb.offsets[E] = acc;
-      rb.act_begin[na] = acc;
-      *rb.n_active = na;
-      if (tile_m > 0) *rb.n_tiles = nt;
+      for (int j = 0; j < ntile_mine; ++j) {
+        rb.tiles[2 * (tpos + j)] = tid;
+        rb.tiles[2 * (tpos + j) + 1] = off + j * tile_m;
+      }
+    }
+    if (tid == 0) {
+      rb.offsets[E] = n_pairs;
+      rb.act_begin[n_act] = n_pairs;
+      *rb.n_active = n_act;
+      if (tile_m > 0) *rb.n_tiles = n_til;
     }
   }
   __syncthreads();
