@@ -80,7 +80,7 @@ __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int ti
   __shared__ int hist[MAX_E];
   __shared__ int wave_tot[16];
   __shared__ int s_off;
-  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = blockIdx.x, tid = threadIdx.x;
   const int P = T * k;
   for (int i = tid; i < E; i += 1024) hist[i] = 0;
   __syncthreads();
@@ -116,26 +116,29 @@ __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int ti
     }
   }
   __syncthreads();
+  // stable compaction of the expert's pairs: thread t takes pairs
+  // base + 4t .. base + 4t + 3, one scan per 4096 pairs places them
   int running = s_off;
-  for (int base = 0; base < P; base += 1024) {
-    const int p = base + tid;
-    const bool mine = p < P && rb.ids[p] == e;
-    const uint64_t bal = __ballot(mine);
-    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wv] = __popcll(bal);
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int i = 0; i < 16; ++i) {
-      before += i < wv ? wave_tot[i] : 0;
-      total += wave_tot[i];
+  for (int base = 0; base < P; base += 4096) {
+    const int p0 = base + 4 * tid;
+    bool mine[4];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mine[i] = p0 + i < P && rb.ids[p0 + i] == e;
+      cnt += mine[i] ? 1 : 0;
     }
-    if (mine) {
-      const int pos = running + before + rank;
-      rb.pairs[pos] = p;
-      rb.pair_pos[p] = pos;
+    int total;
+    int pos = running + block_excl_scan(cnt, wave_tot, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (mine[i]) {
+        rb.pairs[pos] = p0 + i;
+        rb.pair_pos[p0 + i] = pos;
+        ++pos;
+      }
     }
     running += total;
-    __syncthreads();
   }
 }
 
