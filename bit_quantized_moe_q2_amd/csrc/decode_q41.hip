@@ -134,6 +134,9 @@ __global__ __launch_bounds__(1024) void down_q41_t1_kernel(
   const int j = wv / WPS, b0 = (wv % WPS) * BPW;
   const int n = lane & 15, g = lane >> 4;
   const int row = blockIdx.x * 16 + n;
+  // the output row to accumulate into, requested first (the result is
+  // stored last, so waiting for this load there would add its latency)
+  const float y_old = accumulate && !stage && threadIdx.x < 16 ? y[row] : 0.f;
   QuantStage<BPW, true> qs;
   qs.load(h + (int64_t)j * F + b0 * 256, lane);
   const int e = ids[j];
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(1024) void down_q41_t1_kernel(
       out = fmaf(wts[s], ps, out);
     }
     if (stage) stage[row] = out;  // steered by the launch that follows
-    else y[row] = accumulate ? y[row] + out : out;
+    else y[row] = accumulate ? y_old + out : out;
   }
 }
 
