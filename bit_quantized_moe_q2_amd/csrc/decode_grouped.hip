@@ -156,7 +156,10 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
     WTab tb[2];
     WMin<true> wm[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) tb[t].build(raw[b][t], g);
+    for (int t = 0; t < 2; ++t) {
+      raw[b][t].finish();
+      tb[t].build(raw[b][t], g);
+    }
     i32x4 c[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

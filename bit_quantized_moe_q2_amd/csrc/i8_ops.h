@@ -42,14 +42,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // The bytes of one Q2_K block that lane group g uses: code quarter g
 // (16 bytes), the scale/min bytes of sub-blocks 8(g>>1)..8(g>>1)+7, d|dmin.
+// Two requests per lane: the codes, and 8 bytes that are the scale/min bytes
+// of the pair (g even: bytes 8(g>>1)..+7) or end with d|dmin (g odd: bytes
+// 76..83); finish() hands each 16-lane group its partner's part
+// (v_permlane16_swap pairs groups 0/1 and 2/3).
 struct Q2KPart {
   u32x4 q;
   uint32_t s0, s1, dd;
+  uint32_t p0, p1;  // the 8 bytes as loaded, until finish()
   __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
     q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
-    s0 = ld32(blk + 8 * (g >> 1));
-    s1 = ld32(blk + 8 * (g >> 1) + 4);
-    dd = ld32(blk + 80);
+    const uint2 p = *reinterpret_cast<const uint2 *>(blk + ((g & 1) ? 76 : 8 * (g >> 1)));
+    p0 = p.x;
+    p1 = p.y;
+  }
+  __device__ __forceinline__ void finish() {
+    s0 = __builtin_amdgcn_permlane16_swap(p0, p0, false, false)[0];  // the even group's bytes
+    const auto sw = __builtin_amdgcn_permlane16_swap(p1, p1, false, false);
+    s1 = sw[0];  // the even group's bytes 4..7 of its pair
+    dd = sw[1];  // the odd group's bytes 80..83
   }
 };
 
@@ -120,6 +131,15 @@ struct WOps : WMin<EXACT_MIN> {
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = t.bfrag(r, j);
     WMin<EXACT_MIN>::build(r, g);
+  }
+  // Ends the operands' computation here: compiler passes may otherwise sink
+  // it next to its uses, i.e. into a fenced MFMA group (scheduling barriers
+  // do not hold pure arithmetic back; a volatile asm that takes the values
+  // does).
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(b[j]));
+    asm volatile("" : "+v"(this->bmin), "+v"(this->dsc));
   }
 };
 

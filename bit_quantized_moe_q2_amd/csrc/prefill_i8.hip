@@ -182,7 +182,7 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
   // flight or landed during block kb, alternating between rw[0] and rw[1]);
   // the tile of kb+1 is requested before the weights of kb+2, so waiting
   // until only the last NWLD requests are outstanding means the tile landed.
-  constexpr int NWLD = 6;  // weight load instructions per block: 2 x (16 + 8 + 4 bytes)
+  constexpr int NWLD = 4;  // weight load instructions per block: 2 x (16 + 8 bytes)
   Q2KPart rw[2][2];
   issue_tile(0, As0, Xs0);
   issue_w(0, rw[0]);
@@ -194,7 +194,11 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
                   uint8_t *Xn) {
     WOps<false> wo[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) wo[t].build(r[t], g);
+    for (int t = 0; t < 2; ++t) {
+      r[t].finish();
+      wo[t].build(r[t], g);
+      wo[t].pin();
+    }
     // requests for later blocks, in this order: the sum rows and digit-row
     // load 0 before row group 0, digit-row load u before group u, and the
     // weights right after the last one.  SCHED_NOVMEM lets computation and
