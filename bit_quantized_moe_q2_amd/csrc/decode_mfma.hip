@@ -126,6 +126,7 @@ __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
     }
 #pragma unroll
     for (int bl = 0; bl < BPW; ++bl) {
+      rw[bl].finish();
       const Q2KRaw *rr[1] = {&rw[bl]};
       block_dot<1, 1>(rr, frag[quarter][bl], xsum[quarter][bl], sig[quarter][bl], n, g, &main_acc, &min_acc);
       __builtin_amdgcn_sched_barrier(0);
@@ -187,6 +188,7 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
   float main_acc = 0.f, min_acc = 0.f;
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {
+    rw[b].finish();
     const Q2KRaw *rr[1] = {&rw[b]};
     block_dot<1, 4>(rr, frag[wv][b], xsum[wv][b], sig[wv][b], n, g, &main_acc, &min_acc);
     __builtin_amdgcn_sched_barrier(0);

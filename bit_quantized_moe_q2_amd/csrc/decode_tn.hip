@@ -88,7 +88,10 @@ struct WaveRows {
   __device__ __forceinline__ void build(int g) {
     if constexpr (!Q41) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) ops2[c].build(raw2[c], g);
+      for (int c = 0; c < NC; ++c) {
+        raw2[c].finish();
+        ops2[c].build(raw2[c], g);
+      }
     }
   }
   // sum over the chunks of the 16 rows x this token; lane group 0 returns it

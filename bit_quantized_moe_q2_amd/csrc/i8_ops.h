@@ -52,7 +52,8 @@ struct Q2KPart {
   uint32_t p0, p1;  // the 8 bytes as loaded, until finish()
   __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
     q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
-    const uint2 p = *reinterpret_cast<const uint2 *>(blk + ((g & 1) ? 76 : 8 * (g >> 1)));
+    typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+    const u32x2a p = *reinterpret_cast<const u32x2a *>(blk + ((g & 1) ? 76 : 8 * (g >> 1)));
     p0 = p.x;
     p1 = p.y;
   }

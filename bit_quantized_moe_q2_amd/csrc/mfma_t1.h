@@ -165,15 +165,29 @@ struct TokenRoute {
 
 // ---------------------------------------------------------------- Q2_K operands
 
-// Raw bytes of one 256-value Q2_K block that lane group g uses.
+// Raw bytes of one 256-value Q2_K block that lane group g uses: code
+// quarter g, the scale/min bytes of sub-blocks 8(g>>1)..+7, d|dmin.  Two
+// requests per lane: the 16 code bytes, and 8 bytes that are the scale/min
+// bytes of the pair (g even) or end with d|dmin (g odd: bytes 76..83);
+// finish() hands each 16-lane group its partner's part (v_permlane16_swap
+// pairs groups 0/1 and 2/3).
+typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2u __attribute__((ext_vector_type(2), aligned(4)));
 struct Q2KRaw {
   uint32_t q[4], s0, s1, dd;
+  uint32_t p0, p1;  // the 8 bytes as loaded, until finish()
   __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
-    const uint8_t *qs = blk + 16 + 16 * g;
-    q[0] = ld32(qs); q[1] = ld32(qs + 4); q[2] = ld32(qs + 8); q[3] = ld32(qs + 12);
-    s0 = ld32(blk + 8 * (g >> 1));
-    s1 = ld32(blk + 8 * (g >> 1) + 4);
-    dd = ld32(blk + 80);
+    const u32x4u v = *reinterpret_cast<const u32x4u *>(blk + 16 + 16 * g);
+    q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+    const u32x2u p = *reinterpret_cast<const u32x2u *>(blk + ((g & 1) ? 76 : 8 * (g >> 1)));
+    p0 = p.x;
+    p1 = p.y;
+  }
+  __device__ __forceinline__ void finish() {
+    s0 = __builtin_amdgcn_permlane16_swap(p0, p0, false, false)[0];  // the even group's bytes
+    const auto sw = __builtin_amdgcn_permlane16_swap(p1, p1, false, false);
+    s1 = sw[0];
+    dd = sw[1];  // the odd group's bytes 80..83
   }
 };
 
