@@ -578,6 +578,88 @@ def main():
         torch.cuda.synchronize()
         result["calib_copy_bytes"] = n * 4
 
+    # ------------------------------------------------------------ Q4_1 stack (secondary)
+    # the 43-layer stack on Q4_1 weights (173 GB): after the Q2_K layers are
+    # freed, one token and one 4096-token chunk through it
+    if not args.no_stack and not args.no_configs and NL == 43:
+        import gc
+        for lst in (layers, q41, keep):
+            lst.clear()
+        steered = lays = L = Ls = None
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        q41_bytes = 43 * 3 * E * (D * F // 32 * 20)
+        free_b, _ = torch.cuda.mem_get_info()
+        if free_b < q41_bytes + (16 << 30):
+            log(f"Q4_1 stack skipped: {free_b / 1e9:.1f} GB free")
+        else:
+            log("generating 43 layers of Q4_1 experts (173 GB) ...")
+            stack41 = []
+            for l in range(NL):
+                t = {}
+                for name, rows, cols in (("gate", F, D), ("up", F, D), ("down", D, F)):
+                    buf = torch.empty(E * rows * cols // 32 * 20, dtype=torch.uint8, device=dev)
+                    synth.device_fill("q4_1", buf, [synth.layer_key(seed + 2, l, name, e) for e in range(E)],
+                                      rows * cols // 32)
+                    t[name] = buf
+                stack41.append(ds4q.MoeLayer.from_tensors(t["gate"], t["up"], t["down"], D, F, E, K,
+                                                          ds4q.TYPE_Q4_1))
+            torch.cuda.synchronize()
+            # one token (same inputs as the Q2_K stack)
+            ws41 = torch.empty(ds4q.ds4q_moe_workspace_size(stack41[0], 1, 0), dtype=torch.uint8, device=dev)
+
+            def stack41_token():
+                x_run.copy_(x_st)
+                ds4q.ds4q_moe_stack(stack41, 0, x_run, lgs_st, 1, ws41)
+
+            stack41_token()
+            torch.cuda.synchronize()
+            g41 = capture(stack41_token)
+            g41.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(args.stack_tokens):
+                g41.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            t_ms = ev0.elapsed_time(ev1) / args.stack_tokens
+            wbytes = NL * K * 3 * (F * ds4q.row_bytes(ds4q.TYPE_Q4_1, D))
+            log(f"stack q4_1: {t_ms * 1e3:.1f} us/token through {NL} layers, "
+                f"{wbytes / (t_ms / 1e3) / 1e9:.0f} GB/s")
+            result["stack_decode"]["q4_1"] = {
+                "workload": "stack43_decode_1tok_q4_1", "us_per_token": round(t_ms * 1e3, 2),
+                "tokens_per_s": round(1e3 / t_ms, 1), "weight_bytes_per_token": wbytes,
+                "hbm_gbps": round(wbytes / (t_ms / 1e3) / 1e9, 1)}
+            del g41, ws41
+            # one 4096-token chunk
+            Tp = 4096
+            lgs_p = torch.from_numpy(np.stack([synth.logits_normal(synth.stream_key(seed, 14, l), Tp, E)
+                                               for l in range(NL)])).to(dev)
+            x0p = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 15), Tp, D)).to(dev)
+            xrun = torch.empty_like(x0p)
+            wsp = torch.empty(ds4q.ds4q_moe_workspace_size(stack41[0], Tp, 1), dtype=torch.uint8, device=dev)
+
+            def run_stack41():
+                xrun.copy_(x0p)
+                ds4q.ds4q_moe_stack(stack41, 1, xrun, lgs_p, Tp, wsp)
+
+            run_stack41()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(2):
+                run_stack41()
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / 2
+            result["configs"]["stack43_prefill_4096tok_q4_1"] = {
+                "ms_per_chunk": round(ms, 2), "tokens_per_s": round(Tp / (ms / 1e3), 1),
+                "tflops": round(NL * Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
+            log(f"stack q4_1 prefill: {ms:.2f} ms per 4096-token chunk")
+            del wsp, lgs_p, x0p, xrun, stack41
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
         import oracle
