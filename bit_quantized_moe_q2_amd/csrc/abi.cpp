@@ -49,7 +49,8 @@ struct Workspace {
   RouteBufs rb{};
   float *h = nullptr;      // decode: [T*k][F] f32
   uint16_t *hb = nullptr;  // prefill: [T*k][F] bf16 (sorted order)
-  float *o = nullptr;      // [T*k][D] f32
+  float *o = nullptr;      // decode: [T*k][D] f32
+  uint16_t *ob = nullptr;  // prefill: [T*k][D] bf16 (sorted order)
   float *stage = nullptr;  // decode of one token: [D] f32, the unsteered output before steering
   float *imat_part = nullptr;  // imatrix on m-tiles: [max_tiles][max(D, F)] f32 partial rows
   uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
@@ -94,7 +95,7 @@ struct Workspace {
     } else {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * 8);
       hb = (uint16_t *)take(P * F * 2);
-      o = (float *)take(P * D * 4);
+      ob = (uint16_t *)take(P * D * 2);
       if (!i8_in) xb = (uint16_t *)take((size_t)T * D * 2);
       if (i8_in) {
         void *p = take(prep_i8_bytes(T, D));
@@ -434,11 +435,11 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   if (i8_down(L)) {
     const int64_t P = (int64_t)T * m.k;
     TIMED_TRY("prep_i8", launch_prep_i8(w.hb, false, false, nullptr, P, m.F, w.hq, s));
-    TIMED_TRY("prefill_down", launch_prefill_i8_down(m, w.hq, T, w.rb, mt, w.o, s));
+    TIMED_TRY("prefill_down", launch_prefill_i8_down(m, w.hq, T, w.rb, mt, w.ob, s));
   } else {
-    TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.o, s));
+    TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.ob, s));
   }
-  TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, steer_of(L, nullptr), s));
+  TIMED_TRY("combine", launch_combine(w.ob, w.rb, T, m.k, m.D, true, y, acc, steer_of(L, nullptr), s));
   return copy_route(route, w.rb, T, m.E, m.k, s);
 }
 

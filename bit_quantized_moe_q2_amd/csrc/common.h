@@ -41,12 +41,17 @@ __device__ __forceinline__ uint32_t ld32(const uint8_t *p) {
   return *reinterpret_cast<const uint32_t *>(p);
 }
 
-// bf16 round-to-nearest-even of an fp32 value, NaN kept quiet.
+// bf16 round-to-nearest-even of an fp32 value (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32, one instruction and no branch.
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two values rounded as by bf16_rne_bits, packed a (low half), b (high half).
+__device__ __forceinline__ uint32_t bf16_rne_pair(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -133,6 +138,18 @@ constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
 
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// bf16 store of a lane's two output rows r0 = base + n and r1 = base + 16 + n
+// (n = lane & 15; `p` points at row r0 of the token) as one 4-byte store per
+// lane instead of two 2-byte ones: lanes n and n ^ 1 swap one fp32 value,
+// then the even lane writes rows (r0, r0 + 1) and the odd lane rows
+// (r1 - 1, r1).  base must be even, and lanes n and n ^ 1 both active.
+__device__ __forceinline__ void store_bf16_row_pair(uint16_t *p, int n, float v0, float v1) {
+  const bool odd = n & 1;
+  const float got = __builtin_bit_cast(float, dpp<DPP_XOR1>(__builtin_bit_cast(uint32_t, odd ? v0 : v1)));
+  const uint32_t word = odd ? bf16_rne_pair(got, v1) : bf16_rne_pair(v0, got);
+  *reinterpret_cast<uint32_t *>(p + (odd ? 15 : 0)) = word;
 }
 
 // Wave-wide unsigned max; the result is uniform.

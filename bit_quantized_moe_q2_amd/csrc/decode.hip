@@ -198,8 +198,19 @@ __global__ __launch_bounds__(256) void matvec_kernel(const uint8_t *__restrict__
 
 // ---------------------------------------------------------------- combine
 
+// Four consecutive values of a row of o: fp32, or bf16 (prefill).
+__device__ __forceinline__ float4 load4(const float *o, int64_t off) {
+  return *reinterpret_cast<const float4 *>(o + off);
+}
+__device__ __forceinline__ float4 load4(const uint16_t *o, int64_t off) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(o + off);
+  return make_float4(bf16_to_f32(u.x & 0xFFFFu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFFu),
+                     bf16_to_f32(u.y >> 16));
+}
+
 // y[t] (+)= sum_j w[t][j] * o[row(t, j)] in slot order.
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o, RouteBufs rb,
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const OT *__restrict__ o, RouteBufs rb,
                                                       int T, int k, int D, int by_pos,
                                                       float *__restrict__ y, int accumulate) {
   const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   for (int j = 0; j < k; ++j) {
     const int p = t * k + j;
     const int64_t row = by_pos ? rb.pair_pos[p] : p;
-    const float4 v = *reinterpret_cast<const float4 *>(o + row * D + 4 * c);
+    const float4 v = load4(o, row * D + 4 * c);
     const float w = rb.w[p];
     acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
     acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
@@ -226,7 +237,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 // Combine with directional steering: one workgroup per token row (D <= 4096,
 // four float4 per thread), the row's weighted sum kept in registers while its
 // dot product with the direction is reduced, then y (+)= v - scale*dir*(dir.v).
-__global__ __launch_bounds__(256) void combine_steer_kernel(const float *__restrict__ o, RouteBufs rb,
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_steer_kernel(const OT *__restrict__ o, RouteBufs rb,
                                                             int k, int D, int by_pos,
                                                             const float *__restrict__ dir, float scale,
                                                             float *__restrict__ y, int accumulate) {
@@ -242,7 +254,7 @@ __global__ __launch_bounds__(256) void combine_steer_kernel(const float *__restr
       for (int j = 0; j < k; ++j) {
         const int pp = t * k + j;
         const int64_t row = by_pos ? rb.pair_pos[pp] : pp;
-        const float4 a = *reinterpret_cast<const float4 *>(o + row * D + i);
+        const float4 a = load4(o, row * D + i);
         const float w = rb.w[pp];
         v[c].x = fmaf(w, a.x, v[c].x); v[c].y = fmaf(w, a.y, v[c].y);
         v[c].z = fmaf(w, a.z, v[c].z); v[c].w = fmaf(w, a.w, v[c].w);
@@ -310,18 +322,31 @@ hipError_t launch_matvec(int w_type, const void *w, int64_t rows, int64_t cols, 
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
-                          float *y, bool accumulate, const SteerArgs &st, hipStream_t s) {
+namespace {
+template <typename OT>
+hipError_t combine_any(const OT *o, const RouteBufs &rb, int T, int k, int D, bool by_pos, float *y,
+                       bool accumulate, const SteerArgs &st, hipStream_t s) {
   const int64_t n4 = (int64_t)T * (D / 4);
   if (n4 == 0) return hipSuccess;
   if (st.dir) {
-    hipLaunchKernelGGL(combine_steer_kernel, dim3((unsigned)T), dim3(256), 0, s, o, rb, k, D,
+    hipLaunchKernelGGL((combine_steer_kernel<OT>), dim3((unsigned)T), dim3(256), 0, s, o, rb, k, D,
                        by_pos ? 1 : 0, st.dir, st.scale, y, accumulate ? 1 : 0);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, o, rb, T,
+  hipLaunchKernelGGL((combine_kernel<OT>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, o, rb, T,
                      k, D, by_pos ? 1 : 0, y, accumulate ? 1 : 0);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
+                          float *y, bool accumulate, const SteerArgs &st, hipStream_t s) {
+  return combine_any(o, rb, T, k, D, by_pos, y, accumulate, st, s);
+}
+
+hipError_t launch_combine(const uint16_t *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
+                          float *y, bool accumulate, const SteerArgs &st, hipStream_t s) {
+  return combine_any(o, rb, T, k, D, by_pos, y, accumulate, st, s);
 }
 
 }  // namespace ds4q

@@ -75,6 +75,9 @@ hipError_t launch_decode_q41_t1(const MoeDims &m, const float *x, const float *l
 // workgroup per row).
 hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
                           float *y, bool accumulate, const SteerArgs &st, hipStream_t s);
+// The same with o in bf16 (the prefill's down rows).
+hipError_t launch_combine(const uint16_t *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
+                          float *y, bool accumulate, const SteerArgs &st, hipStream_t s);
 
 // Prefill path on Q4_1 weights (bf16 matrix cores).
 hipError_t launch_prep_bf16(const float *x, const float *inv_rms, int T, int D, uint16_t *xb,
@@ -82,7 +85,7 @@ hipError_t launch_prep_bf16(const float *x, const float *inv_rms, int T, int D, 
 hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, const RouteBufs &rb,
                                  int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, const RouteBufs &rb,
-                               int max_tiles, float *o, hipStream_t s);
+                               int max_tiles, uint16_t *ob, hipStream_t s);
 
 // Prefill on Q2_K weights, int8 matrix cores: activation rows prepared as
 // two int8 digits per value (MFMA fragment order), hi/lo bf16 sub-block sums
@@ -101,7 +104,7 @@ hipError_t launch_prep_i8(const void *src, bool f32in, bool round_bf16, const fl
 hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                     int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                  int max_tiles, float *o, hipStream_t s);
+                                  int max_tiles, uint16_t *ob, hipStream_t s);
 // Decode of 2..64 tokens on Q2_K (decode_grouped.hip): m-tiles of at most
 // DECODE_TILE_M sorted pairs; phase 1 writes the fp32 SwiGLU rows [T*k][F]
 // from the prepared token rows, phase 2 the down rows [T*k][D] from the

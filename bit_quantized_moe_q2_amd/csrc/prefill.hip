@@ -194,7 +194,7 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(512) void prefill_q41_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint16_t *__restrict__ A, int gather_tokens, int kslots, RouteBufs rb, int n_ntiles,
-    uint16_t *__restrict__ hb, float *__restrict__ o) {
+    uint16_t *__restrict__ hb, uint16_t *__restrict__ o) {
   __shared__ __attribute__((aligned(1024))) uint8_t As0[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[ASTAGE];
   __shared__ int arow[TM];
@@ -274,8 +274,8 @@ __global__ __launch_bounds__(512) void prefill_q41_kernel(
         const float hv = silu(acc[i][0][q]) * acc[i][1][q];
         hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(hv);
       } else {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) o[pos * rows_per_expert + wrow[t]] = acc[i][t][q];
+        // wrow[1] = wrow[0] + 16; lanes n, n ^ 1 share g, hence m and validity
+        store_bf16_row_pair(o + pos * rows_per_expert + wrow[0], n, acc[i][0][q], acc[i][1][q]);
       }
     }
   }
@@ -321,7 +321,7 @@ hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, co
 }
 
 hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, const RouteBufs &rb,
-                               int max_tiles, float *o, hipStream_t s) {
+                               int max_tiles, uint16_t *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
   const dim3 grid(grid_for(max_tiles, nn));

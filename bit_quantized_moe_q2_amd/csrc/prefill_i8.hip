@@ -289,7 +289,7 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint8_t *__restrict__ aq, const uint16_t *__restrict__ ax, const float *__restrict__ asig,
     int gather_tokens, int kslots, RouteBufs rb, int n_ntiles, uint16_t *__restrict__ hb,
-    float *__restrict__ o) {
+    uint16_t *__restrict__ o) {
   __shared__ __attribute__((aligned(1024))) uint8_t As0[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t Xs0[XSTAGE];
@@ -373,8 +373,8 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
       if constexpr (SWIGLU) {
         hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
       } else {
-        o[pos * rows_per_expert + wrow[0]] = v0;
-        o[pos * rows_per_expert + wrow[1]] = v1;
+        // wrow[1] = wrow[0] + 16; lanes n, n ^ 1 share g, hence m and validity
+        store_bf16_row_pair(o + pos * rows_per_expert + wrow[0], n, v0, v1);
       }
     }
   }
@@ -429,7 +429,7 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
 }
 
 hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                  int max_tiles, float *o, hipStream_t s) {
+                                  int max_tiles, uint16_t *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
   hipLaunchKernelGGL((prefill_i8_kernel<false, NPAIR>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.down,

@@ -215,8 +215,8 @@ int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float 
  * int8 multiplies the input row written as sigma * (a0 + a1/256) with two
  * int8 digits per value (sigma = row max / 127, residual <= sigma/512) on
  * int8 MFMA, and bf16(-dmin * mn) multiplies the sub-block sums of the row
- * (bf16 hi + lo) on bf16 MFMA.  Routing and the final weighted combine are
- * fp32.  x: device [n_tok][n_embd] of x_type; y: device f32 [n_tok][n_embd]
+ * (bf16 hi + lo) on bf16 MFMA.  Each pair's down row is rounded to bf16
+ * once; routing and the final weighted combine are fp32.  x: device [n_tok][n_embd] of x_type; y: device f32 [n_tok][n_embd]
  * (may equal x only when x_type is F32).  workspace
  * >= ds4q_moe_workspace_size(L, n_tok, 1). */
 int ds4q_moe_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const float *logits,
