@@ -146,8 +146,8 @@ __global__ __launch_bounds__(512) void gateup_q2k_t1_kernel(
 
 // Down projection + weighted combine for one token.  Grid D/16; WPS waves per
 // routing slot (blockDim = 64 * k * WPS), each taking NB/WPS blocks of the
-// slot's rows: a wave quantises its part of the slot's SwiGLU row into LDS,
-// then streams its expert's 16 down rows, and the waves meet in LDS:
+// slot's rows: a wave requests its expert's 16 down rows, quantises its part
+// of the slot's SwiGLU row into LDS meanwhile, and the waves meet in LDS:
 // y (+)= sum_j w_j * (W2[e_j] h_j), summed in slot order.
 template <int F>
 __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
@@ -172,11 +172,9 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
   QuantStage<BPW> qs;
   qs.load(h + (int64_t)j * F + b0 * 256, lane);
   const int e = ids[j];
-  // Quantise first: while this wave does, the other waves' weight loads keep
-  // the memory pipeline full, and this wave's blocks can be used as soon as
-  // they arrive.
-  qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
-
+  // The weight loads go out as soon as the expert id is in, before the
+  // quantisation of the SwiGLU row (which waits for that row only), so the
+  // quantisation runs under the weights' latency.
   const int64_t rb = (int64_t)NB * BB_Q2K;
   Q2KRaw rw[BPW];
   const uint8_t *rowp = down + ((int64_t)e * D + row) * rb + b0 * BB_Q2K;
@@ -185,6 +183,7 @@ __global__ __launch_bounds__(1024) void down_q2k_t1_kernel(
     rw[b].load(rowp + b * BB_Q2K, g);
     __builtin_amdgcn_sched_barrier(0);
   }
+  qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
   float main_acc = 0.f, min_acc = 0.f;
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {

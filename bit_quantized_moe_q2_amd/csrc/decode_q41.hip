@@ -140,8 +140,11 @@ __global__ __launch_bounds__(1024) void down_q41_t1_kernel(
   QuantStage<BPW, true> qs;
   qs.load(h + (int64_t)j * F + b0 * 256, lane);
   const int e = ids[j];
-  qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
-
+  // weight loads first, the quantisation of the SwiGLU row runs under them;
+  // at n_ff = 4096 the row and 8 blocks of weights do not fit in registers
+  // together, so there the row is quantised first
+  constexpr bool QFIRST = F >= 4096;
+  if constexpr (QFIRST) qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
   const int64_t rb = (int64_t)(F / 32) * BB_Q41;
   Q41Raw rw[BPW][4];
   const uint8_t *rowp = down + ((int64_t)e * D + row) * rb + b0 * CHUNK_BYTES;
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(1024) void down_q41_t1_kernel(
     for (int t = 0; t < 4; ++t) rw[bl][t].load(rowp + bl * CHUNK_BYTES, t, g);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (!QFIRST) qs.quantise(lane, &frag[wv][0][0], &xsum[wv][0][0], &sig[wv][0]);
   float acc = 0.f;
 #pragma unroll
   for (int bl = 0; bl < BPW; ++bl) {
