@@ -115,8 +115,9 @@ def main():
     if args.steps < 1 or args.warmup < 0 or args.layers < 1:
         ap.error("--steps and --layers must be positive, --warmup non-negative")
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md, 'How the path would shard'); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (a GPU would "
+              "hold its share of the experts, with tokens exchanged all-to-all); run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

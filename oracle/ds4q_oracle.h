@@ -23,7 +23,7 @@
  *       order, y = d*q + m), section on the two lossless conditions, the
  *       q41_blocks code section, the read-back section.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - Q2_K value = d*sc*q - dmin*mn, sc = low nibble, mn = high nibble of the
  *    sub-block byte (the pages give only "scale/min nibble per 16 values").
  *  - 4th bit pair of the Q2_K pack = L[j+l+96] << 6 (elided on the page).
