@@ -209,27 +209,52 @@ __device__ __forceinline__ float4 load4(const uint16_t *o, int64_t off) {
 }
 
 // y[t] (+)= sum_j w[t][j] * o[row(t, j)] in slot order.
-template <typename OT>
+template <typename OT, bool BY_POS, int KC>
 __global__ __launch_bounds__(256) void combine_kernel(const OT *__restrict__ o, RouteBufs rb,
-                                                      int T, int k, int D, int by_pos,
+                                                      int T, int k_rt, int D,
                                                       float *__restrict__ y, int accumulate) {
   const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int D4 = D / 4;
   if (i4 >= (int64_t)T * D4) return;
   const int t = (int)(i4 / D4), c = (int)(i4 % D4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int p = t * k + j;
-    const int64_t row = by_pos ? rb.pair_pos[p] : p;
-    const float4 v = load4(o, row * D + 4 * c);
-    const float w = rb.w[p];
-    acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
-  }
   float4 *yp = reinterpret_cast<float4 *>(y + (int64_t)t * D + 4 * c);
-  if (accumulate) {
-    const float4 old = *yp;
-    acc.x += old.x; acc.y += old.y; acc.z += old.z; acc.w += old.w;
+  if constexpr (KC > 0) {
+    // the slot count known at compile time: straight-line code requests every
+    // slot's position, then every slot's row (and the old y row), before the
+    // sum in slot order
+    const float4 old = accumulate ? *yp : make_float4(0.f, 0.f, 0.f, 0.f);
+    int64_t row[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) row[j] = BY_POS ? rb.pair_pos[t * KC + j] : t * KC + j;
+    float4 v[KC];
+    float w[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      v[j] = load4(o, row[j] * D + 4 * c);
+      w[j] = rb.w[t * KC + j];
+    }
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      acc.x = fmaf(w[j], v[j].x, acc.x); acc.y = fmaf(w[j], v[j].y, acc.y);
+      acc.z = fmaf(w[j], v[j].z, acc.z); acc.w = fmaf(w[j], v[j].w, acc.w);
+    }
+    if (accumulate) {
+      acc.x += old.x; acc.y += old.y; acc.z += old.z; acc.w += old.w;
+    }
+  } else {
+    for (int j = 0; j < k_rt; ++j) {
+      const int p = t * k_rt + j;
+      const int64_t row = BY_POS ? rb.pair_pos[p] : p;
+      const float4 v = load4(o, row * D + 4 * c);
+      const float w = rb.w[p];
+      acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+    }
+    if (accumulate) {
+      const float4 old = *yp;
+      acc.x += old.x; acc.y += old.y; acc.z += old.z; acc.w += old.w;
+    }
   }
   *yp = acc;
 }
@@ -237,31 +262,61 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT *__restrict__ o, 
 // Combine with directional steering: one workgroup per token row (D <= 4096,
 // four float4 per thread), the row's weighted sum kept in registers while its
 // dot product with the direction is reduced, then y (+)= v - scale*dir*(dir.v).
-template <typename OT>
+// KC > 0 (the slot count, with D = 4096 so that every thread owns all four
+// float4): straight-line code requests every slot's position, then all rows,
+// before any arithmetic; the sums keep the same order.
+template <typename OT, bool BY_POS, int KC>
 __global__ __launch_bounds__(256) void combine_steer_kernel(const OT *__restrict__ o, RouteBufs rb,
-                                                            int k, int D, int by_pos,
+                                                            int k, int D,
                                                             const float *__restrict__ dir, float scale,
                                                             float *__restrict__ y, int accumulate) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   float4 v[4];
   float p = 0.f;
+  if constexpr (KC > 0) {
+    int64_t row[KC];
+    float w[KC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int i = 4 * (threadIdx.x + 256 * c);
-    v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < D) {
-      for (int j = 0; j < k; ++j) {
-        const int pp = t * k + j;
-        const int64_t row = by_pos ? rb.pair_pos[pp] : pp;
-        const float4 a = load4(o, row * D + i);
-        const float w = rb.w[pp];
-        v[c].x = fmaf(w, a.x, v[c].x); v[c].y = fmaf(w, a.y, v[c].y);
-        v[c].z = fmaf(w, a.z, v[c].z); v[c].w = fmaf(w, a.w, v[c].w);
+    for (int j = 0; j < KC; ++j) {
+      row[j] = BY_POS ? rb.pair_pos[t * KC + j] : t * KC + j;
+      w[j] = rb.w[t * KC + j];
+    }
+    float4 a[4][KC];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < KC; ++j) a[c][j] = load4(o, row[j] * D + 4 * (threadIdx.x + 256 * c));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        v[c].x = fmaf(w[j], a[c][j].x, v[c].x); v[c].y = fmaf(w[j], a[c][j].y, v[c].y);
+        v[c].z = fmaf(w[j], a[c][j].z, v[c].z); v[c].w = fmaf(w[j], a[c][j].w, v[c].w);
       }
-      const float4 d = *reinterpret_cast<const float4 *>(dir + i);
+      const float4 d = *reinterpret_cast<const float4 *>(dir + 4 * (threadIdx.x + 256 * c));
       p = fmaf(d.x, v[c].x, p); p = fmaf(d.y, v[c].y, p);
       p = fmaf(d.z, v[c].z, p); p = fmaf(d.w, v[c].w, p);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = 4 * (threadIdx.x + 256 * c);
+      v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < D) {
+        for (int j = 0; j < k; ++j) {
+          const int pp = t * k + j;
+          const int64_t row = BY_POS ? rb.pair_pos[pp] : pp;
+          const float4 a = load4(o, row * D + i);
+          const float w = rb.w[pp];
+          v[c].x = fmaf(w, a.x, v[c].x); v[c].y = fmaf(w, a.y, v[c].y);
+          v[c].z = fmaf(w, a.z, v[c].z); v[c].w = fmaf(w, a.w, v[c].w);
+        }
+        const float4 d = *reinterpret_cast<const float4 *>(dir + i);
+        p = fmaf(d.x, v[c].x, p); p = fmaf(d.y, v[c].y, p);
+        p = fmaf(d.z, v[c].z, p); p = fmaf(d.w, v[c].w, p);
+      }
     }
   }
 #pragma unroll
@@ -329,12 +384,39 @@ hipError_t combine_any(const OT *o, const RouteBufs &rb, int T, int k, int D, bo
   const int64_t n4 = (int64_t)T * (D / 4);
   if (n4 == 0) return hipSuccess;
   if (st.dir) {
-    hipLaunchKernelGGL((combine_steer_kernel<OT>), dim3((unsigned)T), dim3(256), 0, s, o, rb, k, D,
-                       by_pos ? 1 : 0, st.dir, st.scale, y, accumulate ? 1 : 0);
+    const int kc = D == 4096 ? k : 0;
+#define DS4Q_STEER(KC)                                                                             \
+  do {                                                                                             \
+    if (by_pos)                                                                                    \
+      hipLaunchKernelGGL((combine_steer_kernel<OT, true, KC>), dim3((unsigned)T), dim3(256), 0, s, o, rb, k, \
+                         D, st.dir, st.scale, y, accumulate ? 1 : 0);                              \
+    else                                                                                           \
+      hipLaunchKernelGGL((combine_steer_kernel<OT, false, KC>), dim3((unsigned)T), dim3(256), 0, s, o, rb, k, \
+                         D, st.dir, st.scale, y, accumulate ? 1 : 0);                              \
+  } while (0)
+    switch (kc) {
+      case 6: DS4Q_STEER(6); break;
+      case 8: DS4Q_STEER(8); break;
+      default: DS4Q_STEER(0); break;
+    }
+#undef DS4Q_STEER
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((combine_kernel<OT>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, o, rb, T,
-                     k, D, by_pos ? 1 : 0, y, accumulate ? 1 : 0);
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  const int acc = accumulate ? 1 : 0;
+#define DS4Q_COMBINE(KC)                                                                           \
+  do {                                                                                             \
+    if (by_pos)                                                                                    \
+      hipLaunchKernelGGL((combine_kernel<OT, true, KC>), grid, dim3(256), 0, s, o, rb, T, k, D, y, acc); \
+    else                                                                                           \
+      hipLaunchKernelGGL((combine_kernel<OT, false, KC>), grid, dim3(256), 0, s, o, rb, T, k, D, y, acc); \
+  } while (0)
+  switch (k) {
+    case 6: DS4Q_COMBINE(6); break;
+    case 8: DS4Q_COMBINE(8); break;
+    default: DS4Q_COMBINE(0); break;
+  }
+#undef DS4Q_COMBINE
   return hipGetLastError();
 }
 }  // namespace
