@@ -238,3 +238,30 @@ def test_steered_stack_layer_major_table(gpu, mode, T):
     _log(f"  end-to-end rel err of the accumulated update {err:.2e}")
     if mode == 0:
         assert err <= 2e-2
+
+
+@pytest.mark.parametrize("steered", [True, False])
+def test_prefill_eight_slots_full_width(gpu, steered):
+    """Eight routed slots at n_embd = 4096: the combine kernels' straight-line
+    path for that slot count, with and without steering."""
+    ds4q = gpu
+    D, F, E, k, T = 4096, 256, 16, 8, 72
+    seed = 1600 + int(steered)
+    lay = SynthLayer(ds4q, DEV, D, F, E, k, 10, seed=seed)
+    x = synth.x_f32(synth.stream_key(seed, 1), T, D)
+    lg = synth.logits_normal(synth.stream_key(seed, 2), T, E)
+    d = _unit(seed, D)
+    if steered:
+        lay.L.set_steering(torch.from_numpy(d).to(DEV), 0.75)
+    ws = torch.empty(ds4q.ds4q_moe_workspace_size(lay.L, T, 1), dtype=torch.uint8, device=DEV)
+    y = torch.empty(T, D, device=DEV)
+    ds4q.ds4q_moe_prefill(lay.L, torch.from_numpy(x).to(DEV), ds4q.TYPE_F32,
+                          torch.from_numpy(lg).to(DEV), T, y, None, ws)
+    torch.cuda.synchronize()
+    n = _bf16(x)
+    ref = lay.oracle_moe(n, lg, n_threads=16)
+    if steered:
+        ref = oracle.steer_f64(d, 0.75, ref)
+    err = _row_err(y.cpu().numpy(), ref, ref)
+    _log(f"prefill k=8 steered={steered}: rel err {err:.2e}")
+    assert err <= 1e-2
