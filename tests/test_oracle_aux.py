@@ -143,3 +143,52 @@ def test_e4m3_rne_matches_brute_force():
     ref = np.array([_e4m3_brute(v) for v in xs], dtype=np.uint8)
     assert np.array_equal(got, ref)
     assert oracle.e4m3_rne(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+# ---------------------------------------------------------------- steering, fp64 form
+
+def test_steer_f64_hand_example_and_sign():
+    # dir = (1, 2), y = (3, 4): dir.y = 11.  s = 0.25 subtracts 0.25*11*(1, 2).
+    d = np.array([1.0, 2.0], np.float32)
+    y = np.array([[3.0, 4.0]])
+    assert np.array_equal(oracle.steer_f64(d, 0.25, y), np.array([[0.25, -1.5]]))
+    # a negative scale adds the direction instead (amplification)
+    assert np.array_equal(oracle.steer_f64(d, -0.25, y), np.array([[5.75, 9.5]]))
+    # the input is left untouched (the binding copies)
+    assert np.array_equal(y, np.array([[3.0, 4.0]]))
+
+
+def test_steer_f64_projection_reflection_and_parallel_rows():
+    rng = np.random.default_rng(5)
+    dd = rng.standard_normal(512)
+    dd /= np.linalg.norm(dd)
+    d = dd.astype(np.float32)
+    d64 = d.astype(np.float64)
+    y = rng.standard_normal((5, 512)) * 3.0
+    a = y @ d64
+    # scale 1 leaves no component along a unit direction; scale 2 reflects it
+    n2 = float(d64 @ d64)                      # 1 up to the f32 rounding of dir
+    assert np.max(np.abs(oracle.steer_f64(d, 1.0, y) @ d64 - a * (1.0 - n2))) < 1e-12
+    assert np.max(np.abs(oracle.steer_f64(d, 2.0, y) @ d64 - a * (1.0 - 2.0 * n2))) < 1e-12
+    # the part orthogonal to dir is unchanged for every scale
+    for s in (0.5, 1.0, -0.75):
+        out = oracle.steer_f64(d, s, y)
+        perp = lambda v: v - np.outer(v @ d64, d64) / n2
+        assert np.max(np.abs(perp(out) - perp(y))) < 1e-12
+    # a row parallel to dir scales by (1 - s |dir|^2)
+    par = np.outer([2.0, -1.0], d64)
+    for s in (0.3, 1.0, 1.7):
+        assert np.allclose(oracle.steer_f64(d, s, par), par * (1.0 - s * n2), rtol=0, atol=1e-14)
+
+
+def test_steer_f64_equals_float_form_on_exact_inputs():
+    # small integers and a power-of-two scale keep every intermediate exact in
+    # both forms, so the fp64 result rounded once equals the float form
+    rng = np.random.default_rng(6)
+    d = rng.integers(-3, 4, 64).astype(np.float32)
+    y = rng.integers(-50, 51, (7, 64)).astype(np.float32)
+    for s in (0.0, 0.25, -0.5, 1.0, 2.0):
+        f64 = oracle.steer_f64(d, s, y.astype(np.float64))
+        ref = y.astype(np.float64) - s * np.outer(y.astype(np.float64) @ d, d)
+        assert np.array_equal(f64, ref)
+        assert np.array_equal(f64.astype(np.float32), oracle.steer(d, s, y))

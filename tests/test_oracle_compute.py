@@ -330,3 +330,75 @@ def test_stack_zero_weights_is_identity_and_one_layer_composes():
     nb = (oracle.bf16_rne(n).astype(np.uint32) << 16).view(np.float32)
     refb = (x.astype(np.float64) + oracle.moe(L, nb, lg[0])).astype(np.float32)
     assert np.array_equal(oracle.stack([L], x, lg[:1], prefill_bf16=True), refb)
+
+
+def _two_layers(qname, D, F, E, k, seed):
+    """Two layers with their own weights (distinct seeds per layer)."""
+    qt = Q2 if qname == "q2_k" else Q4
+    out = []
+    for l in range(2):
+        t = [np.stack([synth.expert_tensor_blocks(qname, synth.layer_key(seed, l, n, e), r, c)
+                       for e in range(E)])
+             for n, r, c in (("gate", F, D), ("up", F, D), ("down", D, F))]
+        out.append(oracle.Layer(D, F, E, k, qt, *t))
+    return out
+
+
+@pytest.mark.parametrize("prefill_bf16", [False, True])
+def test_stack_two_layers_compose_with_their_own_logits_and_weights(prefill_bf16):
+    """x2 = x1 + MoE_1(n(x1)) with x1 = x0 + MoE_0(n(x0)), built by hand from
+    the separately pinned rmsnorm and moe; layer l reads logits[l] and its own
+    weights ("ds4.c 해독하기 1/8": one routed-expert set and router per layer)."""
+    D, F, E, k, T = 256, 256, 8, 3, 3
+    layers = _two_layers("q2_k", D, F, E, k, 120)
+    x0 = synth.x_f32(synth.stream_key(121), T, D)
+    lg = synth.logits_normal(synth.stream_key(122), 2 * T, E).reshape(2, T, E)
+    # the two layers route differently, so a stride mistake changes the result
+    assert not np.array_equal(oracle.route(lg[0], k)[0], oracle.route(lg[1], k)[0])
+
+    def layer(L, x, lgl):
+        n = np.stack([oracle.rmsnorm(x[t]) for t in range(T)]).astype(np.float32)
+        if prefill_bf16:
+            n = (oracle.bf16_rne(n).astype(np.uint32) << 16).view(np.float32)
+        return (x.astype(np.float64) + oracle.moe(L, n, lgl)).astype(np.float32)
+
+    x1 = layer(layers[0], x0, lg[0])
+    x2 = layer(layers[1], x1, lg[1])
+    got = oracle.stack(layers, x0, lg, prefill_bf16=prefill_bf16)
+    assert np.array_equal(got, x2)
+    # the same stack with layer 0's logits for both layers is a different model
+    wrong = layer(layers[1], x1, lg[0])
+    assert not np.array_equal(got, wrong)
+
+
+def test_stack_steering_uses_each_layers_own_direction_row():
+    """Steering ("【#8】ds4.c 해독하기", directional-steering section): layer l
+    projects row l of the layer-major table out of its MoE output before the
+    residual add.  Row 0 = 0 (no change on layer 0), row 1 = basis vector e_c
+    at scale 1: layer 1's output loses exactly its coordinate c, so x2[c]
+    stays where layer 0 put it and every other coordinate equals the
+    unsteered stack bit for bit."""
+    D, F, E, k, T, c = 256, 256, 8, 3, 2, 17
+    layers = _two_layers("q4_1", D, F, E, k, 130)
+    x0 = synth.x_f32(synth.stream_key(131), T, D)
+    lg = synth.logits_normal(synth.stream_key(132), 2 * T, E).reshape(2, T, E)
+    dirs = np.zeros((2, D), np.float32)
+    dirs[1, c] = 1.0
+    x1 = oracle.stack(layers[:1], x0, lg[:1], prefill_bf16=False)
+    plain = oracle.stack(layers, x0, lg, prefill_bf16=False)
+    steered = oracle.stack(layers, x0, lg, prefill_bf16=False, dirs=dirs, steer_scale=1.0)
+    assert np.array_equal(steered[:, c], x1[:, c])
+    assert not np.array_equal(plain[:, c], x1[:, c])   # layer 1 does move coordinate c
+    rest = np.arange(D) != c
+    assert np.array_equal(steered[:, rest], plain[:, rest])
+    # layer 0's row is the one applied to layer 0: a basis row there (and none
+    # on layer 1) removes coordinate c from layer 0's output only
+    dirs0 = np.zeros((2, D), np.float32)
+    dirs0[0, c] = 1.0
+    s0 = oracle.stack(layers[:1], x0, lg[:1], prefill_bf16=False, dirs=dirs0[:1], steer_scale=1.0)
+    assert np.array_equal(s0[:, c], x0[:, c])
+    # scale -1 doubles layer 1's coordinate c instead (the sign of the scale)
+    amp = oracle.stack(layers, x0, lg, prefill_bf16=False, dirs=dirs, steer_scale=-1.0)
+    y1c = plain[:, c].astype(np.float64) - x1[:, c].astype(np.float64)
+    assert np.allclose(amp[:, c].astype(np.float64) - x1[:, c], 2.0 * y1c, rtol=1e-5,
+                       atol=1e-6 * np.abs(x1[:, c]).max())
