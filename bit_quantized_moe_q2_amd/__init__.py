@@ -18,7 +18,7 @@ __all__ = [
     "F_ACCUMULATE", "F_RMSNORM_INPUT", "Ds4qError", "MoeLayer", "RouteOut", "load",
     "ds4q_abi_version", "ds4q_strerror", "ds4q_dequant", "ds4q_matvec", "ds4q_route",
     "ds4q_route_workspace_size", "ds4q_moe_workspace_size", "ds4q_moe_decode",
-    "ds4q_moe_decode_phases", "PHASE_ROUTE", "PHASE_GATEUP", "PHASE_DOWN", "PHASE_ALL",
+    "ds4q_moe_decode_static", "ds4q_moe_decode_phases", "PHASE_ROUTE", "PHASE_GATEUP", "PHASE_DOWN", "PHASE_ALL",
     "ds4q_moe_prefill", "ds4q_moe_stack", "ds4q_steer", "ds4q_act_encode", "ds4q_act_decode",
     "ds4q_timing_enable", "ds4q_timing_read",
     "QK", "BLOCK_BYTES", "row_bytes",
@@ -28,6 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libds4q.so")
 
 TYPE_F32, TYPE_F16, TYPE_Q4_1, TYPE_Q2_K, TYPE_IQ2_XXS, TYPE_BF16 = 0, 1, 3, 10, 16, 30
+SCRATCH_BYTES = 24 << 20  # DS4Q_SCRATCH_BYTES
 F_ACCUMULATE, F_RMSNORM_INPUT = 0x1, 0x2
 PHASE_ROUTE, PHASE_GATEUP, PHASE_DOWN, PHASE_ALL = 0x1, 0x2, 0x4, 0x7
 QK = {TYPE_Q2_K: 256, TYPE_Q4_1: 32}
@@ -118,6 +119,7 @@ def load():
         "ds4q_route": (ctypes.c_int, [P, i32, i32, i32, RP, P, sz, P]),
         "ds4q_moe_workspace_size": (sz, [LP, i32, i32]),
         "ds4q_moe_decode": (ctypes.c_int, [LP, P, P, i32, P, RP, P, sz, P]),
+        "ds4q_moe_decode_static": (ctypes.c_int, [LP, P, P, i32, P, RP, P]),
         "ds4q_moe_decode_phases": (ctypes.c_int, [LP, P, P, i32, P, RP, P, sz, ctypes.c_uint32, P]),
         "ds4q_moe_prefill": (ctypes.c_int, [LP, P, i32, P, i32, P, RP, P, sz, P]),
         "ds4q_moe_stack": (ctypes.c_int, [LP, i32, i32, P, P, i32, P, sz, P]),
@@ -200,6 +202,13 @@ def ds4q_moe_decode(layer: MoeLayer, x, logits, n_tok, y, route: RouteOut | None
         ctypes.byref(layer), _ptr(x), _ptr(logits), n_tok, _ptr(y),
         ctypes.byref(route) if route is not None else None, _ptr(workspace),
         _ws_bytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def ds4q_moe_decode_static(layer: MoeLayer, x, logits, n_tok, y, route: RouteOut | None,
+                           stream=None):
+    _check("ds4q_moe_decode_static", load().ds4q_moe_decode_static(
+        ctypes.byref(layer), _ptr(x), _ptr(logits), n_tok, _ptr(y),
+        ctypes.byref(route) if route is not None else None, _stream(stream)))
 
 
 def ds4q_moe_decode_phases(layer: MoeLayer, x, logits, n_tok, y, route: RouteOut | None,

@@ -1,7 +1,8 @@
 // Host side of libds4q.so: argument validation, workspace layout and kernel
 // launches behind the extern "C" entry points declared in include/ds4q.h.
 // Every check runs before anything is enqueued; no device memory is
-// allocated here.
+// allocated here (the one library-owned device buffer is the static scratch
+// of scratch.hip).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -256,23 +257,30 @@ bool wants_grouping(const ds4q_route_out *r) {
   return r && (r->expert_counts || r->expert_offsets || r->sorted_pairs);
 }
 
-// Shared argument checks of the decode / prefill layer calls.
+// Shared argument checks of the decode / prefill layer calls.  With
+// STATIC_WS the workspace is the library's static scratch (its size is
+// checked by the caller; no caller buffer can overlap it): ws is ignored.
+constexpr void *STATIC_WS = nullptr;
 int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const float *logits, int32_t T,
                int32_t max_T, const float *y, const ds4q_route_out *route, void *ws, size_t ws_bytes,
-               int mode) {
+               int mode, bool static_ws = false) {
   int rc = check_layer(L);
   if (rc) return rc;
   if (T < 0 || T > max_T) return DS4Q_E_SHAPE;
   if (T == 0) return DS4Q_OK;
   if (!x || !logits || !y) return DS4Q_E_INVAL;
-  if (!ws) return DS4Q_E_WORKSPACE;
+  if (!ws && !static_ws) return DS4Q_E_WORKSPACE;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, ALIGN) ||
       route_misaligned(route))
     return DS4Q_E_ALIGN;
   const WsFlags f = i8_flags(L, T, mode);
   const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b,
                        f.stats);
-  if (ws_bytes < need.bytes) return DS4Q_E_WORKSPACE;
+  if (static_ws) {
+    if (need.bytes > DS4Q_SCRATCH_BYTES) return DS4Q_E_SCRATCH;
+  } else if (ws_bytes < need.bytes) {
+    return DS4Q_E_WORKSPACE;
+  }
   const size_t xb = (size_t)T * L->n_embd * x_elem, yb = (size_t)T * L->n_embd * 4;
   const size_t lb = (size_t)T * L->n_expert * 4;
   if (overlap(ws, need.bytes, x, xb) || overlap(ws, need.bytes, y, yb) ||
@@ -457,6 +465,7 @@ DS4Q_API const char *ds4q_strerror(int status) {
     case DS4Q_E_WORKSPACE: return "workspace missing or too small";
     case DS4Q_E_ALIAS: return "output overlaps an input or the workspace";
     case DS4Q_E_HIP: return "HIP runtime error";
+    case DS4Q_E_SCRATCH: return "call needs more than the static scratch (DS4Q_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -540,6 +549,18 @@ DS4Q_API int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const floa
   if (rc || n_tok == 0) return rc;
   return run_decode(L, x, logits, n_tok, y, route, workspace, static_cast<hipStream_t>(stream),
                     L->flags);
+}
+
+DS4Q_API int ds4q_moe_decode_static(const ds4q_moe_layer *L, const float *x, const float *logits,
+                                    int32_t n_tok, float *y, const ds4q_route_out *route,
+                                    void *stream) {
+  // every argument check first (the same as ds4q_moe_decode's), then the
+  // scratch's device address
+  const int rc = check_call(L, x, 4, logits, n_tok, 64, y, route, STATIC_WS, 0, 0, true);
+  if (rc || n_tok == 0) return rc;
+  void *ws = nullptr;
+  HIP_TRY(scratch_address(&ws));
+  return run_decode(L, x, logits, n_tok, y, route, ws, static_cast<hipStream_t>(stream), L->flags);
 }
 
 DS4Q_API int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float *logits,

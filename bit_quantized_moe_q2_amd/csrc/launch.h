@@ -120,6 +120,10 @@ hipError_t launch_steer(const float *dir, float scale, const float *y, int64_t n
 hipError_t launch_act_encode(const float *src, int64_t n, int bits, void *dst, hipStream_t s);
 hipError_t launch_act_decode(const void *src, int64_t n, int bits, float *dst, hipStream_t s);
 
+// Device address of the current device's static scratch (scratch.hip),
+// DS4Q_SCRATCH_BYTES long; looked up once per device.
+hipError_t scratch_address(void **out);
+
 constexpr int PREFILL_TILE_M = 96;
 constexpr int DECODE_TILE_M = 8;
 

@@ -26,7 +26,9 @@
  *    major ([P1] ffn_*_exps).
  *  - Every pointer argument named *_dev or documented "device" is device memory
  *    the caller owns; the library allocates no device memory and keeps no
- *    device state.  Structs are read on the host during the call only.
+ *    device state, except one static scratch array per device that only
+ *    ds4q_moe_decode_static uses.  Structs are read on the host during the
+ *    call only.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *    asynchronously; the call returns once it is enqueued.
  *  - All validation happens on the host before anything is enqueued; on an
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DS4Q_ABI_VERSION 5
+#define DS4Q_ABI_VERSION 6
 
 /* Tensor types.  Numeric values follow the public GGML/GGUF type ids. */
 typedef enum {
@@ -64,7 +66,8 @@ enum {
   DS4Q_E_ALIGN = -4,        /* a pointer misses its required alignment */
   DS4Q_E_WORKSPACE = -5,    /* workspace NULL or smaller than ds4q_moe_workspace_size() */
   DS4Q_E_ALIAS = -6,        /* an output overlaps an input or the workspace */
-  DS4Q_E_HIP = -7           /* a HIP runtime call or launch failed */
+  DS4Q_E_HIP = -7,          /* a HIP runtime call or launch failed */
+  DS4Q_E_SCRATCH = -8       /* the call needs more than DS4Q_SCRATCH_BYTES of static scratch */
 };
 
 /* Flags of ds4q_moe_layer.flags. */
@@ -184,6 +187,29 @@ size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t
 int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int32_t n_tok,
                     float *y, const ds4q_route_out *route, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* Size of the library's static device scratch: one array of this many bytes
+ * per device, reserved when the library's code is loaded on that device and
+ * kept until the process ends.  It holds the workspace of every decode call
+ * the ABI accepts (the largest, n_tok 64 with n_embd = n_ff = 4096, 1024
+ * experts and 8 slots, needs 21.1 MiB). */
+#define DS4Q_SCRATCH_BYTES (24u << 20)
+
+/* ds4q_moe_decode without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid the allocator.  Same mathematics, kernels, argument
+ * rules and errors as ds4q_moe_decode, with the workspace taken from the
+ * static scratch of the calling thread's current device (the stream must
+ * belong to that device).  The call itself allocates nothing: the scratch's
+ * device address is looked up once per device (first call on it) and kept.
+ * DS4Q_E_SCRATCH if the call would need more than DS4Q_SCRATCH_BYTES (no
+ * shape the ABI accepts does).  All calls on one device share its scratch:
+ * calls that overlap in time on one device (concurrent streams, threads)
+ * race and must be serialised by the caller; a call leaves its workspace
+ * contents in the scratch, and no call reads scratch bytes it did not write
+ * itself. */
+int ds4q_moe_decode_static(const ds4q_moe_layer *L, const float *x, const float *logits,
+                           int32_t n_tok, float *y, const ds4q_route_out *route, void *stream);
 
 /* Phases of the decode launches, for ds4q_moe_decode_phases. */
 #define DS4Q_PHASE_ROUTE 0x1u  /* routing (nothing of its own for one Q2_K token, see below) */

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_strerror(lib):
     m = re.search(r"#define DS4Q_ABI_VERSION (\d+)", open(HEADER).read())
     assert ds4q.ds4q_abi_version() == int(m.group(1))
-    for code in (OK, E_INVAL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ALIAS, -7):
+    for code in (OK, E_INVAL, E_UNSUPPORTED, E_SHAPE, E_ALIGN, E_WORKSPACE, E_ALIAS, -7, -8):
         assert ds4q.ds4q_strerror(code) != "unknown status"
     assert ds4q.ds4q_strerror(-99) == "unknown status"
 
@@ -124,6 +124,14 @@ def test_decode_call_validation(lib):
     assert ph(0) == E_INVAL and ph(8) == E_INVAL and ph(0x17) == E_INVAL
     assert lib.ds4q_moe_decode_phases(ctypes.byref(L), x, lg, 65, y, None, w, need,
                                       ds4q.PHASE_GATEUP, None) == E_SHAPE
+    # the allocation-free variant checks its arguments the same way, before
+    # it looks up the static scratch on the device
+    st = lambda x=x, lg=lg, T=4, y=y: lib.ds4q_moe_decode_static(ctypes.byref(L), x, lg, T, y, None, None)
+    assert st(T=65) == E_SHAPE and st(T=-1) == E_SHAPE and st(T=0) == OK
+    assert st(x=None) == E_INVAL and st(x=x + 4) == E_ALIGN
+    assert st(y=x + 4096 * 4) == E_ALIAS and st(lg=y + 64) == E_ALIAS
+    assert lib.ds4q_moe_decode_static(ctypes.byref(_layer(n_expert_used=9)), x, lg, 4, y, None,
+                                      None) == E_INVAL
 
 
 def test_prefill_and_stack_validation(lib):
