@@ -42,6 +42,13 @@ Q2K_ROW_D = D // 256 * 84       # bytes of one gate/up row (1344)
 Q2K_ROW_F = F // 256 * 84       # bytes of one down row (672)
 PAIR_FLOPS = 2 * 2 * D * F + 2 * F * D
 
+# Arithmetic each workload computes in (what the kernels multiply, not a
+# precision claim).
+DTYPE_T1 = "i8x3limb+f32"          # one token: three int8 limbs per activation
+DTYPE_I8X2 = "i8x2digit+bf16min"   # Q2_K prefill and 2..64-token Q2_K decode:
+                                   # two int8 digits per activation, min term on bf16 hi+lo
+DTYPE_BF16 = "bf16"                # Q4_1 prefill: bf16 weights and inputs, fp32 accumulation
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -90,6 +97,104 @@ def decode_bytes(T_pairs, T):
     return gateup_w + down_w + acts
 
 
+def host_cpu():
+    """The host's CPU model, logical CPU count and the CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_usable": usable}
+
+
+def oracle_configs():
+    """The CPU oracle (fp64 C, built -O2 without fast-math) timed on each
+    workload: the single 2048 x 4096 matvec, one-layer decode of 1 and of 64
+    tokens on one core; the 4096-token prefill chunk in full with OpenMP over
+    tokens on every usable core (each output element still summed by one
+    thread); one token through the 43-layer Q2_K stack on one core (one token
+    has no token parallelism); the 43-layer prefill chunk on 8 sampled tokens
+    (one thread each), extrapolated linearly (4096 / threads rounds) to 4096 tokens (tokens are
+    independent given the logits).  Expert weights are generated on the host
+    first (not timed)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    seed = 20260601
+    cpu = host_cpu()
+    threads = max(1, min(16, cpu["cpus_usable"] or 1))
+    out = {"kind": "oracle", **cpu, "threads_parallel": threads, "workloads": {}}
+    shapes = (("gate", F, D), ("up", F, D), ("down", D, F))
+
+    def host_layer(l, experts):
+        host = {n: np.zeros((E, r * c // 256 * 84), dtype=np.uint8) for n, r, c in shapes}
+        for e in experts:
+            for n, r, c in shapes:
+                host[n][e] = synth.expert_tensor_blocks("q2_k", synth.layer_key(seed, l, n, int(e)), r, c).ravel()
+        return oracle.Layer(D, F, E, K, oracle.Q2_K, host["gate"], host["up"], host["down"])
+
+    def rec(name, seconds, work, unit, note):
+        out["workloads"][name] = {"seconds": round(seconds, 3), "value": round(work / seconds, 4),
+                                  "unit": unit, "note": note}
+        log(f"oracle {name}: {seconds:.2f} s, {work / seconds:.4g} {unit}")
+
+    # single matvec (one core)
+    w = synth.expert_tensor_blocks("q2_k", synth.layer_key(seed, 0, "gate", 0), F, D)
+    xv = synth.x_f32(synth.stream_key(seed, 10), 1, D)[0]
+    t0 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        oracle.matvec(oracle.Q2_K, w, F, D, xv)
+    rec("matvec_q2_k_2048x4096", (time.perf_counter() - t0) / reps, 1.0, "matvecs/s", "1 core")
+    # one-layer decode, 1 and 64 tokens (one core)
+    for T, key in ((1, 2), (64, 12)):
+        lg = synth.logits_normal(synth.stream_key(seed, key, 0), T, E)
+        x = synth.x_f32(synth.stream_key(seed, key - 1, 0), T, D)
+        L = host_layer(0, np.unique(oracle.route(lg, K)[0]))
+        t0 = time.perf_counter()
+        oracle.moe(L, x, lg, n_threads=1)
+        rec(f"decode_{T}tok_q2_k", time.perf_counter() - t0, T, "tokens/s", "1 core")
+    # 4096-token chunk, in full (all usable cores)
+    Tp = 4096
+    lg = synth.logits_normal(synth.stream_key(seed, 4), Tp, E)
+    xb = synth.x_bf16(synth.stream_key(seed, 3), Tp, D)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    L = host_layer(0, np.arange(E))
+    t0 = time.perf_counter()
+    oracle.moe(L, xf, lg, n_threads=threads)
+    rec("prefill_4096tok_q2_k_uniform", time.perf_counter() - t0, Tp, "tokens/s",
+        f"in full, OpenMP over tokens on {threads} threads")
+    del L
+    # 43-layer stack: one decode token (one core), 16 prefill tokens
+    lgs = np.stack([synth.logits_normal(synth.stream_key(seed, 5, l), 1, E) for l in range(43)])
+    lays = [host_layer(l, np.unique(oracle.route(lgs[l], K)[0])) for l in range(43)]
+    x1 = synth.x_f32(synth.stream_key(seed, 6), 1, D)
+    t0 = time.perf_counter()
+    oracle.stack(lays, x1, lgs, prefill_bf16=False, n_threads=1)
+    rec("stack43_decode_1tok_q2_k", time.perf_counter() - t0, 1, "tokens/s", "1 core, in full")
+    S = 8
+    lgp = np.stack([synth.logits_normal(synth.stream_key(seed, 14, l), S, E) for l in range(43)])
+    lays = [host_layer(l, np.unique(oracle.route(lgp[l], K)[0])) for l in range(43)]
+    xp = synth.x_f32(synth.stream_key(seed, 15), S, D)
+    t0 = time.perf_counter()
+    oracle.stack(lays, xp, lgp, prefill_bf16=True, n_threads=S)
+    dt = time.perf_counter() - t0
+    rec("stack43_prefill_4096tok_q2_k", dt * Tp / threads, Tp, "tokens/s",
+        f"{S} sampled tokens, one thread each ({dt:.1f} s); the {Tp}-token chunk extrapolated to "
+        f"{threads} threads as {Tp}/{threads} such rounds")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +214,10 @@ def main():
                     help="tokens timed through each 43-layer stack")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="decode tokens the oracle runs (about 15 s on 16 host threads)")
+    ap.add_argument("--oracle-configs", action="store_true",
+                    help="only time the CPU oracle on each workload (single matvec, 1- and "
+                         "64-token decode on one core; the 4096-token chunk on all cores; the "
+                         "43-layer stack) and print those figures; no GPU work")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run plain device copies of this size (counter calibration)")
     args = ap.parse_args()
@@ -119,6 +228,10 @@ def main():
               "hold its share of the experts, with tokens exchanged all-to-all); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.oracle_configs:
+        print(json.dumps(oracle_configs()), flush=True)
+        return
 
     import numpy as np
     import torch
@@ -185,14 +298,22 @@ def main():
 
     rem_graphs = {}
 
-    def capture_rem(r):
-        if r not in rem_graphs:
-            rem_graphs[r] = capture(lambda: [decode_step(l) for l in range(r)])
-        return rem_graphs[r]
+    def capture_rem(r, tail=False):
+        key = (r, tail)
+        if key not in rem_graphs:
+            ls = range(NL - r, NL) if tail else range(r)
+            rem_graphs[key] = capture(lambda: [decode_step(l) for l in ls])
+        return rem_graphs[key]
 
     if args.steps % NL:
         capture_rem(args.steps % NL)
-    run_steps(args.warmup)
+    # warm-up: the LAST --warmup layers of the cycle (whole cycles first), so
+    # the timed steps start on layer 0, whose weights the warm-up did not
+    # just read (the 256 MB memory-side cache holds about five layers' experts)
+    if args.warmup % NL:
+        capture_rem(args.warmup % NL, tail=True).replay()
+    for _ in range(args.warmup // NL):
+        g.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -249,7 +370,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the arithmetic of the one-token path: int8 matrix cores on the exact
+        # integer weights against three int8 limbs of each activation (about
+        # 24 bits), int32 sums, fp32 scales, min term and accumulation
+        "dtype": DTYPE_T1,
         "data": "synthetic (seeded Q2_K blocks: codes U{0..3}, scale/min nibbles U{0..15}, "
                 "d/dmin |N(0,0.01)|; x, logits N(0,1))",
         "config": {"workload": "moe_layer_decode_1tok", "weights": "q2_k", "n_expert": E,
@@ -334,7 +458,8 @@ def main():
         log(f"prefill: {p_ms:.3f} ms/chunk, {flops / (p_ms / 1e3) / 1e12:.1f} TFLOP/s; "
             f"gateup {g1_ms:.3f} ms ({g1_tf:.1f} TFLOP/s)")
         result["prefill"] = {
-            "workload": "moe_layer_prefill_4096tok_bf16_uniform", "ms_per_chunk": round(p_ms, 4),
+            "workload": "moe_layer_prefill_4096tok_bf16_uniform", "dtype": DTYPE_I8X2,
+            "ms_per_chunk": round(p_ms, 4),
             "tflops": round(flops / (p_ms / 1e3) / 1e12, 2),
             "tokens_per_s": round(T / (p_ms / 1e3), 1),
             # algorithmic GEMM operations per second against the dense int8 peak;
@@ -471,7 +596,8 @@ def main():
                                  for l in range(NL)], 5) / NL
         touched = np.mean([len(np.unique(np.argsort(-lg64n[l], axis=1, kind="stable")[:, :K])) for l in range(NL)])
         b = touched * 3 * 2048 * 4096 // 256 * 84
-        cf["decode_64tok_q2_k"] = {"us_per_layer": round(ms * 1e3, 2), "tokens_per_s": round(T64 / (ms / 1e3), 1),
+        cf["decode_64tok_q2_k"] = {"dtype": DTYPE_I8X2,
+                                   "us_per_layer": round(ms * 1e3, 2), "tokens_per_s": round(T64 / (ms / 1e3), 1),
                                    "experts_touched": round(float(touched), 1), "weight_bytes": int(b),
                                    "gbps": round(b / (ms / 1e3) / 1e9, 1)}
         del x64, lg64, y64, ws64
@@ -484,12 +610,13 @@ def main():
             ypz = torch.empty(Tp, D, device=dev)
             wsz = torch.empty(ds4q.ds4q_moe_workspace_size(layers[0], Tp, 1), dtype=torch.uint8, device=dev)
             ms = graph_time(lambda: ds4q.ds4q_moe_prefill(layers[0], xbz, ds4q.TYPE_BF16, lgz, Tp, ypz, None, wsz), 10)
-            cf["prefill_4096tok_q2_k_zipf"] = {"ms": round(ms, 4), "tflops": round(Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
+            cf["prefill_4096tok_q2_k_zipf"] = {"dtype": DTYPE_I8X2, "ms": round(ms, 4),
+                                               "tflops": round(Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
             if q41:
                 lgu = torch.from_numpy(synth.logits_normal(synth.stream_key(seed, 4), Tp, E)).to(dev)
                 wsq = torch.empty(ds4q.ds4q_moe_workspace_size(q41[0], Tp, 1), dtype=torch.uint8, device=dev)
                 ms = graph_time(lambda: ds4q.ds4q_moe_prefill(q41[0], xbz, ds4q.TYPE_BF16, lgu, Tp, ypz, None, wsq), 10)
-                cf["prefill_4096tok_q4_1_uniform"] = {"ms": round(ms, 4),
+                cf["prefill_4096tok_q4_1_uniform"] = {"dtype": DTYPE_BF16, "ms": round(ms, 4),
                                                       "tflops": round(Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
                 del wsq, lgu
             del wsz, lgz
@@ -682,7 +809,8 @@ def main():
         result["cpu_baseline"] = {"value": round(S / dt, 3), "unit": "tokens/s", "cores": threads,
                                   "kind": "oracle",
                                   "sample": f"{S} decode tokens through layer-0 weights (fp64 C oracle, "
-                                            f"OpenMP over tokens), {dt:.1f} s wall"}
+                                            f"OpenMP over tokens), {dt:.1f} s wall",
+                                  **host_cpu()}
         log(f"cpu oracle: {S / dt:.2f} tok/s on {threads} threads")
 
     print(json.dumps(result), flush=True)

@@ -1,19 +1,22 @@
 """GPU parity of the prefill path (grouped GEMMs: int8 MFMA on Q2_K weights,
-bf16 MFMA on Q4_1 weights) through the C ABI against the oracle: max relative error <= 1e-2 — per token row (max |err| /
-max |ref| of the row) at the DeepSeek-V4-Flash expert shape, tensor-wide at
-the smaller test shapes (see helpers.normwise_err_tensor); routing ids and
-grouping bit-exact."""
+bf16 MFMA on Q4_1 weights) through the C ABI against the oracle: max relative
+error <= 1e-2 per token row (max |err| / max |ref| of the row) at every
+shape; routing ids and grouping bit-exact.  The path rounds the SwiGLU rows
+and each pair's down row to bf16 (and Q4_1 weights to bf16); measured per-row
+errors are 2.5e-3..8.1e-3 at the small shapes and 5.2e-3..6.2e-3 at the
+DeepSeek-V4-Flash shape, where an emulation of those roundings alone on exact
+products gives 4.0e-3 (5.3e-3 at 512 x 256, 300 tokens)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from helpers import SynthLayer, normwise_err, normwise_err_tensor
+from helpers import BAR_PREFILL, report, SynthLayer, normwise_err, normwise_err_tensor, tile_cover_tokens
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL_BF16 = 1e-2
+TOL_BF16 = BAR_PREFILL
 
 
 def _log(msg):
@@ -68,7 +71,9 @@ def test_prefill_small(gpu, qt, qtd, T):
     lg = synth.logits_normal(synth.stream_key(31, T), T, 16)
     y, r = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg)
     _check_route(lg, 6, 16, r)
-    assert normwise_err_tensor(y, lay.oracle_moe(xf, lg, n_threads=16)) <= TOL_BF16
+    ref = lay.oracle_moe(xf, lg, n_threads=16)
+    report(normwise_err_tensor(y, ref), "tensor")
+    assert report(normwise_err(y, ref)) <= TOL_BF16
 
 
 def test_prefill_skewed_multi_tile(gpu):
@@ -82,7 +87,7 @@ def test_prefill_skewed_multi_tile(gpu):
     _check_route(lg, 6, 32, r)
     assert r[1].max() > 3 * 128
     sample = np.arange(0, T, 7)
-    assert normwise_err_tensor(y[sample], lay.oracle_moe(xf[sample], lg[sample], n_threads=16)) <= TOL_BF16
+    assert report(normwise_err(y[sample], lay.oracle_moe(xf[sample], lg[sample], n_threads=16))) <= TOL_BF16
 
 
 @pytest.mark.parametrize("qt", [10, 3])
@@ -95,7 +100,9 @@ def test_prefill_shapes(gpu, qt, D, F):
     bits, xf = _bf16_input(synth.stream_key(34, D), 40, D)
     lg = synth.logits_normal(synth.stream_key(35, D), 40, 8)
     y, _ = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg, route=False)
-    assert normwise_err_tensor(y, lay.oracle_moe(xf, lg, n_threads=16)) <= TOL_BF16
+    ref = lay.oracle_moe(xf, lg, n_threads=16)
+    report(normwise_err_tensor(y, ref), "tensor")
+    assert report(normwise_err(y, ref)) <= TOL_BF16
 
 
 def test_prefill_f32_input_rmsnorm_accumulate(gpu):
@@ -109,22 +116,33 @@ def test_prefill_f32_input_rmsnorm_accumulate(gpu):
     y0 = synth.x_f32(synth.stream_key(38), T, 512)
     y, _ = _prefill(ds4q, lay, x, ds4q.TYPE_F32, lg, flags=ds4q.F_RMSNORM_INPUT | ds4q.F_ACCUMULATE,
                     y0=y0, route=False)
-    assert normwise_err_tensor(y - y0, lay.oracle_moe(nb, lg, n_threads=16)) <= TOL_BF16
+    assert report(normwise_err(y - y0, lay.oracle_moe(nb, lg, n_threads=16))) <= TOL_BF16
 
 
+# tokens per m-tile of the grouped GEMMs (sorted pairs of one expert)
+PREFILL_TILE_M = 96
+
+
+@pytest.mark.parametrize("qt", [10, 3])
 @pytest.mark.parametrize("kind", ["uniform", "zipf"])
-def test_prefill_full_chunk(gpu, kind):
+def test_prefill_full_chunk(gpu, qt, kind):
     """One-layer prefill chunk: 4096 bf16 tokens, DeepSeek-V4-Flash expert
-    shape, Q2_K; 16 sampled tokens against the oracle."""
+    shape ("【#6】ds4.c 분석하기": prefill runs in 4096-token chunks), Q2_K or
+    Q4_1 weights, uniform or Zipf(1.1) routing.  The rows checked against the
+    oracle are chosen so that every 16-pair group of every m-tile, and every
+    position of a tile, holds a checked pair (tokens are independent given the
+    logits)."""
     ds4q = gpu
-    _log(f"prefill full {kind}")
+    _log(f"prefill full qt={qt} {kind}")
     T = 4096
-    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, 10, seed=640)
+    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, qt, seed=640 + qt)
     bits, xf = _bf16_input(synth.stream_key(39), T, 4096)
     gen = synth.logits_normal if kind == "uniform" else synth.logits_zipf
     lg = gen(synth.stream_key(40, 0 if kind == "uniform" else 1), T, 256)
     y, r = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg)
     _check_route(lg, 6, 256, r)
     assert np.all(np.isfinite(y))
-    sample = np.linspace(0, T - 1, 16).astype(int)
-    assert normwise_err(y[sample], lay.oracle_moe(xf[sample], lg[sample], n_threads=16)) <= TOL_BF16
+    sample = tile_cover_tokens(r[0], 256, PREFILL_TILE_M)
+    _log(f"checking {len(sample)} rows")
+    ref = lay.oracle_moe(xf[sample], lg[sample], n_threads=16)
+    assert report(normwise_err(y[sample], ref)) <= TOL_BF16

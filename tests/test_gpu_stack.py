@@ -21,7 +21,7 @@ import torch
 
 import oracle
 import synth
-from helpers import SynthLayer, normwise_err
+from helpers import PATH_LIMBS3, report, SynthLayer, normwise_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -106,7 +106,7 @@ def test_stack_decode_one_token(gpu, qt):
     lays, x0, lg, x_stack, x_lbl, errs = _stack_case(ds4q, qt, 0, 1, set(range(L_FLASH)), _seed(700, qt))
     assert np.array_equal(x_stack.view(np.uint32), x_lbl.view(np.uint32))
     for l, e in errs:
-        assert e <= 2e-3, (l, e)
+        assert e <= 2e-3 and e <= PATH_LIMBS3, (l, e)   # one token: the three-limb path
     # end to end against the oracle's own 43-layer run
     ref = oracle.stack([l.orc for l in lays], x0, lg, prefill_bf16=False, n_threads=1)
     drift = normwise_err(x_stack, ref.astype(np.float64))

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from helpers import SynthLayer
+from helpers import report, SynthLayer
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

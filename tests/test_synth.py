@@ -79,3 +79,29 @@ def test_zipf_logits_skew():
     assert load.sum() == 4096 * 6
     srt = np.sort(load)[::-1]
     assert srt[0] > 2000 and np.median(load) < 60           # heavy head, light tail
+
+
+def test_tile_cover_tokens_covers_every_group_and_position():
+    """The GPU tests' sample of tokens at the 4096-token chunk: every 16-pair
+    group of every m-tile and every position of a tile holds a pair of a
+    chosen token (checked here by brute force on a small routing)."""
+    import oracle
+    from helpers import tile_cover_tokens
+    T, E, k, tm = 300, 8, 6, 96
+    lg = synth.logits_zipf(synth.stream_key(77), T, E)
+    ids, _ = oracle.route(lg, k)
+    chosen = set(tile_cover_tokens(ids, E, tm).tolist())
+    _, offsets, pairs = oracle.group(ids, E)
+    cells, positions = set(), set()
+    need_cells, need_positions = set(), set()
+    for e in range(E):
+        for i in range(offsets[e], offsets[e + 1]):
+            local = i - offsets[e]
+            cell = (e, local // tm, (local % tm) // 16)
+            need_cells.add(cell)
+            need_positions.add(local % tm)
+            if pairs[i] // k in chosen:
+                cells.add(cell)
+                positions.add(local % tm)
+    assert cells == need_cells and positions == need_positions
+    assert len(chosen) < T
