@@ -478,7 +478,7 @@ DS4Q_API int ds4q_dequant(int32_t src_type, const void *src, int64_t rows, int64
   if (cols % qk_of(src_type)) return DS4Q_E_SHAPE;
   if (rows == 0) return DS4Q_OK;
   if (!src || !dst) return DS4Q_E_INVAL;
-  if (!aligned(src, 4) || !aligned(dst, 16)) return DS4Q_E_ALIGN;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return DS4Q_E_ALIGN;
   const size_t sb = (size_t)rows * row_bytes(src_type, cols);
   const size_t db = (size_t)rows * cols * (dst_type == DS4Q_TYPE_F32 ? 4 : 2);
   if (overlap(src, sb, dst, db)) return DS4Q_E_ALIAS;

@@ -132,8 +132,9 @@ typedef struct {
 } ds4q_route_out;
 
 /* Dequantise a [rows][cols] tensor ([P1] Q2_K table, [P5] Q4_1 section).
- * src_type: Q2_K (cols % 256 == 0) or Q4_1 (cols % 32 == 0); src 4-byte
- * aligned device pointer to rows*cols/QK blocks.  dst_type: F32 (value =
+ * src_type: Q2_K (cols % 256 == 0) or Q4_1 (cols % 32 == 0); src 16-byte
+ * aligned device pointer to rows*cols/QK blocks (read in 16-byte chunks;
+ * never past the last block).  dst_type: F32 (value =
  * fp32 of d*sc*q - dmin*mn, resp. d*q + m, rounded once) or BF16 (that fp32
  * value rounded to nearest even); dst device [rows][cols], 16-byte aligned,
  * not overlapping src.  rows == 0 is a no-op. */
@@ -231,9 +232,13 @@ int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float 
                            int32_t n_tok, float *y, const ds4q_route_out *route, void *workspace,
                            size_t workspace_bytes, uint32_t phases, void *stream);
 
-/* Prefill-path MoE layer: same mathematics as ds4q_moe_decode for a chunk
- * of n_tok tokens (0..65536), computed as grouped GEMMs on matrix cores
- * with fp32 accumulation.  The expert input rows are bf16 (x_type BF16, or
+/* Prefill-path MoE layer ("【#6】ds4.c 분석하기", chunked-prefill passage: the
+ * prompt is processed in chunks of 4096 tokens; "【#2】ds4.c 해독하기": the
+ * routed expert is a SwiGLU FFN, w1 = gate, w3 = up, w2 = down, and the
+ * routing weight scales the SwiGLU row that the down projection reads): the
+ * same mathematics as ds4q_moe_decode for a chunk of n_tok tokens
+ * (0..65536), computed as grouped GEMMs on matrix cores with fp32
+ * accumulation.  The expert input rows are bf16 (x_type BF16, or
  * x_type F32 which is normalised per DS4Q_F_RMSNORM_INPUT if set and rounded
  * to bf16); the SwiGLU row is rounded to bf16 before the down projection.
  * Q4_1 weights are dequantised to bf16 (fp32 d*q + m rounded once) for bf16

@@ -65,6 +65,7 @@ def test_dequant_validation(lib):
     assert f(ds4q.TYPE_Q2_K, src, 0, 256, ds4q.TYPE_F32, dst, None) == OK       # no-op
     assert f(ds4q.TYPE_Q2_K, None, 4, 256, ds4q.TYPE_F32, dst, None) == E_INVAL
     assert f(ds4q.TYPE_Q2_K, src, 4, 256, ds4q.TYPE_F32, dst + 8, None) == E_ALIGN
+    assert f(ds4q.TYPE_Q2_K, src + 4, 4, 256, ds4q.TYPE_F32, dst, None) == E_ALIGN
     assert f(ds4q.TYPE_Q2_K, src, 4, 256, ds4q.TYPE_BF16, src + 64, None) == E_ALIAS
 
 
