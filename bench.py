@@ -45,8 +45,10 @@ PAIR_FLOPS = 2 * 2 * D * F + 2 * F * D
 # Arithmetic each workload computes in (what the kernels multiply, not a
 # precision claim).
 DTYPE_T1 = "i8x3limb+f32"          # one token: three int8 limbs per activation
-DTYPE_I8X2 = "i8x2digit+bf16min"   # Q2_K prefill and 2..64-token Q2_K decode:
-                                   # two int8 digits per activation, min term on bf16 hi+lo
+DTYPE_I8X3 = "i8x3digit+i8min"     # 2..64-token Q2_K decode: three int8 digits per
+                                   # activation, min term exact on int8 matrix cores
+DTYPE_I8X2 = "i8x2digit+bf16min"   # Q2_K prefill: two int8 digits per activation,
+                                   # min term on bf16 hi+lo
 DTYPE_BF16 = "bf16"                # Q4_1 prefill: bf16 weights and inputs, fp32 accumulation
 
 
@@ -596,7 +598,7 @@ def main():
                                  for l in range(NL)], 5) / NL
         touched = np.mean([len(np.unique(np.argsort(-lg64n[l], axis=1, kind="stable")[:, :K])) for l in range(NL)])
         b = touched * 3 * 2048 * 4096 // 256 * 84
-        cf["decode_64tok_q2_k"] = {"dtype": DTYPE_I8X2,
+        cf["decode_64tok_q2_k"] = {"dtype": DTYPE_I8X3,
                                    "us_per_layer": round(ms * 1e3, 2), "tokens_per_s": round(T64 / (ms / 1e3), 1),
                                    "experts_touched": round(float(touched), 1), "weight_bytes": int(b),
                                    "gbps": round(b / (ms / 1e3) / 1e9, 1)}

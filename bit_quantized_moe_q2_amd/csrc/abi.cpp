@@ -56,6 +56,7 @@ struct Workspace {
   float *imat_part = nullptr;  // imatrix on m-tiles: [max_tiles][max(D, F)] f32 partial rows
   uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
   PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
+  PrepD3 xd{}, hd{};       // decode of 2..64 tokens on Q2_K: int8 digit rows of x and of h
   size_t bytes = 0;
 
   // mode 1 (prefill): i8_in / i8_h = Q2_K gate/up resp. down (int8 matrix
@@ -88,10 +89,10 @@ struct Workspace {
       else stage = (float *)take((size_t)D * 4);
       if (i8_in) {  // decode of 2..64 tokens on Q2_K: the grouped int8 kernels
         rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k, DECODE_TILE_M) * 8);
-        void *p = take(prep_i8_bytes(T, D));
-        if (base) xq = prep_i8_view(p, T, D);
-        p = take(prep_i8_bytes(P, F));
-        if (base) hq = prep_i8_view(p, P, F);
+        void *p = take(prep_d3_bytes(T, D));
+        if (base) xd = prep_d3_view(p, T, D);
+        p = take(prep_d3_bytes(P, F));
+        if (base) hd = prep_d3_view(p, P, F);
       }
     } else {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * 8);
@@ -379,15 +380,15 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
       TIMED_TRY("group", launch_group(T, m.E, m.k, DECODE_TILE_M, w.rb, s));
     }
     if (p_gu) {
-      TIMED_TRY("prep_i8", launch_prep_i8(x, true, false, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xq, s));
-      TIMED_TRY("decode_gateup", launch_decode_grouped(m, w.xq, T, w.rb, mt, w.h, 1, s));
+      TIMED_TRY("prep_d3", launch_prep_d3(x, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xd, s));
+      TIMED_TRY("decode_gateup", launch_decode_grouped(m, w.xd, T, w.rb, mt, w.h, 1, s));
       const int na = T * m.k < m.E ? T * m.k : m.E;
       if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_ACTIVE, na, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
                                         rows_of(w.h, false, nullptr, true), s));
     }
     if (p_down) {
-      TIMED_TRY("prep_i8", launch_prep_i8(w.h, true, false, nullptr, (int64_t)T * m.k, m.F, w.hq, s));
-      TIMED_TRY("decode_down", launch_decode_grouped(m, w.hq, T, w.rb, mt, w.o, 2, s));
+      TIMED_TRY("prep_d3", launch_prep_d3(w.h, nullptr, (int64_t)T * m.k, m.F, w.hd, s));
+      TIMED_TRY("decode_down", launch_decode_grouped(m, w.hd, T, w.rb, mt, w.o, 2, s));
       TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, st, s));
     }
     return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;

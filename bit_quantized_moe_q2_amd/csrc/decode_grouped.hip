@@ -3,27 +3,30 @@
 // At decode sizes an expert holds a few of the call's token-expert pairs,
 // so the work is the weight stream of the routed experts ("【#2】ds4.c
 // 해독하기": only the routed experts' bytes move per token).  A work item is an
-// m-tile of at most DECODE_TILE_M sorted pairs of one expert and an n-tile of
-// weight rows.  Each of the eight waves owns 32 weight rows (two 16-row
-// subtiles) and a quarter or half of K (four blocks), and requests all of its
-// raw weight bytes as soon as the expert is known; the tile's prepared
-// activation rows (i8_ops.h) for the whole K then go to LDS by direct
-// global->LDS loads, only for the pairs that are present.  One wait and one
-// barrier later each wave runs its blocks on the matrix cores, the K parts
-// meet in LDS, and the epilogue writes SwiGLU rows (gate/up) or the down rows,
-// in sorted-pair order.
+// m-tile of at most DECODE_TILE_M (4) sorted pairs of one expert and an
+// n-tile of weight rows; each of the eight waves owns 16 weight rows over a
+// quarter or half of K (four 256-value blocks).  The workgroups are
+// persistent and stream the next item's weights while computing the current
+// one (see decode_grouped_kernel).
 //
-// Arithmetic as in the prefill GEMMs (prefill_i8.hip), with the bf16 residues
-// of -dmin*mn applied as well (min term to about 16 bits): the integer MFMA's
-// 16 A rows are the 8 pairs x 2 digits (row 2*pair + digit); the min-term
-// MFMA's A row i is pair 2(i>>2) + (i&1), so that accumulator rows 0 and 1 of
-// a lane with group g are pairs 2g and 2g+1 in both (rows 2 and 3 repeat them
-// and are not used).
+// Arithmetic.  For one block of a weight row ("【#2】ds4.c 해독하기", Q2_K
+// block-layout table) and an activation row a,
+//   sum_v w_v a_v = d * sum_v (sc*q)_v a_v  -  dmin * sum_s mn_s A_s,
+// A_s the sums of a over the 16 sub-blocks.  Each activation row is prepared
+// once per call (prep_d3_kernel): sigma = max|a| / 127 over the row and
+// N = round(a / sigma * 65536) as three balanced base-256 digits a0 (high),
+// a1, a2, all int8, so a = sigma * (a0 + a1/256 + a2/65536) up to
+// sigma/131072 (2^-24 of the row maximum).  On v_mfma_i32_16x16x64_i8 the 16
+// A rows are the 4 pairs x 4 (three digits and an unused row: row
+// 4*pair + digit), so each lane's four accumulator rows are one pair's
+// digits.  Two B operands per block: the integer weights sc*q in 0..45
+// (v_perm of the byte table [0, sc, 2sc, 3sc] with the 2-bit codes), and the
+// min nibble of each value's sub-block (min_bfrag), whose MFMAs sum to
+// sum_s mn_s A_s; both sums are exact in int32 and meet d and dmin in fp32.
 //
-// LDS: digit rows [pair][block][digit][16 chunks] with data chunk c of row
-// r = 2*pair + digit stored at chunk c ^ r (the 16 lanes reading one chunk
-// column of the 16 A rows hit 16 different bank groups), then the sums
-// [block][pair][64 bytes].
+// LDS: digit rows [digit][pair][block][16 chunks] with data chunk c of row
+// r = 4*pair + digit stored at chunk c ^ r (the lanes reading one chunk
+// column of the A rows hit different bank groups), then the K parts.
 #include "common.h"
 #include "i8_ops.h"
 #include "launch.h"
@@ -32,206 +35,378 @@ namespace ds4q {
 namespace {
 
 constexpr int GT = DECODE_TILE_M;
-static_assert(GT == 8, "the A operand holds 8 pairs x 2 digits");
+static_assert(GT == 4, "the A operand holds 4 pairs x 4 rows");
+constexpr int QROW3 = 768;  // digit bytes of one row's 256-column block (3 digits)
+
+// One workgroup per activation row, one thread per 16-value sub-block: the
+// row (times inv_rms[row] when given) as three digit rows per block in the
+// B order of the weights (byte i of dword k of chunk 4j+g is value
+// 128(g>>1) + 32k + 16(g&1) + 4j + i), and sigma.
+__global__ __launch_bounds__(256) void prep_d3_kernel(const float *__restrict__ src,
+                                                      const float *__restrict__ inv_rms, int K,
+                                                      uint8_t *__restrict__ aq, float *__restrict__ asig) {
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nsub = K >> 4, nb = K >> 8;
+  __shared__ float red[4];
+  float v[16];
+  float m = 0.f;
+  const bool act = t < nsub;
+  if (act) {
+    const float sc = inv_rms ? inv_rms[row] : 1.0f;
+    const float4 *x = reinterpret_cast<const float4 *>(src + row * K + 16 * t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = x[i];
+      v[4 * i] = f.x * sc;
+      v[4 * i + 1] = f.y * sc;
+      v[4 * i + 2] = f.z * sc;
+      v[4 * i + 3] = f.w * sc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = mx > 0.f ? 127.0f / mx : 0.0f;
+  if (t == 0) asig[row] = mx * (1.0f / 127.0f);
+  if (!act) return;
+  const int b = t >> 4, s = t & 15;
+  const int g = 2 * (s >> 3) + (s & 1), k = (s >> 1) & 3;
+  uint32_t *qb = reinterpret_cast<uint32_t *>(aq + (row * nb + b) * QROW3);
+  const float scale = inv * 65536.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // N + 0x808080 = 65536 (a0 + 128) + 256 (a1 + 128) + (a2 + 128), in
+    // [0, 2^24) for |N| <= 127 * 65536 (an integer-valued float there)
+    uint32_t n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n[i] = (uint32_t)__builtin_rintf(fmaf(v[4 * j + i], scale, 8421504.0f));
+    const uint32_t p01 = __builtin_amdgcn_perm(n[1], n[0], 0x05010400u);  // bytes 0, 1
+    const uint32_t p23 = __builtin_amdgcn_perm(n[3], n[2], 0x05010400u);
+    const uint32_t q01 = __builtin_amdgcn_perm(n[1], n[0], 0x0C0C0602u);  // byte 2
+    const uint32_t q23 = __builtin_amdgcn_perm(n[3], n[2], 0x0C0C0602u);
+    const int off = (4 * j + g) * 4 + k;
+    qb[off] = __builtin_amdgcn_perm(q23, q01, 0x05040100u) ^ 0x80808080u;        // a0
+    qb[64 + off] = __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u;   // a1
+    qb[128 + off] = __builtin_amdgcn_perm(p23, p01, 0x05040100u) ^ 0x80808080u;  // a2
+  }
+}
 
 template <int NB>
 struct GLayout {
-  static constexpr int BPW = NB < 4 ? NB : 4;  // blocks per wave
-  static constexpr int KS = NB / BPW;          // K parts
-  static constexpr int DIG = GT * NB * QROW;   // digit rows
-  static constexpr int SUM = GT * NB * XROW < 1024 ? 1024 : GT * NB * XROW;
-  static constexpr int NDMA_S = SUM / 1024;    // 1-KiB direct loads of the sums
-  static constexpr int PART = 8 * GT * 32 * 4;  // K parts of the eight waves
-  static constexpr int BYTES = DIG + SUM > PART ? DIG + SUM : PART;
+  static constexpr int BPW = NB < 4 ? NB : 4;   // blocks per wave
+  static constexpr int KS = NB / BPW;           // K parts
+  static constexpr int DIG = GT * NB * QROW3;   // digit rows
+  static constexpr int NDMA = DIG / 1024;       // 1-KiB direct loads of the digit rows
+  static constexpr int PART = 8 * 64 * 4;       // K parts of the eight waves (a float per lane)
+  static constexpr int BYTES = DIG + PART;
 };
 
-// Weight rows of one work item: 32 per wave over the waves that share a K part.
-constexpr int rows_per_item(bool swiglu, int nb) { return 32 * 8 / ((swiglu ? 2 : 1) * (nb < 4 ? 1 : nb / 4)); }
+// Weight rows of one work item: 16 per wave over the waves that share a K part.
+constexpr int rows_per_item(bool swiglu, int nb) { return 16 * 8 / ((swiglu ? 2 : 1) * (nb < 4 ? 1 : nb / 4)); }
 
-// SWIGLU: W0 = gate, W1 = up, rows = n_ff, the A rows are the pairs' token
-// rows (gathered through the sorted pair list); out = SwiGLU rows [pos][n_ff].
-// Otherwise W0 = down, rows = n_embd, the A rows are the sorted positions;
-// out = down rows [pos][n_embd].  Waves: w = (mat * RG + rg) * KS + kq.
-template <bool SWIGLU, int NB>
-__global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
-    const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int rows_per_expert,
-    const uint8_t *__restrict__ aq, const uint8_t *__restrict__ ax, const float *__restrict__ asig,
-    int kslots, int n_pairs, RouteBufs rb, int n_ntiles, float *__restrict__ out) {
-  using L = GLayout<NB>;
-  constexpr int BPW = L::BPW, KS = L::KS, NMAT = SWIGLU ? 2 : 1, RG = 8 / (NMAT * KS);
-  constexpr int ROWS = RG * 32;  // weight rows per work item
-  static_assert(NMAT * KS * RG == 8 && ROWS == rows_per_item(SWIGLU, NB), "eight waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
-  __shared__ float sig_s[GT];
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(4))) i32x2 *const_i32x2_ptr;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
 
-  // Work item: m-tile blockIdx.x / n_ntiles, n-tile blockIdx.x % n_ntiles
-  // (a tile's activation rows are small, so keeping its n-tiles on one XCD
-  // buys little; this mapping lets the tile and the live tile count be read
-  // together).  Items past the live m-tiles exit at once.
-  const int mtile = blockIdx.x / n_ntiles, ntile = blockIdx.x % n_ntiles;
-  const int n_live = *rb.n_tiles;
-  const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];  // in the array (grid bound)
-  if (mtile >= n_live || e < 0) return;  // uniform; testing e keeps both loads ahead of the branch
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const int kq = w % KS, rg = (w / KS) % RG, mat = w / (KS * RG);
-
-  // the pair list entries of the tile (clamped into the list; entries past
-  // the tile's end are never used)
-  int pr = 0;
-  if constexpr (SWIGLU) pr = rb.pairs[min(start + (lane & (GT - 1)), n_pairs - 1)];
-  const int end = rb.offsets[e + 1];
+// Barrier for LDS only: the workgroup's LDS accesses so far are complete;
+// global loads in flight stay in flight (a full __syncthreads would wait for
+// them too).
+__device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-
-  // all raw weight bytes of the wave: blocks kq*BPW .. +BPW-1 of rows
-  // ntile*ROWS + rg*32 + 16t + n
-  const int64_t rbytes = (int64_t)NB * BB_Q2K;
-  const uint8_t *wm = mat ? W1 : W0;
-  Q2KPart raw[BPW][2];
-#pragma unroll
-  for (int b = 0; b < BPW; ++b)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = ntile * ROWS + rg * 32 + 16 * t + n;
-      raw[b][t].load(wm + ((int64_t)e * rows_per_expert + row) * rbytes + (int64_t)(kq * BPW + b) * BB_Q2K, g);
-    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+}
 
-  const int valid = min(end - start, GT);  // >= 1
-  // source row of pair m (m < GT; pairs past the end repeat the last one)
-  auto arow = [&](int m) {
-    const int mm = min(m, valid - 1);
-    if constexpr (SWIGLU) return __shfl(pr, mm, 64) / kslots;
-    else return start + mm;
-  };
-  // Activation rows to LDS, every load 1 KiB (64 lanes x 16 bytes).  Digit
-  // rows: wave w loads those of pair w (NB/2 loads), or with one block per
-  // row waves 0..3 load pairs 2w and 2w+1; pairs that are absent are not
-  // loaded.  Sums: wave w loads bytes [1024 w, 1024 w + 1024) of the sum
-  // area (blocks 2w, 2w+1 of all pairs).  Each lane's source rows are found
-  // before the first load, so the loads are straight-line code.
-  const int lane_pair = NB >= 2 ? w : 2 * w + (lane >> 5);
-  const int row_dig = arow(lane_pair);
-  const int row_sum = arow((lane >> 2) & (GT - 1));
-  // the row scales of the tile's pairs, requested with the activation rows
-  // and kept in registers until the K parts meet
-  const float sig_r = tid < GT ? asig[arow(tid)] : 0.f;
-  {
-    const int d = (lane >> 4) & 1, c = (lane & 15) ^ ((2 * lane_pair + d) & 15);
-    const uint8_t *src = aq + (int64_t)row_dig * NB * QROW + (NB >= 2 ? (lane >> 5) * QROW : 0) + d * 256 + c * 16;
-    if (NB >= 2 ? w < valid : (w < 4 && 2 * w < valid)) {
-      uint8_t *dst = lds + (NB >= 2 ? w * NB * QROW : 1024 * w);
-#pragma unroll
-      for (int u = 0; u < (NB >= 2 ? NB / 2 : 1); ++u) dma16(src + u * 2 * QROW, dst + 1024 * u);
-    }
-    if (w < L::NDMA_S) {
-      const int b = min(2 * w + (lane >> 5), NB - 1);
-      dma16(ax + ((int64_t)row_sum * NB + b) * XROW + (lane & 3) * 16, lds + L::DIG + 1024 * w);
-    }
-  }
-  // the wave's loads (weights and LDS) landed; the barrier publishes LDS
+// Barrier after every load of the wave has landed (direct loads to LDS
+// included).
+__device__ __forceinline__ void full_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-
-  f32x4 acc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
-  const int aoff = (n >> 1) * NB * QROW + (n & 1) * 256;
-  const int soff = L::DIG + (2 * (n >> 2) + (n & 1)) * XROW;
-#pragma unroll
-  for (int b = 0; b < BPW; ++b) {
-    const int kb = kq * BPW + b;
-    i32x4 a[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      a[j] = *reinterpret_cast<const i32x4 *>(lds + aoff + kb * QROW + (((4 * j + g) ^ n) << 4));
-    const uint8_t *sp = lds + soff + kb * (GT * XROW);
-    const bf16x8 xa = *reinterpret_cast<const bf16x8 *>(sp + (g & 1) * 32 + (g >> 1) * 16);
-    const s16x4 xh = *reinterpret_cast<const s16x4 *>(sp + 8 * g);
-    // the two subtiles' chains are independent: they are issued in pairs per
-    // K tile (B fragments built just before), each pair a fenced MFMA group
-    WTab tb[2];
-    WMin<true> wm[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      raw[b][t].finish();
-      tb[t].build(raw[b][t], g);
-    }
-    i32x4 c[2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      i32x4 bj[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) bj[t] = tb[t].bfrag(raw[b][t], j);
-      mfma_group_begin();
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        c[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], bj[t], j ? c[t] : (i32x4){0, 0, 0, 0}, 0, 0, 0);
-      mfma_fence();
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) wm[t].build(raw[b][t], g);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t][0] = fmaf(wm[t].dsc, (float)((c[t].x << 8) + c[t].y), acc[t][0]);
-      acc[t][1] = fmaf(wm[t].dsc, (float)((c[t].z << 8) + c[t].w), acc[t][1]);
-    }
-    // the min-term MFMAs one at a time (their accumulators are assembled by
-    // vector moves, which must not fall between two of them)
-    mfma_fence();
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wm[t].bmin, acc[t], 0, 0, 0);
-      mfma_fence();
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, wm[t].bminlo, acc[t], 0, 0, 0);
-      mfma_fence();
-    }
-  }
-
-  // K parts: part[w][pair][32 rows] over the (no longer needed) digit rows
-  __syncthreads();
-  float *part = reinterpret_cast<float *>(lds);
-  if (tid < GT) sig_s[tid] = sig_r;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    part[(w * GT + 2 * g) * 32 + 16 * t + n] = acc[t][0];
-    part[(w * GT + 2 * g + 1) * 32 + 16 * t + n] = acc[t][1];
-  }
-  __syncthreads();
-  for (int i = tid; i < GT * ROWS; i += 512) {
-    const int m = i / ROWS, r = i % ROWS;
-    if (m >= valid) break;  // i grows with m
-    const int rgi = r / 32, rr = r % 32;
-    float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-    for (int q = 0; q < KS; ++q) {
-      v0 += part[(((0 * RG + rgi) * KS + q) * GT + m) * 32 + rr];
-      if constexpr (SWIGLU) v1 += part[(((1 * RG + rgi) * KS + q) * GT + m) * 32 + rr];
-    }
-    const float sg = sig_s[m];
-    const int64_t pos = start + m;
-    const int row = ntile * ROWS + r;
-    if constexpr (SWIGLU) out[pos * rows_per_expert + row] = silu(v0 * sg) * (v1 * sg);
-    else out[pos * rows_per_expert + row] = v0 * sg;
-  }
 }
 
+// Raw bytes of one block for lane group g, as Q2KPart::load requests them
+// (the 16 code bytes of quarter g; 8 bytes that are scale/min bytes or end
+// with d|dmin), kept as two vectors so that a loop can reload them in place.
+struct RawBlk {
+  u32x4 q;
+  u32x2 p;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
+    q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
+    p = *reinterpret_cast<const u32x2a *>(blk + ((g & 1) ? 76 : 8 * (g >> 1)));
+  }
+};
+
+// The operand bytes of a raw block, as Q2KPart::finish makes them, with one
+// exchange per result: the raw registers are only read (an exchange rewrites
+// both of its operands), so they can take the next block in place.
+__device__ __forceinline__ Q2KPart take_block(const RawBlk &r) {
+  Q2KPart o;
+  o.q = r.q;
+  o.p0 = o.p1 = 0;
+  o.s0 = __builtin_amdgcn_permlane16_swap(r.p.x, r.p.x, false, false)[0];  // the even group's bytes
+  o.s1 = __builtin_amdgcn_permlane16_swap(r.p.y, r.p.y, false, false)[0];  // its bytes 4..7
+  o.dd = __builtin_amdgcn_permlane16_swap(r.p.y, r.p.y, true, false)[1];   // the odd group's d|dmin
+  return o;
+}
+
+// Integer B fragment of the min term: dword k is the min nibble of the
+// lane's sub-block for bit pair k (the sub-block of that dword in every
+// K-tile's code fragment) in all four bytes, so the K-tiles' MFMAs against
+// the digit rows sum to sum_s mn_s A_s exactly.  sel_lo / sel_hi replicate
+// byte p / 2 + p (p = g & 1) of a dword.
+__device__ __forceinline__ i32x4 min_bfrag(const Q2KPart &r, uint32_t sel_lo, uint32_t sel_hi) {
+  const uint32_t m0 = (r.s0 >> 4) & 0x0F0F0F0Fu, m1 = (r.s1 >> 4) & 0x0F0F0F0Fu;
+  i32x4 b;
+  b.x = (int)__builtin_amdgcn_perm(0u, m0, sel_lo);
+  b.y = (int)__builtin_amdgcn_perm(0u, m0, sel_hi);
+  b.z = (int)__builtin_amdgcn_perm(0u, m1, sel_lo);
+  b.w = (int)__builtin_amdgcn_perm(0u, m1, sel_hi);
+  return b;
+}
+
+// The three digit sums of a pair as one value in units of the high digit:
+// C0 + C1/256 + C2/65536 (C0*256 + C1 is exact in int32).
+__device__ __forceinline__ float digits3(i32x4 c) {
+  return fmaf((float)c.z, 1.0f / 65536.0f, (float)((c.x << 8) + c.y) * (1.0f / 256.0f));
+}
+
+// SWIGLU: W0 = gate, W1 = up, rows = n_ff, the A rows are the pairs' token
+// rows (gathered through the sorted pair list); out = SwiGLU rows [pos][n_ff].
+// Otherwise W0 = down, rows = n_embd, the A rows are the sorted positions;
+// out = down rows [pos][n_embd].  Waves: w = (mat * RG + rg) * KS + kq; a
+// wave owns 16 weight rows over BPW blocks of K.
+//
+// Persistent, two workgroups per CU: workgroup i takes the contiguous run of
+// work items [i n / G, (i + 1) n / G) (item = m-tile * n_ntiles + n-tile, n
+// counted on the device), so consecutive items mostly share their m-tile and
+// its digit rows stay in LDS.  The next item's weights stream in while the
+// current one is computed: once a block's MFMAs are issued, the registers
+// that held its raw bytes receive the same block of the next item.
+// Barriers wait for LDS only, so those loads stay in flight across them.
+// When the m-tile changes, the new digit rows are requested once the old
+// ones are no longer read, and waited for then.  An item's outputs are
+// stored once the next item has started, so no wait covers their completion.
+template <bool SWIGLU, int NB>
+__global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
+    const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int rows_per_expert,
+    const uint8_t *__restrict__ aq, const float *__restrict__ asig, int kslots, int n_pairs,
+    RouteBufs rb, int n_ntiles, float *__restrict__ out) {
+  using L = GLayout<NB>;
+  constexpr int BPW = L::BPW, KS = L::KS, NMAT = SWIGLU ? 2 : 1, RG = 8 / (NMAT * KS);
+  constexpr int ROWS = RG * 16;  // weight rows per work item
+  static_assert(NMAT * KS * RG == 8 && ROWS == rows_per_item(SWIGLU, NB), "eight waves");
+  static_assert(GT * ROWS <= 512, "one output per thread and item");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
+  __shared__ float sig_s[GT];
+
+  const int n_items = *rb.n_tiles * n_ntiles;
+  const int G = gridDim.x;
+  int item = (int)((int64_t)blockIdx.x * n_items / G);
+  const int item_end = (int)((int64_t)(blockIdx.x + 1) * n_items / G);
+  if (item >= item_end) return;  // uniform
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int kq = w % KS, rg = (w / KS) % RG, mat = w / (KS * RG);
+  const int64_t rbytes = (int64_t)NB * BB_Q2K;
+  const uint8_t *wm = mat ? W1 : W0;
+  const uint32_t sel_lo = (g & 1) ? 0x01010101u : 0x00000000u;
+  const uint32_t sel_hi = (g & 1) ? 0x03030303u : 0x02020202u;
+
+  // m-tile context: expert, first sorted position, pairs present (>= 1), the
+  // lane's pair-list entry (SWIGLU; entries past the tile's end are never
+  // used) and the row scale of pair tid (tid < GT).  The tile entry is read
+  // through the scalar cache (uniform); the pair count and list entry are
+  // requested early and taken (tile_take) when they are needed.
+  struct MTile {
+    int e, start, valid, pr;
+    float sig;
+  };
+  auto tile_head = [&](int mt, MTile &c) {
+    const i32x2 v = *((const_i32x2_ptr)(const void *)rb.tiles + mt);
+    c.e = v.x;
+    c.start = v.y;
+  };
+  auto tile_rest = [&](MTile &c) {
+    c.valid = *((const __attribute__((address_space(4))) int *)(const void *)rb.offsets + c.e + 1);
+    c.pr = 0;
+    if constexpr (SWIGLU) c.pr = rb.pairs[min(c.start + (lane & (GT - 1)), n_pairs - 1)];
+  };
+  auto tile_take = [&](MTile &c) { c.valid = min(c.valid - c.start, GT); };
+  // source row of pair m (m < GT; pairs past the end repeat the last one)
+  auto arow = [&](const MTile &c, int m) {
+    const int mm = min(m, c.valid - 1);
+    if constexpr (SWIGLU) return __shfl(c.pr, mm, 64) / kslots;
+    else return c.start + mm;
+  };
+  // raw bytes of block b of the wave's K part: row nt*ROWS + rg*16 + n
+  auto load_block = [&](int e, int nt, int b, RawBlk &r) {
+    const int row = nt * ROWS + rg * 16 + n;
+    r.load(wm + ((int64_t)e * rows_per_expert + row) * rbytes + (int64_t)(kq * BPW + b) * BB_Q2K, g);
+  };
+  // Digit rows of an m-tile to LDS as NDMA direct loads of 1 KiB (64 lanes
+  // x 16 bytes), load u by wave u % 8.  LDS layout [digit][pair][block][16
+  // chunks]; with four or more blocks a load holds one (digit, pair) row, and
+  // loads of absent pairs are skipped.  The row scales go to registers until
+  // the K parts meet.
+  auto issue_act = [&](MTile &c) {
+    const int src_row = arow(c, lane & 3);  // source row of pair lane & 3
+#pragma unroll
+    for (int u0 = 0; u0 < L::NDMA; u0 += 8) {
+      int u = u0 + w;
+      asm volatile("" : "+s"(u));  // the slot arithmetic below stays here (not hoisted out of the loop)
+      if (u < L::NDMA) {
+        const int sl = 64 * u + lane;    // 16-byte slot
+        const int rix = sl / (NB * 16);  // 4 * digit + pair
+        const int pair = rix & 3, d = rix >> 2;
+        const int blk = (sl >> 4) & (NB - 1), pos = sl & 15;
+        int srow;
+        bool live = true;
+        if constexpr (NB >= 4) {
+          const int upair = ((64 * u) / (NB * 16)) & 3;  // the load's pair (uniform)
+          live = upair < c.valid;
+          srow = __builtin_amdgcn_readlane(src_row, upair);
+        } else {
+          srow = __shfl(src_row, pair, 64);
+        }
+        if (live)
+          dma16(aq + (int64_t)srow * (NB * QROW3) + (blk * QROW3 + d * 256 + ((pos ^ (4 * pair + d)) << 4)),
+                lds + 1024 * u);
+      }
+    }
+    c.sig = tid < GT ? asig[arow(c, tid)] : 0.f;
+  };
+
+  int mt = item / n_ntiles, nt = item % n_ntiles;
+  MTile cur;
+  tile_head(mt, cur);
+  tile_rest(cur);
+  RawBlk raw[BPW];
+#pragma unroll
+  for (int b = 0; b < BPW; ++b) load_block(cur.e, nt, b, raw[b]);
+  tile_take(cur);
+  issue_act(cur);
+  full_barrier();
+
+  // the previous item's output: value and index, or index < 0
+  float pv = 0.f;
+  int pi = -1;
+
+  // A row of this lane: pair n >> 2, digit n & 3 (row 3 of a pair repeats
+  // digit 2; its results are not used)
+  const int arw = 4 * (n >> 2) + min(n & 3, 2);
+  const int aoff = (4 * (arw & 3) + (n >> 2)) * NB * 256;
+  float *part = reinterpret_cast<float *>(lds + L::DIG);
+  for (;;) {
+    const bool more = item + 1 < item_end;  // uniform
+    const int mt2 = (item + 1) / n_ntiles, nt2 = (item + 1) % n_ntiles;
+    const bool newm = more && mt2 != mt;
+    MTile nx = cur;
+    if (newm) {
+      tile_head(mt2, nx);
+      tile_rest(nx);
+    }
+    if (pi >= 0) out[pi] = pv;
+    // the next item's weights (on the last item: this item's again, so every
+    // path issues the same requests)
+    const int e_next = more ? nx.e : cur.e, nt_next = more ? nt2 : nt;
+
+    float acc = 0.f;  // pair g, weight row n
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      const int kb = kq * BPW + b;
+      // A fragment of K tile j (the digit rows), read one K tile ahead
+      auto afrag = [&](int j) {
+        return *reinterpret_cast<const i32x4 *>(lds + aoff + kb * 256 + (((4 * j + g) ^ arw) << 4));
+      };
+      i32x4 aj = afrag(0);
+      // this block's operands from its raw bytes (the B fragments one K tile
+      // at a time); once its MFMAs are issued, the raw registers take the
+      // same block of the next item in place
+      const Q2KPart rc = take_block(raw[b]);
+      WTab tb;
+      tb.build(rc, g);
+      const i32x4 bmn = min_bfrag(rc, sel_lo, sel_hi);
+      float dsc = f16lo(rc.dd), ndm = -f16hi(rc.dd);
+      asm volatile("" : "+v"(dsc), "+v"(ndm));  // computed here, so d|dmin is free before the reload
+      // per K tile the code and min MFMAs as one fenced group
+      i32x4 c, cm;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const i32x4 an = afrag(j < 3 ? j + 1 : 3);
+        const i32x4 bj = tb.bfrag(rc, j);
+        mfma_group_begin();
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, bj, j ? c : (i32x4){0, 0, 0, 0}, 0, 0, 0);
+        cm = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, bmn, j ? cm : (i32x4){0, 0, 0, 0}, 0, 0, 0);
+        mfma_fence();
+        aj = an;
+      }
+      load_block(e_next, nt_next, b, raw[b]);
+      acc = fmaf(dsc, digits3(c), acc);
+      acc = fmaf(ndm, digits3(cm), acc);
+    }
+
+    // every wave is done with the digit rows; the K parts meet
+    lds_barrier();
+    if (tid < GT) sig_s[tid] = cur.sig;
+    part[(w * GT + g) * 16 + n] = acc;
+    lds_barrier();
+    pi = -1;
+    if (tid < GT * ROWS) {
+      const int m = tid / ROWS, r = tid % ROWS;
+      if (m < cur.valid) {
+        const int rgi = r / 16, rr = r % 16;
+        float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+          v0 += part[(((0 * RG + rgi) * KS + q) * GT + m) * 16 + rr];
+          if constexpr (SWIGLU) v1 += part[(((1 * RG + rgi) * KS + q) * GT + m) * 16 + rr];
+        }
+        const float sg = sig_s[m];
+        if constexpr (SWIGLU) pv = silu(v0 * sg) * (v1 * sg);
+        else pv = v0 * sg;
+        pi = (cur.start + m) * rows_per_expert + nt * ROWS + r;
+      }
+    }
+    if (!more) break;
+    if (newm) {
+      // the digit rows are no longer read: the new m-tile's land, and are
+      // waited for here (with the weights in flight)
+      tile_take(nx);
+      issue_act(nx);
+      full_barrier();
+    }
+    cur = nx;
+    mt = mt2;
+    nt = nt2;
+    ++item;
+  }
+  if (pi >= 0) out[pi] = pv;
+}
 
 template <bool SWIGLU>
-hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, const PrepI8 &a, int k,
-                     int P, const RouteBufs &rb, int max_tiles, float *out, hipStream_t s) {
+hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, const PrepD3 &a, int k,
+                     int P, const RouteBufs &rb, int max_tiles, int n_cu, float *out, hipStream_t s) {
   const int nn = rows / rows_per_item(SWIGLU, nb);
-  const dim3 grid((unsigned)max_tiles * nn);  // exactly: every item's m-tile is in the tile array
-  const uint8_t *ax = reinterpret_cast<const uint8_t *>(a.x);
-#define DS4Q_DG(NBV)                                                                                 \
-  hipLaunchKernelGGL((decode_grouped_kernel<SWIGLU, NBV>), grid, dim3(512), 0, s, W0, W1, rows, a.q, \
-                     ax, a.sig, k, P, rb, nn, out)
+  // persistent workgroups, two per CU (at most one per item)
+  const int64_t items = (int64_t)max_tiles * nn;
+  const dim3 grid((unsigned)(items < 2 * n_cu ? items : 2 * n_cu));
+#define DS4Q_DG(NBV)                                                                                      \
+  hipLaunchKernelGGL((decode_grouped_kernel<SWIGLU, NBV>), grid, dim3(512), 0, s, W0, W1, rows, a.q, a.sig, \
+                     k, P, rb, nn, out)
   switch (nb) {
     case 1: DS4Q_DG(1); break;
     case 2: DS4Q_DG(2); break;
@@ -246,13 +421,46 @@ hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, con
 
 }  // namespace
 
-hipError_t launch_decode_grouped(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+size_t prep_d3_bytes(int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  return up((size_t)rows * (K / 256) * QROW3) + up((size_t)rows * 4);
+}
+
+PrepD3 prep_d3_view(void *base, int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  PrepD3 p;
+  p.q = static_cast<uint8_t *>(base);
+  p.sig = reinterpret_cast<float *>(p.q + up((size_t)rows * (K / 256) * QROW3));
+  return p;
+}
+
+hipError_t launch_prep_d3(const float *src, const float *inv_rms, int64_t rows, int K, const PrepD3 &p,
+                          hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(prep_d3_kernel, dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms, K, p.q, p.sig);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_grouped(const MoeDims &m, const PrepD3 &a, int T, const RouteBufs &rb,
                                  int max_tiles, float *out, int phase, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (T > 64) return hipErrorInvalidValue;
   const int P = T * m.k;
-  if (phase == 1) return launch_nb<true>(m.D / 256, m.gate, m.up, m.F, a, m.k, P, rb, max_tiles, out, s);
-  if (phase == 2) return launch_nb<false>(m.F / 256, m.down, nullptr, m.D, a, m.k, P, rb, max_tiles, out, s);
+  // compute units of the stream's device, looked up once per device
+  static int n_cu_of[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!n_cu_of[dev]) {
+    int v = 0;
+    err = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    n_cu_of[dev] = v > 0 ? v : 256;
+  }
+  const int n_cu = n_cu_of[dev];
+  if (phase == 1) return launch_nb<true>(m.D / 256, m.gate, m.up, m.F, a, m.k, P, rb, max_tiles, n_cu, out, s);
+  if (phase == 2) return launch_nb<false>(m.F / 256, m.down, nullptr, m.D, a, m.k, P, rb, max_tiles, n_cu, out, s);
   return hipErrorInvalidValue;
 }
 

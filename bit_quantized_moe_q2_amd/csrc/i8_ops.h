@@ -1,6 +1,6 @@
-// Int8 matrix-core operands of Q2_K weights and of the two-digit activation
-// rows, shared by the prefill GEMMs (prefill_i8.hip) and the expert-grouped
-// decode (decode_grouped.hip).
+// Int8 matrix-core operands of Q2_K weights (shared by the prefill GEMMs,
+// prefill_i8.hip, and the expert-grouped decode, decode_grouped.hip) and the
+// two-digit activation rows of the prefill GEMMs.
 //
 // Arithmetic (block layout of "【#2】ds4.c 해독하기", Q2_K table): one
 // 256-value block of a weight row dotted with an activation row a is

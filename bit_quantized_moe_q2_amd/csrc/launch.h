@@ -105,11 +105,22 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
                                     int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                   int max_tiles, uint16_t *ob, hipStream_t s);
-// Decode of 2..64 tokens on Q2_K (decode_grouped.hip): m-tiles of at most
-// DECODE_TILE_M sorted pairs; phase 1 writes the fp32 SwiGLU rows [T*k][F]
-// from the prepared token rows, phase 2 the down rows [T*k][D] from the
-// prepared SwiGLU rows, both in sorted-pair order.
-hipError_t launch_decode_grouped(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
+// Decode of 2..64 tokens on Q2_K (decode_grouped.hip): activation rows
+// prepared as three int8 digits per value (MFMA fragment order) and a
+// per-row scale; m-tiles of at most DECODE_TILE_M sorted pairs; phase 1
+// writes the fp32 SwiGLU rows [T*k][F] from the prepared token rows, phase 2
+// the down rows [T*k][D] from the prepared SwiGLU rows, both in sorted-pair
+// order.
+struct PrepD3 {
+  uint8_t *q;  // [rows][K/256][3][256]
+  float *sig;  // [rows]
+};
+size_t prep_d3_bytes(int64_t rows, int K);
+PrepD3 prep_d3_view(void *base, int64_t rows, int K);
+// src: f32 rows [rows][K], times inv_rms[row] when given.
+hipError_t launch_prep_d3(const float *src, const float *inv_rms, int64_t rows, int K, const PrepD3 &p,
+                          hipStream_t s);
+hipError_t launch_decode_grouped(const MoeDims &m, const PrepD3 &a, int T, const RouteBufs &rb,
                                  int max_tiles, float *out, int phase, hipStream_t s);
 
 // Directional steering: out_r (+)= y_r - scale * dir * (dir . y_r), rows of n
@@ -125,7 +136,7 @@ hipError_t launch_act_decode(const void *src, int64_t n, int bits, float *dst, h
 hipError_t scratch_address(void **out);
 
 constexpr int PREFILL_TILE_M = 96;
-constexpr int DECODE_TILE_M = 8;
+constexpr int DECODE_TILE_M = 4;
 
 // imatrix statistics of one layer call (imatrix.hip).  Segments of an
 // expert's pairs: the k slots of one token, the active experts (pairs grouped

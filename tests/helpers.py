@@ -30,19 +30,16 @@ BAR_DECODE = 2e-3
 BAR_PREFILL = 1e-2
 # Each decode path's own bound, a few times above what its arithmetic was
 # measured to reach on the GPU (so that a lost limb or digit fails), far below
-# the bar: three int8 limbs per activation (one token, and 2..64 tokens with
-# Q4_1 or mixed formats) measured up to 4.9e-6; two int8 digits (2..64 tokens
-# on Q2_K weights throughout) up to 4.2e-4; the fp32 vector matvec up to
+# the bar: every decode path takes its activations as three int8 digits per
+# value (one token; 2..64 tokens, grouped on Q2_K weights or per expert with
+# Q4_1 / mixed formats), measured up to 4.9e-6; the fp32 vector matvec up to
 # 2.1e-7.
 PATH_LIMBS3 = 1e-5
-PATH_DIGITS2 = 1e-3
 PATH_MATVEC = 2e-6
 
 
 def decode_path_bound(T, qt, qtd):
     """The measured-error bound of the decode path a call takes."""
-    if T > 1 and qt == 10 and qtd == 10:
-        return PATH_DIGITS2
     return PATH_LIMBS3
 
 

@@ -39,7 +39,8 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &, const PrepI8 &, int, const 
                                     hipStream_t) STUB()
 hipError_t launch_prefill_i8_down(const MoeDims &, const PrepI8 &, int, const RouteBufs &, int, uint16_t *,
                                   hipStream_t) STUB()
-hipError_t launch_decode_grouped(const MoeDims &, const PrepI8 &, int, const RouteBufs &, int, float *, int,
+hipError_t launch_prep_d3(const float *, const float *, int64_t, int, const PrepD3 &, hipStream_t) STUB()
+hipError_t launch_decode_grouped(const MoeDims &, const PrepD3 &, int, const RouteBufs &, int, float *, int,
                                  hipStream_t) STUB()
 hipError_t launch_steer(const float *, float, const float *, int64_t, int, float *, bool, hipStream_t) STUB()
 hipError_t launch_act_encode(const float *, int64_t, int, void *, hipStream_t) STUB()
@@ -63,6 +64,17 @@ PrepI8 prep_i8_view(void *base, int64_t rows, int K) {
   p.q = b;
   p.x = reinterpret_cast<uint16_t *>(b + up((size_t)rows * nb * 512));
   p.sig = reinterpret_cast<float *>(b + up((size_t)rows * nb * 512) + up((size_t)rows * nb * 64));
+  return p;
+}
+size_t prep_d3_bytes(int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  return up((size_t)rows * (K / 256) * 768) + up((size_t)rows * 4);
+}
+PrepD3 prep_d3_view(void *base, int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  PrepD3 p;
+  p.q = static_cast<uint8_t *>(base);
+  p.sig = reinterpret_cast<float *>(p.q + up((size_t)rows * (K / 256) * 768));
   return p;
 }
 }  // namespace ds4q
