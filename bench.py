@@ -574,17 +574,24 @@ def main():
         xv = torch.from_numpy(synth.x_f32(synth.stream_key(seed, 10), 1, D)).to(dev)
         yv = torch.empty(NM, F, device=dev)
         deq = [torch.empty(F * D, device=dev) for _ in range(8)]
+        # the least a kernel costs in such a graph: NM one-element fills
+        tiny = torch.zeros(NM, device=dev)
+        floor_us = graph_time(lambda: [tiny[i:i + 1].fill_(1.0) for i in range(NM)], 20) / NM * 1e3
+        cf["launch_floor_graph"] = {"us": round(floor_us, 3),
+                                    "what": "one-element fill kernel per graph node, same graph shape"}
         for qn, (qt, base, mb) in mats.items():
             ms = graph_time(lambda: [ds4q.ds4q_matvec(qt, base + i * mb, F, D, xv, 1, yv[i]) for i in range(NM)], 20) / NM
             b = mb + D * 4 + F * 4
             cf[f"matvec_{qn}_2048x4096"] = {"us": round(ms * 1e3, 3), "bytes": b,
-                                            "gbps": round(b / (ms / 1e3) / 1e9, 1)}
+                                            "gbps": round(b / (ms / 1e3) / 1e9, 1),
+                                            "launch_floor_us": round(floor_us, 3),
+                                            "us_above_floor": round(ms * 1e3 - floor_us, 3)}
             ms = graph_time(lambda: [ds4q.ds4q_dequant(qt, base + i * mb, F, D, ds4q.TYPE_F32, deq[i % 8])
                                      for i in range(NM)], 10) / NM
             b = mb + F * D * 4
             cf[f"dequant_{qn}_f32_2048x4096"] = {"us": round(ms * 1e3, 3), "bytes": b,
                                                  "gbps": round(b / (ms / 1e3) / 1e9, 1)}
-        del deq, yv
+        del deq, yv, tiny
 
         # one layer decode of 64 tokens, cycling over the 43 layers
         T64 = 64
