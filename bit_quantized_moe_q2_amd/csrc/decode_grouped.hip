@@ -24,9 +24,7 @@
 // min nibble of each value's sub-block (min_bfrag), whose MFMAs sum to
 // sum_s mn_s A_s; both sums are exact in int32 and meet d and dmin in fp32.
 //
-// LDS: digit rows [digit][pair][block][16 chunks] with data chunk c of row
-// r = 4*pair + digit stored at chunk c ^ r (the lanes reading one chunk
-// column of the A rows hit different bank groups), then the K parts.
+// LDS: the digit rows (GLayout), then the K parts.
 #include "common.h"
 #include "i8_ops.h"
 #include "launch.h"
@@ -96,18 +94,37 @@ __global__ __launch_bounds__(256) void prep_d3_kernel(const float *__restrict__ 
   }
 }
 
+// Eight waves of at most four blocks each, two workgroups per CU.  (Four
+// waves of up to eight blocks, three workgroups per CU, hold half as many
+// weight bytes in flight again and measured the same for the down rows and
+// slower for gate/up: the weight stream of this access pattern runs at the
+// same rate either way.)
+constexpr int NWV = 8;   // waves per workgroup
+constexpr int BPWM = 4;  // blocks of K per wave at most
+constexpr int WG_PER_CU = 2;
+
+// LDS digit rows: 12 rows (4 * digit + pair) of NB * 256 bytes.  With four
+// or more blocks a row is followed by 16 bytes of padding (row stride
+// NB*256 + 16), so the lanes reading one 16-byte chunk column of the 12 rows
+// hit 12 different bank groups and a lane's reads are one base address plus
+// immediate offsets; with fewer blocks the rows are packed and the chunks of
+// row r are XOR-swizzled by r instead.
 template <int NB>
 struct GLayout {
-  static constexpr int BPW = NB < 4 ? NB : 4;   // blocks per wave
+  static constexpr int BPW = NB < BPWM ? NB : BPWM;  // blocks per wave
   static constexpr int KS = NB / BPW;           // K parts
-  static constexpr int DIG = GT * NB * QROW3;   // digit rows
-  static constexpr int NDMA = DIG / 1024;       // 1-KiB direct loads of the digit rows
-  static constexpr int PART = 8 * 64 * 4;       // K parts of the eight waves (a float per lane)
+  static constexpr bool PAD = NB >= 4;
+  static constexpr int RSTRIDE = NB * 256 + (PAD ? 16 : 0);
+  static constexpr int DIG = 12 * RSTRIDE;      // digit rows
+  static constexpr int NDMA = 12 * NB / 4;      // 1-KiB direct loads of the digit rows
+  static constexpr int PART = NWV * 64 * 4;     // K parts of the waves (a float per lane)
   static constexpr int BYTES = DIG + PART;
 };
 
 // Weight rows of one work item: 16 per wave over the waves that share a K part.
-constexpr int rows_per_item(bool swiglu, int nb) { return 16 * 8 / ((swiglu ? 2 : 1) * (nb < 4 ? 1 : nb / 4)); }
+constexpr int rows_per_item(bool swiglu, int nb) {
+  return 16 * NWV / ((swiglu ? 2 : 1) * (nb < BPWM ? 1 : nb / BPWM));
+}
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(4))) i32x2 *const_i32x2_ptr;
@@ -189,7 +206,7 @@ __device__ __forceinline__ float digits3(i32x4 c) {
 // out = down rows [pos][n_embd].  Waves: w = (mat * RG + rg) * KS + kq; a
 // wave owns 16 weight rows over BPW blocks of K.
 //
-// Persistent, two workgroups per CU: workgroup i takes the contiguous run of
+// Persistent, WG_PER_CU workgroups per CU: workgroup i takes the contiguous run of
 // work items [i n / G, (i + 1) n / G) (item = m-tile * n_ntiles + n-tile, n
 // counted on the device), so consecutive items mostly share their m-tile and
 // its digit rows stay in LDS.  The next item's weights stream in while the
@@ -200,15 +217,15 @@ __device__ __forceinline__ float digits3(i32x4 c) {
 // ones are no longer read, and waited for then.  An item's outputs are
 // stored once the next item has started, so no wait covers their completion.
 template <bool SWIGLU, int NB>
-__global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
+__global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int rows_per_expert,
     const uint8_t *__restrict__ aq, const float *__restrict__ asig, int kslots, int n_pairs,
     RouteBufs rb, int n_ntiles, float *__restrict__ out) {
   using L = GLayout<NB>;
-  constexpr int BPW = L::BPW, KS = L::KS, NMAT = SWIGLU ? 2 : 1, RG = 8 / (NMAT * KS);
+  constexpr int BPW = L::BPW, KS = L::KS, NMAT = SWIGLU ? 2 : 1, RG = NWV / (NMAT * KS);
   constexpr int ROWS = RG * 16;  // weight rows per work item
-  static_assert(NMAT * KS * RG == 8 && ROWS == rows_per_item(SWIGLU, NB), "eight waves");
-  static_assert(GT * ROWS <= 512, "one output per thread and item");
+  static_assert(NMAT * KS * RG == NWV && ROWS == rows_per_item(SWIGLU, NB), "waves");
+  static_assert(GT * ROWS <= 64 * NWV, "one output per thread and item");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
   __shared__ float sig_s[GT];
 
@@ -258,33 +275,32 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
     r.load(wm + ((int64_t)e * rows_per_expert + row) * rbytes + (int64_t)(kq * BPW + b) * BB_Q2K, g);
   };
   // Digit rows of an m-tile to LDS as NDMA direct loads of 1 KiB (64 lanes
-  // x 16 bytes), load u by wave u % 8.  LDS layout [digit][pair][block][16
-  // chunks]; with four or more blocks a load holds one (digit, pair) row, and
-  // loads of absent pairs are skipped.  The row scales go to registers until
-  // the K parts meet.
+  // x 16 bytes), load u by wave u % NWV.  With four or more blocks a load
+  // holds four blocks of one (digit, pair) row, and loads of absent pairs
+  // are skipped.  The row scales go to registers until the K parts meet.
   auto issue_act = [&](MTile &c) {
     const int src_row = arow(c, lane & 3);  // source row of pair lane & 3
 #pragma unroll
-    for (int u0 = 0; u0 < L::NDMA; u0 += 8) {
+    for (int u0 = 0; u0 < L::NDMA; u0 += NWV) {
       int u = u0 + w;
       asm volatile("" : "+s"(u));  // the slot arithmetic below stays here (not hoisted out of the loop)
       if (u < L::NDMA) {
-        const int sl = 64 * u + lane;    // 16-byte slot
-        const int rix = sl / (NB * 16);  // 4 * digit + pair
-        const int pair = rix & 3, d = rix >> 2;
-        const int blk = (sl >> 4) & (NB - 1), pos = sl & 15;
-        int srow;
-        bool live = true;
-        if constexpr (NB >= 4) {
-          const int upair = ((64 * u) / (NB * 16)) & 3;  // the load's pair (uniform)
-          live = upair < c.valid;
-          srow = __builtin_amdgcn_readlane(src_row, upair);
+        if constexpr (L::PAD) {
+          const int rix = u / (NB / 4), pair = rix & 3, d = rix >> 2;  // uniform
+          const int blk = 4 * (u % (NB / 4)) + (lane >> 4);
+          if (pair < c.valid)
+            dma16(aq + (int64_t)__builtin_amdgcn_readlane(src_row, pair) * (NB * QROW3) +
+                      (blk * QROW3 + d * 256 + (lane & 15) * 16),
+                  lds + rix * L::RSTRIDE + (u % (NB / 4)) * 1024);
         } else {
-          srow = __shfl(src_row, pair, 64);
-        }
-        if (live)
-          dma16(aq + (int64_t)srow * (NB * QROW3) + (blk * QROW3 + d * 256 + ((pos ^ (4 * pair + d)) << 4)),
+          const int sl = 64 * u + lane;    // 16-byte slot
+          const int rix = sl / (NB * 16);  // 4 * digit + pair
+          const int pair = rix & 3, d = rix >> 2;
+          const int blk = (sl >> 4) & (NB - 1), pos = sl & 15;
+          dma16(aq + (int64_t)__shfl(src_row, pair, 64) * (NB * QROW3) +
+                    (blk * QROW3 + d * 256 + ((pos ^ (4 * pair + d)) << 4)),
                 lds + 1024 * u);
+        }
       }
     }
     c.sig = tid < GT ? asig[arow(c, tid)] : 0.f;
@@ -308,7 +324,8 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
   // A row of this lane: pair n >> 2, digit n & 3 (row 3 of a pair repeats
   // digit 2; its results are not used)
   const int arw = 4 * (n >> 2) + min(n & 3, 2);
-  const int aoff = (4 * (arw & 3) + (n >> 2)) * NB * 256;
+  const int rixa = 4 * (arw & 3) + (n >> 2);  // LDS row: 4 * digit + pair
+  const int aoff = L::PAD ? rixa * L::RSTRIDE + 16 * g : rixa * L::RSTRIDE;
   float *part = reinterpret_cast<float *>(lds + L::DIG);
   for (;;) {
     const bool more = item + 1 < item_end;  // uniform
@@ -330,7 +347,8 @@ __global__ __launch_bounds__(512, 4) void decode_grouped_kernel(
       const int kb = kq * BPW + b;
       // A fragment of K tile j (the digit rows), read one K tile ahead
       auto afrag = [&](int j) {
-        return *reinterpret_cast<const i32x4 *>(lds + aoff + kb * 256 + (((4 * j + g) ^ arw) << 4));
+        if constexpr (L::PAD) return *reinterpret_cast<const i32x4 *>(lds + aoff + kb * 256 + 64 * j);
+        else return *reinterpret_cast<const i32x4 *>(lds + aoff + kb * 256 + (((4 * j + g) ^ arw) << 4));
       };
       i32x4 aj = afrag(0);
       // this block's operands from its raw bytes (the B fragments one K tile
@@ -401,11 +419,11 @@ template <bool SWIGLU>
 hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, const PrepD3 &a, int k,
                      int P, const RouteBufs &rb, int max_tiles, int n_cu, float *out, hipStream_t s) {
   const int nn = rows / rows_per_item(SWIGLU, nb);
-  // persistent workgroups, two per CU (at most one per item)
+  // persistent workgroups, WG_PER_CU per CU (at most one per item)
   const int64_t items = (int64_t)max_tiles * nn;
-  const dim3 grid((unsigned)(items < 2 * n_cu ? items : 2 * n_cu));
+  const dim3 grid((unsigned)(items < WG_PER_CU * n_cu ? items : WG_PER_CU * n_cu));
 #define DS4Q_DG(NBV)                                                                                      \
-  hipLaunchKernelGGL((decode_grouped_kernel<SWIGLU, NBV>), grid, dim3(512), 0, s, W0, W1, rows, a.q, a.sig, \
+  hipLaunchKernelGGL((decode_grouped_kernel<SWIGLU, NBV>), grid, dim3(64 * NWV), 0, s, W0, W1, rows, a.q, a.sig, \
                      k, P, rb, nn, out)
   switch (nb) {
     case 1: DS4Q_DG(1); break;
