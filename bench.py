@@ -47,6 +47,8 @@ PAIR_FLOPS = 2 * 2 * D * F + 2 * F * D
 DTYPE_T1 = "i8x3limb+f32"          # one token: three int8 limbs per activation
 DTYPE_I8X3 = "i8x3digit+i8min"     # 2..64-token Q2_K decode: three int8 digits per
                                    # activation, min term exact on int8 matrix cores
+DTYPE_I8X3_Q41 = "i8x3digit+f32offset"  # 2..64-token Q4_1 decode: the same digits, the
+                                        # offset term from fp32 sums of 32 inputs
 DTYPE_I8X2 = "i8x2digit+bf16min"   # Q2_K prefill: two int8 digits per activation,
                                    # min term on bf16 hi+lo
 DTYPE_BF16 = "bf16"                # Q4_1 prefill: bf16 weights and inputs, fp32 accumulation
@@ -609,6 +611,17 @@ def main():
                                    "us_per_layer": round(ms * 1e3, 2), "tokens_per_s": round(T64 / (ms / 1e3), 1),
                                    "experts_touched": round(float(touched), 1), "weight_bytes": int(b),
                                    "gbps": round(b / (ms / 1e3) / 1e9, 1)}
+        if q41:
+            # the same on the Q4_1 layers (the mixed stack's last six)
+            nq = len(q41)
+            ms = graph_time(lambda: [ds4q.ds4q_moe_decode(q41[l], x64[l], lg64[l], T64, y64[l], None, ws64[l])
+                                     for l in range(nq)], 5) / nq
+            touched = np.mean([len(np.unique(np.argsort(-lg64n[l], axis=1, kind="stable")[:, :K])) for l in range(nq)])
+            b = touched * 3 * 2048 * 4096 // 32 * 20
+            cf["decode_64tok_q4_1"] = {"dtype": DTYPE_I8X3_Q41,
+                                       "us_per_layer": round(ms * 1e3, 2), "tokens_per_s": round(T64 / (ms / 1e3), 1),
+                                       "experts_touched": round(float(touched), 1), "weight_bytes": int(b),
+                                       "gbps": round(b / (ms / 1e3) / 1e9, 1)}
         del x64, lg64, y64, ws64
 
         # 4096-token prefill chunks: Zipf(1.1) routing, and Q4_1 weights

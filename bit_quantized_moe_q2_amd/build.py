@@ -11,7 +11,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libds4q.so")
 SOURCES = ["abi.cpp", "dequant.hip", "route.hip", "decode.hip", "decode_mfma.hip", "prefill.hip",
            "prefill_i8.hip", "steer_codec.hip", "imatrix.hip",
-           "decode_q41.hip", "decode_tn.hip", "decode_grouped.hip", "scratch.hip"]
+           "decode_q41.hip", "decode_grouped.hip", "scratch.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of every kernel (the compiler would
 # otherwise form v_pk_* fp32 ops from ordinary float code).

@@ -56,11 +56,11 @@ struct Workspace {
   float *imat_part = nullptr;  // imatrix on m-tiles: [max_tiles][max(D, F)] f32 partial rows
   uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
   PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
-  PrepD3 xd{}, hd{};       // decode of 2..64 tokens on Q2_K: int8 digit rows of x and of h
+  PrepD3 xd{}, hd{};       // decode of 2..64 tokens: int8 digit rows of x and of h
   size_t bytes = 0;
 
   // mode 1 (prefill): i8_in / i8_h = Q2_K gate/up resp. down (int8 matrix
-  // cores); mode 0 (decode): i8_in = the grouped int8 path (see i8_flags)
+  // cores); unused in the other modes
   Workspace(uint8_t *base, int D, int F, int E, int k, int T, int mode, bool i8_in = false,
             bool i8_h = false, bool stats = false) {
     size_t off = 0;
@@ -85,9 +85,10 @@ struct Workspace {
       // routing only
     } else if (mode == 0) {
       h = (float *)take(P * F * 4);
-      if (T > 1) o = (float *)take(P * D * 4);
-      else stage = (float *)take((size_t)D * 4);
-      if (i8_in) {  // decode of 2..64 tokens on Q2_K: the grouped int8 kernels
+      if (T == 1) {
+        stage = (float *)take((size_t)D * 4);
+      } else {  // decode of 2..64 tokens: the grouped int8 kernels
+        o = (float *)take(P * D * 4);
         rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k, DECODE_TILE_M) * 8);
         void *p = take(prep_d3_bytes(T, D));
         if (base) xd = prep_d3_view(p, T, D);
@@ -150,18 +151,15 @@ SteerArgs steer_of(const ds4q_moe_layer *L, float *stage) {
 
 bool i8_gateup(const ds4q_moe_layer *L) { return L->type_gate == DS4Q_TYPE_Q2_K; }
 bool i8_down(const ds4q_moe_layer *L) { return L->type_down == DS4Q_TYPE_Q2_K; }
-// Decode of 2..64 tokens with Q2_K weights throughout runs on the grouped
-// int8 kernels (one token has its own kernels).
-bool i8_decode(const ds4q_moe_layer *L, int T) { return T > 1 && i8_gateup(L) && i8_down(L); }
 
 // Workspace flags of a call (see Workspace).
 struct WsFlags {
   bool a, b, stats;
 };
 bool wants_stats(const ds4q_moe_layer *L) { return L->imatrix_in || L->imatrix_down; }
-WsFlags i8_flags(const ds4q_moe_layer *L, int T, int mode) {
+WsFlags i8_flags(const ds4q_moe_layer *L, int mode) {
   if (mode == 1) return {i8_gateup(L), i8_down(L), wants_stats(L)};
-  return {i8_decode(L, T), false, wants_stats(L)};
+  return {false, false, wants_stats(L)};
 }
 
 MoeDims dims_of(const ds4q_moe_layer *L) {
@@ -274,7 +272,7 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, ALIGN) ||
       route_misaligned(route))
     return DS4Q_E_ALIGN;
-  const WsFlags f = i8_flags(L, T, mode);
+  const WsFlags f = i8_flags(L, mode);
   const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b,
                        f.stats);
   if (static_ws) {
@@ -342,7 +340,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
                const ds4q_route_out *route, void *ws, hipStream_t s, uint32_t flags,
                uint32_t phases = DS4Q_PHASE_ALL) {
   const MoeDims m = dims_of(L);
-  const WsFlags f = i8_flags(L, T, 0);
+  const WsFlags f = i8_flags(L, 0);
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0, f.a, f.b, f.stats);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const SteerArgs st = steer_of(L, w.stage);
@@ -371,44 +369,24 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     if (p_down) TIMED_TRY("decode_down", t1(2));
     return p_gu ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
   }
-  if (f.a) {
-    // 2..64 tokens on Q2_K: expert-grouped m-tiles of at most DECODE_TILE_M
-    // pairs on int8 matrix cores; h and o in sorted-pair order
-    const int mt = max_tiles(T, m.E, m.k, DECODE_TILE_M);
-    if (p_route) {
-      TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, s));
-      TIMED_TRY("group", launch_group(T, m.E, m.k, DECODE_TILE_M, w.rb, s));
-    }
-    if (p_gu) {
-      TIMED_TRY("prep_d3", launch_prep_d3(x, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xd, s));
-      TIMED_TRY("decode_gateup", launch_decode_grouped(m, w.xd, T, w.rb, mt, w.h, 1, s));
-      const int na = T * m.k < m.E ? T * m.k : m.E;
-      if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_ACTIVE, na, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
-                                        rows_of(w.h, false, nullptr, true), s));
-    }
-    if (p_down) {
-      TIMED_TRY("prep_d3", launch_prep_d3(w.h, nullptr, (int64_t)T * m.k, m.F, w.hd, s));
-      TIMED_TRY("decode_down", launch_decode_grouped(m, w.hd, T, w.rb, mt, w.o, 2, s));
-      TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, st, s));
-    }
-    return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
-  }
+  // 2..64 tokens: expert-grouped m-tiles of at most DECODE_TILE_M pairs on
+  // int8 matrix cores, either format per tensor; h and o in sorted-pair order
+  const int mt = max_tiles(T, m.E, m.k, DECODE_TILE_M);
   if (p_route) {
     TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, s));
-    TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+    TIMED_TRY("group", launch_group(T, m.E, m.k, DECODE_TILE_M, w.rb, s));
   }
-  // 2..64 tokens with Q4_1 or mixed types: grouped by expert on int8 matrix
-  // cores, h and o per pair index
   if (p_gu) {
-    TIMED_TRY("decode_gateup", launch_decode_tn(m, x, norm ? w.rb.inv_rms : nullptr, T, w.rb, w.h, w.o, 1, s));
+    TIMED_TRY("prep_d3", launch_prep_d3(x, norm ? w.rb.inv_rms : nullptr, T, m.D, m.tg, w.xd, s));
+    TIMED_TRY("decode_gateup", launch_decode_grouped(m, w.xd, T, w.rb, mt, w.h, 1, s));
     const int na = T * m.k < m.E ? T * m.k : m.E;
-    if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_ACTIVE, na,
-                                      rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
-                                      rows_of(w.h, false, nullptr, false), s));
+    if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_ACTIVE, na, rows_of(x, false, norm ? w.rb.inv_rms : nullptr, false),
+                                      rows_of(w.h, false, nullptr, true), s));
   }
   if (p_down) {
-    TIMED_TRY("decode_down", launch_decode_tn(m, x, nullptr, T, w.rb, w.h, w.o, 2, s));
-    TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, false, y, acc, st, s));
+    TIMED_TRY("prep_d3", launch_prep_d3(w.h, nullptr, (int64_t)T * m.k, m.F, m.td, w.hd, s));
+    TIMED_TRY("decode_down", launch_decode_grouped(m, w.hd, T, w.rb, mt, w.o, 2, s));
+    TIMED_TRY("combine", launch_combine(w.o, w.rb, T, m.k, m.D, true, y, acc, st, s));
   }
   return p_route ? copy_route(route, w.rb, T, m.E, m.k, s) : DS4Q_OK;
 }
@@ -417,7 +395,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
                 int32_t T, float *y, const ds4q_route_out *route, void *ws, hipStream_t s,
                 uint32_t flags) {
   const MoeDims m = dims_of(L);
-  const WsFlags f = i8_flags(L, T, 1);
+  const WsFlags f = i8_flags(L, 1);
   Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, f.a, f.b, f.stats);
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
@@ -538,7 +516,7 @@ DS4Q_API int ds4q_route(const float *logits, int32_t n_tok, int32_t n_expert, in
 DS4Q_API size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t mode) {
   if (check_layer(L) || max_tok < 0 || (mode != 0 && mode != 1)) return 0;
   const int T = max_tok > 0 ? max_tok : 1;
-  const WsFlags f = i8_flags(L, T, mode);
+  const WsFlags f = i8_flags(L, mode);
   return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b,
                    f.stats).bytes;
 }

@@ -1,4 +1,4 @@
-// Decode of 2..64 tokens on Q2_K weights: expert-grouped, streaming.
+// Decode of 2..64 tokens on Q2_K or Q4_1 weights: expert-grouped, streaming.
 //
 // At decode sizes an expert holds a few of the call's token-expert pairs,
 // so the work is the weight stream of the routed experts ("【#2】ds4.c
@@ -23,8 +23,13 @@
 // (v_perm of the byte table [0, sc, 2sc, 3sc] with the 2-bit codes), and the
 // min nibble of each value's sub-block (min_bfrag), whose MFMAs sum to
 // sum_s mn_s A_s; both sums are exact in int32 and meet d and dmin in fp32.
+// A Q4_1 block (ThakiCloud "...GGUF Q4_1 재부호화", Q4_1 block section: 32
+// values, y = d*q + m) gives d * sum q a + m * sum a: the integer sums on
+// the same MFMA (see the kernel), the sums of a prepared with the digits.
 //
 // LDS: the digit rows (GLayout), then the K parts.
+#include <type_traits>
+
 #include "common.h"
 #include "i8_ops.h"
 #include "launch.h"
@@ -37,12 +42,18 @@ static_assert(GT == 4, "the A operand holds 4 pairs x 4 rows");
 constexpr int QROW3 = 768;  // digit bytes of one row's 256-column block (3 digits)
 
 // One workgroup per activation row, one thread per 16-value sub-block: the
-// row (times inv_rms[row] when given) as three digit rows per block in the
-// B order of the weights (byte i of dword k of chunk 4j+g is value
-// 128(g>>1) + 32k + 16(g&1) + 4j + i), and sigma.
+// row (times inv_rms[row] when given) as three digit rows per 256-value block
+// in the B order of the weights, and sigma.  Q2_K order: byte i of dword k of
+// chunk 4j+g is value 128(g>>1) + 32k + 16(g&1) + 4j + i.  Q4_1 order (K tile
+// j holds the 32-value blocks 2j and 2j+1, lane group g half g&1 of block
+// 2j + (g>>1): the low nibbles of its 8 code bytes, then the high ones):
+// value 64j + 32(g>>1) + 16(k>>1) + 8(g&1) + 4(k&1) + i; with it, the sum of
+// each 32 values over sigma.
+template <bool Q41>
 __global__ __launch_bounds__(256) void prep_d3_kernel(const float *__restrict__ src,
                                                       const float *__restrict__ inv_rms, int K,
-                                                      uint8_t *__restrict__ aq, float *__restrict__ asig) {
+                                                      uint8_t *__restrict__ aq, float *__restrict__ asig,
+                                                      float *__restrict__ axs) {
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int nsub = K >> 4, nb = K >> 8;
@@ -73,7 +84,14 @@ __global__ __launch_bounds__(256) void prep_d3_kernel(const float *__restrict__ 
   if (t == 0) asig[row] = mx * (1.0f / 127.0f);
   if (!act) return;
   const int b = t >> 4, s = t & 15;
-  const int g = 2 * (s >> 3) + (s & 1), k = (s >> 1) & 3;
+  if constexpr (Q41) {
+    // threads t and t ^ 1 hold the two halves of 32-value block t / 2
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm += v[i];
+    sm += __shfl_xor(sm, 1, 64);
+    if ((t & 1) == 0) axs[row * (K >> 5) + (t >> 1)] = sm * inv;
+  }
   uint32_t *qb = reinterpret_cast<uint32_t *>(aq + (row * nb + b) * QROW3);
   const float scale = inv * 65536.0f;
 #pragma unroll
@@ -87,7 +105,10 @@ __global__ __launch_bounds__(256) void prep_d3_kernel(const float *__restrict__ 
     const uint32_t p23 = __builtin_amdgcn_perm(n[3], n[2], 0x05010400u);
     const uint32_t q01 = __builtin_amdgcn_perm(n[1], n[0], 0x0C0C0602u);  // byte 2
     const uint32_t q23 = __builtin_amdgcn_perm(n[3], n[2], 0x0C0C0602u);
-    const int off = (4 * j + g) * 4 + k;
+    // values 16s + 4j .. +3 of the block
+    int off;
+    if constexpr (Q41) off = (4 * (s >> 2) + 2 * ((s >> 1) & 1) + (j >> 1)) * 4 + 2 * (s & 1) + (j & 1);
+    else off = (4 * j + 2 * (s >> 3) + (s & 1)) * 4 + ((s >> 1) & 3);
     qb[off] = __builtin_amdgcn_perm(q23, q01, 0x05040100u) ^ 0x80808080u;        // a0
     qb[64 + off] = __builtin_amdgcn_perm(p23, p01, 0x07060302u) ^ 0x80808080u;   // a1
     qb[128 + off] = __builtin_amdgcn_perm(p23, p01, 0x05040100u) ^ 0x80808080u;  // a2
@@ -109,7 +130,7 @@ constexpr int WG_PER_CU = 2;
 // hit 12 different bank groups and a lane's reads are one base address plus
 // immediate offsets; with fewer blocks the rows are packed and the chunks of
 // row r are XOR-swizzled by r instead.
-template <int NB>
+template <int NB, bool Q41>
 struct GLayout {
   static constexpr int BPW = NB < BPWM ? NB : BPWM;  // blocks per wave
   static constexpr int KS = NB / BPW;           // K parts
@@ -118,7 +139,12 @@ struct GLayout {
   static constexpr int DIG = 12 * RSTRIDE;      // digit rows
   static constexpr int NDMA = 12 * NB / 4;      // 1-KiB direct loads of the digit rows
   static constexpr int PART = NWV * 64 * 4;     // K parts of the waves (a float per lane)
-  static constexpr int BYTES = DIG + PART;
+  // Q4_1: the 4 pairs' sums of 32 values (NB * 8 floats each), brought in by
+  // NXD direct loads of 1 KiB
+  static constexpr int NXD = Q41 ? (NB * 128 + 1023) / 1024 : 0;
+  static constexpr int XB = 1024 * NXD;
+  static constexpr int BYTES = DIG + PART + XB;
+  static constexpr int CHUNK = Q41 ? 8 * BB_Q41 : BB_Q2K;  // weight bytes per 256 values of a row
 };
 
 // Weight rows of one work item: 16 per wave over the waves that share a K part.
@@ -153,6 +179,22 @@ __device__ __forceinline__ void full_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
+
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x3g __attribute__((ext_vector_type(3), aligned(4)));
+
+// Raw bytes of one Q4_1 chunk (256 values = 8 blocks of one row) for lane
+// group g: per K tile j, 12 bytes of block 2j + (g>>1) at offset 8(g&1) (the
+// even group: d|m and code bytes 0..7; the odd one: code bytes 4..15, of
+// which 8..15 are its own).
+struct RawQ41 {
+  u32x3 v[4];
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ chunk, int g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = *reinterpret_cast<const u32x3g *>(chunk + (2 * j + (g >> 1)) * BB_Q41 + 8 * (g & 1));
+  }
+};
 
 // Raw bytes of one block for lane group g, as Q2KPart::load requests them
 // (the 16 code bytes of quarter g; 8 bytes that are scale/min bytes or end
@@ -200,6 +242,14 @@ __device__ __forceinline__ float digits3(i32x4 c) {
   return fmaf((float)c.z, 1.0f / 65536.0f, (float)((c.x << 8) + c.y) * (1.0f / 256.0f));
 }
 
+// Q4_1 (Q41): per K tile the lane's 8 code bytes give the B operand (low
+// nibbles, then high nibbles, in the prepared activation order), once masked
+// to lane groups 0-1 (block 2j) and once to groups 2-3 (block 2j+1), so the
+// two MFMAs sum each 32-value block on its own; lane (g, n) then holds both
+// blocks' sums for pair g and weight row n and takes both blocks' (d, m) by
+// two lane exchanges: sum w a = d * sum q a + m * sum a, the last from the
+// prepared sums of 32 values.
+//
 // SWIGLU: W0 = gate, W1 = up, rows = n_ff, the A rows are the pairs' token
 // rows (gathered through the sorted pair list); out = SwiGLU rows [pos][n_ff].
 // Otherwise W0 = down, rows = n_embd, the A rows are the sorted positions;
@@ -216,12 +266,12 @@ __device__ __forceinline__ float digits3(i32x4 c) {
 // When the m-tile changes, the new digit rows are requested once the old
 // ones are no longer read, and waited for then.  An item's outputs are
 // stored once the next item has started, so no wait covers their completion.
-template <bool SWIGLU, int NB>
+template <bool SWIGLU, int NB, bool Q41>
 __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int rows_per_expert,
-    const uint8_t *__restrict__ aq, const float *__restrict__ asig, int kslots, int n_pairs,
-    RouteBufs rb, int n_ntiles, float *__restrict__ out) {
-  using L = GLayout<NB>;
+    const uint8_t *__restrict__ aq, const float *__restrict__ asig, const float *__restrict__ axs, int kslots,
+    int n_pairs, RouteBufs rb, int n_ntiles, float *__restrict__ out) {
+  using L = GLayout<NB, Q41>;
   constexpr int BPW = L::BPW, KS = L::KS, NMAT = SWIGLU ? 2 : 1, RG = NWV / (NMAT * KS);
   constexpr int ROWS = RG * 16;  // weight rows per work item
   static_assert(NMAT * KS * RG == NWV && ROWS == rows_per_item(SWIGLU, NB), "waves");
@@ -238,10 +288,11 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int kq = w % KS, rg = (w / KS) % RG, mat = w / (KS * RG);
-  const int64_t rbytes = (int64_t)NB * BB_Q2K;
+  const int64_t rbytes = (int64_t)NB * L::CHUNK;
   const uint8_t *wm = mat ? W1 : W0;
   const uint32_t sel_lo = (g & 1) ? 0x01010101u : 0x00000000u;
   const uint32_t sel_hi = (g & 1) ? 0x03030303u : 0x02020202u;
+  const uint32_t mask_e = g < 2 ? 0x0F0F0F0Fu : 0u, mask_o = mask_e ^ 0x0F0F0F0Fu;  // Q4_1 code masks
 
   // m-tile context: expert, first sorted position, pairs present (>= 1), the
   // lane's pair-list entry (SWIGLU; entries past the tile's end are never
@@ -270,9 +321,10 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
     else return c.start + mm;
   };
   // raw bytes of block b of the wave's K part: row nt*ROWS + rg*16 + n
-  auto load_block = [&](int e, int nt, int b, RawBlk &r) {
+  using Raw = typename std::conditional<Q41, RawQ41, RawBlk>::type;
+  auto load_block = [&](int e, int nt, int b, Raw &r) {
     const int row = nt * ROWS + rg * 16 + n;
-    r.load(wm + ((int64_t)e * rows_per_expert + row) * rbytes + (int64_t)(kq * BPW + b) * BB_Q2K, g);
+    r.load(wm + ((int64_t)e * rows_per_expert + row) * rbytes + (int64_t)(kq * BPW + b) * L::CHUNK, g);
   };
   // Digit rows of an m-tile to LDS as NDMA direct loads of 1 KiB (64 lanes
   // x 16 bytes), load u by wave u % NWV.  With four or more blocks a load
@@ -303,6 +355,17 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
         }
       }
     }
+    if constexpr (Q41) {
+      // the sums of 32 values: byte o of the area is pair o / (NB*32)'s
+      // byte o % (NB*32); lanes past the area re-read pair 0 (never used)
+      for (int u = w; u < L::NXD; u += NWV) {
+        const int o = 1024 * u + 16 * lane;
+        const bool in = o < NB * 128;
+        const int pair = in ? o / (NB * 32) : 0, off = in ? o % (NB * 32) : 0;
+        dma16(reinterpret_cast<const uint8_t *>(axs) + (int64_t)arow(c, pair) * (NB * 32) + off,
+              lds + L::DIG + L::PART + 1024 * u);
+      }
+    }
     c.sig = tid < GT ? asig[arow(c, tid)] : 0.f;
   };
 
@@ -310,7 +373,7 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
   MTile cur;
   tile_head(mt, cur);
   tile_rest(cur);
-  RawBlk raw[BPW];
+  Raw raw[BPW];
 #pragma unroll
   for (int b = 0; b < BPW; ++b) load_block(cur.e, nt, b, raw[b]);
   tile_take(cur);
@@ -327,6 +390,7 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
   const int rixa = 4 * (arw & 3) + (n >> 2);  // LDS row: 4 * digit + pair
   const int aoff = L::PAD ? rixa * L::RSTRIDE + 16 * g : rixa * L::RSTRIDE;
   float *part = reinterpret_cast<float *>(lds + L::DIG);
+  const float *xsl = reinterpret_cast<const float *>(lds + L::DIG + L::PART) + g * (NB * 8);  // pair g's sums
   for (;;) {
     const bool more = item + 1 < item_end;  // uniform
     const int mt2 = (item + 1) / n_ntiles, nt2 = (item + 1) % n_ntiles;
@@ -351,30 +415,69 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
         else return *reinterpret_cast<const i32x4 *>(lds + aoff + kb * 256 + (((4 * j + g) ^ arw) << 4));
       };
       i32x4 aj = afrag(0);
-      // this block's operands from its raw bytes (the B fragments one K tile
-      // at a time); once its MFMAs are issued, the raw registers take the
-      // same block of the next item in place
-      const Q2KPart rc = take_block(raw[b]);
-      WTab tb;
-      tb.build(rc, g);
-      const i32x4 bmn = min_bfrag(rc, sel_lo, sel_hi);
-      float dsc = f16lo(rc.dd), ndm = -f16hi(rc.dd);
-      asm volatile("" : "+v"(dsc), "+v"(ndm));  // computed here, so d|dmin is free before the reload
-      // per K tile the code and min MFMAs as one fenced group
-      i32x4 c, cm;
+      if constexpr (!Q41) {
+        // this block's operands from its raw bytes (the B fragments one K tile
+        // at a time); once its MFMAs are issued, the raw registers take the
+        // same block of the next item in place
+        const Q2KPart rc = take_block(raw[b]);
+        WTab tb;
+        tb.build(rc, g);
+        const i32x4 bmn = min_bfrag(rc, sel_lo, sel_hi);
+        float dsc = f16lo(rc.dd), ndm = -f16hi(rc.dd);
+        asm volatile("" : "+v"(dsc), "+v"(ndm));  // computed here, so d|dmin is free before the reload
+        // per K tile the code and min MFMAs as one fenced group
+        i32x4 c, cm;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const i32x4 an = afrag(j < 3 ? j + 1 : 3);
-        const i32x4 bj = tb.bfrag(rc, j);
-        mfma_group_begin();
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, bj, j ? c : (i32x4){0, 0, 0, 0}, 0, 0, 0);
-        cm = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, bmn, j ? cm : (i32x4){0, 0, 0, 0}, 0, 0, 0);
-        mfma_fence();
-        aj = an;
+        for (int j = 0; j < 4; ++j) {
+          const i32x4 an = afrag(j < 3 ? j + 1 : 3);
+          const i32x4 bj = tb.bfrag(rc, j);
+          mfma_group_begin();
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, bj, j ? c : (i32x4){0, 0, 0, 0}, 0, 0, 0);
+          cm = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, bmn, j ? cm : (i32x4){0, 0, 0, 0}, 0, 0, 0);
+          mfma_fence();
+          aj = an;
+        }
+        load_block(e_next, nt_next, b, raw[b]);
+        acc = fmaf(dsc, digits3(c), acc);
+        acc = fmaf(ndm, digits3(cm), acc);
+      } else {
+        // per K tile: the two blocks' MFMAs as one fenced group; the sums of
+        // K tile j are scaled while the MFMAs of tile j + 1 run
+        i32x4 ce[2], co[2];
+        uint32_t dme[2], dmo[2];
+        float2 xv[2];
+        auto scale = [&](int q) {
+          acc = fmaf(f16lo(dme[q]), digits3(ce[q]), acc);
+          acc = fmaf(f16lo(dmo[q]), digits3(co[q]), acc);
+          acc = fmaf(f16hi(dme[q]), xv[q].x, acc);
+          acc = fmaf(f16hi(dmo[q]), xv[q].y, acc);
+          asm volatile("" : "+v"(acc));  // here, not sunk below later MFMAs (their results would pile up)
+        };
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = j & 1;
+          const i32x4 an = afrag(j < 3 ? j + 1 : 3);
+          const u32x3 rv = raw[b].v[j];
+          const uint32_t h1 = rv.y >> 4, h2 = rv.z >> 4;
+          const i32x4 be = {(int)(rv.y & mask_e), (int)(rv.z & mask_e), (int)(h1 & mask_e), (int)(h2 & mask_e)};
+          const i32x4 bo = {(int)(rv.y & mask_o), (int)(rv.z & mask_o), (int)(h1 & mask_o), (int)(h2 & mask_o)};
+          mfma_group_begin();
+          ce[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, be, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+          co[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aj, bo, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+          mfma_fence();
+          // d|m of block 2j + (g>>1) from the even lane group, then of blocks
+          // 2j (lower half of the wave) and 2j + 1 (upper half) to every lane
+          const uint32_t own = __builtin_amdgcn_permlane16_swap(rv.x, rv.x, false, false)[0];
+          const auto pr = __builtin_amdgcn_permlane32_swap(own, own, false, false);
+          dme[q] = pr[0];
+          dmo[q] = pr[1];
+          xv[q] = *reinterpret_cast<const float2 *>(xsl + kb * 8 + 2 * j);
+          if (j) scale(q ^ 1);
+          aj = an;
+        }
+        load_block(e_next, nt_next, b, raw[b]);
+        scale(1);
       }
-      load_block(e_next, nt_next, b, raw[b]);
-      acc = fmaf(dsc, digits3(c), acc);
-      acc = fmaf(ndm, digits3(cm), acc);
     }
 
     // every wave is done with the digit rows; the K parts meet
@@ -415,7 +518,7 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
   if (pi >= 0) out[pi] = pv;
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool Q41>
 hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, const PrepD3 &a, int k,
                      int P, const RouteBufs &rb, int max_tiles, int n_cu, float *out, hipStream_t s) {
   const int nn = rows / rows_per_item(SWIGLU, nb);
@@ -423,8 +526,8 @@ hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, con
   const int64_t items = (int64_t)max_tiles * nn;
   const dim3 grid((unsigned)(items < WG_PER_CU * n_cu ? items : WG_PER_CU * n_cu));
 #define DS4Q_DG(NBV)                                                                                      \
-  hipLaunchKernelGGL((decode_grouped_kernel<SWIGLU, NBV>), grid, dim3(64 * NWV), 0, s, W0, W1, rows, a.q, a.sig, \
-                     k, P, rb, nn, out)
+  hipLaunchKernelGGL((decode_grouped_kernel<SWIGLU, NBV, Q41>), grid, dim3(64 * NWV), 0, s, W0, W1, rows, a.q, \
+                     a.sig, a.xs, k, P, rb, nn, out)
   switch (nb) {
     case 1: DS4Q_DG(1); break;
     case 2: DS4Q_DG(2); break;
@@ -441,7 +544,7 @@ hipError_t launch_nb(int nb, const uint8_t *W0, const uint8_t *W1, int rows, con
 
 size_t prep_d3_bytes(int64_t rows, int K) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  return up((size_t)rows * (K / 256) * QROW3) + up((size_t)rows * 4);
+  return up((size_t)rows * (K / 256) * QROW3) + up((size_t)rows * 4) + up((size_t)rows * (K / 32) * 4);
 }
 
 PrepD3 prep_d3_view(void *base, int64_t rows, int K) {
@@ -449,13 +552,19 @@ PrepD3 prep_d3_view(void *base, int64_t rows, int K) {
   PrepD3 p;
   p.q = static_cast<uint8_t *>(base);
   p.sig = reinterpret_cast<float *>(p.q + up((size_t)rows * (K / 256) * QROW3));
+  p.xs = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(p.sig) + up((size_t)rows * 4));
   return p;
 }
 
-hipError_t launch_prep_d3(const float *src, const float *inv_rms, int64_t rows, int K, const PrepD3 &p,
-                          hipStream_t s) {
+hipError_t launch_prep_d3(const float *src, const float *inv_rms, int64_t rows, int K, int type,
+                          const PrepD3 &p, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(prep_d3_kernel, dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms, K, p.q, p.sig);
+  if (type == TYPE_Q4_1)
+    hipLaunchKernelGGL(prep_d3_kernel<true>, dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms, K, p.q, p.sig,
+                       p.xs);
+  else
+    hipLaunchKernelGGL(prep_d3_kernel<false>, dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms, K, p.q, p.sig,
+                       p.xs);
   return hipGetLastError();
 }
 
@@ -477,8 +586,14 @@ hipError_t launch_decode_grouped(const MoeDims &m, const PrepD3 &a, int T, const
     n_cu_of[dev] = v > 0 ? v : 256;
   }
   const int n_cu = n_cu_of[dev];
-  if (phase == 1) return launch_nb<true>(m.D / 256, m.gate, m.up, m.F, a, m.k, P, rb, max_tiles, n_cu, out, s);
-  if (phase == 2) return launch_nb<false>(m.F / 256, m.down, nullptr, m.D, a, m.k, P, rb, max_tiles, n_cu, out, s);
+  if (phase == 1)
+    return m.tg == TYPE_Q4_1
+               ? launch_nb<true, true>(m.D / 256, m.gate, m.up, m.F, a, m.k, P, rb, max_tiles, n_cu, out, s)
+               : launch_nb<true, false>(m.D / 256, m.gate, m.up, m.F, a, m.k, P, rb, max_tiles, n_cu, out, s);
+  if (phase == 2)
+    return m.td == TYPE_Q4_1
+               ? launch_nb<false, true>(m.F / 256, m.down, nullptr, m.D, a, m.k, P, rb, max_tiles, n_cu, out, s)
+               : launch_nb<false, false>(m.F / 256, m.down, nullptr, m.D, a, m.k, P, rb, max_tiles, n_cu, out, s);
   return hipErrorInvalidValue;
 }
 

@@ -56,13 +56,6 @@ struct MoeDims {
 hipError_t launch_decode_q2k_t1(const MoeDims &m, const float *x, const float *logits,
                                 bool rmsnorm, float eps, const RouteBufs &rb, float *h, float *y,
                                 bool accumulate, int phase, const SteerArgs &st, hipStream_t s);
-// Decode of 2..64 tokens grouped by expert on int8 matrix cores, either
-// format (decode_tn.hip): phase 1 = gate/up + SwiGLU into h [T*k][F] (pair
-// index), phase 2 = down into o [T*k][D] (pair index, unweighted); then
-// launch_combine(by_pos = false).  Needs the routing and the grouping
-// without m-tiles (act_expert / act_begin / pairs).
-hipError_t launch_decode_tn(const MoeDims &m, const float *x, const float *inv_rms, int T,
-                            const RouteBufs &rb, float *h, float *o, int phase, hipStream_t s);
 // The same two phases on Q4_1 tensors (decode_q41.hip).  The gate/up and down
 // kernels of the two formats share the workspace contract, so a layer may mix
 // them (phase 1 by the gate/up type, phase 2 by the down type).
@@ -105,21 +98,23 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
                                     int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                   int max_tiles, uint16_t *ob, hipStream_t s);
-// Decode of 2..64 tokens on Q2_K (decode_grouped.hip): activation rows
-// prepared as three int8 digits per value (MFMA fragment order) and a
-// per-row scale; m-tiles of at most DECODE_TILE_M sorted pairs; phase 1
-// writes the fp32 SwiGLU rows [T*k][F] from the prepared token rows, phase 2
-// the down rows [T*k][D] from the prepared SwiGLU rows, both in sorted-pair
-// order.
+// Decode of 2..64 tokens (decode_grouped.hip): activation rows prepared as
+// three int8 digits per value, in the MFMA fragment order of the weight
+// format they meet, and a per-row scale (plus, for Q4_1, the sums of every
+// 32 values); m-tiles of at most DECODE_TILE_M sorted pairs; phase 1 writes
+// the fp32 SwiGLU rows [T*k][F] from the prepared token rows, phase 2 the
+// down rows [T*k][D] from the prepared SwiGLU rows, both in sorted-pair order.
 struct PrepD3 {
   uint8_t *q;  // [rows][K/256][3][256]
   float *sig;  // [rows]
+  float *xs;   // [rows][K/32]: sums of 32 values over sig (Q4_1 order only)
 };
 size_t prep_d3_bytes(int64_t rows, int K);
 PrepD3 prep_d3_view(void *base, int64_t rows, int K);
-// src: f32 rows [rows][K], times inv_rms[row] when given.
-hipError_t launch_prep_d3(const float *src, const float *inv_rms, int64_t rows, int K, const PrepD3 &p,
-                          hipStream_t s);
+// src: f32 rows [rows][K], times inv_rms[row] when given; type: the weight
+// format (DS4Q_TYPE_Q2_K or DS4Q_TYPE_Q4_1) whose fragment order to write.
+hipError_t launch_prep_d3(const float *src, const float *inv_rms, int64_t rows, int K, int type,
+                          const PrepD3 &p, hipStream_t s);
 hipError_t launch_decode_grouped(const MoeDims &m, const PrepD3 &a, int T, const RouteBufs &rb,
                                  int max_tiles, float *out, int phase, hipStream_t s);
 

@@ -1,5 +1,5 @@
-// Shared parts of the decode kernels on int8 matrix cores (one token: Q2_K in
-// decode_mfma.hip, Q4_1 in decode_q41.hip; 2..64 tokens: decode_tn.hip):
+// Shared parts of the one-token decode kernels on int8 matrix cores (Q2_K in
+// decode_mfma.hip, Q4_1 in decode_q41.hip):
 // operand types, the quantisation of an activation vector into three int8
 // limbs per value in a wave's LDS area (in the fragment order of either block
 // format), the routing of one token by a wave, and the weight operands and

@@ -173,12 +173,11 @@ size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t
  * the input and SwiGLU vectors enter as three int8 digits per value times a
  * scale per 256 values (residual below 2^-23 of the chunk maximum) against
  * the exact integers sc*q (Q2_K) or q (Q4_1), with the min / offset term in
- * fp32.  2..64 tokens on Q2_K weights throughout run on int8 matrix cores
- * grouped by expert in tiles of at most 4 token-expert pairs, with three int8
+ * fp32.  2..64 tokens run on int8 matrix cores grouped by expert in tiles of
+ * at most 4 token-expert pairs (either format per tensor), with three int8
  * digits per value and a scale per row (residual below 2^-24 of the row
- * maximum) and the min term exact in int32; with Q4_1 or mixed types, on
- * per-expert int8 kernels with the three-digit activations of the one-token
- * path.  The SwiGLU rows stay fp32.
+ * maximum); the Q2_K min term is exact in int32, the Q4_1 offset term takes
+ * fp32 sums of 32 input values.  The SwiGLU rows stay fp32.
  * x: device f32 [n_tok][n_embd]; logits: device f32 [n_tok][n_expert];
  * y: device f32 [n_tok][n_embd] — may be the same pointer as x (in-place
  * residual with DS4Q_F_ACCUMULATE), must not partially overlap it.

@@ -21,8 +21,6 @@ hipError_t launch_topk(const float *, int, int, int, const float *, int, float, 
 hipError_t launch_group(int, int, int, int, const RouteBufs &, hipStream_t) STUB()
 hipError_t launch_decode_q2k_t1(const MoeDims &, const float *, const float *, bool, float, const RouteBufs &,
                                 float *, float *, bool, int, const SteerArgs &, hipStream_t) STUB()
-hipError_t launch_decode_tn(const MoeDims &, const float *, const float *, int, const RouteBufs &, float *, float *,
-                            int, hipStream_t) STUB()
 hipError_t launch_decode_q41_t1(const MoeDims &, const float *, const float *, bool, float, const RouteBufs &,
                                 float *, float *, bool, int, const SteerArgs &, hipStream_t) STUB()
 hipError_t launch_combine(const float *, const RouteBufs &, int, int, int, bool, float *, bool, const SteerArgs &,
@@ -39,7 +37,7 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &, const PrepI8 &, int, const 
                                     hipStream_t) STUB()
 hipError_t launch_prefill_i8_down(const MoeDims &, const PrepI8 &, int, const RouteBufs &, int, uint16_t *,
                                   hipStream_t) STUB()
-hipError_t launch_prep_d3(const float *, const float *, int64_t, int, const PrepD3 &, hipStream_t) STUB()
+hipError_t launch_prep_d3(const float *, const float *, int64_t, int, int, const PrepD3 &, hipStream_t) STUB()
 hipError_t launch_decode_grouped(const MoeDims &, const PrepD3 &, int, const RouteBufs &, int, float *, int,
                                  hipStream_t) STUB()
 hipError_t launch_steer(const float *, float, const float *, int64_t, int, float *, bool, hipStream_t) STUB()
@@ -68,13 +66,14 @@ PrepI8 prep_i8_view(void *base, int64_t rows, int K) {
 }
 size_t prep_d3_bytes(int64_t rows, int K) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  return up((size_t)rows * (K / 256) * 768) + up((size_t)rows * 4);
+  return up((size_t)rows * (K / 256) * 768) + up((size_t)rows * 4) + up((size_t)rows * (K / 32) * 4);
 }
 PrepD3 prep_d3_view(void *base, int64_t rows, int K) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   PrepD3 p;
   p.q = static_cast<uint8_t *>(base);
   p.sig = reinterpret_cast<float *>(p.q + up((size_t)rows * (K / 256) * 768));
+  p.xs = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(p.sig) + up((size_t)rows * 4));
   return p;
 }
 }  // namespace ds4q

@@ -208,16 +208,19 @@ def test_decode_small(gpu, qt, qtd, T):
     _check(report(normwise_err(y, lay.oracle_moe(x, lg))), T, qt, qtd)
 
 
+@pytest.mark.parametrize("qt", [10, 3])
 @pytest.mark.parametrize("T", [1, 3])
 @pytest.mark.parametrize("D,F", [(256, 4096), (4096, 256), (1024, 512), (2048, 1024), (512, 2048)])
-def test_decode_shapes(gpu, D, F, T):
+def test_decode_shapes(gpu, D, F, T, qt):
+    """Every count of 256-value blocks per row (1..16) on both sides of the
+    layer, for both formats (the grouped kernels have one instance each)."""
     ds4q = gpu
-    _log(f"decode shapes D={D} F={F} T={T}")
-    lay = SynthLayer(ds4q, DEV, D, F, 8, 2, 10, seed=200 + D)
+    _log(f"decode shapes D={D} F={F} T={T} qt={qt}")
+    lay = SynthLayer(ds4q, DEV, D, F, 8, 2, qt, seed=200 + D)
     x = synth.x_f32(synth.stream_key(14, D), T, D)
     lg = synth.logits_normal(synth.stream_key(15, D), T, 8)
     y, _ = _decode(ds4q, lay, x, lg)
-    _check(report(normwise_err(y, lay.oracle_moe(x, lg))), T)
+    _check(report(normwise_err(y, lay.oracle_moe(x, lg))), T, qt)
 
 
 @pytest.mark.parametrize("T", [1, 4])
@@ -266,26 +269,28 @@ def test_decode_full_layer_64_tokens(gpu, qt):
     _check(report(normwise_err(y, ref)), 64, qt)
 
 
+@pytest.mark.parametrize("qt,qtd", [(10, 10), (3, 3), (3, 10)])
 @pytest.mark.parametrize("T", [9, 64])
-def test_decode_experts_over_several_tiles(gpu, T):
+def test_decode_experts_over_several_tiles(gpu, T, qt, qtd):
     """Every expert routed every token (E = k = 8): experts hold T pairs, i.e.
-    several m-tiles of the grouped decode (8 pairs each, the last one partial)."""
+    several m-tiles of the grouped decode (4 pairs each, the last one partial)."""
     ds4q = gpu
-    _log(f"decode several tiles per expert T={T}")
-    lay = SynthLayer(ds4q, DEV, 512, 256, 8, 8, 10, seed=700 + T)
+    _log(f"decode several tiles per expert T={T} qt={qt} qtd={qtd}")
+    lay = SynthLayer(ds4q, DEV, 512, 256, 8, 8, qt, seed=700 + T, qtype_down=qtd)
     x = synth.x_f32(synth.stream_key(40, T), T, 512)
     lg = synth.logits_normal(synth.stream_key(41, T), T, 8)
     y, ids = _decode(ds4q, lay, x, lg)
     assert np.array_equal(ids, oracle.route(lg, 8)[0])
-    _check(report(normwise_err(y, lay.oracle_moe(x, lg))), T)
+    _check(report(normwise_err(y, lay.oracle_moe(x, lg))), T, qt, qtd)
 
 
-def test_decode_64_tokens_zipf(gpu):
+@pytest.mark.parametrize("qt", [10, 3])
+def test_decode_64_tokens_zipf(gpu, qt):
     """64 tokens with Zipf(1.1)-skewed routing, full shape: the popular experts
     hold tens of pairs (several tiles each); every token row vs the oracle."""
     ds4q = gpu
-    _log("decode full T=64 zipf")
-    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, 10, seed=710)
+    _log(f"decode full T=64 zipf qt={qt}")
+    lay = SynthLayer(ds4q, DEV, 4096, 2048, 256, 6, qt, seed=710)
     x = synth.x_f32(synth.stream_key(42), 64, 4096)
     lg = synth.logits_zipf(synth.stream_key(43), 64, 256)
     y, ids = _decode(ds4q, lay, x, lg)
@@ -293,7 +298,7 @@ def test_decode_64_tokens_zipf(gpu):
     counts = np.bincount(ids.ravel(), minlength=256)
     assert counts.max() > 8  # the case this test is for
     ref = lay.oracle_moe(x, lg, n_threads=16)
-    _check(report(normwise_err(y, ref)), 64)
+    _check(report(normwise_err(y, ref)), 64, qt)
 
 
 @pytest.mark.parametrize("qt,T", [(10, 1), (10, 3), (3, 1)])
