@@ -593,6 +593,11 @@ def main():
             b = mb + F * D * 4
             cf[f"dequant_{qn}_f32_2048x4096"] = {"us": round(ms * 1e3, 3), "bytes": b,
                                                  "gbps": round(b / (ms / 1e3) / 1e9, 1)}
+        # the write side alone: a fill of the same f32 output per graph node
+        ms = graph_time(lambda: [deq[i % 8].fill_(1.0) for i in range(NM)], 10) / NM
+        b = F * D * 4
+        cf["fill_f32_2048x4096"] = {"us": round(ms * 1e3, 3), "bytes": b, "gbps": round(b / (ms / 1e3) / 1e9, 1),
+                                    "what": "torch fill of one dequant output, same graph shape"}
         del deq, yv, tiny
 
         # one layer decode of 64 tokens, cycling over the 43 layers
