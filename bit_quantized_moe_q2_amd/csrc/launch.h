@@ -130,7 +130,7 @@ hipError_t launch_act_decode(const void *src, int64_t n, int bits, float *dst, h
 // DS4Q_SCRATCH_BYTES long; looked up once per device.
 hipError_t scratch_address(void **out);
 
-constexpr int PREFILL_TILE_M = 96;
+constexpr int PREFILL_TILE_M = 128;
 constexpr int DECODE_TILE_M = 4;
 
 // imatrix statistics of one layer call (imatrix.hip).  Segments of an

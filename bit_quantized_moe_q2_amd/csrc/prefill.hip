@@ -15,7 +15,7 @@
 //
 // Data movement (eight waves; wave w owns 16 gate + 16 up rows, or 32 down
 // rows, and all the tile's rows of A).  K advances in steps of 256 values
-// (eight Q4_1 blocks).  The next step's A tile (96 rows x 512 B of bf16) goes
+// (eight Q4_1 blocks).  The next step's A tile (128 rows x 512 B of bf16) goes
 // to the other of two LDS buffers by global_load_lds_dwordx4 (one 1-KiB
 // instruction = 2 rows x 32 chunks; chunk c of row r is stored at chunk
 // position c ^ (r & 15), so the 16 lanes reading one chunk column touch 16
@@ -47,7 +47,8 @@ constexpr int MT = TM / 16;               // 16-row MFMA subtiles along M
 constexpr int KS = 256;                   // K per step (eight Q4_1 blocks)
 constexpr int NJ = KS / 64;               // Q4_1 block pairs per step (two MFMAs each)
 constexpr int AROWB = KS * 2;             // bytes of one A row per step
-constexpr int ASTAGE = TM * AROWB;        // one LDS buffer (48 KiB)
+constexpr int ASTAGE = TM * AROWB;        // one LDS buffer (64 KiB)
+static_assert(MT >= 4 && MT <= 8, "m-tiles of 64..128 rows (the step-loop instances below)");
 constexpr int STEP_BYTES = KS / 32 * BB_Q41;  // bytes of one weight row per step
 
 
@@ -153,11 +154,15 @@ __device__ __forceinline__ void q41_loop(const StepCtx &cx, int ns, uint8_t *As0
 #pragma unroll
         for (int i = 0; i < NMT; ++i)
           a[i] = *reinterpret_cast<const bf16x8 *>(As + i * (16 * AROWB) + cx.aoffj[2 * j + h]);
+        // one fenced MFMA group (no later instruction within 8 wait states of
+        // any of them)
+        mfma_group_begin();
 #pragma unroll
         for (int i = 0; i < NMT; ++i) {
           acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[0][h], acc[i][0], 0, 0, 0);
           acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[1][h], acc[i][1], 0, 0, 0);
         }
+        mfma_fence();
       }
     }
   };
@@ -258,8 +263,10 @@ __global__ __launch_bounds__(512) void prefill_q41_kernel(
     case 2: q41_loop<2>(cx, ns, As0, As1, acc); break;
     case 3: q41_loop<3>(cx, ns, As0, As1, acc); break;
     case 4: q41_loop<4>(cx, ns, As0, As1, acc); break;
-    case 5: q41_loop<5>(cx, ns, As0, As1, acc); break;
-    default: q41_loop<6>(cx, ns, As0, As1, acc); break;
+    case 5: if constexpr (MT >= 5) q41_loop<5>(cx, ns, As0, As1, acc); break;
+    case 6: if constexpr (MT >= 6) q41_loop<6>(cx, ns, As0, As1, acc); break;
+    case 7: if constexpr (MT >= 7) q41_loop<7>(cx, ns, As0, As1, acc); break;
+    default: if constexpr (MT >= 8) q41_loop<8>(cx, ns, As0, As1, acc); break;
   }
 
   // epilogue: rows of live pairs only

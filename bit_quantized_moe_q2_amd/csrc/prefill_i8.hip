@@ -353,14 +353,18 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[ip][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  static_assert(NPMAX >= 1 && NPMAX <= NPAIR, "1..6 groups of 16 tokens");
+  static_assert(NPMAX >= 1 && NPMAX <= NPAIR && NPAIR <= 8, "1..8 groups of 16 tokens");
+  // np <= NPMAX: the number of live groups picks the instance (each case
+  // exists when NPMAX allows it)
   switch (np) {
     case 1: block_loop<1, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
     case 2: if constexpr (NPMAX >= 2) block_loop<2, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
     case 3: if constexpr (NPMAX >= 3) block_loop<3, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
     case 4: if constexpr (NPMAX >= 4) block_loop<4, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
     case 5: if constexpr (NPMAX >= 5) block_loop<5, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
-    default: if constexpr (NPMAX >= 6) block_loop<6, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 6: if constexpr (NPMAX >= 6) block_loop<6, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    case 7: if constexpr (NPMAX >= 7) block_loop<7, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
+    default: if constexpr (NPMAX >= 8) block_loop<8, NPMAX>(cx, As0, As1, Xs0, Xs1, acc); break;
   }
 
   // epilogue: lane (g, n) holds, for group ip, rows q = 0..3 = tokens

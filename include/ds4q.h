@@ -108,7 +108,7 @@ enum {
  * expert's pairs in sorted order, then added to the arrays (deterministic, no
  * atomics; accumulate over calls, the caller zeroes them).  16-byte aligned,
  * overlapping nothing else.  When either is set the workspace of the prefill
- * grows by (min(P, n_expert) + P/96 + 1) * max(n_embd, n_ff) * 4 bytes,
+ * grows by (min(P, n_expert) + P/128 + 1) * max(n_embd, n_ff) * 4 bytes,
  * P = n_tok * n_expert_used (ds4q_moe_workspace_size reads the descriptor). */
 typedef struct {
   int32_t n_embd, n_ff, n_expert, n_expert_used;

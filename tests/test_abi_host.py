@@ -204,7 +204,7 @@ def test_layer_imatrix_validation(lib):
     assert pre(_layer(imatrix_in=sa, imatrix_down=sb), T=0) == OK
     plain = lib.ds4q_moe_workspace_size(ctypes.byref(_layer()), 4096, 1)
     stats = lib.ds4q_moe_workspace_size(ctypes.byref(_layer(imatrix_in=sa)), 4096, 1)
-    assert stats - plain >= (256 + 4096 * 6 // 96 + 1) * 4096 * 4
+    assert stats - plain >= (256 + 4096 * 6 // 128 + 1) * 4096 * 4
     assert (lib.ds4q_moe_workspace_size(ctypes.byref(_layer(imatrix_in=sa)), 1, 0)
             == lib.ds4q_moe_workspace_size(ctypes.byref(_layer()), 1, 0))
 

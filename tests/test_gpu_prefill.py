@@ -120,7 +120,7 @@ def test_prefill_f32_input_rmsnorm_accumulate(gpu):
 
 
 # tokens per m-tile of the grouped GEMMs (sorted pairs of one expert)
-PREFILL_TILE_M = 96
+PREFILL_TILE_M = 128
 
 
 @pytest.mark.parametrize("qt", [10, 3])

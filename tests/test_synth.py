@@ -87,7 +87,7 @@ def test_tile_cover_tokens_covers_every_group_and_position():
     chosen token (checked here by brute force on a small routing)."""
     import oracle
     from helpers import tile_cover_tokens
-    T, E, k, tm = 300, 8, 6, 96
+    T, E, k, tm = 300, 8, 6, 128
     lg = synth.logits_zipf(synth.stream_key(77), T, E)
     ids, _ = oracle.route(lg, k)
     chosen = set(tile_cover_tokens(ids, E, tm).tolist())
