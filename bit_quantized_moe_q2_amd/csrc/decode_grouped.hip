@@ -154,8 +154,6 @@ constexpr int rows_per_item(bool swiglu, int nb) {
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(4))) i32x2 *const_i32x2_ptr;
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
 
 // Barrier for LDS only: the workgroup's LDS accesses so far are complete;
 // global loads in flight stay in flight (a full __syncthreads would wait for
@@ -195,31 +193,6 @@ struct RawQ41 {
       v[j] = *reinterpret_cast<const u32x3g *>(chunk + (2 * j + (g >> 1)) * BB_Q41 + 8 * (g & 1));
   }
 };
-
-// Raw bytes of one block for lane group g, as Q2KPart::load requests them
-// (the 16 code bytes of quarter g; 8 bytes that are scale/min bytes or end
-// with d|dmin), kept as two vectors so that a loop can reload them in place.
-struct RawBlk {
-  u32x4 q;
-  u32x2 p;
-  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
-    q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
-    p = *reinterpret_cast<const u32x2a *>(blk + ((g & 1) ? 76 : 8 * (g >> 1)));
-  }
-};
-
-// The operand bytes of a raw block, as Q2KPart::finish makes them, with one
-// exchange per result: the raw registers are only read (an exchange rewrites
-// both of its operands), so they can take the next block in place.
-__device__ __forceinline__ Q2KPart take_block(const RawBlk &r) {
-  Q2KPart o;
-  o.q = r.q;
-  o.p0 = o.p1 = 0;
-  o.s0 = __builtin_amdgcn_permlane16_swap(r.p.x, r.p.x, false, false)[0];  // the even group's bytes
-  o.s1 = __builtin_amdgcn_permlane16_swap(r.p.y, r.p.y, false, false)[0];  // its bytes 4..7
-  o.dd = __builtin_amdgcn_permlane16_swap(r.p.y, r.p.y, true, false)[1];   // the odd group's d|dmin
-  return o;
-}
 
 // Integer B fragment of the min term: dword k is the min nibble of the
 // lane's sub-block for bit pair k (the sub-block of that dword in every
@@ -573,19 +546,9 @@ hipError_t launch_decode_grouped(const MoeDims &m, const PrepD3 &a, int T, const
   if (T == 0) return hipSuccess;
   if (T > 64) return hipErrorInvalidValue;
   const int P = T * m.k;
-  // compute units of the stream's device, looked up once per device
-  static int n_cu_of[64] = {};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  int n_cu = 256;
+  const hipError_t err = cu_count(&n_cu);
   if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!n_cu_of[dev]) {
-    int v = 0;
-    err = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    n_cu_of[dev] = v > 0 ? v : 256;
-  }
-  const int n_cu = n_cu_of[dev];
   if (phase == 1)
     return m.tg == TYPE_Q4_1
                ? launch_nb<true, true>(m.D / 256, m.gate, m.up, m.F, a, m.k, P, rb, max_tiles, n_cu, out, s)

@@ -65,6 +65,34 @@ struct Q2KPart {
   }
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+
+// Raw bytes of one block for lane group g, as Q2KPart::load requests them
+// (the 16 code bytes of quarter g; 8 bytes that are scale/min bytes or end
+// with d|dmin), kept as two vectors so that a loop can reload them in place.
+struct RawBlk {
+  u32x4 q;
+  u32x2 p;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
+    q = *reinterpret_cast<const u32x4a *>(blk + 16 + 16 * g);
+    p = *reinterpret_cast<const u32x2a *>(blk + ((g & 1) ? 76 : 8 * (g >> 1)));
+  }
+};
+
+// The operand bytes of a raw block, as Q2KPart::finish makes them, with one
+// exchange per result: the raw registers are only read (an exchange rewrites
+// both of its operands), so they can take the next block in place.
+__device__ __forceinline__ Q2KPart take_block(const RawBlk &r) {
+  Q2KPart o;
+  o.q = r.q;
+  o.p0 = o.p1 = 0;
+  o.s0 = __builtin_amdgcn_permlane16_swap(r.p.x, r.p.x, false, false)[0];  // the even group's bytes
+  o.s1 = __builtin_amdgcn_permlane16_swap(r.p.y, r.p.y, false, false)[0];  // its bytes 4..7
+  o.dd = __builtin_amdgcn_permlane16_swap(r.p.y, r.p.y, true, false)[1];   // the odd group's d|dmin
+  return o;
+}
+
 // Weight operands of one block for one 16-row n-subtile.  Code byte c of
 // dword j of quarter g holds, in bit pair k, value
 // 128(g>>1) + 32k + 16(g&1) + 4j + c, of sub-block 8(g>>1) + 2k + (g&1);

@@ -131,6 +131,22 @@ hipError_t launch_act_decode(const void *src, int64_t n, int bits, float *dst, h
 hipError_t scratch_address(void **out);
 
 constexpr int PREFILL_TILE_M = 128;
+// Compute units of the current device, looked up once per device.
+inline hipError_t cu_count(int *out) {
+  static int cache[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!cache[dev]) {
+    int v = 0;
+    err = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    cache[dev] = v > 0 ? v : 256;
+  }
+  *out = cache[dev];
+  return hipSuccess;
+}
 constexpr int DECODE_TILE_M = 4;
 
 // imatrix statistics of one layer call (imatrix.hip).  Segments of an
