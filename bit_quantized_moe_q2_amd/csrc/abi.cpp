@@ -97,6 +97,7 @@ struct Workspace {
       }
     } else {
       rb.tiles = (int32_t *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * 8);
+      rb.tiles_sz = (int32_t *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * 8);
       hb = (uint16_t *)take(P * F * 2);
       ob = (uint16_t *)take(P * D * 2);
       if (!i8_in) xb = (uint16_t *)take((size_t)T * D * 2);
@@ -360,7 +361,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
     if (p_gu) {
       TIMED_TRY("decode_gateup", t1(1));
       // the grouping pass (expert order) runs only when asked for
-      if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, w.rb, s));
+      if (wants_grouping(route)) TIMED_TRY("group", launch_group(T, m.E, m.k, 0, false, w.rb, s));
       ImatRows in = rows_of(x, false, nullptr, false);
       in.norm_self = norm;  // the gate/up launch keeps the inverse RMS to itself
       in.eps = L->norm_eps;
@@ -374,7 +375,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
   const int mt = max_tiles(T, m.E, m.k, DECODE_TILE_M);
   if (p_route) {
     TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? x : nullptr, m.D, L->norm_eps, w.rb, s));
-    TIMED_TRY("group", launch_group(T, m.E, m.k, DECODE_TILE_M, w.rb, s));
+    TIMED_TRY("group", launch_group(T, m.E, m.k, DECODE_TILE_M, false, w.rb, s));
   }
   if (p_gu) {
     TIMED_TRY("prep_d3", launch_prep_d3(x, norm ? w.rb.inv_rms : nullptr, T, m.D, m.tg, w.xd, s));
@@ -400,7 +401,7 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
   TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, s));
-  TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, w.rb, s));
+  TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, true, w.rb, s));
   const int mt = max_tiles(T, m.E, m.k, PREFILL_TILE_M);
   if (i8_gateup(L)) {
     TIMED_TRY("prep_i8", launch_prep_i8(x, xf != nullptr, true, norm && xf ? w.rb.inv_rms : nullptr, T,
@@ -509,7 +510,7 @@ DS4Q_API int ds4q_route(const float *logits, int32_t n_tok, int32_t n_expert, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace w(static_cast<uint8_t *>(workspace), 0, 0, n_expert, k, n_tok, 2);
   HIP_TRY(launch_topk(logits, n_tok, n_expert, k, nullptr, 0, 0.f, w.rb, s));
-  if (wants_grouping(out)) HIP_TRY(launch_group(n_tok, n_expert, k, 0, w.rb, s));
+  if (wants_grouping(out)) HIP_TRY(launch_group(n_tok, n_expert, k, 0, false, w.rb, s));
   return copy_route(out, w.rb, n_tok, n_expert, k, s);
 }
 

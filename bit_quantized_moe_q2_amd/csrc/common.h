@@ -87,20 +87,24 @@ __device__ __forceinline__ void mfma_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Grouped-GEMM work item -> (m-tile, n-tile).  The live items
-// (n_live_m * n_ntiles; the m-tile count is known on the device only) are
-// cut into 8 contiguous ranges, one per XCD (workgroup i runs on XCD i % 8),
-// so every XCD gets work and the n-tiles of one m-tile share that XCD's L2.
-// Returns false for a workgroup without work.
+// Grouped-GEMM work item -> (m-tile, n-tile).  The live m-tiles, largest
+// first (the grouping's size-ordered list; their count is known on the
+// device only), are dealt to the 8 XCDs in turn: m-tile t to XCD t % 8, and
+// workgroup i runs on XCD i % 8 as slot i / 8, which is n-tile
+// slot % n_ntiles of that XCD's (slot / n_ntiles)-th m-tile.  So every XCD
+// gets about the same work, the n-tiles of an m-tile share one XCD's L2, and
+// each XCD runs its largest items first.  The grid is 8 * ceil(max m-tiles /
+// 8) * n_ntiles (xcd_grid); returns false for a workgroup without work.
 __device__ __forceinline__ bool xcd_tile_of(int n_live_m, int n_ntiles, int *mtile, int *ntile) {
-  const int live = n_live_m * n_ntiles;
-  const int per = (live + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
-  const int logical = (blockIdx.x & 7) * per + slot;
-  if (slot >= per || logical >= live) return false;
-  *mtile = logical / n_ntiles;
-  *ntile = logical % n_ntiles;
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int t = x + 8 * (slot / n_ntiles);
+  if (t >= n_live_m) return false;
+  *mtile = t;
+  *ntile = slot % n_ntiles;
   return true;
+}
+inline unsigned xcd_grid(int max_tiles, int n_ntiles) {
+  return (unsigned)(8 * ((max_tiles + 7) / 8) * n_ntiles);
 }
 
 // ---------------------------------------------------------------- routing

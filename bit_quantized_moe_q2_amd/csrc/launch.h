@@ -27,13 +27,16 @@ struct RouteBufs {
   int32_t *n_active;   // [1]
   int32_t *tiles;      // [max_tiles][2] (expert, first sorted position) m-tiles
   int32_t *n_tiles;    // [1]
+  int32_t *tiles_sz;   // [max_tiles][2] prefill: the same m-tiles, full ones first, then by
+                       // falling count of 16-pair groups (each class in expert order)
 };
 
 // Top-k + softmax per token; with x != NULL also the per-token inverse RMS.
 hipError_t launch_topk(const float *logits, int T, int E, int k, const float *x, int D, float eps,
                        const RouteBufs &rb, hipStream_t s);
-// Counting-sort grouping of the T*k pairs; tile_m > 0 also builds m-tiles.
-hipError_t launch_group(int T, int E, int k, int tile_m, const RouteBufs &rb, hipStream_t s);
+// Counting-sort grouping of the T*k pairs; tile_m > 0 also builds m-tiles,
+// by_size also their size-ordered copy (rb.tiles_sz).
+hipError_t launch_group(int T, int E, int k, int tile_m, bool by_size, const RouteBufs &rb, hipStream_t s);
 
 // Directional steering of a layer's MoE output (dir == nullptr: none).
 // stage ([D] f32) is one-token decode workspace: the down kernel writes the

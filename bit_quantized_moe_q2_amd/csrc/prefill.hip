@@ -210,7 +210,7 @@ __global__ __launch_bounds__(512) void prefill_q41_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];
+  const int e = rb.tiles_sz[2 * mtile], start = rb.tiles_sz[2 * mtile + 1];
   const int end = rb.offsets[e + 1];
   const int valid = end - start < TM ? end - start : TM;
   const int nmt = (valid + 15) >> 4;
@@ -301,11 +301,6 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(const float *__restrict_
   *reinterpret_cast<uint2 *>(xb + 4 * i) = out;
 }
 
-unsigned grid_for(int max_tiles, int n_ntiles) {
-  const int64_t total = (int64_t)max_tiles * n_ntiles;
-  return (unsigned)((total + 7) / 8 * 8);
-}
-
 }  // namespace
 
 hipError_t launch_prep_bf16(const float *x, const float *inv_rms, int T, int D, uint16_t *xb,
@@ -321,7 +316,7 @@ hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, co
                                  int max_tiles, uint16_t *hb, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.F / 128;
-  const dim3 grid(grid_for(max_tiles, nn));
+  const dim3 grid(xcd_grid(max_tiles, nn));
   hipLaunchKernelGGL((prefill_q41_kernel<true>), grid, dim3(512), 0, s, m.gate, m.up, m.D, m.F, xb,
                      1, m.k, rb, nn, hb, nullptr);
   return hipGetLastError();
@@ -331,7 +326,7 @@ hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, cons
                                int max_tiles, uint16_t *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
-  const dim3 grid(grid_for(max_tiles, nn));
+  const dim3 grid(xcd_grid(max_tiles, nn));
   hipLaunchKernelGGL((prefill_q41_kernel<false>), grid, dim3(512), 0, s, m.down, nullptr, m.F, m.D,
                      hb, 0, m.k, rb, nn, nullptr, o);
   return hipGetLastError();

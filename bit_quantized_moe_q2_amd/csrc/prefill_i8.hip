@@ -306,7 +306,7 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int e = rb.tiles[2 * mtile], start = rb.tiles[2 * mtile + 1];
+  const int e = rb.tiles_sz[2 * mtile], start = rb.tiles_sz[2 * mtile + 1];
   const int end = rb.offsets[e + 1];
   const int cap = 16 * NPMAX < TMI ? 16 * NPMAX : TMI;
   const int valid = end - start < cap ? end - start : cap;
@@ -389,11 +389,6 @@ __global__ __launch_bounds__(512, 1) void prefill_i8_kernel(
   }
 }
 
-unsigned grid_of(int max_tiles, int n_ntiles) {
-  const int64_t total = (int64_t)max_tiles * n_ntiles;
-  return (unsigned)((total + 7) / 8 * 8);
-}
-
 }  // namespace
 
 size_t prep_i8_bytes(int64_t rows, int K) {
@@ -432,7 +427,7 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
                                     int max_tiles, uint16_t *hb, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.F / 128;
-  hipLaunchKernelGGL((prefill_i8_kernel<true, NPAIR>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.gate,
+  hipLaunchKernelGGL((prefill_i8_kernel<true, NPAIR>), dim3(xcd_grid(max_tiles, nn)), dim3(512), 0, s, m.gate,
                      m.up, m.D, m.F, a.q, a.x, a.sig, 1, m.k, rb, nn, hb, nullptr);
   return hipGetLastError();
 }
@@ -441,7 +436,7 @@ hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, cons
                                   int max_tiles, uint16_t *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256;
-  hipLaunchKernelGGL((prefill_i8_kernel<false, NPAIR>), dim3(grid_of(max_tiles, nn)), dim3(512), 0, s, m.down,
+  hipLaunchKernelGGL((prefill_i8_kernel<false, NPAIR>), dim3(xcd_grid(max_tiles, nn)), dim3(512), 0, s, m.down,
                      nullptr, m.F, m.D, a.q, a.x, a.sig, 0, m.k, rb, nn, nullptr, o);
   return hipGetLastError();
 }

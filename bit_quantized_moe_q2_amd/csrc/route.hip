@@ -75,8 +75,9 @@ __device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) 
 
 // One workgroup per expert: histogram of all pair experts (for its offset),
 // then a stable, order-preserving compaction of its own pairs.  Workgroup 0
-// also writes counts, offsets, the active-expert list and the m-tile list.
-__global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int tile_m, RouteBufs rb) {
+// also writes counts, offsets, the active-expert list and the m-tile list
+// (and, by_size, its size-ordered copy).
+__global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int tile_m, int by_size, RouteBufs rb) {
   __shared__ int hist[MAX_E];
   __shared__ int wave_tot[16];
   __shared__ int s_off;
@@ -106,6 +107,40 @@ __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int ti
       for (int j = 0; j < ntile_mine; ++j) {
         rb.tiles[2 * (tpos + j)] = tid;
         rb.tiles[2 * (tpos + j) + 1] = off + j * tile_m;
+      }
+    }
+    if (by_size && tile_m > 0) {
+      // The same tiles, the full ones first (expert order), then the
+      // partial ones by falling count of 16-pair groups, each class in
+      // expert order: ranks by ballots per wave, class bases from the
+      // per-wave counts.  (Prefill GEMMs deal this list to the XCDs in turn,
+      // largest work first.)
+      __shared__ int cls_cnt[16][17];
+      const int lane = tid & 63, wv = tid >> 6;
+      const int full = c / tile_m, rem = c - full * tile_m;
+      const int ncls = (tile_m + 15) >> 4;  // <= 16
+      const int cls = rem > 0 ? (rem + 15) >> 4 : 0;
+      int n_full;
+      const int fpos = block_excl_scan(full, wave_tot, &n_full);
+      for (int j = 0; j < full; ++j) {
+        rb.tiles_sz[2 * (fpos + j)] = tid;
+        rb.tiles_sz[2 * (fpos + j) + 1] = off + j * tile_m;
+      }
+      int rank_w = 0;
+      for (int q = 1; q <= ncls; ++q) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(cls == q);
+        if (lane == 0) cls_cnt[wv][q] = __builtin_popcountll(m);
+        if (cls == q) rank_w = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      }
+      __syncthreads();
+      if (cls > 0) {
+        int pos = n_full;
+        for (int q = ncls; q > cls; --q)
+          for (int v = 0; v < 16; ++v) pos += cls_cnt[v][q];
+        for (int v = 0; v < wv; ++v) pos += cls_cnt[v][cls];
+        pos += rank_w;
+        rb.tiles_sz[2 * pos] = tid;
+        rb.tiles_sz[2 * pos + 1] = off + full * tile_m;
       }
     }
     if (tid == 0) {
@@ -152,9 +187,10 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, const float *x,
   return hipGetLastError();
 }
 
-hipError_t launch_group(int T, int E, int k, int tile_m, const RouteBufs &rb, hipStream_t s) {
+hipError_t launch_group(int T, int E, int k, int tile_m, bool by_size, const RouteBufs &rb, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(group_kernel, dim3(E), dim3(1024), 0, s, T, E, k, tile_m, rb);
+  if (by_size && !rb.tiles_sz) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(group_kernel, dim3(E), dim3(1024), 0, s, T, E, k, tile_m, by_size ? 1 : 0, rb);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ namespace ds4q {
 hipError_t launch_dequant(int, const void *, int64_t, int64_t, bool, void *, hipStream_t) STUB()
 hipError_t launch_matvec(int, const void *, int64_t, int64_t, const float *, int, float *, hipStream_t) STUB()
 hipError_t launch_topk(const float *, int, int, int, const float *, int, float, const RouteBufs &, hipStream_t) STUB()
-hipError_t launch_group(int, int, int, int, const RouteBufs &, hipStream_t) STUB()
+hipError_t launch_group(int, int, int, int, bool, const RouteBufs &, hipStream_t) STUB()
 hipError_t launch_decode_q2k_t1(const MoeDims &, const float *, const float *, bool, float, const RouteBufs &,
                                 float *, float *, bool, int, const SteerArgs &, hipStream_t) STUB()
 hipError_t launch_decode_q41_t1(const MoeDims &, const float *, const float *, bool, float, const RouteBufs &,
