@@ -454,7 +454,9 @@ def main():
         ds4q.ds4q_timing_enable(False)
         im_us = pti["imatrix"][0] / pti["imatrix"][1] * 1e3
         P = T * K
-        n_tiles = E + P // 96 + 1
+        # live m-tiles of this routing (up to 128 sorted pairs of one expert each)
+        cnt = np.bincount(np.argsort(-lgp.cpu().numpy(), axis=1, kind="stable")[:, :K].ravel(), minlength=E)
+        n_tiles = int(((cnt + 127) // 128).sum())
         # bf16 input rows and SwiGLU rows read once per pair, partial rows
         # written and read back, the statistics read and written
         im_bytes = P * (D + F) * 2 + n_tiles * (D + F) * 4 * 2 + E * (D + F) * 4 * 2
