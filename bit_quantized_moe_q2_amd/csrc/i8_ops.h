@@ -170,6 +170,23 @@ struct WOps : WMin<EXACT_MIN> {
     for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(b[j]));
     asm volatile("" : "+v"(this->bmin), "+v"(this->dsc));
   }
+  // The same in two parts: the integer fragments and d first (pinned), the
+  // min operand later (build_min), so that the first MFMAs need not wait
+  // for it.
+  __device__ __forceinline__ void build_int(const Q2KPart &r, int g) {
+    WTab t;
+    t.build(r, g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = t.bfrag(r, j);
+    this->dsc = f16lo(r.dd) * (1.0f / 256.0f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(b[j]));
+    asm volatile("" : "+v"(this->dsc));
+  }
+  __device__ __forceinline__ void build_min(const Q2KPart &r, int g) {
+    WMin<EXACT_MIN>::build(r, g);
+    asm volatile("" : "+v"(this->bmin));
+  }
 };
 
 // sched_barrier mask: ALU, MFMA and LDS instructions may be scheduled

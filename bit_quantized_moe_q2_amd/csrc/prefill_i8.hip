@@ -196,12 +196,19 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
 
   auto step = [&](int kb, Q2KPart (&r)[2], const uint8_t *As, const uint8_t *Xs, uint8_t *An,
                   uint8_t *Xn) {
+    // the integer operands first; the min-term operand is built once the
+    // first row group's integer MFMAs are issued (r is reloaded before then
+    // when NP = 1, so its scale/min bytes and d|dmin are kept apart)
     WOps<false> wo[2];
+    Q2KPart mp[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       r[t].finish();
-      wo[t].build(r[t], g);
-      wo[t].pin();
+      wo[t].build_int(r[t], g);
+      mp[t].s0 = r[t].s0;
+      mp[t].s1 = r[t].s1;
+      mp[t].dd = r[t].dd;
+      asm volatile("" : "+v"(mp[t].s0), "+v"(mp[t].s1), "+v"(mp[t].dd));
     }
     // requests for later blocks, in this order: the sum rows and digit-row
     // load 0 before row group 0, digit-row load u before group u, and the
@@ -251,6 +258,10 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
           acc[ip][t][2 * h] = fmaf(wo[t].dsc, (float)((c[t].x << 8) + c[t].y), acc[ip][t][2 * h]);
           acc[ip][t][2 * h + 1] = fmaf(wo[t].dsc, (float)((c[t].z << 8) + c[t].w), acc[ip][t][2 * h + 1]);
         }
+      }
+      if (ip == 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) wo[t].build_min(mp[t], g);
       }
       mfma_group_begin();
 #pragma unroll
