@@ -27,7 +27,8 @@
 // values, y = d*q + m) gives d * sum q a + m * sum a: the integer sums on
 // the same MFMA (see the kernel), the sums of a prepared with the digits.
 //
-// LDS: the digit rows (GLayout), then the K parts.
+// LDS: the digit rows (GLayout), then the K parts, then (Q4_1) the m-tile's
+// sums of 32 values.
 #include <type_traits>
 
 #include "common.h"
