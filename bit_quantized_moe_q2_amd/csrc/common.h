@@ -87,6 +87,24 @@ __device__ __forceinline__ void mfma_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Direct global-to-LDS copy of 16 bytes per lane (lane i's bytes land at
+// lds + 16 i, lds wave-uniform) from base + soff + voff, soff wave-uniform,
+// as buffer_load_dwordx4 ... lds.  global_load_lds copies the same way, but
+// the compiler counts a pending global_load_lds as an access that may
+// complete LDS operations out of order, so every later wait for an LDS read
+// becomes a wait for all of them and LDS reads issued ahead of their use no
+// longer overlap anything; with the buffer form those waits stay exact.  No
+// range limit is set: callers keep offsets in bounds (and below 2^32).
+struct DmaSrc {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ explicit DmaSrc(const void *base)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000)) {}
+  __device__ __forceinline__ void copy16(uint32_t voff, uint32_t soff, uint8_t *lds) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff,
+                                             soff, 0, 0);
+  }
+};
+
 // Grouped-GEMM work item -> (m-tile, n-tile).  The live m-tiles, largest
 // first (the grouping's size-ordered list; their count is known on the
 // device only), are dealt to the 8 XCDs in turn: m-tile t to XCD t % 8, and

@@ -304,6 +304,7 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
   // x 16 bytes), load u by wave u % NWV.  With four or more blocks a load
   // holds four blocks of one (digit, pair) row, and loads of absent pairs
   // are skipped.  The row scales go to registers until the K parts meet.
+  const DmaSrc qsrc(aq), xssrc(axs);
   auto issue_act = [&](MTile &c) {
     const int src_row = arow(c, lane & 3);  // source row of pair lane & 3
 #pragma unroll
@@ -315,17 +316,17 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
           const int rix = u / (NB / 4), pair = rix & 3, d = rix >> 2;  // uniform
           const int blk = 4 * (u % (NB / 4)) + (lane >> 4);
           if (pair < c.valid)
-            dma16(aq + (int64_t)__builtin_amdgcn_readlane(src_row, pair) * (NB * QROW3) +
-                      (blk * QROW3 + d * 256 + (lane & 15) * 16),
-                  lds + rix * L::RSTRIDE + (u % (NB / 4)) * 1024);
+            qsrc.copy16(blk * QROW3 + d * 256 + (lane & 15) * 16,
+                        (uint32_t)__builtin_amdgcn_readlane(src_row, pair) * (NB * QROW3),
+                        lds + rix * L::RSTRIDE + (u % (NB / 4)) * 1024);
         } else {
           const int sl = 64 * u + lane;    // 16-byte slot
           const int rix = sl / (NB * 16);  // 4 * digit + pair
           const int pair = rix & 3, d = rix >> 2;
           const int blk = (sl >> 4) & (NB - 1), pos = sl & 15;
-          dma16(aq + (int64_t)__shfl(src_row, pair, 64) * (NB * QROW3) +
-                    (blk * QROW3 + d * 256 + ((pos ^ (4 * pair + d)) << 4)),
-                lds + 1024 * u);
+          qsrc.copy16((uint32_t)__shfl(src_row, pair, 64) * (NB * QROW3) +
+                          (blk * QROW3 + d * 256 + ((pos ^ (4 * pair + d)) << 4)),
+                      0, lds + 1024 * u);
         }
       }
     }
@@ -336,8 +337,7 @@ __global__ __launch_bounds__(64 * NWV, WG_PER_CU) void decode_grouped_kernel(
         const int o = 1024 * u + 16 * lane;
         const bool in = o < NB * 128;
         const int pair = in ? o / (NB * 32) : 0, off = in ? o % (NB * 32) : 0;
-        dma16(reinterpret_cast<const uint8_t *>(axs) + (int64_t)arow(c, pair) * (NB * 32) + off,
-              lds + L::DIG + L::PART + 1024 * u);
+        xssrc.copy16((uint32_t)arow(c, pair) * (NB * 32) + off, 0, lds + L::DIG + L::PART + 1024 * u);
       }
     }
     c.sig = tid < GT ? asig[arow(c, tid)] : 0.f;

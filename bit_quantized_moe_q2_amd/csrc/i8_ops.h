@@ -193,9 +193,5 @@ struct WOps : WMin<EXACT_MIN> {
 // across, global memory instructions may not.
 constexpr int SCHED_NOVMEM = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200;
 
-__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-
 }  // namespace
 }  // namespace ds4q

@@ -16,7 +16,7 @@
 // Data movement (eight waves; wave w owns 16 gate + 16 up rows, or 32 down
 // rows, and all the tile's rows of A).  K advances in steps of 256 values
 // (eight Q4_1 blocks).  The next step's A tile (128 rows x 512 B of bf16) goes
-// to the other of two LDS buffers by global_load_lds_dwordx4 (one 1-KiB
+// to the other of two LDS buffers by direct buffer loads to LDS (one 1-KiB
 // instruction = 2 rows x 32 chunks; chunk c of row r is stored at chunk
 // position c ^ (r & 15), so the 16 lanes reading one chunk column touch 16
 // distinct bank groups), and the raw bytes of the next step's weights go to
@@ -62,10 +62,6 @@ __device__ __forceinline__ bf16x8 to_frag(uint32_t a, uint32_t b, uint32_t c, ui
   return __builtin_bit_cast(bf16x8, (u32x4){a, b, c, d});
 }
 
-__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-
 // Raw bytes of a pair of Q4_1 blocks (2jp, 2jp+1) for lane group g: block
 // b = 2jp + (g >> 1), half p = g & 1 -- 12 bytes from offset 8p, i.e. (d, m)
 // and code bytes 0..7 for p = 0, code bytes 4..15 for p = 1; the lane's code
@@ -105,8 +101,8 @@ struct Q41Raw {
 };
 
 struct StepCtx {
-  const uint8_t *abase;     // A rows (bytes)
-  int64_t aoff[MT];         // byte offsets of the lane's DMA chunks (row part + chunk)
+  const uint8_t *abase;     // A rows (bytes) from row rbase
+  uint32_t aoff[MT];        // byte offsets of the lane's DMA chunks from abase (row part + chunk)
   int aoffj[2 * NJ];        // LDS offsets of the lane's A chunks, low and high MFMA of pair jp
   const uint8_t *brow[2];   // the lane's two weight rows
   int w, g;
@@ -131,10 +127,10 @@ __device__ __forceinline__ void q41_loop(const StepCtx &cx, int ns, uint8_t *As0
                                          f32x4 (&acc)[MT][2]) {
   constexpr int NU = NMT;  // DMA loads per wave (2 rows each): rows 0 .. 16*NU-1
   const int w = cx.w, g = cx.g;
+  const DmaSrc asrc(cx.abase);
   auto issue_a = [&](int s, uint8_t *As) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
-      dma16(cx.abase + (int64_t)s * AROWB + cx.aoff[u], As + (8 * u + w) * 1024);
+    for (int u = 0; u < NU; ++u) asrc.copy16(cx.aoff[u], (uint32_t)s * AROWB, As + (8 * u + w) * 1024);
   };
   auto issue_w = [&](int s, Q41Raw (&r)[2][NJ]) {
 #pragma unroll
@@ -224,14 +220,17 @@ __global__ __launch_bounds__(512) void prefill_q41_kernel(
   StepCtx cx;
   cx.w = w;
   cx.g = g;
-  cx.abase = reinterpret_cast<const uint8_t *>(A);
+  // offsets from the tile's first row (gathered token rows: from row 0;
+  // T * K * 2 < 2^29 bytes), so they fit the 32-bit buffer offsets
+  const int rbase = gather_tokens ? 0 : start;
+  cx.abase = reinterpret_cast<const uint8_t *>(A) + (int64_t)rbase * (2 * K);
   // DMA load I = 8u + w covers rows 2I, 2I+1: lane l takes row 2I + l/32 and
   // stores it at chunk position l%32, which holds data chunk (l%32) ^ (row%16)
 #pragma unroll
   for (int u = 0; u < MT; ++u) {
     const int r = 2 * (8 * u + w) + (lane >> 5);
     const int c = (lane & 31) ^ (r & 15);
-    cx.aoff[u] = (int64_t)arow[r] * (2 * K) + c * 16;
+    cx.aoff[u] = (uint32_t)(arow[r] - rbase) * (2 * K) + c * 16;
   }
   // pair jp: block b = 2jp + (g >> 1); the low MFMA reads chunk 4b + (g & 1)
   // (values 8p..8p+7), the high one chunk 4b + 2 + (g & 1)

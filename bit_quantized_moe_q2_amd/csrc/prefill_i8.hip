@@ -23,7 +23,7 @@
 // scales by sigma (then SwiGLU, or the plain store of the down rows).
 //
 // Data movement: the activation tiles reach LDS by direct global->LDS loads
-// (global_load_lds_dwordx4), double-buffered one 256-column block ahead;
+// (buffer_load_dwordx4 ... lds), double-buffered one 256-column block ahead;
 // each 256-byte digit row is stored with its 16-byte chunks XOR-swizzled by
 // the row index, so the 16 lanes that read one chunk column hit 16
 // different bank groups.  Weights go straight to registers, also one block
@@ -168,10 +168,11 @@ __device__ __forceinline__ void block_loop(const ItemCtx &cx, uint8_t *As0, uint
   const int xtok = 16 * (w % NP) + (lane >> 2);
   const uint32_t xoffs = (uint32_t)((cx.arow[xtok] - cx.rbase) * rowx) + (lane & 3) * 16;
 
+  const DmaSrc asrc(cx.abase), xsrc(cx.xbase);
   auto issue_a = [&](int u, int kb, uint8_t *As) {
-    if (w < 4) dma16(cx.abase + (int64_t)kb * QROW + aoffs[u], As + (4 * u + w) * 1024);
+    if (w < 4) asrc.copy16(aoffs[u], (uint32_t)kb * QROW, As + (4 * u + w) * 1024);
   };
-  auto issue_x = [&](int kb, uint8_t *Xs) { dma16(cx.xbase + (int64_t)kb * XROW + xoffs, Xs + w * 1024); };
+  auto issue_x = [&](int kb, uint8_t *Xs) { xsrc.copy16(xoffs, (uint32_t)kb * XROW, Xs + w * 1024); };
   auto issue_tile = [&](int kb, uint8_t *As, uint8_t *Xs) {
     issue_x(kb, Xs);
 #pragma unroll

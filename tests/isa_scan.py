@@ -49,6 +49,8 @@ def _writes(inst: str) -> set[tuple[str, int]]:
     if op.startswith(("v_cmp", "v_cmpx", "ds_write", "ds_store", "global_store", "buffer_store",
                       "global_atomic", "buffer_atomic", "global_load_lds", "buffer_load_lds")):
         return set()
+    if op.startswith("buffer_load") and rest.split()[-1] == "lds":
+        return set()  # direct-to-LDS form: the first operand is the offset it reads
     if op.startswith(("v_", "ds_", "global_load", "buffer_load", "flat_load", "scratch_load")):
         return _regs(rest.split(",")[0])
     return set()

@@ -69,6 +69,12 @@ def test_scanner_finds_planted_gap():
     # a write of an unrelated register, or a read of the accumulator, is no hit
     assert not mfma_srcc_gaps(text.replace("v_cndmask_b32_e64 v14,", "v_cndmask_b32_e64 v15x,"), limit=8)
     assert not mfma_srcc_gaps(text.replace("v_cndmask_b32_e64 v14, v19", "v_cndmask_b32_e64 v40, v14"), limit=8)
+    # a buffer load writes its first operand, unless it loads to LDS (then
+    # that operand is the offset it reads)
+    load = text.replace("\tv_cndmask_b32_e64 v14, v19, v21, s[0:1]", "\tbuffer_load_dwordx4 v[14:17], v20, s[4:7], 0 offen")
+    assert len(mfma_srcc_gaps(load, limit=8)) == 1
+    assert not mfma_srcc_gaps(text.replace("\tv_cndmask_b32_e64 v14, v19, v21, s[0:1]",
+                                           "\tbuffer_load_dwordx4 v14, s[4:7], s62 offen lds"), limit=8)
 
 
 def test_forbidden_scan_finds_planted():
