@@ -55,7 +55,7 @@ struct Workspace {
   float *stage = nullptr;  // decode of one token: [D] f32, the unsteered output before steering
   float *imat_part = nullptr;  // imatrix on m-tiles: [max_tiles][max(D, F)] f32 partial rows
   uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
-  PrepI8 xq{}, hq{};       // prefill on Q2_K weights: int8 digit rows of x and of hb
+  PrepF16 xq{}, hq{};      // prefill on Q2_K weights: fp16 rows of x and of hb
   PrepD3 xd{}, hd{};       // decode of 2..64 tokens: int8 digit rows of x and of h
   size_t bytes = 0;
 
@@ -102,12 +102,12 @@ struct Workspace {
       ob = (uint16_t *)take(P * D * 2);
       if (!i8_in) xb = (uint16_t *)take((size_t)T * D * 2);
       if (i8_in) {
-        void *p = take(prep_i8_bytes(T, D));
-        if (base) xq = prep_i8_view(p, T, D);
+        void *p = take(prep_f16_bytes(T, D));
+        if (base) xq = prep_f16_view(p, T, D);
       }
       if (i8_h) {
-        void *p = take(prep_i8_bytes(P, F));
-        if (base) hq = prep_i8_view(p, P, F);
+        void *p = take(prep_f16_bytes(P, F));
+        if (base) hq = prep_f16_view(p, P, F);
       }
       if (stats) imat_part = (float *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * (D > F ? D : F) * 4);
     }
@@ -404,9 +404,9 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, true, w.rb, s));
   const int mt = max_tiles(T, m.E, m.k, PREFILL_TILE_M);
   if (i8_gateup(L)) {
-    TIMED_TRY("prep_i8", launch_prep_i8(x, xf != nullptr, true, norm && xf ? w.rb.inv_rms : nullptr, T,
-                                        m.D, w.xq, s));
-    TIMED_TRY("prefill_gateup", launch_prefill_i8_gateup(m, w.xq, T, w.rb, mt, w.hb, s));
+    TIMED_TRY("prep_f16", launch_prep_f16(x, xf != nullptr, true, norm && xf ? w.rb.inv_rms : nullptr, T,
+                                          m.D, w.xq, s));
+    TIMED_TRY("prefill_gateup", launch_prefill_f16_gateup(m, w.xq, T, w.rb, mt, w.hb, s));
   } else {
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     if (xf) {
@@ -422,8 +422,8 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
   }
   if (i8_down(L)) {
     const int64_t P = (int64_t)T * m.k;
-    TIMED_TRY("prep_i8", launch_prep_i8(w.hb, false, false, nullptr, P, m.F, w.hq, s));
-    TIMED_TRY("prefill_down", launch_prefill_i8_down(m, w.hq, T, w.rb, mt, w.ob, s));
+    TIMED_TRY("prep_f16", launch_prep_f16(w.hb, false, false, nullptr, P, m.F, w.hq, s));
+    TIMED_TRY("prefill_down", launch_prefill_f16_down(m, w.hq, T, w.rb, mt, w.ob, s));
   } else {
     TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.ob, s));
   }

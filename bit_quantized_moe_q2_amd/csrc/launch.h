@@ -101,6 +101,22 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, co
                                     int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
                                   int max_tiles, uint16_t *ob, hipStream_t s);
+// Prefill on Q2_K weights, fp16 matrix cores (prefill_f16.hip): activation
+// rows scaled per row by a power of two and stored as fp16 in the MFMA
+// fragment order, with the factor that undoes the scaling.
+struct PrepF16 {
+  uint16_t *q;  // [rows][K/256][32][8] fp16
+  float *sig;   // [rows]
+};
+size_t prep_f16_bytes(int64_t rows, int K);
+PrepF16 prep_f16_view(void *base, int64_t rows, int K);
+// src as for launch_prep_i8.
+hipError_t launch_prep_f16(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
+                           int64_t rows, int K, const PrepF16 &p, hipStream_t s);
+hipError_t launch_prefill_f16_gateup(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,
+                                     int max_tiles, uint16_t *hb, hipStream_t s);
+hipError_t launch_prefill_f16_down(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,
+                                   int max_tiles, uint16_t *ob, hipStream_t s);
 // Decode of 2..64 tokens (decode_grouped.hip): activation rows prepared as
 // three int8 digits per value, in the MFMA fragment order of the weight
 // format they meet, and a per-row scale (plus, for Q4_1, the sums of every

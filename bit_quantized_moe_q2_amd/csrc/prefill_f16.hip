@@ -1,0 +1,442 @@
+// Prefill path on Q2_K weights with fp16 matrix cores.
+//
+// Arithmetic.  A weight of a 256-value Q2_K block ("【#2】ds4.c 해독하기",
+// Q2_K block-layout table and code-packing expression) is
+//   w = d * sc * q - dmin * mn,
+// q the 2-bit code, sc / mn the 4-bit scale and min of its 16-value
+// sub-block, d / dmin the block's fp16 fields.  For each sub-block the four
+// possible weights (q = 0..3) are evaluated in fp32 (d*sc*q and dmin*mn are
+// exact there, the difference rounds once) and rounded to fp16; each
+// weight of the B operand is then one table lookup (v_perm_b32 on the lane's
+// 2-bit codes).  The activation rows are prepared once per call
+// (prep_f16_kernel): each row is scaled by the power of two 2^k that puts its
+// largest magnitude in [2^14, 2^15) and stored as fp16 (exact for bf16
+// input: 8 significant bits fit fp16's 11 down to 2^-17 of the scaled
+// maximum, below which values round to fp16's subnormal grid), with 2^-k kept
+// per row.  The products run on v_mfma_f32_16x16x32_f16 and accumulate over
+// the whole K range in the matrix core's fp32 registers; the epilogue scales
+// by 2^-k (then SwiGLU, or the plain store of the down rows).
+//
+// K order.  Any permutation of K serves as long as both operands use it.
+// Lane group g (lanes 16g..16g+15) of K-tile j = 2p + h of a block takes the
+// 8 values 128(g>>1) + 32p + 16(g&1) + 8h + i, i = 0..7: code bytes
+// 16g + 8h + i of the block's code area, bit pair p, all of sub-block
+// 8(g>>1) + 2p + (g&1).  So a lane's 16 code bytes (one 16-byte load) cover
+// K-tiles 0..7 of its weight row, and each of its four sub-blocks feeds
+// exactly two K-tiles.  The prepared activation row holds, per block, 32
+// chunks of 16 bytes, chunk 4j + g = those 8 values of K-tile j as fp16.
+//
+// Data movement as in the int8 form: activation tiles reach LDS by direct
+// global->LDS loads (buffer_load_dwordx4 ... lds), double-buffered one block
+// ahead, each 512-byte row with its 16-byte chunks XOR-swizzled by the row
+// index within its 16-row group; raw weight bytes go to registers two blocks
+// ahead.
+#include "common.h"
+#include "i8_ops.h"
+#include "launch.h"
+
+namespace ds4q {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int TMF = PREFILL_TILE_M;  // tokens (sorted pairs) per m-tile
+constexpr int NGF = TMF / 16;        // MFMA row groups of 16 tokens
+constexpr int HROW = 512;            // fp16 bytes of one row's 256-value block
+constexpr int HSTAGE = TMF * HROW;   // LDS bytes of one activation stage
+static_assert(TMF % 16 == 0 && TMF <= 128, "m-tile must be a multiple of 16, at most 128");
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+
+// One workgroup per activation row, one thread per 16-value sub-block.
+// F32IN: the row is x * inv_rms (or x), rounded to bf16 first when ROUND
+// (the prefill input contract); otherwise the row is bf16 bits.  Output per
+// (row, block): 32 chunks [4j + g][8 fp16] in the K order above, and per row
+// the factor 2^-k that undoes the scaling.
+template <bool F32IN, bool ROUND>
+__global__ __launch_bounds__(256) void prep_f16_kernel(const void *__restrict__ src,
+                                                       const float *__restrict__ inv_rms, int K,
+                                                       uint16_t *__restrict__ aq,
+                                                       float *__restrict__ asig) {
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nsub = K >> 4, nb = K >> 8;
+  __shared__ float red[4];
+  float v[16];
+  float m = 0.f;
+  const bool act = t < nsub;
+  if (act) {
+    if constexpr (F32IN) {
+      const float s = inv_rms ? inv_rms[row] : 1.0f;
+      const float4 *x = reinterpret_cast<const float4 *>(static_cast<const float *>(src) + row * K + 16 * t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = x[i];
+        v[4 * i] = ROUND ? bf16_to_f32(bf16_rne_bits(f.x * s)) : f.x * s;
+        v[4 * i + 1] = ROUND ? bf16_to_f32(bf16_rne_bits(f.y * s)) : f.y * s;
+        v[4 * i + 2] = ROUND ? bf16_to_f32(bf16_rne_bits(f.z * s)) : f.z * s;
+        v[4 * i + 3] = ROUND ? bf16_to_f32(bf16_rne_bits(f.w * s)) : f.w * s;
+      }
+    } else {
+      const u32x4 *x = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(src) + row * K + 16 * t);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x4 u = x[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[8 * i + 2 * c] = bf16_to_f32(u[c] & 0xFFFFu);
+          v[8 * i + 2 * c + 1] = bf16_to_f32(u[c] >> 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // mx = f * 2^e with f in [0.5, 1): mx * 2^(15 - e) lies in [2^14, 2^15)
+  int k = 0;
+  if (mx > 0.f && mx <= 3.402823466e38f) k = 15 - __builtin_amdgcn_frexp_expf(mx);
+  if (t == 0) asig[row] = ldexpf(1.0f, -k);
+  if (!act) return;
+  const int b = t >> 4, s = t & 15;
+  const int g = 2 * (s >> 3) + (s & 1), p = (s >> 1) & 3;
+  u32x4 *out = reinterpret_cast<u32x4 *>(aq + (row * nb + b) * (HROW / 2));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      o[c] = pack_f16x2(ldexpf(v[8 * h + 2 * c], k), ldexpf(v[8 * h + 2 * c + 1], k));
+    out[4 * (2 * p + h) + g] = o;
+  }
+}
+
+// The fp16 weight tables of one weight row's four sub-blocks in lane group
+// g: sub-block p (bit pair p of the lane's code bytes) is
+// 8(g>>1) + 2p + (g&1); lo[p] / hi[p] hold the low / high bytes of its
+// weights for codes 0..3 (byte q = code q).
+struct HTab {
+  uint32_t lo[4], hi[4];
+  // Tables of sub-block P from the block's scale/min bytes and d|dmin
+  // (bytes 0 and 2 of a0 = sub-blocks 0 and 1, of a1 = 2 and 3).
+  template <int P>
+  __device__ __forceinline__ void build(uint32_t a0, uint32_t a1, float d, float dm) {
+    const uint32_t byte = ((P < 2 ? a0 : a1) >> (16 * (P & 1))) & 0xFFu;
+    const float ds = d * (float)(byte & 15u), mn = dm * (float)(byte >> 4);
+    const uint32_t e01 = pack_f16x2(-mn, ds - mn);
+    const uint32_t e23 = pack_f16x2(fmaf(2.0f, ds, -mn), fmaf(3.0f, ds, -mn));
+    lo[P] = __builtin_amdgcn_perm(e23, e01, 0x06040200u);
+    hi[P] = __builtin_amdgcn_perm(e23, e01, 0x07050301u);
+  }
+  // B fragment of K-tile j = 2p + h: the codes of bytes 8h..8h+7 (dwords
+  // 2h, 2h+1 of q), bit pair p, looked up and interleaved into fp16 pairs.
+  template <int J>
+  __device__ __forceinline__ f16x8 bfrag(const u32x4 &q) const {
+    constexpr int P = J >> 1, H = J & 1;
+    u32x4 o;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t sel = (q[2 * H + c] >> (2 * P)) & 0x03030303u;
+      const uint32_t l = __builtin_amdgcn_perm(0u, lo[P], sel), h = __builtin_amdgcn_perm(0u, hi[P], sel);
+      o[2 * c] = __builtin_amdgcn_perm(h, l, 0x05010400u);
+      o[2 * c + 1] = __builtin_amdgcn_perm(h, l, 0x07030602u);
+    }
+    return __builtin_bit_cast(f16x8, o);
+  }
+};
+
+// Per-wave state of one work item (set up once, shared by every block).
+struct FCtx {
+  const uint8_t *abase;    // uniform: prepared rows of row rbase
+  const int *arow;         // LDS: source row of each of the tile's TMF tokens
+  int rbase;               // 0 (gathered token rows) or the tile's first sorted row
+  const uint8_t *brow[2];  // weight rows of the two n-subtiles (lane's row)
+  uint32_t aoff[4];        // LDS offsets of the lane's A chunks, K-tiles 0..3 (+256 for 4..7)
+  int nb, w, g, lane;      // w wave-uniform
+};
+
+// The block loop for NP live 16-token groups (tokens >= 16*NP are absent):
+// acc[i][t] += the products of blocks 0..nb-1.
+template <int NP, int NPMAX>
+__device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uint8_t *As1,
+                                               f32x4 (&acc)[NPMAX][2]) {
+  const int w = cx.w, g = cx.g, nb = cx.nb, lane = cx.lane;
+  // Activation requests per block: waves 0..3 issue the 2*NP row-pair loads
+  // (load I = 4u + w covers token rows 2I, 2I+1; lane -> row 2I + lane/32,
+  // stored chunk lane%32 = data chunk (lane%32) ^ (row%16)), so the MFMAs of
+  // waves 4..7 on the same SIMDs run while they issue; every wave issues the
+  // raw weight bytes of its two n-subtiles last, so the block-end wait count
+  // is exact for both kinds of wave.  Offsets are relative to row rbase
+  // (gathered token rows: < 2^29 bytes).  Blocks past the end are requested
+  // again as the last block, so the loop has no branches.
+  const int64_t rowq = (int64_t)nb * HROW;
+  uint32_t aoffs[2 * NP];
+#pragma unroll
+  for (int u = 0; u < 2 * NP; ++u) {
+    const int I = 4 * u + (w & 3);
+    const int r = 2 * I + (lane >> 5);
+    const int c = (lane & 31) ^ (r & 15);
+    aoffs[u] = (uint32_t)((cx.arow[r] - cx.rbase) * rowq) + c * 16;
+  }
+  const DmaSrc asrc(cx.abase);
+  auto issue_a = [&](int u, int kb, uint8_t *As) {
+    if (w < 4) asrc.copy16(aoffs[u], (uint32_t)kb * HROW, As + (4 * u + w) * 1024);
+  };
+  auto issue_w = [&](int kb, RawBlk (&r)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t] + (int64_t)kb * BB_Q2K, g);
+  };
+
+  constexpr int NWLD = 4;  // weight load instructions per block: 2 x (16 + 8 bytes)
+  RawBlk rw[2][2];
+#pragma unroll
+  for (int u = 0; u < 2 * NP; ++u) issue_a(u, 0, As0);
+  issue_w(0, rw[0]);
+  issue_w(nb > 1 ? 1 : 0, rw[1]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  auto step = [&](int kb, RawBlk (&r)[2], const uint8_t *As, uint8_t *An) {
+    // this block's operands: the code bytes, and per weight row the scale /
+    // min bytes of the lane's sub-blocks and d|dmin; then r is free for block
+    // kb + 2
+    u32x4 q[2];
+    uint32_t sa0[2], sa1[2];
+    float sd[2], sm[2];
+    HTab tb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const Q2KPart o = take_block(r[t]);
+      q[t] = o.q;
+      sa0[t] = o.s0 >> (8 * (g & 1));
+      sa1[t] = o.s1 >> (8 * (g & 1));
+      sd[t] = f16lo(o.dd);
+      sm[t] = f16hi(o.dd);
+      tb[t].template build<0>(sa0[t], sa1[t], sd[t], sm[t]);
+    }
+    const int kn = kb + 1 < nb ? kb + 1 : nb - 1, kw = kb + 2 < nb ? kb + 2 : nb - 1;
+    // Per K-tile j: the requests of this step, then the next K-tile's A
+    // fragments (LDS reads) and B fragments (table lookups; a sub-block's
+    // tables just before its first K-tile), then K-tile j's MFMAs as one
+    // fenced group.  So each wave alternates a vector phase and a matrix
+    // phase, and the two waves of a SIMD overlap one's with the other's.
+    f16x8 a[2][NP], b[2][2];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) a[0][i] = *reinterpret_cast<const f16x8 *>(As + cx.aoff[0] + i * 16 * HROW);
+    b[0][0] = tb[0].template bfrag<0>(q[0]);
+    b[0][1] = tb[1].template bfrag<0>(q[1]);
+#define DS4Q_F16_KTILE(J)                                                                         \
+    {                                                                                             \
+      constexpr int C = (J) & 1, U0 = (2 * NP * (J)) / 8, U1 = (2 * NP * ((J) + 1)) / 8;          \
+      __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                               \
+      _Pragma("unroll") for (int u = U0; u < U1; ++u) issue_a(u, kn, An);                         \
+      if ((J) == 7) {                                                                             \
+        __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                             \
+        issue_w(kw, r);                                                                           \
+      }                                                                                           \
+      __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                               \
+      if ((J) < 7) {                                                                              \
+        constexpr int JN = ((J) + 1) & 7;                                                         \
+        _Pragma("unroll") for (int i = 0; i < NP; ++i) a[C ^ 1][i] =                              \
+            *reinterpret_cast<const f16x8 *>(As + cx.aoff[JN & 3] + (JN >> 2) * 256 + i * 16 * HROW); \
+        if ((JN & 1) == 0) {                                                                      \
+          _Pragma("unroll") for (int t = 0; t < 2; ++t)                                           \
+            tb[t].template build<(JN >> 1)>(sa0[t], sa1[t], sd[t], sm[t]);                        \
+        }                                                                                         \
+        b[C ^ 1][0] = tb[0].template bfrag<JN>(q[0]);                                             \
+        b[C ^ 1][1] = tb[1].template bfrag<JN>(q[1]);                                             \
+      }                                                                                           \
+      mfma_group_begin();                                                                         \
+      _Pragma("unroll") for (int i = 0; i < NP; ++i) {                                            \
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[C][i], b[C][0], acc[i][0], 0, 0, 0); \
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[C][i], b[C][1], acc[i][1], 0, 0, 0); \
+      }                                                                                           \
+      mfma_fence();                                                                               \
+    }
+    DS4Q_F16_KTILE(0)
+    DS4Q_F16_KTILE(1)
+    DS4Q_F16_KTILE(2)
+    DS4Q_F16_KTILE(3)
+    DS4Q_F16_KTILE(4)
+    DS4Q_F16_KTILE(5)
+    DS4Q_F16_KTILE(6)
+    DS4Q_F16_KTILE(7)
+#undef DS4Q_F16_KTILE
+    // Each wave waits for its own tile requests and LDS reads; then the
+    // barrier alone publishes the tile (a workgroup fence would also wait
+    // for the weight requests still in flight).
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | NWLD);  // vmcnt(NWLD) lgkmcnt(0): tile of kb+1 landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // nb is a power of two; the loop body is exactly two blocks, so every path
+  // into a block leaves the same requests outstanding
+  if (nb == 1) {
+    step(0, rw[0], As0, As1);
+  } else {
+    for (int kb = 0; kb < nb; kb += 2) {
+      step(kb, rw[0], As0, As1);
+      step(kb + 1, rw[1], As1, As0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no request outlives the loop
+}
+
+// SWIGLU: an n-tile is 128 rows of F; wave w owns rows 16w..16w+15 of both
+// gate (t = 0) and up (t = 1).  Otherwise an n-tile is 256 down rows, wave w
+// owning rows 32w + 16t .. +15.  Eight waves; m-tile = up to TMF sorted pairs
+// of one expert.  SwiGLU rows are written as bf16 (hb), down rows as bf16 (o).
+template <bool SWIGLU>
+__global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
+    const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
+    const uint16_t *__restrict__ aq, const float *__restrict__ asig, int gather_tokens, int kslots,
+    RouteBufs rb, int n_ntiles, uint16_t *__restrict__ hb, uint16_t *__restrict__ o) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[HSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[HSTAGE];
+  __shared__ int arow[TMF];
+
+  int mtile, ntile;
+  if (!xcd_tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int e = rb.tiles_sz[2 * mtile], start = rb.tiles_sz[2 * mtile + 1];
+  const int end = rb.offsets[e + 1];
+  const int valid = end - start < TMF ? end - start : TMF;
+  const int np = (valid + 15) >> 4;  // live 16-token groups
+
+  if (tid < TMF) {
+    const int m = tid < valid ? tid : 0;  // absent rows repeat row 0; never stored
+    arow[tid] = gather_tokens ? rb.pairs[start + m] / kslots : start + m;
+  }
+  __syncthreads();
+
+  FCtx cx;
+  cx.nb = K >> 8;
+  cx.w = __builtin_amdgcn_readfirstlane(w);
+  cx.g = g;
+  cx.lane = lane;
+  cx.arow = arow;
+  cx.rbase = gather_tokens ? 0 : start;
+  cx.abase = reinterpret_cast<const uint8_t *>(aq) + (int64_t)cx.rbase * cx.nb * HROW;
+  const int64_t rbytes = (int64_t)cx.nb * BB_Q2K;
+  int wrow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if constexpr (SWIGLU) {
+      wrow[t] = ntile * 128 + 16 * w + n;
+      cx.brow[t] = (t == 0 ? W0 : W1) + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
+    } else {
+      wrow[t] = ntile * 256 + 32 * w + 16 * t + n;
+      cx.brow[t] = W0 + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
+    }
+  }
+  // LDS read offsets: token row n of a 16-row group, data chunk 4j + g
+  // stored at (4j + g) ^ n, i.e. byte (j << 6) ^ ((g ^ n) << 4) of the row;
+  // K-tiles 4..7 add 256 to those of 0..3
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cx.aoff[j] = n * HROW + (uint32_t)((j << 6) ^ ((g ^ n) << 4));
+
+  f32x4 acc[NGF][2];
+#pragma unroll
+  for (int i = 0; i < NGF; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  switch (np) {
+    case 1: block_loop_f16<1, NGF>(cx, As0, As1, acc); break;
+    case 2: block_loop_f16<2, NGF>(cx, As0, As1, acc); break;
+    case 3: block_loop_f16<3, NGF>(cx, As0, As1, acc); break;
+    case 4: block_loop_f16<4, NGF>(cx, As0, As1, acc); break;
+    case 5: block_loop_f16<5, NGF>(cx, As0, As1, acc); break;
+    case 6: block_loop_f16<6, NGF>(cx, As0, As1, acc); break;
+    case 7: block_loop_f16<7, NGF>(cx, As0, As1, acc); break;
+    default: block_loop_f16<8, NGF>(cx, As0, As1, acc); break;
+  }
+  // the accumulators are read below; no instruction rewrites them until the
+  // last MFMAs have read them
+  mfma_fence();
+
+  // epilogue: lane (g, n) holds, for group i, rows q = 0..3 = tokens
+  // 16i + 4g + q of weight row n of each n-subtile t
+#pragma unroll
+  for (int i = 0; i < NGF; ++i) {
+    if (i >= np) break;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = 16 * i + 4 * g + q;
+      if (m >= valid) continue;
+      const float sg = asig[arow[m]];
+      const int64_t pos = start + m;
+      const float v0 = acc[i][0][q] * sg, v1 = acc[i][1][q] * sg;
+      if constexpr (SWIGLU) {
+        hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
+      } else {
+        // wrow[1] = wrow[0] + 16; lanes n, n ^ 1 share g, hence m and validity
+        store_bf16_row_pair(o + pos * rows_per_expert + wrow[0], n, v0, v1);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t prep_f16_bytes(int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  return up((size_t)rows * K * 2) + up((size_t)rows * 4);
+}
+
+PrepF16 prep_f16_view(void *base, int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  PrepF16 p;
+  uint8_t *b = static_cast<uint8_t *>(base);
+  p.q = reinterpret_cast<uint16_t *>(b);
+  p.sig = reinterpret_cast<float *>(b + up((size_t)rows * K * 2));
+  return p;
+}
+
+hipError_t launch_prep_f16(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
+                           int64_t rows, int K, const PrepF16 &p, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (f32in && round_bf16)
+    hipLaunchKernelGGL((prep_f16_kernel<true, true>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms,
+                       K, p.q, p.sig);
+  else if (f32in)
+    hipLaunchKernelGGL((prep_f16_kernel<true, false>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms,
+                       K, p.q, p.sig);
+  else
+    hipLaunchKernelGGL((prep_f16_kernel<false, false>), dim3((unsigned)rows), dim3(256), 0, s, src,
+                       nullptr, K, p.q, p.sig);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f16_gateup(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,
+                                     int max_tiles, uint16_t *hb, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nn = m.F / 128;
+  hipLaunchKernelGGL((prefill_f16_kernel<true>), dim3(xcd_grid(max_tiles, nn)), dim3(512), 0, s, m.gate,
+                     m.up, m.D, m.F, a.q, a.sig, 1, m.k, rb, nn, hb, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f16_down(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,
+                                   int max_tiles, uint16_t *o, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nn = m.D / 256;
+  hipLaunchKernelGGL((prefill_f16_kernel<false>), dim3(xcd_grid(max_tiles, nn)), dim3(512), 0, s, m.down,
+                     nullptr, m.F, m.D, a.q, a.sig, 0, m.k, rb, nn, nullptr, o);
+  return hipGetLastError();
+}
+
+}  // namespace ds4q

@@ -37,6 +37,11 @@ hipError_t launch_prefill_i8_gateup(const MoeDims &, const PrepI8 &, int, const 
                                     hipStream_t) STUB()
 hipError_t launch_prefill_i8_down(const MoeDims &, const PrepI8 &, int, const RouteBufs &, int, uint16_t *,
                                   hipStream_t) STUB()
+hipError_t launch_prep_f16(const void *, bool, bool, const float *, int64_t, int, const PrepF16 &, hipStream_t) STUB()
+hipError_t launch_prefill_f16_gateup(const MoeDims &, const PrepF16 &, int, const RouteBufs &, int, uint16_t *,
+                                     hipStream_t) STUB()
+hipError_t launch_prefill_f16_down(const MoeDims &, const PrepF16 &, int, const RouteBufs &, int, uint16_t *,
+                                   hipStream_t) STUB()
 hipError_t launch_prep_d3(const float *, const float *, int64_t, int, int, const PrepD3 &, hipStream_t) STUB()
 hipError_t launch_decode_grouped(const MoeDims &, const PrepD3 &, int, const RouteBufs &, int, float *, int,
                                  hipStream_t) STUB()
@@ -62,6 +67,18 @@ PrepI8 prep_i8_view(void *base, int64_t rows, int K) {
   p.q = b;
   p.x = reinterpret_cast<uint16_t *>(b + up((size_t)rows * nb * 512));
   p.sig = reinterpret_cast<float *>(b + up((size_t)rows * nb * 512) + up((size_t)rows * nb * 64));
+  return p;
+}
+size_t prep_f16_bytes(int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  return up((size_t)rows * K * 2) + up((size_t)rows * 4);
+}
+PrepF16 prep_f16_view(void *base, int64_t rows, int K) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  uint8_t *b = static_cast<uint8_t *>(base);
+  PrepF16 p;
+  p.q = reinterpret_cast<uint16_t *>(b);
+  p.sig = reinterpret_cast<float *>(b + up((size_t)rows * K * 2));
   return p;
 }
 size_t prep_d3_bytes(int64_t rows, int K) {
