@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libds4q.so")
 SOURCES = ["abi.cpp", "dequant.hip", "route.hip", "decode.hip", "decode_mfma.hip", "prefill.hip",
-           "prefill_i8.hip", "prefill_f16.hip", "steer_codec.hip", "imatrix.hip",
+           "prefill_f16.hip", "steer_codec.hip", "imatrix.hip",
            "decode_q41.hip", "decode_grouped.hip", "scratch.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of every kernel (the compiler would

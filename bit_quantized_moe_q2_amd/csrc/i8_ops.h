@@ -1,16 +1,11 @@
-// Int8 matrix-core operands of Q2_K weights (shared by the prefill GEMMs,
-// prefill_i8.hip, and the expert-grouped decode, decode_grouped.hip) and the
-// two-digit activation rows of the prefill GEMMs.
+// Q2_K block loads shared by the matrix-core kernels that stream Q2_K weight
+// rows (the expert-grouped decode, decode_grouped.hip, and the fp16 prefill
+// GEMMs, prefill_f16.hip), and the int8 B operands of the grouped decode.
 //
 // Arithmetic (block layout of "【#2】ds4.c 해독하기", Q2_K table): one
 // 256-value block of a weight row dotted with an activation row a is
 //   d * sum_v (sc*q)_v a_v  -  dmin * sum_s mn_s A_s,
-// A_s the sums of a over the 16 sub-blocks.  An activation row is prepared
-// once (prep_i8_kernel): sigma = max|a| / 127 over the row, N = round(a /
-// sigma * 256) as balanced base-256 digits a0 (high) and a1 (low), both int8,
-// and A_s / sigma as two bf16 halves hi + lo.  Per (row, block) the prepared
-// row holds QROW digit bytes [digit][chunk c = 4j + g][16 bytes] and XROW
-// bytes of sums [hi | lo][16 sub-blocks].
+// A_s the sums of a over the 16 sub-blocks.
 #pragma once
 #include "common.h"
 
@@ -22,22 +17,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int QROW = 512;  // digit bytes of one row's 256-column block
-constexpr int XROW = 64;   // hi/lo sub-block sums (bf16) of one row's block
 
 // 24-bit unsigned multiply (full-rate v_mul_u32_u24; both operands < 2^24).
 __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
   uint32_t r;
   asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // The bytes of one Q2_K block that lane group g uses: code quarter g
@@ -119,73 +105,6 @@ struct WTab {
     b.z = (int)__builtin_amdgcn_perm(0u, tab[2], (w >> 4) & 0x03030303u);
     b.w = (int)__builtin_amdgcn_perm(0u, tab[3], (w >> 6) & 0x03030303u);
     return b;
-  }
-};
-
-// Min-term and scale operands of the block.
-template <bool EXACT_MIN>
-struct WMin {
-  bf16x8 bmin;   // -dmin * mn of sub-blocks 8(g>>1)..8(g>>1)+7, rounded to bf16
-  s16x4 bminlo;  // EXACT_MIN: the rounding residues of sub-blocks 4g..4g+3 (bf16)
-  float dsc;     // d / 256
-  __device__ __forceinline__ void build(const Q2KPart &r, int g) {
-    const float nd = -f16hi(r.dd);
-    const uint32_t m0 = (r.s0 >> 4) & 0x0F0F0F0Fu, m1 = (r.s1 >> 4) & 0x0F0F0F0Fu;
-    const float v[8] = {nd * ub0(m0), nd * ub1(m0), nd * ub2(m0), nd * ub3(m0),
-                        nd * ub0(m1), nd * ub1(m1), nd * ub2(m1), nd * ub3(m1)};
-    const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7])};
-    bmin = __builtin_bit_cast(bf16x8, pk);
-    if constexpr (EXACT_MIN) {
-      // residues of the lane's sub-blocks 4g..4g+3 (= 8(g>>1) + 4(g&1) + i);
-      // one select per value (an index into v[] would become select chains)
-      const bool hi = g & 1;
-      const float q0 = hi ? v[4] : v[0], q1 = hi ? v[5] : v[1], q2 = hi ? v[6] : v[2], q3 = hi ? v[7] : v[3];
-      const uint32_t h01 = hi ? pk.z : pk.x, h23 = hi ? pk.w : pk.y;
-      const uint32_t l01 = pack_bf16x2(q0 - bf16_to_f32(h01 & 0xFFFFu), q1 - bf16_to_f32(h01 >> 16));
-      const uint32_t l23 = pack_bf16x2(q2 - bf16_to_f32(h23 & 0xFFFFu), q3 - bf16_to_f32(h23 >> 16));
-      bminlo = __builtin_bit_cast(s16x4, ((unsigned long long)l23 << 32) | l01);
-    }
-    dsc = f16lo(r.dd) * (1.0f / 256.0f);
-  }
-};
-
-// All operands of the block at once.
-template <bool EXACT_MIN>
-struct WOps : WMin<EXACT_MIN> {
-  i32x4 b[4];  // integer B fragments of K-tiles 0..3
-  __device__ __forceinline__ void build(const Q2KPart &r, int g) {
-    WTab t;
-    t.build(r, g);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = t.bfrag(r, j);
-    WMin<EXACT_MIN>::build(r, g);
-  }
-  // Ends the operands' computation here: compiler passes may otherwise sink
-  // it next to its uses, i.e. into a fenced MFMA group (scheduling barriers
-  // do not hold pure arithmetic back; a volatile asm that takes the values
-  // does).
-  __device__ __forceinline__ void pin() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(b[j]));
-    asm volatile("" : "+v"(this->bmin), "+v"(this->dsc));
-  }
-  // The same in two parts: the integer fragments and d first (pinned), the
-  // min operand later (build_min), so that the first MFMAs need not wait
-  // for it.
-  __device__ __forceinline__ void build_int(const Q2KPart &r, int g) {
-    WTab t;
-    t.build(r, g);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = t.bfrag(r, j);
-    this->dsc = f16lo(r.dd) * (1.0f / 256.0f);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(b[j]));
-    asm volatile("" : "+v"(this->dsc));
-  }
-  __device__ __forceinline__ void build_min(const Q2KPart &r, int g) {
-    WMin<EXACT_MIN>::build(r, g);
-    asm volatile("" : "+v"(this->bmin));
   }
 };
 

@@ -83,24 +83,6 @@ hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, co
 hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, const RouteBufs &rb,
                                int max_tiles, uint16_t *ob, hipStream_t s);
 
-// Prefill on Q2_K weights, int8 matrix cores: activation rows prepared as
-// two int8 digits per value (MFMA fragment order), hi/lo bf16 sub-block sums
-// and a per-row scale.
-struct PrepI8 {
-  uint8_t *q;    // [rows][K/256][2][256]
-  uint16_t *x;   // [rows][K/256][2][16] bf16
-  float *sig;    // [rows]
-};
-size_t prep_i8_bytes(int64_t rows, int K);
-PrepI8 prep_i8_view(void *base, int64_t rows, int K);
-// src: f32 (f32in; times inv_rms[row] when given, then rounded to bf16 when
-// round_bf16) or bf16 rows [rows][K].
-hipError_t launch_prep_i8(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
-                          int64_t rows, int K, const PrepI8 &p, hipStream_t s);
-hipError_t launch_prefill_i8_gateup(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                    int max_tiles, uint16_t *hb, hipStream_t s);
-hipError_t launch_prefill_i8_down(const MoeDims &m, const PrepI8 &a, int T, const RouteBufs &rb,
-                                  int max_tiles, uint16_t *ob, hipStream_t s);
 // Prefill on Q2_K weights, fp16 matrix cores (prefill_f16.hip): activation
 // rows scaled per row by a power of two and stored as fp16 in the MFMA
 // fragment order, with the factor that undoes the scaling.
@@ -110,7 +92,8 @@ struct PrepF16 {
 };
 size_t prep_f16_bytes(int64_t rows, int K);
 PrepF16 prep_f16_view(void *base, int64_t rows, int K);
-// src as for launch_prep_i8.
+// src: f32 (f32in; times inv_rms[row] when given, then rounded to bf16 when
+// round_bf16) or bf16 rows [rows][K].
 hipError_t launch_prep_f16(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
                            int64_t rows, int K, const PrepF16 &p, hipStream_t s);
 hipError_t launch_prefill_f16_gateup(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,

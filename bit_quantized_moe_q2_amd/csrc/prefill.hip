@@ -1,5 +1,5 @@
 // Prefill path on Q4_1 weights: grouped GEMMs over experts on gfx950 bf16
-// matrix cores.  (Q2_K weights take the int8 path in prefill_i8.hip.)
+// matrix cores.  (Q2_K weights take the fp16 path in prefill_f16.hip.)
 //
 // The pairs (token, slot) are grouped by expert (route.hip); the m-tile list
 // holds up to PREFILL_TILE_M consecutive sorted pairs of one expert.  For one

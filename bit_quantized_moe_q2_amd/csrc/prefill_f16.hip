@@ -163,8 +163,14 @@ struct FCtx {
 };
 
 // The block loop for NP live 16-token groups (tokens >= 16*NP are absent):
-// acc[i][t] += the products of blocks 0..nb-1.
-template <int NP, int NPMAX>
+// acc[i][t] += the products of blocks 0..nb-1.  Each K-tile j has a vector
+// phase (the A fragments of K-tile j + 1 from LDS, the lookups that build its
+// B fragments) and a matrix phase (K-tile j's MFMAs as one fenced group).
+// MFIRST (waves 4..7) runs the matrix phase first, the other waves the vector
+// phase first: waves w and w + 4 share a SIMD, and after every block barrier
+// they would otherwise be in the same phase, competing for the vector unit
+// and then for the matrix core, instead of one using each.
+template <int NP, int NPMAX, bool MFIRST>
 __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uint8_t *As1,
                                                f32x4 (&acc)[NPMAX][2]) {
   const int w = cx.w, g = cx.g, nb = cx.nb, lane = cx.lane;
@@ -222,19 +228,36 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
       tb[t].template build<0>(sa0[t], sa1[t], sd[t], sm[t]);
     }
     const int kn = kb + 1 < nb ? kb + 1 : nb - 1, kw = kb + 2 < nb ? kb + 2 : nb - 1;
-    // Per K-tile j: the requests of this step, then the next K-tile's A
-    // fragments (LDS reads) and B fragments (table lookups; a sub-block's
-    // tables just before its first K-tile), then K-tile j's MFMAs as one
-    // fenced group.  So each wave alternates a vector phase and a matrix
-    // phase, and the two waves of a SIMD overlap one's with the other's.
+    // Per K-tile j: the requests of this step, then the two phases in the
+    // wave's order; a sub-block's tables are built just before its first
+    // K-tile's lookups.
     f16x8 a[2][NP], b[2][2];
 #pragma unroll
     for (int i = 0; i < NP; ++i) a[0][i] = *reinterpret_cast<const f16x8 *>(As + cx.aoff[0] + i * 16 * HROW);
     b[0][0] = tb[0].template bfrag<0>(q[0]);
     b[0][1] = tb[1].template bfrag<0>(q[1]);
+#define VPART(J)                                                                                  \
+      if ((J) < 7) {                                                                              \
+        constexpr int JN = ((J) + 1) & 7;                                                         \
+        _Pragma("unroll") for (int i = 0; i < NP; ++i) a[((J) & 1) ^ 1][i] =                      \
+            *reinterpret_cast<const f16x8 *>(As + cx.aoff[JN & 3] + (JN >> 2) * 256 + i * 16 * HROW); \
+        if ((JN & 1) == 0) {                                                                      \
+          _Pragma("unroll") for (int t = 0; t < 2; ++t)                                           \
+            tb[t].template build<(JN >> 1)>(sa0[t], sa1[t], sd[t], sm[t]);                        \
+        }                                                                                         \
+        b[((J) & 1) ^ 1][0] = tb[0].template bfrag<JN>(q[0]);                                     \
+        b[((J) & 1) ^ 1][1] = tb[1].template bfrag<JN>(q[1]);                                     \
+      }
+#define MPART(J)                                                                                  \
+      mfma_group_begin();                                                                         \
+      _Pragma("unroll") for (int i = 0; i < NP; ++i) {                                            \
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[(J) & 1][i], b[(J) & 1][0], acc[i][0], 0, 0, 0); \
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[(J) & 1][i], b[(J) & 1][1], acc[i][1], 0, 0, 0); \
+      }                                                                                           \
+      mfma_fence();
 #define DS4Q_F16_KTILE(J)                                                                         \
     {                                                                                             \
-      constexpr int C = (J) & 1, U0 = (2 * NP * (J)) / 8, U1 = (2 * NP * ((J) + 1)) / 8;          \
+      constexpr int U0 = (2 * NP * (J)) / 8, U1 = (2 * NP * ((J) + 1)) / 8;                        \
       __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                               \
       _Pragma("unroll") for (int u = U0; u < U1; ++u) issue_a(u, kn, An);                         \
       if ((J) == 7) {                                                                             \
@@ -242,23 +265,7 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
         issue_w(kw, r);                                                                           \
       }                                                                                           \
       __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                               \
-      if ((J) < 7) {                                                                              \
-        constexpr int JN = ((J) + 1) & 7;                                                         \
-        _Pragma("unroll") for (int i = 0; i < NP; ++i) a[C ^ 1][i] =                              \
-            *reinterpret_cast<const f16x8 *>(As + cx.aoff[JN & 3] + (JN >> 2) * 256 + i * 16 * HROW); \
-        if ((JN & 1) == 0) {                                                                      \
-          _Pragma("unroll") for (int t = 0; t < 2; ++t)                                           \
-            tb[t].template build<(JN >> 1)>(sa0[t], sa1[t], sd[t], sm[t]);                        \
-        }                                                                                         \
-        b[C ^ 1][0] = tb[0].template bfrag<JN>(q[0]);                                             \
-        b[C ^ 1][1] = tb[1].template bfrag<JN>(q[1]);                                             \
-      }                                                                                           \
-      mfma_group_begin();                                                                         \
-      _Pragma("unroll") for (int i = 0; i < NP; ++i) {                                            \
-        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[C][i], b[C][0], acc[i][0], 0, 0, 0); \
-        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[C][i], b[C][1], acc[i][1], 0, 0, 0); \
-      }                                                                                           \
-      mfma_fence();                                                                               \
+      if constexpr (MFIRST) { MPART(J) VPART(J) } else { VPART(J) MPART(J) }                      \
     }
     DS4Q_F16_KTILE(0)
     DS4Q_F16_KTILE(1)
@@ -269,6 +276,8 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
     DS4Q_F16_KTILE(6)
     DS4Q_F16_KTILE(7)
 #undef DS4Q_F16_KTILE
+#undef VPART
+#undef MPART
     // Each wave waits for its own tile requests and LDS reads; then the
     // barrier alone publishes the tile (a workgroup fence would also wait
     // for the weight requests still in flight).
@@ -354,15 +363,28 @@ __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  switch (np) {
-    case 1: block_loop_f16<1, NGF>(cx, As0, As1, acc); break;
-    case 2: block_loop_f16<2, NGF>(cx, As0, As1, acc); break;
-    case 3: block_loop_f16<3, NGF>(cx, As0, As1, acc); break;
-    case 4: block_loop_f16<4, NGF>(cx, As0, As1, acc); break;
-    case 5: block_loop_f16<5, NGF>(cx, As0, As1, acc); break;
-    case 6: block_loop_f16<6, NGF>(cx, As0, As1, acc); break;
-    case 7: block_loop_f16<7, NGF>(cx, As0, As1, acc); break;
-    default: block_loop_f16<8, NGF>(cx, As0, As1, acc); break;
+  if (cx.w >= 4) {
+    switch (np) {
+      case 1: block_loop_f16<1, NGF, true>(cx, As0, As1, acc); break;
+      case 2: block_loop_f16<2, NGF, true>(cx, As0, As1, acc); break;
+      case 3: block_loop_f16<3, NGF, true>(cx, As0, As1, acc); break;
+      case 4: block_loop_f16<4, NGF, true>(cx, As0, As1, acc); break;
+      case 5: block_loop_f16<5, NGF, true>(cx, As0, As1, acc); break;
+      case 6: block_loop_f16<6, NGF, true>(cx, As0, As1, acc); break;
+      case 7: block_loop_f16<7, NGF, true>(cx, As0, As1, acc); break;
+      default: block_loop_f16<8, NGF, true>(cx, As0, As1, acc); break;
+    }
+  } else {
+    switch (np) {
+      case 1: block_loop_f16<1, NGF, false>(cx, As0, As1, acc); break;
+      case 2: block_loop_f16<2, NGF, false>(cx, As0, As1, acc); break;
+      case 3: block_loop_f16<3, NGF, false>(cx, As0, As1, acc); break;
+      case 4: block_loop_f16<4, NGF, false>(cx, As0, As1, acc); break;
+      case 5: block_loop_f16<5, NGF, false>(cx, As0, As1, acc); break;
+      case 6: block_loop_f16<6, NGF, false>(cx, As0, As1, acc); break;
+      case 7: block_loop_f16<7, NGF, false>(cx, As0, As1, acc); break;
+      default: block_loop_f16<8, NGF, false>(cx, As0, As1, acc); break;
+    }
   }
   // the accumulators are read below; no instruction rewrites them until the
   // last MFMAs have read them

@@ -32,11 +32,6 @@ hipError_t launch_prefill_gateup(const MoeDims &, const uint16_t *, int, const R
                                  hipStream_t) STUB()
 hipError_t launch_prefill_down(const MoeDims &, const uint16_t *, int, const RouteBufs &, int, uint16_t *,
                                hipStream_t) STUB()
-hipError_t launch_prep_i8(const void *, bool, bool, const float *, int64_t, int, const PrepI8 &, hipStream_t) STUB()
-hipError_t launch_prefill_i8_gateup(const MoeDims &, const PrepI8 &, int, const RouteBufs &, int, uint16_t *,
-                                    hipStream_t) STUB()
-hipError_t launch_prefill_i8_down(const MoeDims &, const PrepI8 &, int, const RouteBufs &, int, uint16_t *,
-                                  hipStream_t) STUB()
 hipError_t launch_prep_f16(const void *, bool, bool, const float *, int64_t, int, const PrepF16 &, hipStream_t) STUB()
 hipError_t launch_prefill_f16_gateup(const MoeDims &, const PrepF16 &, int, const RouteBufs &, int, uint16_t *,
                                      hipStream_t) STUB()
@@ -54,21 +49,6 @@ static unsigned char g_scratch[DS4Q_SCRATCH_BYTES];
 hipError_t scratch_address(void **out) { *out = g_scratch; return hipSuccess; }
 
 // the workspace layout of the prep rows (as in the library)
-size_t prep_i8_bytes(int64_t rows, int K) {
-  const size_t nb = (size_t)K / 256;
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  return up((size_t)rows * nb * 512) + up((size_t)rows * nb * 64) + up((size_t)rows * 4);
-}
-PrepI8 prep_i8_view(void *base, int64_t rows, int K) {
-  const size_t nb = (size_t)K / 256;
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  uint8_t *b = static_cast<uint8_t *>(base);
-  PrepI8 p;
-  p.q = b;
-  p.x = reinterpret_cast<uint16_t *>(b + up((size_t)rows * nb * 512));
-  p.sig = reinterpret_cast<float *>(b + up((size_t)rows * nb * 512) + up((size_t)rows * nb * 64));
-  return p;
-}
 size_t prep_f16_bytes(int64_t rows, int K) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   return up((size_t)rows * K * 2) + up((size_t)rows * 4);
