@@ -45,6 +45,10 @@ constexpr int TMF = PREFILL_TILE_M;  // tokens (sorted pairs) per m-tile
 constexpr int NGF = TMF / 16;        // MFMA row groups of 16 tokens
 constexpr int HROW = 512;            // fp16 bytes of one row's 256-value block
 constexpr int HSTAGE = TMF * HROW;   // LDS bytes of one activation stage
+// consecutive n-tiles of one m-tile per work item (fewer when the matrix has
+// fewer): the next n-tile's first blocks are requested during the current
+// one's last, so only an item's first n-tile waits for its start-up
+constexpr int NTILES_PER_ITEM = 2;
 static_assert(TMF % 16 == 0 && TMF <= 128, "m-tile must be a multiple of 16, at most 128");
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
@@ -158,30 +162,38 @@ struct FCtx {
   const int *arow;         // LDS: source row of each of the tile's TMF tokens
   int rbase;               // 0 (gathered token rows) or the tile's first sorted row
   const uint8_t *brow[2];  // weight rows of the two n-subtiles (lane's row)
+  int64_t nstride;         // bytes from a weight row to the same row of the next n-tile
   uint32_t aoff[4];        // LDS offsets of the lane's A chunks, K-tiles 0..3 (+256 for 4..7)
-  int nb, w, g, lane;      // w wave-uniform
+  int nb, nvt, w, g, lane; // nvt = blocks of all the item's n-tiles; w wave-uniform
 };
 
-// The block loop for NP live 16-token groups (tokens >= 16*NP are absent):
-// acc[i][t] += the products of blocks 0..nb-1.  Each K-tile j has a vector
+// The block loop for NP live 16-token groups (tokens >= 16*NP are absent)
+// over the item's n-tiles one after the other: nvt = n-tiles * nb blocks in
+// one stream, v = nt * nb + kb; after the last block of n-tile nt, epi(nt)
+// stores acc and acc restarts at zero.  The requests run two blocks ahead
+// across n-tile boundaries (the activation rows are the same, the weight
+// rows move by nstride), so only the item's first n-tile waits for its first
+// blocks.  Each K-tile j has a vector
 // phase (the A fragments of K-tile j + 1 from LDS, the lookups that build its
 // B fragments) and a matrix phase (K-tile j's MFMAs as one fenced group).
 // MFIRST (waves 4..7) runs the matrix phase first, the other waves the vector
 // phase first: waves w and w + 4 share a SIMD, and after every block barrier
 // they would otherwise be in the same phase, competing for the vector unit
 // and then for the matrix core, instead of one using each.
-template <int NP, int NPMAX, bool MFIRST>
+template <int NP, int NPMAX, bool MFIRST, class EPI>
 __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uint8_t *As1,
-                                               f32x4 (&acc)[NPMAX][2]) {
-  const int w = cx.w, g = cx.g, nb = cx.nb, lane = cx.lane;
+                                               f32x4 (&acc)[NPMAX][2], const EPI &epi) {
+  const int w = cx.w, g = cx.g, nb = cx.nb, nvt = cx.nvt, lane = cx.lane;
   // Activation requests per block: waves 0..3 issue the 2*NP row-pair loads
   // (load I = 4u + w covers token rows 2I, 2I+1; lane -> row 2I + lane/32,
   // stored chunk lane%32 = data chunk (lane%32) ^ (row%16)), so the MFMAs of
-  // waves 4..7 on the same SIMDs run while they issue; every wave issues the
-  // raw weight bytes of its two n-subtiles last, so the block-end wait count
-  // is exact for both kinds of wave.  Offsets are relative to row rbase
+  // waves 4..7 on the same SIMDs run while they issue; every wave requests
+  // the raw weight bytes of its two n-subtiles for the next block at the
+  // start of a block, and the block ends waiting for all of its requests.
+  // Offsets are relative to row rbase
   // (gathered token rows: < 2^29 bytes).  Blocks past the end are requested
-  // again as the last block, so the loop has no branches.
+  // again as the last block, so the loop has no branches.  Requests name
+  // virtual blocks v.
   const int64_t rowq = (int64_t)nb * HROW;
   uint32_t aoffs[2 * NP];
 #pragma unroll
@@ -192,27 +204,28 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
     aoffs[u] = (uint32_t)((cx.arow[r] - cx.rbase) * rowq) + c * 16;
   }
   const DmaSrc asrc(cx.abase);
-  auto issue_a = [&](int u, int kb, uint8_t *As) {
-    if (w < 4) asrc.copy16(aoffs[u], (uint32_t)kb * HROW, As + (4 * u + w) * 1024);
+  auto issue_a = [&](int u, int v, uint8_t *As) {
+    if (w < 4) asrc.copy16(aoffs[u], (uint32_t)(v % nb) * HROW, As + (4 * u + w) * 1024);
   };
-  auto issue_w = [&](int kb, RawBlk (&r)[2]) {
+  auto issue_w = [&](int v, RawBlk (&r)[2]) {
+    const int64_t off = (int64_t)(v / nb) * cx.nstride + (int64_t)(v % nb) * BB_Q2K;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t] + (int64_t)kb * BB_Q2K, g);
+    for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t] + off, g);
   };
 
-  constexpr int NWLD = 4;  // weight load instructions per block: 2 x (16 + 8 bytes)
-  RawBlk rw[2][2];
+  // One set of raw weight registers: a block's bytes are taken apart at its
+  // start, and the next block's are requested right after, a whole block
+  // ahead of their use.
+  RawBlk rw[2];
 #pragma unroll
   for (int u = 0; u < 2 * NP; ++u) issue_a(u, 0, As0);
-  issue_w(0, rw[0]);
-  issue_w(nb > 1 ? 1 : 0, rw[1]);
+  issue_w(0, rw);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
   auto step = [&](int kb, RawBlk (&r)[2], const uint8_t *As, uint8_t *An) {
     // this block's operands: the code bytes, and per weight row the scale /
-    // min bytes of the lane's sub-blocks and d|dmin; then r is free for block
-    // kb + 2
+    // min bytes of the lane's sub-blocks and d|dmin; then r takes block kb + 1
     u32x4 q[2];
     uint32_t sa0[2], sa1[2];
     float sd[2], sm[2];
@@ -227,7 +240,10 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
       sm[t] = f16hi(o.dd);
       tb[t].template build<0>(sa0[t], sa1[t], sd[t], sm[t]);
     }
-    const int kn = kb + 1 < nb ? kb + 1 : nb - 1, kw = kb + 2 < nb ? kb + 2 : nb - 1;
+    const int kn = kb + 1 < nvt ? kb + 1 : nvt - 1;
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(kn, r);
+    __builtin_amdgcn_sched_barrier(0);
     // Per K-tile j: the requests of this step, then the two phases in the
     // wave's order; a sub-block's tables are built just before its first
     // K-tile's lookups.
@@ -260,10 +276,6 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
       constexpr int U0 = (2 * NP * (J)) / 8, U1 = (2 * NP * ((J) + 1)) / 8;                        \
       __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                               \
       _Pragma("unroll") for (int u = U0; u < U1; ++u) issue_a(u, kn, An);                         \
-      if ((J) == 7) {                                                                             \
-        __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                             \
-        issue_w(kw, r);                                                                           \
-      }                                                                                           \
       __builtin_amdgcn_sched_barrier(SCHED_NOVMEM);                                               \
       if constexpr (MFIRST) { MPART(J) VPART(J) } else { VPART(J) MPART(J) }                      \
     }
@@ -282,21 +294,39 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
     // barrier alone publishes the tile (a workgroup fence would also wait
     // for the weight requests still in flight).
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0070 | NWLD);  // vmcnt(NWLD) lgkmcnt(0): tile of kb+1 landed
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): tile and weights of kb+1 landed
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // nb is a power of two; the loop body is exactly two blocks, so every path
-  // into a block leaves the same requests outstanding
+  // after the last block of an n-tile: its results out, the sums restarted
+  auto ntile_end = [&](int v) {
+    if ((v + 1) % nb == 0) {
+      mfma_fence();
+      epi(v / nb);
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // nb is a power of two and nvt is 1 or even; the loop body is exactly two
+  // blocks, so every path into a block leaves the same requests outstanding,
+  // and with nb >= 2 an n-tile ends after the second of them
   if (nb == 1) {
-    step(0, rw[0], As0, As1);
+    step(0, rw, As0, As1);
+    ntile_end(0);
+    if (nvt == 2) {
+      step(1, rw, As1, As0);
+      ntile_end(1);
+    }
   } else {
-    for (int kb = 0; kb < nb; kb += 2) {
-      step(kb, rw[0], As0, As1);
-      step(kb + 1, rw[1], As1, As0);
+    for (int v = 0; v < nvt; v += 2) {
+      step(v, rw, As0, As1);
+      step(v + 1, rw, As1, As0);
+      ntile_end(v + 1);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no request outlives the loop
@@ -304,19 +334,23 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
 
 // SWIGLU: an n-tile is 128 rows of F; wave w owns rows 16w..16w+15 of both
 // gate (t = 0) and up (t = 1).  Otherwise an n-tile is 256 down rows, wave w
-// owning rows 32w + 16t .. +15.  Eight waves; m-tile = up to TMF sorted pairs
-// of one expert.  SwiGLU rows are written as bf16 (hb), down rows as bf16 (o).
+// owning rows 32w + 16t .. +15.  Eight waves; a work item is an m-tile (up to
+// TMF sorted pairs of one expert) and ntper consecutive n-tiles, run as one
+// block stream.  SwiGLU rows are written as bf16 (hb), down rows as bf16 (o).
 template <bool SWIGLU>
 __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint16_t *__restrict__ aq, const float *__restrict__ asig, int gather_tokens, int kslots,
-    RouteBufs rb, int n_ntiles, uint16_t *__restrict__ hb, uint16_t *__restrict__ o) {
+    RouteBufs rb, int n_groups, int ntper, uint16_t *__restrict__ hb, uint16_t *__restrict__ o) {
+  constexpr int NTROWS = SWIGLU ? 128 : 256;  // weight rows of one matrix per n-tile
   __shared__ __attribute__((aligned(1024))) uint8_t As0[HSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[HSTAGE];
   __shared__ int arow[TMF];
+  __shared__ float asg[TMF];
 
-  int mtile, ntile;
-  if (!xcd_tile_of(*rb.n_tiles, n_ntiles, &mtile, &ntile)) return;
+  int mtile, ngrp;
+  if (!xcd_tile_of(*rb.n_tiles, n_groups, &mtile, &ngrp)) return;
+  const int ntile0 = ngrp * ntper;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -327,12 +361,15 @@ __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
 
   if (tid < TMF) {
     const int m = tid < valid ? tid : 0;  // absent rows repeat row 0; never stored
-    arow[tid] = gather_tokens ? rb.pairs[start + m] / kslots : start + m;
+    const int r = gather_tokens ? rb.pairs[start + m] / kslots : start + m;
+    arow[tid] = r;
+    asg[tid] = asig[r];
   }
   __syncthreads();
 
   FCtx cx;
   cx.nb = K >> 8;
+  cx.nvt = ntper * cx.nb;
   cx.w = __builtin_amdgcn_readfirstlane(w);
   cx.g = g;
   cx.lane = lane;
@@ -340,14 +377,15 @@ __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
   cx.rbase = gather_tokens ? 0 : start;
   cx.abase = reinterpret_cast<const uint8_t *>(aq) + (int64_t)cx.rbase * cx.nb * HROW;
   const int64_t rbytes = (int64_t)cx.nb * BB_Q2K;
+  cx.nstride = NTROWS * rbytes;
   int wrow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if constexpr (SWIGLU) {
-      wrow[t] = ntile * 128 + 16 * w + n;
+      wrow[t] = ntile0 * 128 + 16 * w + n;
       cx.brow[t] = (t == 0 ? W0 : W1) + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
     } else {
-      wrow[t] = ntile * 256 + 32 * w + 16 * t + n;
+      wrow[t] = ntile0 * 256 + 32 * w + 16 * t + n;
       cx.brow[t] = W0 + ((int64_t)e * rows_per_expert + wrow[t]) * rbytes;
     }
   }
@@ -363,51 +401,57 @@ __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[i][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  // n-tile nt of the item done: lane (g, n) holds, for group i, rows
+  // q = 0..3 = tokens 16i + 4g + q of weight row n of each n-subtile t
+  // (the caller has fenced the last MFMAs)
+  // Stores go through the uniform row base of the tile and 32-bit per-lane
+  // offsets (fewer live registers inside the block loop).
+  uint16_t *const obase = (SWIGLU ? hb : o) + (int64_t)start * rows_per_expert;
+  auto epi = [&](int nt) {
+    const uint32_t r0 = (uint32_t)(wrow[0] + nt * NTROWS);
+#pragma unroll
+    for (int i = 0; i < NGF; ++i) {
+      if (i >= np) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 16 * i + 4 * g + q;
+        if (m >= valid) continue;
+        const float sg = asg[m];
+        const uint32_t off = (uint32_t)m * (uint32_t)rows_per_expert + r0;
+        const float v0 = acc[i][0][q] * sg, v1 = acc[i][1][q] * sg;
+        if constexpr (SWIGLU) {
+          // silu(v0) * v1 with a hardware reciprocal: the result is rounded to bf16
+          const float sl = v0 * __builtin_amdgcn_rcpf(1.0f + __expf(-v0));
+          obase[off] = (uint16_t)bf16_rne_bits(sl * v1);
+        } else {
+          // the second subtile's row is r0 + 16; lanes n, n ^ 1 share g, hence m and validity
+          store_bf16_row_pair(obase + off, n, v0, v1);
+        }
+      }
+    }
+  };
+
   if (cx.w >= 4) {
     switch (np) {
-      case 1: block_loop_f16<1, NGF, true>(cx, As0, As1, acc); break;
-      case 2: block_loop_f16<2, NGF, true>(cx, As0, As1, acc); break;
-      case 3: block_loop_f16<3, NGF, true>(cx, As0, As1, acc); break;
-      case 4: block_loop_f16<4, NGF, true>(cx, As0, As1, acc); break;
-      case 5: block_loop_f16<5, NGF, true>(cx, As0, As1, acc); break;
-      case 6: block_loop_f16<6, NGF, true>(cx, As0, As1, acc); break;
-      case 7: block_loop_f16<7, NGF, true>(cx, As0, As1, acc); break;
-      default: block_loop_f16<8, NGF, true>(cx, As0, As1, acc); break;
+      case 1: block_loop_f16<1, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 2: block_loop_f16<2, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 3: block_loop_f16<3, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 4: block_loop_f16<4, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 5: block_loop_f16<5, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 6: block_loop_f16<6, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 7: block_loop_f16<7, NGF, true>(cx, As0, As1, acc, epi); break;
+      default: block_loop_f16<8, NGF, true>(cx, As0, As1, acc, epi); break;
     }
   } else {
     switch (np) {
-      case 1: block_loop_f16<1, NGF, false>(cx, As0, As1, acc); break;
-      case 2: block_loop_f16<2, NGF, false>(cx, As0, As1, acc); break;
-      case 3: block_loop_f16<3, NGF, false>(cx, As0, As1, acc); break;
-      case 4: block_loop_f16<4, NGF, false>(cx, As0, As1, acc); break;
-      case 5: block_loop_f16<5, NGF, false>(cx, As0, As1, acc); break;
-      case 6: block_loop_f16<6, NGF, false>(cx, As0, As1, acc); break;
-      case 7: block_loop_f16<7, NGF, false>(cx, As0, As1, acc); break;
-      default: block_loop_f16<8, NGF, false>(cx, As0, As1, acc); break;
-    }
-  }
-  // the accumulators are read below; no instruction rewrites them until the
-  // last MFMAs have read them
-  mfma_fence();
-
-  // epilogue: lane (g, n) holds, for group i, rows q = 0..3 = tokens
-  // 16i + 4g + q of weight row n of each n-subtile t
-#pragma unroll
-  for (int i = 0; i < NGF; ++i) {
-    if (i >= np) break;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int m = 16 * i + 4 * g + q;
-      if (m >= valid) continue;
-      const float sg = asig[arow[m]];
-      const int64_t pos = start + m;
-      const float v0 = acc[i][0][q] * sg, v1 = acc[i][1][q] * sg;
-      if constexpr (SWIGLU) {
-        hb[pos * rows_per_expert + wrow[0]] = (uint16_t)bf16_rne_bits(silu(v0) * v1);
-      } else {
-        // wrow[1] = wrow[0] + 16; lanes n, n ^ 1 share g, hence m and validity
-        store_bf16_row_pair(o + pos * rows_per_expert + wrow[0], n, v0, v1);
-      }
+      case 1: block_loop_f16<1, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 2: block_loop_f16<2, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 3: block_loop_f16<3, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 4: block_loop_f16<4, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 5: block_loop_f16<5, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 6: block_loop_f16<6, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 7: block_loop_f16<7, NGF, false>(cx, As0, As1, acc, epi); break;
+      default: block_loop_f16<8, NGF, false>(cx, As0, As1, acc, epi); break;
     }
   }
 }
@@ -446,18 +490,18 @@ hipError_t launch_prep_f16(const void *src, bool f32in, bool round_bf16, const f
 hipError_t launch_prefill_f16_gateup(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,
                                      int max_tiles, uint16_t *hb, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int nn = m.F / 128;
-  hipLaunchKernelGGL((prefill_f16_kernel<true>), dim3(xcd_grid(max_tiles, nn)), dim3(512), 0, s, m.gate,
-                     m.up, m.D, m.F, a.q, a.sig, 1, m.k, rb, nn, hb, nullptr);
+  const int nn = m.F / 128, per = nn >= NTILES_PER_ITEM ? NTILES_PER_ITEM : nn;
+  hipLaunchKernelGGL((prefill_f16_kernel<true>), dim3(xcd_grid(max_tiles, nn / per)), dim3(512), 0, s,
+                     m.gate, m.up, m.D, m.F, a.q, a.sig, 1, m.k, rb, nn / per, per, hb, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_f16_down(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,
                                    int max_tiles, uint16_t *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int nn = m.D / 256;
-  hipLaunchKernelGGL((prefill_f16_kernel<false>), dim3(xcd_grid(max_tiles, nn)), dim3(512), 0, s, m.down,
-                     nullptr, m.F, m.D, a.q, a.sig, 0, m.k, rb, nn, nullptr, o);
+  const int nn = m.D / 256, per = nn >= NTILES_PER_ITEM ? NTILES_PER_ITEM : nn;
+  hipLaunchKernelGGL((prefill_f16_kernel<false>), dim3(xcd_grid(max_tiles, nn / per)), dim3(512), 0, s,
+                     m.down, nullptr, m.F, m.D, a.q, a.sig, 0, m.k, rb, nn / per, per, nullptr, o);
   return hipGetLastError();
 }
 
