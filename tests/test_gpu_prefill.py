@@ -120,6 +120,28 @@ def test_prefill_f32_input_rmsnorm_accumulate(gpu):
     assert report(normwise_err(y - y0, lay.oracle_moe(nb, lg, n_threads=16))) <= TOL_BF16
 
 
+@pytest.mark.parametrize("qt", [10, 3])
+def test_prefill_row_magnitudes(gpu, qt):
+    """Token rows whose magnitudes span 1e-15..1e15, and an all-zero row: the
+    Q2_K path stores each input and SwiGLU row as fp16 under its own
+    power-of-two scale, so every row keeps the same relative precision (a
+    plain fp16 copy would overflow the large rows and flush the small ones)."""
+    ds4q = gpu
+    T, D, F, E = 64, 512, 256, 16
+    lay = SynthLayer(ds4q, DEV, D, F, E, 6, qt, seed=650 + qt)
+    x = synth.x_f32(synth.stream_key(41), T, D)
+    x *= (10.0 ** np.linspace(-15.0, 15.0, T)).astype(np.float32)[:, None]
+    x[T // 2] = 0.0
+    bits = synth.bf16_bits_from_f32(x)
+    xf = (bits.astype(np.uint32) << 16).view(np.float32)
+    lg = synth.logits_normal(synth.stream_key(42), T, E)
+    y, _ = _prefill(ds4q, lay, bits, ds4q.TYPE_BF16, lg, route=False)
+    ref = lay.oracle_moe(xf, lg, n_threads=16)
+    assert np.all(np.isfinite(y))
+    assert np.all(y[T // 2] == 0.0)
+    assert report(normwise_err(y, ref)) <= TOL_BF16
+
+
 # tokens per m-tile of the grouped GEMMs (sorted pairs of one expert)
 PREFILL_TILE_M = 128
 
