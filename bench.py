@@ -49,10 +49,10 @@ DTYPE_I8X3 = "i8x3digit+i8min"     # 2..64-token Q2_K decode: three int8 digits 
                                    # activation, min term exact on int8 matrix cores
 DTYPE_I8X3_Q41 = "i8x3digit+f32offset"  # 2..64-token Q4_1 decode: the same digits, the
                                         # offset term from fp32 sums of 32 inputs
-DTYPE_F16 = "f16"                  # Q2_K prefill: fp16 weights (each rounded once from
-                                   # its exact fp32 value) and fp16 inputs (bf16 values
-                                   # scaled by a power of two), fp32 accumulation
-DTYPE_BF16 = "bf16"                # Q4_1 prefill: bf16 weights and inputs, fp32 accumulation
+DTYPE_F16 = "f16"                  # prefill: fp16 weights (each Q2_K weight rounded once
+                                   # from its exact fp32 value, each Q4_1 weight d*q + m by
+                                   # one fp16 fma) and fp16 inputs (bf16 values scaled by a
+                                   # power of two), fp32 accumulation
 
 
 def log(*a):
@@ -644,7 +644,7 @@ def main():
                 lgu = torch.from_numpy(synth.logits_normal(synth.stream_key(seed, 4), Tp, E)).to(dev)
                 wsq = torch.empty(ds4q.ds4q_moe_workspace_size(q41[0], Tp, 1), dtype=torch.uint8, device=dev)
                 ms = graph_time(lambda: ds4q.ds4q_moe_prefill(q41[0], xbz, ds4q.TYPE_BF16, lgu, Tp, ypz, None, wsq), 10)
-                cf["prefill_4096tok_q4_1_uniform"] = {"dtype": DTYPE_BF16, "ms": round(ms, 4),
+                cf["prefill_4096tok_q4_1_uniform"] = {"dtype": DTYPE_F16, "ms": round(ms, 4),
                                                       "tflops": round(Tp * K * PAIR_FLOPS / (ms / 1e3) / 1e12, 1)}
                 del wsq, lgu
             del wsz, lgz

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libds4q.so")
-SOURCES = ["abi.cpp", "dequant.hip", "route.hip", "decode.hip", "decode_mfma.hip", "prefill.hip",
+SOURCES = ["abi.cpp", "dequant.hip", "route.hip", "decode.hip", "decode_mfma.hip",
            "prefill_f16.hip", "steer_codec.hip", "imatrix.hip",
            "decode_q41.hip", "decode_grouped.hip", "scratch.hip"]
 ARCH = "gfx950"

@@ -54,15 +54,13 @@ struct Workspace {
   uint16_t *ob = nullptr;  // prefill: [T*k][D] bf16 (sorted order)
   float *stage = nullptr;  // decode of one token: [D] f32, the unsteered output before steering
   float *imat_part = nullptr;  // imatrix on m-tiles: [max_tiles][max(D, F)] f32 partial rows
-  uint16_t *xb = nullptr;  // prefill on Q4_1 gate/up: [T][D] bf16
-  PrepF16 xq{}, hq{};      // prefill on Q2_K weights: fp16 rows of x and of hb
+  PrepF16 xq{}, hq{};      // prefill: fp16 rows of x and of hb
   PrepD3 xd{}, hd{};       // decode of 2..64 tokens: int8 digit rows of x and of h
   size_t bytes = 0;
 
-  // mode 1 (prefill): i8_in / i8_h = Q2_K gate/up resp. down (int8 matrix
-  // cores); unused in the other modes
-  Workspace(uint8_t *base, int D, int F, int E, int k, int T, int mode, bool i8_in = false,
-            bool i8_h = false, bool stats = false) {
+  // mode 0 = decode, 1 = prefill, 2 = routing only; stats: the imatrix
+  // partial rows of the prefill
+  Workspace(uint8_t *base, int D, int F, int E, int k, int T, int mode, bool stats = false) {
     size_t off = 0;
     auto take = [&](size_t n) -> void * {
       void *p = base ? base + off : nullptr;
@@ -100,13 +98,10 @@ struct Workspace {
       rb.tiles_sz = (int32_t *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * 8);
       hb = (uint16_t *)take(P * F * 2);
       ob = (uint16_t *)take(P * D * 2);
-      if (!i8_in) xb = (uint16_t *)take((size_t)T * D * 2);
-      if (i8_in) {
+      {
         void *p = take(prep_f16_bytes(T, D));
         if (base) xq = prep_f16_view(p, T, D);
-      }
-      if (i8_h) {
-        void *p = take(prep_f16_bytes(P, F));
+        p = take(prep_f16_bytes(P, F));
         if (base) hq = prep_f16_view(p, P, F);
       }
       if (stats) imat_part = (float *)take((size_t)max_tiles(T, E, k, PREFILL_TILE_M) * (D > F ? D : F) * 4);
@@ -150,18 +145,8 @@ SteerArgs steer_of(const ds4q_moe_layer *L, float *stage) {
   return st;
 }
 
-bool i8_gateup(const ds4q_moe_layer *L) { return L->type_gate == DS4Q_TYPE_Q2_K; }
-bool i8_down(const ds4q_moe_layer *L) { return L->type_down == DS4Q_TYPE_Q2_K; }
 
-// Workspace flags of a call (see Workspace).
-struct WsFlags {
-  bool a, b, stats;
-};
 bool wants_stats(const ds4q_moe_layer *L) { return L->imatrix_in || L->imatrix_down; }
-WsFlags i8_flags(const ds4q_moe_layer *L, int mode) {
-  if (mode == 1) return {i8_gateup(L), i8_down(L), wants_stats(L)};
-  return {false, false, wants_stats(L)};
-}
 
 MoeDims dims_of(const ds4q_moe_layer *L) {
   MoeDims m;
@@ -273,9 +258,7 @@ int check_call(const ds4q_moe_layer *L, const void *x, size_t x_elem, const floa
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, ALIGN) ||
       route_misaligned(route))
     return DS4Q_E_ALIGN;
-  const WsFlags f = i8_flags(L, mode);
-  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b,
-                       f.stats);
+  const Workspace need(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, wants_stats(L));
   if (static_ws) {
     if (need.bytes > DS4Q_SCRATCH_BYTES) return DS4Q_E_SCRATCH;
   } else if (ws_bytes < need.bytes) {
@@ -341,8 +324,7 @@ int run_decode(const ds4q_moe_layer *L, const float *x, const float *logits, int
                const ds4q_route_out *route, void *ws, hipStream_t s, uint32_t flags,
                uint32_t phases = DS4Q_PHASE_ALL) {
   const MoeDims m = dims_of(L);
-  const WsFlags f = i8_flags(L, 0);
-  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0, f.a, f.b, f.stats);
+  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 0, wants_stats(L));
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const SteerArgs st = steer_of(L, w.stage);
   const bool p_route = phases & DS4Q_PHASE_ROUTE, p_gu = phases & DS4Q_PHASE_GATEUP,
@@ -396,37 +378,23 @@ int run_prefill(const ds4q_moe_layer *L, const void *x, int32_t x_type, const fl
                 int32_t T, float *y, const ds4q_route_out *route, void *ws, hipStream_t s,
                 uint32_t flags) {
   const MoeDims m = dims_of(L);
-  const WsFlags f = i8_flags(L, 1);
-  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, f.a, f.b, f.stats);
+  Workspace w(static_cast<uint8_t *>(ws), m.D, m.F, m.E, m.k, T, 1, wants_stats(L));
   const bool norm = flags & DS4Q_F_RMSNORM_INPUT, acc = flags & DS4Q_F_ACCUMULATE;
   const float *xf = x_type == DS4Q_TYPE_F32 ? static_cast<const float *>(x) : nullptr;
   TIMED_TRY("topk", launch_topk(logits, T, m.E, m.k, norm ? xf : nullptr, m.D, L->norm_eps, w.rb, s));
   TIMED_TRY("group", launch_group(T, m.E, m.k, PREFILL_TILE_M, true, w.rb, s));
   const int mt = max_tiles(T, m.E, m.k, PREFILL_TILE_M);
-  if (i8_gateup(L)) {
-    TIMED_TRY("prep_f16", launch_prep_f16(x, xf != nullptr, true, norm && xf ? w.rb.inv_rms : nullptr, T,
-                                          m.D, w.xq, s));
-    TIMED_TRY("prefill_gateup", launch_prefill_f16_gateup(m, w.xq, T, w.rb, mt, w.hb, s));
-  } else {
-    const uint16_t *xb = static_cast<const uint16_t *>(x);
-    if (xf) {
-      TIMED_TRY("prep_bf16", launch_prep_bf16(xf, norm ? w.rb.inv_rms : nullptr, T, m.D, w.xb, s));
-      xb = w.xb;
-    }
-    TIMED_TRY("prefill_gateup", launch_prefill_gateup(m, xb, T, w.rb, mt, w.hb, s));
-  }
+  TIMED_TRY("prep_f16", launch_prep_f16(x, xf != nullptr, true, norm && xf ? w.rb.inv_rms : nullptr, T, m.D,
+                                        m.tg, w.xq, s));
+  TIMED_TRY("prefill_gateup", launch_prefill_f16_gateup(m, w.xq, T, w.rb, mt, w.hb, s));
   {
     ImatRows in = rows_of(x, xf == nullptr, norm && xf ? w.rb.inv_rms : nullptr, false);
     in.round_bf16 = xf != nullptr;  // the expert GEMMs read the bf16 rounding of the f32 input
     if (wants_stats(L)) TIMED_TRY("imatrix", launch_stats(L, m, w, IMAT_SEG_TILES, mt, in, rows_of(w.hb, true, nullptr, true), s));
   }
-  if (i8_down(L)) {
-    const int64_t P = (int64_t)T * m.k;
-    TIMED_TRY("prep_f16", launch_prep_f16(w.hb, false, false, nullptr, P, m.F, w.hq, s));
-    TIMED_TRY("prefill_down", launch_prefill_f16_down(m, w.hq, T, w.rb, mt, w.ob, s));
-  } else {
-    TIMED_TRY("prefill_down", launch_prefill_down(m, w.hb, T, w.rb, mt, w.ob, s));
-  }
+  const int64_t P = (int64_t)T * m.k;
+  TIMED_TRY("prep_f16", launch_prep_f16(w.hb, false, false, nullptr, P, m.F, m.td, w.hq, s));
+  TIMED_TRY("prefill_down", launch_prefill_f16_down(m, w.hq, T, w.rb, mt, w.ob, s));
   TIMED_TRY("combine", launch_combine(w.ob, w.rb, T, m.k, m.D, true, y, acc, steer_of(L, nullptr), s));
   return copy_route(route, w.rb, T, m.E, m.k, s);
 }
@@ -517,9 +485,7 @@ DS4Q_API int ds4q_route(const float *logits, int32_t n_tok, int32_t n_expert, in
 DS4Q_API size_t ds4q_moe_workspace_size(const ds4q_moe_layer *L, int32_t max_tok, int32_t mode) {
   if (check_layer(L) || max_tok < 0 || (mode != 0 && mode != 1)) return 0;
   const int T = max_tok > 0 ? max_tok : 1;
-  const WsFlags f = i8_flags(L, mode);
-  return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, f.a, f.b,
-                   f.stats).bytes;
+  return Workspace(nullptr, L->n_embd, L->n_ff, L->n_expert, L->n_expert_used, T, mode, wants_stats(L)).bytes;
 }
 
 DS4Q_API int ds4q_moe_decode(const ds4q_moe_layer *L, const float *x, const float *logits,

@@ -75,17 +75,10 @@ hipError_t launch_combine(const float *o, const RouteBufs &rb, int T, int k, int
 hipError_t launch_combine(const uint16_t *o, const RouteBufs &rb, int T, int k, int D, bool by_pos,
                           float *y, bool accumulate, const SteerArgs &st, hipStream_t s);
 
-// Prefill path on Q4_1 weights (bf16 matrix cores).
-hipError_t launch_prep_bf16(const float *x, const float *inv_rms, int T, int D, uint16_t *xb,
-                            hipStream_t s);
-hipError_t launch_prefill_gateup(const MoeDims &m, const uint16_t *xb, int T, const RouteBufs &rb,
-                                 int max_tiles, uint16_t *hb, hipStream_t s);
-hipError_t launch_prefill_down(const MoeDims &m, const uint16_t *hb, int T, const RouteBufs &rb,
-                               int max_tiles, uint16_t *ob, hipStream_t s);
-
-// Prefill on Q2_K weights, fp16 matrix cores (prefill_f16.hip): activation
-// rows scaled per row by a power of two and stored as fp16 in the MFMA
-// fragment order, with the factor that undoes the scaling.
+// Prefill on fp16 matrix cores, Q2_K or Q4_1 weights per tensor
+// (prefill_f16.hip): activation rows scaled per row by a power of two and
+// stored as fp16 in the MFMA fragment order of the weights they meet, with
+// the factor that undoes the scaling.
 struct PrepF16 {
   uint16_t *q;  // [rows][K/256][32][8] fp16
   float *sig;   // [rows]
@@ -93,9 +86,10 @@ struct PrepF16 {
 size_t prep_f16_bytes(int64_t rows, int K);
 PrepF16 prep_f16_view(void *base, int64_t rows, int K);
 // src: f32 (f32in; times inv_rms[row] when given, then rounded to bf16 when
-// round_bf16) or bf16 rows [rows][K].
+// round_bf16) or bf16 rows [rows][K]; wtype: the weight format (Q2_K or
+// Q4_1) whose K order the rows are written in.
 hipError_t launch_prep_f16(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
-                           int64_t rows, int K, const PrepF16 &p, hipStream_t s);
+                           int64_t rows, int K, int wtype, const PrepF16 &p, hipStream_t s);
 hipError_t launch_prefill_f16_gateup(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,
                                      int max_tiles, uint16_t *hb, hipStream_t s);
 hipError_t launch_prefill_f16_down(const MoeDims &m, const PrepF16 &a, int T, const RouteBufs &rb,

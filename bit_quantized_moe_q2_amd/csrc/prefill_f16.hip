@@ -31,6 +31,8 @@
 // ahead, each 512-byte row with its 16-byte chunks XOR-swizzled by the row
 // index within its 16-row group; raw weight bytes go to registers two blocks
 // ahead.
+#include <type_traits>
+
 #include "common.h"
 #include "i8_ops.h"
 #include "launch.h"
@@ -40,6 +42,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int TMF = PREFILL_TILE_M;  // tokens (sorted pairs) per m-tile
 constexpr int NGF = TMF / 16;        // MFMA row groups of 16 tokens
@@ -55,12 +58,13 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
 }
 
-// One workgroup per activation row, one thread per 16-value sub-block.
+// One workgroup per activation row, one thread per 16 values.
 // F32IN: the row is x * inv_rms (or x), rounded to bf16 first when ROUND
 // (the prefill input contract); otherwise the row is bf16 bits.  Output per
-// (row, block): 32 chunks [4j + g][8 fp16] in the K order above, and per row
-// the factor 2^-k that undoes the scaling.
-template <bool F32IN, bool ROUND>
+// (row, 256-value block): 32 chunks [4j + g][8 fp16] in the K order of the
+// weight format the row meets (Q41: the Q4_1 order, else the Q2_K one), and
+// per row the factor 2^-k that undoes the scaling.
+template <bool F32IN, bool ROUND, bool Q41>
 __global__ __launch_bounds__(256) void prep_f16_kernel(const void *__restrict__ src,
                                                        const float *__restrict__ inv_rms, int K,
                                                        uint16_t *__restrict__ aq,
@@ -110,15 +114,29 @@ __global__ __launch_bounds__(256) void prep_f16_kernel(const void *__restrict__ 
   if (t == 0) asig[row] = ldexpf(1.0f, -k);
   if (!act) return;
   const int b = t >> 4, s = t & 15;
-  const int g = 2 * (s >> 3) + (s & 1), p = (s >> 1) & 3;
-  u32x4 *out = reinterpret_cast<u32x4 *>(aq + (row * nb + b) * (HROW / 2));
+  if constexpr (Q41) {
+    // values 16s..16s+15: the low (s even) or high nibbles of Q4_1 block
+    // jb = s/2, code bytes 0..15; code dword cd goes to chunk
+    // 4(4(jb&1) + cd) + jb/2, half s&1, in the order bytes 0, 2, 1, 3
+    const int jb = s >> 1;
+    u32x2 *out = reinterpret_cast<u32x2 *>(aq + (row * nb + b) * (HROW / 2));
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    u32x4 o;
+    for (int cd = 0; cd < 4; ++cd) {
+      const float *q = v + 4 * cd;
+      out[2 * (4 * (4 * (jb & 1) + cd) + (jb >> 1)) + (s & 1)] =
+          (u32x2){pack_f16x2(ldexpf(q[0], k), ldexpf(q[2], k)), pack_f16x2(ldexpf(q[1], k), ldexpf(q[3], k))};
+    }
+  } else {
+    const int g = 2 * (s >> 3) + (s & 1), p = (s >> 1) & 3;
+    u32x4 *out = reinterpret_cast<u32x4 *>(aq + (row * nb + b) * (HROW / 2));
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      o[c] = pack_f16x2(ldexpf(v[8 * h + 2 * c], k), ldexpf(v[8 * h + 2 * c + 1], k));
-    out[4 * (2 * p + h) + g] = o;
+    for (int h = 0; h < 2; ++h) {
+      u32x4 o;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        o[c] = pack_f16x2(ldexpf(v[8 * h + 2 * c], k), ldexpf(v[8 * h + 2 * c + 1], k));
+      out[4 * (2 * p + h) + g] = o;
+    }
   }
 }
 
@@ -156,6 +174,97 @@ struct HTab {
   }
 };
 
+// Weight operands of one block of one weight row for lane group g, per
+// format.  BYTES: the row bytes of one 256-value block; KEEP_RAW: the B
+// fragments read the raw registers during the whole block (then the next
+// block goes to a second set of raw registers).
+
+// Q2_K: the code bytes are copied out and the scale/min bytes exchanged at
+// the block's start (take), the raw registers are free after that.
+struct OpsQ2K {
+  using Raw = RawBlk;
+  static constexpr int BYTES = BB_Q2K;
+  static constexpr bool KEEP_RAW = false;
+  u32x4 q;
+  uint32_t sa0, sa1;
+  float sd, sm;
+  HTab tb;
+  __device__ __forceinline__ void take(const Raw &r, int g) {
+    const Q2KPart o = take_block(r);
+    q = o.q;
+    sa0 = o.s0 >> (8 * (g & 1));
+    sa1 = o.s1 >> (8 * (g & 1));
+    sd = f16lo(o.dd);
+    sm = f16hi(o.dd);
+    tb.template build<0>(sa0, sa1, sd, sm);
+  }
+  // before K-tile J's lookups: the tables of its sub-block when it is new
+  template <int J>
+  __device__ __forceinline__ void ahead() {
+    if constexpr (J > 0 && (J & 1) == 0) tb.template build<(J >> 1)>(sa0, sa1, sd, sm);
+  }
+  template <int J>
+  __device__ __forceinline__ f16x8 bfrag(const Raw &) const { return tb.template bfrag<J>(q); }
+};
+
+// Q4_1 ("자체 저비트 포맷을 llama.cpp로 옮기기", Q4_1 block section: fp16 d at
+// byte 0, fp16 m at 2, code bytes 4..19 with value j the low nibble of byte
+// j and value j + 16 its high nibble; value = d*code + m).  A 256-value block
+// is 8 Q4_1 blocks, 160 bytes; lane group g loads its two whole Q4_1 blocks
+// 2g and 2g + 1 (40 bytes at 40g: dwords 0 and 5 are their d|m, 1..4 and
+// 6..9 their codes).  K order: K-tile j takes, in lane group g, code dword
+// j & 3 of Q4_1 block 2g + (j >> 2): the low nibbles of its bytes 0, 2, 1, 3,
+// then the high ones.  Each weight is q*d + m by one packed fp16 fma on the
+// exact fp16 q (1024 + q - 1024): one rounding.
+struct RawQ41 {
+  u32x4 a, b;
+  u32x2 c;
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ blk, int g) {
+    const uint8_t *p = blk + 40 * g;
+    a = *reinterpret_cast<const u32x4a *>(p);
+    b = *reinterpret_cast<const u32x4a *>(p + 16);
+    c = *reinterpret_cast<const u32x2a *>(p + 32);
+  }
+};
+struct OpsQ41 {
+  using Raw = RawQ41;
+  static constexpr int BYTES = 8 * BB_Q41;
+  static constexpr bool KEEP_RAW = true;
+  h2 d2[2], m2[2];  // d and m of the lane's two Q4_1 blocks, in both halves
+  __device__ __forceinline__ void take(const Raw &r, int) {
+    d2[0] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(r.a[0], r.a[0], 0x01000100u));
+    m2[0] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(r.a[0], r.a[0], 0x03020302u));
+    d2[1] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(r.b[1], r.b[1], 0x01000100u));
+    m2[1] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(r.b[1], r.b[1], 0x03020302u));
+  }
+  template <int J>
+  __device__ __forceinline__ void ahead() {}
+  // the nibble mask and the fp16 exponent bits of 1024 in registers (a
+  // vector instruction cannot encode two literals), so that each code pair
+  // is one v_and_or_b32
+  uint32_t nib, magic;
+  __device__ __forceinline__ OpsQ41() {
+    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(nib));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  }
+  template <int J>
+  __device__ __forceinline__ f16x8 bfrag(const Raw &r) const {
+    constexpr int JB = J >> 2, CD = J & 3;
+    const uint32_t w = JB == 0 ? (CD == 0 ? r.a[1] : CD == 1 ? r.a[2] : CD == 2 ? r.a[3] : r.b[0])
+                               : (CD == 0 ? r.b[2] : CD == 1 ? r.b[3] : CD == 2 ? r.c[0] : r.c[1]);
+    const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // i = 0: low nibbles of bytes 0, 2; 1: of bytes 1, 3; 2, 3: the high nibbles
+      const uint32_t sh = (i & 1) * 8 + (i >> 1) * 4;
+      const h2 qv = __builtin_bit_cast(h2, ((w >> sh) & nib) | magic) - k1024;
+      o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qv, d2[JB], m2[JB]));
+    }
+    return __builtin_bit_cast(f16x8, o);
+  }
+};
+
 // Per-wave state of one work item (set up once, shared by every block).
 struct FCtx {
   const uint8_t *abase;    // uniform: prepared rows of row rbase
@@ -180,9 +289,11 @@ struct FCtx {
 // phase first: waves w and w + 4 share a SIMD, and after every block barrier
 // they would otherwise be in the same phase, competing for the vector unit
 // and then for the matrix core, instead of one using each.
-template <int NP, int NPMAX, bool MFIRST, class EPI>
+template <class OPS, int NP, int NPMAX, bool MFIRST, class EPI>
 __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uint8_t *As1,
                                                f32x4 (&acc)[NPMAX][2], const EPI &epi) {
+  using Raw = typename OPS::Raw;
+  constexpr int KR = OPS::KEEP_RAW ? 1 : 0;  // index of the second raw register set
   const int w = cx.w, g = cx.g, nb = cx.nb, nvt = cx.nvt, lane = cx.lane;
   // Activation requests per block: waves 0..3 issue the 2*NP row-pair loads
   // (load I = 4u + w covers token rows 2I, 2I+1; lane -> row 2I + lane/32,
@@ -207,42 +318,32 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
   auto issue_a = [&](int u, int v, uint8_t *As) {
     if (w < 4) asrc.copy16(aoffs[u], (uint32_t)(v % nb) * HROW, As + (4 * u + w) * 1024);
   };
-  auto issue_w = [&](int v, RawBlk (&r)[2]) {
-    const int64_t off = (int64_t)(v / nb) * cx.nstride + (int64_t)(v % nb) * BB_Q2K;
+  auto issue_w = [&](int v, Raw (&r)[2]) {
+    const int64_t off = (int64_t)(v / nb) * cx.nstride + (int64_t)(v % nb) * OPS::BYTES;
 #pragma unroll
     for (int t = 0; t < 2; ++t) r[t].load(cx.brow[t] + off, g);
   };
 
-  // One set of raw weight registers: a block's bytes are taken apart at its
-  // start, and the next block's are requested right after, a whole block
-  // ahead of their use.
-  RawBlk rw[2];
+  // Raw weight registers: a block's bytes are taken apart at its start and
+  // the next block's requested right after, a whole block ahead of their use,
+  // into the same registers (Q2_K) or, when the lookups read them during the
+  // block (Q4_1), into a second set.
+  Raw rw[KR + 1][2];
 #pragma unroll
   for (int u = 0; u < 2 * NP; ++u) issue_a(u, 0, As0);
-  issue_w(0, rw);
+  issue_w(0, rw[0]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  auto step = [&](int kb, RawBlk (&r)[2], const uint8_t *As, uint8_t *An) {
-    // this block's operands: the code bytes, and per weight row the scale /
-    // min bytes of the lane's sub-blocks and d|dmin; then r takes block kb + 1
-    u32x4 q[2];
-    uint32_t sa0[2], sa1[2];
-    float sd[2], sm[2];
-    HTab tb[2];
+  auto step = [&](int kb, Raw (&r)[2], Raw (&rn)[2], const uint8_t *As, uint8_t *An) {
+    // this block's operands, then the next block's request (rn is r when the
+    // raw registers are free after take)
+    OPS op[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const Q2KPart o = take_block(r[t]);
-      q[t] = o.q;
-      sa0[t] = o.s0 >> (8 * (g & 1));
-      sa1[t] = o.s1 >> (8 * (g & 1));
-      sd[t] = f16lo(o.dd);
-      sm[t] = f16hi(o.dd);
-      tb[t].template build<0>(sa0[t], sa1[t], sd[t], sm[t]);
-    }
+    for (int t = 0; t < 2; ++t) op[t].take(r[t], g);
     const int kn = kb + 1 < nvt ? kb + 1 : nvt - 1;
     __builtin_amdgcn_sched_barrier(0);
-    issue_w(kn, r);
+    issue_w(kn, rn);
     __builtin_amdgcn_sched_barrier(0);
     // Per K-tile j: the requests of this step, then the two phases in the
     // wave's order; a sub-block's tables are built just before its first
@@ -250,19 +351,17 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
     f16x8 a[2][NP], b[2][2];
 #pragma unroll
     for (int i = 0; i < NP; ++i) a[0][i] = *reinterpret_cast<const f16x8 *>(As + cx.aoff[0] + i * 16 * HROW);
-    b[0][0] = tb[0].template bfrag<0>(q[0]);
-    b[0][1] = tb[1].template bfrag<0>(q[1]);
+    b[0][0] = op[0].template bfrag<0>(r[0]);
+    b[0][1] = op[1].template bfrag<0>(r[1]);
 #define VPART(J)                                                                                  \
       if ((J) < 7) {                                                                              \
         constexpr int JN = ((J) + 1) & 7;                                                         \
         _Pragma("unroll") for (int i = 0; i < NP; ++i) a[((J) & 1) ^ 1][i] =                      \
             *reinterpret_cast<const f16x8 *>(As + cx.aoff[JN & 3] + (JN >> 2) * 256 + i * 16 * HROW); \
-        if ((JN & 1) == 0) {                                                                      \
-          _Pragma("unroll") for (int t = 0; t < 2; ++t)                                           \
-            tb[t].template build<(JN >> 1)>(sa0[t], sa1[t], sd[t], sm[t]);                        \
-        }                                                                                         \
-        b[((J) & 1) ^ 1][0] = tb[0].template bfrag<JN>(q[0]);                                     \
-        b[((J) & 1) ^ 1][1] = tb[1].template bfrag<JN>(q[1]);                                     \
+        op[0].template ahead<JN>();                                                               \
+        op[1].template ahead<JN>();                                                               \
+        b[((J) & 1) ^ 1][0] = op[0].template bfrag<JN>(r[0]);                                     \
+        b[((J) & 1) ^ 1][1] = op[1].template bfrag<JN>(r[1]);                                     \
       }
 #define MPART(J)                                                                                  \
       mfma_group_begin();                                                                         \
@@ -316,16 +415,16 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
   // blocks, so every path into a block leaves the same requests outstanding,
   // and with nb >= 2 an n-tile ends after the second of them
   if (nb == 1) {
-    step(0, rw, As0, As1);
+    step(0, rw[0], rw[KR], As0, As1);
     ntile_end(0);
     if (nvt == 2) {
-      step(1, rw, As1, As0);
+      step(1, rw[KR], rw[0], As1, As0);
       ntile_end(1);
     }
   } else {
     for (int v = 0; v < nvt; v += 2) {
-      step(v, rw, As0, As1);
-      step(v + 1, rw, As1, As0);
+      step(v, rw[0], rw[KR], As0, As1);
+      step(v + 1, rw[KR], rw[0], As1, As0);
       ntile_end(v + 1);
     }
   }
@@ -337,11 +436,12 @@ __device__ __forceinline__ void block_loop_f16(const FCtx &cx, uint8_t *As0, uin
 // owning rows 32w + 16t .. +15.  Eight waves; a work item is an m-tile (up to
 // TMF sorted pairs of one expert) and ntper consecutive n-tiles, run as one
 // block stream.  SwiGLU rows are written as bf16 (hb), down rows as bf16 (o).
-template <bool SWIGLU>
+template <bool SWIGLU, bool Q41>
 __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1, int K, int rows_per_expert,
     const uint16_t *__restrict__ aq, const float *__restrict__ asig, int gather_tokens, int kslots,
     RouteBufs rb, int n_groups, int ntper, uint16_t *__restrict__ hb, uint16_t *__restrict__ o) {
+  using OPS = typename std::conditional<Q41, OpsQ41, OpsQ2K>::type;
   constexpr int NTROWS = SWIGLU ? 128 : 256;  // weight rows of one matrix per n-tile
   __shared__ __attribute__((aligned(1024))) uint8_t As0[HSTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[HSTAGE];
@@ -376,7 +476,7 @@ __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
   cx.arow = arow;
   cx.rbase = gather_tokens ? 0 : start;
   cx.abase = reinterpret_cast<const uint8_t *>(aq) + (int64_t)cx.rbase * cx.nb * HROW;
-  const int64_t rbytes = (int64_t)cx.nb * BB_Q2K;
+  const int64_t rbytes = (int64_t)cx.nb * OPS::BYTES;
   cx.nstride = NTROWS * rbytes;
   int wrow[2];
 #pragma unroll
@@ -433,25 +533,25 @@ __global__ __launch_bounds__(512, 1) void prefill_f16_kernel(
 
   if (cx.w >= 4) {
     switch (np) {
-      case 1: block_loop_f16<1, NGF, true>(cx, As0, As1, acc, epi); break;
-      case 2: block_loop_f16<2, NGF, true>(cx, As0, As1, acc, epi); break;
-      case 3: block_loop_f16<3, NGF, true>(cx, As0, As1, acc, epi); break;
-      case 4: block_loop_f16<4, NGF, true>(cx, As0, As1, acc, epi); break;
-      case 5: block_loop_f16<5, NGF, true>(cx, As0, As1, acc, epi); break;
-      case 6: block_loop_f16<6, NGF, true>(cx, As0, As1, acc, epi); break;
-      case 7: block_loop_f16<7, NGF, true>(cx, As0, As1, acc, epi); break;
-      default: block_loop_f16<8, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 1: block_loop_f16<OPS, 1, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 2: block_loop_f16<OPS, 2, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 3: block_loop_f16<OPS, 3, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 4: block_loop_f16<OPS, 4, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 5: block_loop_f16<OPS, 5, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 6: block_loop_f16<OPS, 6, NGF, true>(cx, As0, As1, acc, epi); break;
+      case 7: block_loop_f16<OPS, 7, NGF, true>(cx, As0, As1, acc, epi); break;
+      default: block_loop_f16<OPS, 8, NGF, true>(cx, As0, As1, acc, epi); break;
     }
   } else {
     switch (np) {
-      case 1: block_loop_f16<1, NGF, false>(cx, As0, As1, acc, epi); break;
-      case 2: block_loop_f16<2, NGF, false>(cx, As0, As1, acc, epi); break;
-      case 3: block_loop_f16<3, NGF, false>(cx, As0, As1, acc, epi); break;
-      case 4: block_loop_f16<4, NGF, false>(cx, As0, As1, acc, epi); break;
-      case 5: block_loop_f16<5, NGF, false>(cx, As0, As1, acc, epi); break;
-      case 6: block_loop_f16<6, NGF, false>(cx, As0, As1, acc, epi); break;
-      case 7: block_loop_f16<7, NGF, false>(cx, As0, As1, acc, epi); break;
-      default: block_loop_f16<8, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 1: block_loop_f16<OPS, 1, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 2: block_loop_f16<OPS, 2, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 3: block_loop_f16<OPS, 3, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 4: block_loop_f16<OPS, 4, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 5: block_loop_f16<OPS, 5, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 6: block_loop_f16<OPS, 6, NGF, false>(cx, As0, As1, acc, epi); break;
+      case 7: block_loop_f16<OPS, 7, NGF, false>(cx, As0, As1, acc, epi); break;
+      default: block_loop_f16<OPS, 8, NGF, false>(cx, As0, As1, acc, epi); break;
     }
   }
 }
@@ -473,17 +573,20 @@ PrepF16 prep_f16_view(void *base, int64_t rows, int K) {
 }
 
 hipError_t launch_prep_f16(const void *src, bool f32in, bool round_bf16, const float *inv_rms,
-                           int64_t rows, int K, const PrepF16 &p, hipStream_t s) {
+                           int64_t rows, int K, int wtype, const PrepF16 &p, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (f32in && round_bf16)
-    hipLaunchKernelGGL((prep_f16_kernel<true, true>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms,
-                       K, p.q, p.sig);
-  else if (f32in)
-    hipLaunchKernelGGL((prep_f16_kernel<true, false>), dim3((unsigned)rows), dim3(256), 0, s, src, inv_rms,
-                       K, p.q, p.sig);
-  else
-    hipLaunchKernelGGL((prep_f16_kernel<false, false>), dim3((unsigned)rows), dim3(256), 0, s, src,
-                       nullptr, K, p.q, p.sig);
+  const bool q41 = wtype == TYPE_Q4_1;
+  const dim3 grid((unsigned)rows), block(256);
+  if (f32in && round_bf16) {
+    if (q41) hipLaunchKernelGGL((prep_f16_kernel<true, true, true>), grid, block, 0, s, src, inv_rms, K, p.q, p.sig);
+    else hipLaunchKernelGGL((prep_f16_kernel<true, true, false>), grid, block, 0, s, src, inv_rms, K, p.q, p.sig);
+  } else if (f32in) {
+    if (q41) hipLaunchKernelGGL((prep_f16_kernel<true, false, true>), grid, block, 0, s, src, inv_rms, K, p.q, p.sig);
+    else hipLaunchKernelGGL((prep_f16_kernel<true, false, false>), grid, block, 0, s, src, inv_rms, K, p.q, p.sig);
+  } else {
+    if (q41) hipLaunchKernelGGL((prep_f16_kernel<false, false, true>), grid, block, 0, s, src, nullptr, K, p.q, p.sig);
+    else hipLaunchKernelGGL((prep_f16_kernel<false, false, false>), grid, block, 0, s, src, nullptr, K, p.q, p.sig);
+  }
   return hipGetLastError();
 }
 
@@ -491,8 +594,13 @@ hipError_t launch_prefill_f16_gateup(const MoeDims &m, const PrepF16 &a, int T, 
                                      int max_tiles, uint16_t *hb, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.F / 128, per = nn >= NTILES_PER_ITEM ? NTILES_PER_ITEM : nn;
-  hipLaunchKernelGGL((prefill_f16_kernel<true>), dim3(xcd_grid(max_tiles, nn / per)), dim3(512), 0, s,
-                     m.gate, m.up, m.D, m.F, a.q, a.sig, 1, m.k, rb, nn / per, per, hb, nullptr);
+  const dim3 grid(xcd_grid(max_tiles, nn / per)), block(512);
+  if (m.tg == TYPE_Q4_1)
+    hipLaunchKernelGGL((prefill_f16_kernel<true, true>), grid, block, 0, s, m.gate, m.up, m.D, m.F, a.q, a.sig,
+                       1, m.k, rb, nn / per, per, hb, nullptr);
+  else
+    hipLaunchKernelGGL((prefill_f16_kernel<true, false>), grid, block, 0, s, m.gate, m.up, m.D, m.F, a.q, a.sig,
+                       1, m.k, rb, nn / per, per, hb, nullptr);
   return hipGetLastError();
 }
 
@@ -500,8 +608,13 @@ hipError_t launch_prefill_f16_down(const MoeDims &m, const PrepF16 &a, int T, co
                                    int max_tiles, uint16_t *o, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nn = m.D / 256, per = nn >= NTILES_PER_ITEM ? NTILES_PER_ITEM : nn;
-  hipLaunchKernelGGL((prefill_f16_kernel<false>), dim3(xcd_grid(max_tiles, nn / per)), dim3(512), 0, s,
-                     m.down, nullptr, m.F, m.D, a.q, a.sig, 0, m.k, rb, nn / per, per, nullptr, o);
+  const dim3 grid(xcd_grid(max_tiles, nn / per)), block(512);
+  if (m.td == TYPE_Q4_1)
+    hipLaunchKernelGGL((prefill_f16_kernel<false, true>), grid, block, 0, s, m.down, nullptr, m.F, m.D, a.q,
+                       a.sig, 0, m.k, rb, nn / per, per, nullptr, o);
+  else
+    hipLaunchKernelGGL((prefill_f16_kernel<false, false>), grid, block, 0, s, m.down, nullptr, m.F, m.D, a.q,
+                       a.sig, 0, m.k, rb, nn / per, per, nullptr, o);
   return hipGetLastError();
 }
 

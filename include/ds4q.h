@@ -240,12 +240,12 @@ int ds4q_moe_decode_phases(const ds4q_moe_layer *L, const float *x, const float 
  * accumulation.  The expert input rows are bf16 (x_type BF16, or
  * x_type F32 which is normalised per DS4Q_F_RMSNORM_INPUT if set and rounded
  * to bf16); the SwiGLU row is rounded to bf16 before the down projection.
- * Q4_1 weights are dequantised to bf16 (fp32 d*q + m rounded once) for bf16
- * MFMA.  Q2_K weights are dequantised to fp16 (the fp32 value
- * d*sc*q - dmin*mn, exact up to its one fp32 rounding, rounded once to fp16)
- * for fp16 MFMA, and each bf16 input or SwiGLU row is scaled by the power of
- * two that puts its largest magnitude in [2^14, 2^15) and stored as fp16
- * (exact down to 2^-17 of the scaled maximum; the scale is undone in fp32).
+ * The weights are dequantised to fp16 for fp16 MFMA: Q2_K weights as the
+ * fp32 value d*sc*q - dmin*mn (exact up to its one fp32 rounding) rounded
+ * once to fp16, Q4_1 weights as d*q + m by one fp16 fma (one rounding); each
+ * bf16 input or SwiGLU row is scaled by the power of two that puts its
+ * largest magnitude in [2^14, 2^15) and stored as fp16 (exact down to 2^-17
+ * of the scaled maximum; the scale is undone in fp32).
  * Each pair's down row is rounded to bf16 once; routing and the final
  * weighted combine are fp32.  x: device [n_tok][n_embd] of x_type; y: device f32 [n_tok][n_embd]
  * (may equal x only when x_type is F32).  workspace
@@ -298,7 +298,7 @@ int ds4q_act_decode(const void *src, int64_t n, int32_t bits, float *dst, void *
 int ds4q_timing_enable(int on);
 /* Waits for the recorded events, then returns one entry per launch site:
  * names (max_names x name_len chars, NUL-terminated: "topk", "group",
- * "decode_gateup", "decode_down", "prep_bf16",
+ * "decode_gateup", "decode_down",
  * "prep_f16", "prefill_gateup", "prefill_down", "combine", "steer", "act_encode",
  * "act_decode"), summed milliseconds and
  * launch counts (host arrays).  Clears the record. */

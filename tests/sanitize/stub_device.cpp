@@ -27,12 +27,7 @@ hipError_t launch_combine(const float *, const RouteBufs &, int, int, int, bool,
                           hipStream_t) STUB()
 hipError_t launch_combine(const uint16_t *, const RouteBufs &, int, int, int, bool, float *, bool,
                           const SteerArgs &, hipStream_t) STUB()
-hipError_t launch_prep_bf16(const float *, const float *, int, int, uint16_t *, hipStream_t) STUB()
-hipError_t launch_prefill_gateup(const MoeDims &, const uint16_t *, int, const RouteBufs &, int, uint16_t *,
-                                 hipStream_t) STUB()
-hipError_t launch_prefill_down(const MoeDims &, const uint16_t *, int, const RouteBufs &, int, uint16_t *,
-                               hipStream_t) STUB()
-hipError_t launch_prep_f16(const void *, bool, bool, const float *, int64_t, int, const PrepF16 &, hipStream_t) STUB()
+hipError_t launch_prep_f16(const void *, bool, bool, const float *, int64_t, int, int, const PrepF16 &, hipStream_t) STUB()
 hipError_t launch_prefill_f16_gateup(const MoeDims &, const PrepF16 &, int, const RouteBufs &, int, uint16_t *,
                                      hipStream_t) STUB()
 hipError_t launch_prefill_f16_down(const MoeDims &, const PrepF16 &, int, const RouteBufs &, int, uint16_t *,
