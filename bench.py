@@ -62,32 +62,40 @@ def log(*a):
 # Algorithmic bytes of one gate/up launch at one token: the six experts'
 # gate and up rows, the input vector and the SwiGLU rows written.
 GATEUP_BYTES = K * 2 * F * Q2K_ROW_D + D * 4 + K * F * 4
+# Algorithmic HBM bytes of one prefill gate/up launch at 4096 tokens, uniform
+# routing (every expert one m-tile): all experts' gate and up rows once, the
+# fp16 input rows once, the bf16 SwiGLU rows written once.
+PREFILL_GATEUP_BYTES = E * 2 * F * Q2K_ROW_D + 4096 * D * 2 + 4096 * K * F * 2
 COUNTER_FILE = os.path.join(ROOT, "profiles", "decode_q2k_1tok_hbm_counters.txt")
 KERNEL_SOURCES = ("bit_quantized_moe_q2_amd/csrc/decode_mfma.hip",
                   "bit_quantized_moe_q2_amd/csrc/mfma_t1.h",
                   "bit_quantized_moe_q2_amd/csrc/common.h")
+PREFILL_COUNTER_FILE = os.path.join(ROOT, "profiles", "prefill_q2k_4096tok_hbm_counters.txt")
+PREFILL_SOURCES = ("bit_quantized_moe_q2_amd/csrc/prefill_f16.hip",
+                   "bit_quantized_moe_q2_amd/csrc/i8_ops.h",
+                   "bit_quantized_moe_q2_amd/csrc/common.h")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
-    WRITE_SIZE summary, each scaled by its plain-copy calibration factor;
-    None when there is no summary or the kernel sources have changed since
-    the counters were taken."""
+def counter_traffic(kernel, path=None, sources=None):
+    """HBM bytes per launch of `kernel` from a committed FETCH_SIZE /
+    WRITE_SIZE summary (default: the one-token decode's), each scaled by its
+    plain-copy calibration factor; None when there is no summary or the
+    kernel sources have changed since the counters were taken."""
     try:
-        with open(COUNTER_FILE) as f:
+        with open(path or COUNTER_FILE) as f:
             rows = [json.loads(ln.split(":", 1)[1]) for ln in f if ln.startswith("traffic_json:")]
     except OSError:
         return None
     for r in rows:
-        if r.get("kernel") == kernel and r.get("src_sha256") == kernel_source_hash():
+        if r.get("kernel") == kernel and r.get("src_sha256") == kernel_source_hash(sources):
             return int(round((r["fetch_kib"] * r["fetch_factor"] + r["write_kib"] * r["write_factor"])
                              * 1024))
     return None
@@ -473,7 +481,9 @@ def main():
             # dense fp16 peak (one fp16 MAC per algorithmic MAC)
             "roofline": {"bound": "mfma", "kernel": "prefill_gateup", "achieved": round(g1_tf, 2),
                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(g1_tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None},
+                         "frac": round(g1_tf / MFMA_F16_PEAK_TFLOPS, 4),
+                         "traffic": counter_traffic("prefill_gateup", PREFILL_COUNTER_FILE, PREFILL_SOURCES),
+                         "bytes_algorithmic": PREFILL_GATEUP_BYTES},
             "kernels_us": {k: round(v[0] / v[1] * 1e3, 2) for k, v in pt.items()},
             # combine of the 4096 x 6 expert rows, plain and with the steering
             # epilogue (row dot product + projection in the same launch)

@@ -54,10 +54,10 @@ def test_counter_traffic_needs_matching_sources(bench, monkeypatch, tmp_path):
     f = tmp_path / "counters.txt"
     f.write_text("header\n" + line)
     monkeypatch.setattr(bench, "COUNTER_FILE", str(f))
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda sources=None: "abc")
     assert bench.counter_traffic("decode_gateup") == (100 * 2 + 10) * 1024
     assert bench.counter_traffic("decode_down") is None
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "changed")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda sources=None: "changed")
     assert bench.counter_traffic("decode_gateup") is None
     monkeypatch.setattr(bench, "COUNTER_FILE", str(tmp_path / "missing.txt"))
     assert bench.counter_traffic("decode_gateup") is None
