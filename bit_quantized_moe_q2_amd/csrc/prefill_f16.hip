@@ -1,4 +1,5 @@
-// Prefill path on Q2_K weights with fp16 matrix cores.
+// Prefill path (grouped GEMMs over expert-sorted token-expert pairs) with
+// fp16 matrix cores, on Q2_K or Q4_1 weights per tensor.
 //
 // Arithmetic.  A weight of a 256-value Q2_K block ("【#2】ds4.c 해독하기",
 // Q2_K block-layout table and code-packing expression) is
@@ -8,29 +9,30 @@
 // possible weights (q = 0..3) are evaluated in fp32 (d*sc*q and dmin*mn are
 // exact there, the difference rounds once) and rounded to fp16; each
 // weight of the B operand is then one table lookup (v_perm_b32 on the lane's
-// 2-bit codes).  The activation rows are prepared once per call
-// (prep_f16_kernel): each row is scaled by the power of two 2^k that puts its
-// largest magnitude in [2^14, 2^15) and stored as fp16 (exact for bf16
-// input: 8 significant bits fit fp16's 11 down to 2^-17 of the scaled
-// maximum, below which values round to fp16's subnormal grid), with 2^-k kept
-// per row.  The products run on v_mfma_f32_16x16x32_f16 and accumulate over
-// the whole K range in the matrix core's fp32 registers; the epilogue scales
-// by 2^-k (then SwiGLU, or the plain store of the down rows).
+// 2-bit codes).  A Q4_1 weight is d*q + m, one packed fp16 fma (OpsQ41).
+// The activation rows are prepared once per call (prep_f16_kernel): each row
+// is scaled by the power of two 2^k that puts its largest magnitude in
+// [2^14, 2^15) and stored as fp16 (exact for bf16 input: 8 significant bits
+// fit fp16's 11 down to 2^-17 of the scaled maximum, below which values round
+// to fp16's subnormal grid), with 2^-k kept per row.  The products run on
+// v_mfma_f32_16x16x32_f16 and accumulate over the whole K range in the
+// matrix core's fp32 registers; the epilogue scales by 2^-k (then SwiGLU, or
+// the plain store of the down rows).
 //
-// K order.  Any permutation of K serves as long as both operands use it.
-// Lane group g (lanes 16g..16g+15) of K-tile j = 2p + h of a block takes the
-// 8 values 128(g>>1) + 32p + 16(g&1) + 8h + i, i = 0..7: code bytes
-// 16g + 8h + i of the block's code area, bit pair p, all of sub-block
-// 8(g>>1) + 2p + (g&1).  So a lane's 16 code bytes (one 16-byte load) cover
-// K-tiles 0..7 of its weight row, and each of its four sub-blocks feeds
-// exactly two K-tiles.  The prepared activation row holds, per block, 32
-// chunks of 16 bytes, chunk 4j + g = those 8 values of K-tile j as fp16.
+// K order (Q2_K; Q4_1 at OpsQ41).  Any permutation of K serves as long as
+// both operands use it.  Lane group g (lanes 16g..16g+15) of K-tile
+// j = 2p + h of a block takes the 8 values 128(g>>1) + 32p + 16(g&1) + 8h + i,
+// i = 0..7: code bytes 16g + 8h + i of the block's code area, bit pair p, all
+// of sub-block 8(g>>1) + 2p + (g&1).  So a lane's 16 code bytes (one 16-byte
+// load) cover K-tiles 0..7 of its weight row, and each of its four
+// sub-blocks feeds exactly two K-tiles.  The prepared activation row holds,
+// per block, 32 chunks of 16 bytes, chunk 4j + g = those 8 values of K-tile j
+// as fp16.
 //
-// Data movement as in the int8 form: activation tiles reach LDS by direct
-// global->LDS loads (buffer_load_dwordx4 ... lds), double-buffered one block
-// ahead, each 512-byte row with its 16-byte chunks XOR-swizzled by the row
-// index within its 16-row group; raw weight bytes go to registers two blocks
-// ahead.
+// Data movement: activation tiles reach LDS by direct global->LDS loads
+// (buffer_load_dwordx4 ... lds), double-buffered one block ahead, each
+// 512-byte row with its 16-byte chunks XOR-swizzled by the row index within
+// its 16-row group; raw weight bytes go to registers one block ahead.
 #include <type_traits>
 
 #include "common.h"
@@ -279,7 +281,7 @@ struct FCtx {
 // The block loop for NP live 16-token groups (tokens >= 16*NP are absent)
 // over the item's n-tiles one after the other: nvt = n-tiles * nb blocks in
 // one stream, v = nt * nb + kb; after the last block of n-tile nt, epi(nt)
-// stores acc and acc restarts at zero.  The requests run two blocks ahead
+// stores acc and acc restarts at zero.  The requests run one block ahead
 // across n-tile boundaries (the activation rows are the same, the weight
 // rows move by nstride), so only the item's first n-tile waits for its first
 // blocks.  Each K-tile j has a vector
