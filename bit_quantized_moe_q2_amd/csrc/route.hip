@@ -73,30 +73,67 @@ __device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) 
   return before + incl - v;
 }
 
+// Pairs per thread and round of the grouping: 24 consecutive pair indices,
+// so that a round covers 24,576 pairs (4096 tokens x 6 slots) and each thread
+// requests its ids as six 16-byte loads.
+constexpr int GROUP_CH = 24;
+
+// The expert ids of pairs p .. p + GROUP_CH - 1 (-1 past the last pair).  p is
+// a multiple of 4 and the ids array 16-byte aligned.
+__device__ __forceinline__ void load_pair_ids(const int32_t *__restrict__ ids, int p, int P,
+                                              int v[GROUP_CH]) {
+#pragma unroll
+  for (int i = 0; i < GROUP_CH; i += 4) {
+    if (p + i + 3 < P) {
+      const int4 q = *reinterpret_cast<const int4 *>(ids + p + i);
+      v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[i + j] = p + i + j < P ? ids[p + i + j] : -1;
+    }
+  }
+}
+
 // One workgroup per expert: histogram of all pair experts (for its offset),
 // then a stable, order-preserving compaction of its own pairs.  Workgroup 0
-// also writes counts, offsets, the active-expert list and the m-tile list
-// (and, by_size, its size-ordered copy).
+// also writes counts, offsets, the active-expert list and the m-tile list;
+// by_size, workgroup 1 writes the size-ordered copy.  Thread t takes pairs
+// base + 24t .. base + 24t + 23 of each round of 24,576; the first round's ids
+// stay in registers from the histogram to the compaction.
 __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int tile_m, int by_size, RouteBufs rb) {
   __shared__ int hist[MAX_E];
   __shared__ int wave_tot[16];
   __shared__ int s_off;
   const int e = blockIdx.x, tid = threadIdx.x;
   const int P = T * k;
+  constexpr int ROUND = 1024 * GROUP_CH;
+  const int pt = GROUP_CH * tid;
+  int v0[GROUP_CH];
+  load_pair_ids(rb.ids, pt, P, v0);
   for (int i = tid; i < E; i += 1024) hist[i] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += 1024) atomicAdd(&hist[rb.ids[p]], 1);
+#pragma unroll
+  for (int i = 0; i < GROUP_CH; ++i)
+    if ((unsigned)v0[i] < (unsigned)E) atomicAdd(&hist[v0[i]], 1);
+  for (int base = ROUND; base < P; base += ROUND) {
+    int v[GROUP_CH];
+    load_pair_ids(rb.ids, base + pt, P, v);
+#pragma unroll
+    for (int i = 0; i < GROUP_CH; ++i)
+      if ((unsigned)v[i] < (unsigned)E) atomicAdd(&hist[v[i]], 1);
+  }
   __syncthreads();
   // thread i < E takes expert i: its offset, its place among the active
   // experts and its first m-tile, by exclusive scans over the workgroup
   const int c = tid < E ? hist[tid] : 0;
-  int n_pairs, n_act, n_til;
+  int n_pairs;
   const int off = block_excl_scan(c, wave_tot, &n_pairs);
-  const int apos = block_excl_scan(c > 0 ? 1 : 0, wave_tot, &n_act);
-  const int ntile_mine = tile_m > 0 ? (c + tile_m - 1) / tile_m : 0;
-  const int tpos = block_excl_scan(ntile_mine, wave_tot, &n_til);
   if (tid == e) s_off = off;
   if (e == 0) {
+    int n_act, n_til;
+    const int apos = block_excl_scan(c > 0 ? 1 : 0, wave_tot, &n_act);
+    const int ntile_mine = tile_m > 0 ? (c + tile_m - 1) / tile_m : 0;
+    const int tpos = block_excl_scan(ntile_mine, wave_tot, &n_til);
     if (tid < E) {
       rb.counts[tid] = c;
       rb.offsets[tid] = off;
@@ -109,40 +146,6 @@ __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int ti
         rb.tiles[2 * (tpos + j) + 1] = off + j * tile_m;
       }
     }
-    if (by_size && tile_m > 0) {
-      // The same tiles, the full ones first (expert order), then the
-      // partial ones by falling count of 16-pair groups, each class in
-      // expert order: ranks by ballots per wave, class bases from the
-      // per-wave counts.  (Prefill GEMMs deal this list to the XCDs in turn,
-      // largest work first.)
-      __shared__ int cls_cnt[16][17];
-      const int lane = tid & 63, wv = tid >> 6;
-      const int full = c / tile_m, rem = c - full * tile_m;
-      const int ncls = (tile_m + 15) >> 4;  // <= 16
-      const int cls = rem > 0 ? (rem + 15) >> 4 : 0;
-      int n_full;
-      const int fpos = block_excl_scan(full, wave_tot, &n_full);
-      for (int j = 0; j < full; ++j) {
-        rb.tiles_sz[2 * (fpos + j)] = tid;
-        rb.tiles_sz[2 * (fpos + j) + 1] = off + j * tile_m;
-      }
-      int rank_w = 0;
-      for (int q = 1; q <= ncls; ++q) {
-        const uint64_t m = __builtin_amdgcn_ballot_w64(cls == q);
-        if (lane == 0) cls_cnt[wv][q] = __builtin_popcountll(m);
-        if (cls == q) rank_w = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      }
-      __syncthreads();
-      if (cls > 0) {
-        int pos = n_full;
-        for (int q = ncls; q > cls; --q)
-          for (int v = 0; v < 16; ++v) pos += cls_cnt[v][q];
-        for (int v = 0; v < wv; ++v) pos += cls_cnt[v][cls];
-        pos += rank_w;
-        rb.tiles_sz[2 * pos] = tid;
-        rb.tiles_sz[2 * pos + 1] = off + full * tile_m;
-      }
-    }
     if (tid == 0) {
       rb.offsets[E] = n_pairs;
       rb.act_begin[n_act] = n_pairs;
@@ -150,26 +153,63 @@ __global__ __launch_bounds__(1024) void group_kernel(int T, int E, int k, int ti
       if (tile_m > 0) *rb.n_tiles = n_til;
     }
   }
+  // The size-ordered m-tile list, written by workgroup 1 (0 with a single
+  // expert) while workgroup 0 writes the others.
+  if (by_size && tile_m > 0 && e == (E > 1 ? 1 : 0)) {
+    // The same tiles, the full ones first (expert order), then the
+    // partial ones by falling count of 16-pair groups, each class in
+    // expert order: ranks by ballots per wave, class bases from the
+    // per-wave counts.  (Prefill GEMMs deal this list to the XCDs in turn,
+    // largest work first.)
+    __shared__ int cls_cnt[16][17];
+    const int lane = tid & 63, wv = tid >> 6;
+    const int full = c / tile_m, rem = c - full * tile_m;
+    const int ncls = (tile_m + 15) >> 4;  // <= 16
+    const int cls = rem > 0 ? (rem + 15) >> 4 : 0;
+    int n_full;
+    const int fpos = block_excl_scan(full, wave_tot, &n_full);
+    for (int j = 0; j < full; ++j) {
+      rb.tiles_sz[2 * (fpos + j)] = tid;
+      rb.tiles_sz[2 * (fpos + j) + 1] = off + j * tile_m;
+    }
+    int rank_w = 0;
+    for (int q = 1; q <= ncls; ++q) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(cls == q);
+      if (lane == 0) cls_cnt[wv][q] = __builtin_popcountll(m);
+      if (cls == q) rank_w = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    }
+    __syncthreads();
+    if (cls > 0) {
+      int pos = n_full;
+      for (int q = ncls; q > cls; --q)
+        for (int v = 0; v < 16; ++v) pos += cls_cnt[v][q];
+      for (int v = 0; v < wv; ++v) pos += cls_cnt[v][cls];
+      pos += rank_w;
+      rb.tiles_sz[2 * pos] = tid;
+      rb.tiles_sz[2 * pos + 1] = off + full * tile_m;
+    }
+  }
   __syncthreads();
-  // stable compaction of the expert's pairs: thread t takes pairs
-  // base + 4t .. base + 4t + 3, one scan per 4096 pairs places them
+  // stable compaction of the expert's pairs, one scan per round
   int running = s_off;
-  for (int base = 0; base < P; base += 4096) {
-    const int p0 = base + 4 * tid;
-    bool mine[4];
+  for (int base = 0; base < P; base += ROUND) {
+    int v[GROUP_CH];
+    if (base == 0) {
+#pragma unroll
+      for (int i = 0; i < GROUP_CH; ++i) v[i] = v0[i];
+    } else {
+      load_pair_ids(rb.ids, base + pt, P, v);
+    }
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mine[i] = p0 + i < P && rb.ids[p0 + i] == e;
-      cnt += mine[i] ? 1 : 0;
-    }
+    for (int i = 0; i < GROUP_CH; ++i) cnt += v[i] == e ? 1 : 0;
     int total;
     int pos = running + block_excl_scan(cnt, wave_tot, &total);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (mine[i]) {
-        rb.pairs[pos] = p0 + i;
-        rb.pair_pos[p0 + i] = pos;
+    for (int i = 0; i < GROUP_CH; ++i) {
+      if (v[i] == e) {
+        rb.pairs[pos] = base + pt + i;
+        rb.pair_pos[base + pt + i] = pos;
         ++pos;
       }
     }

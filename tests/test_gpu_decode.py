@@ -177,6 +177,20 @@ def test_route_shapes(gpu, E, k):
     assert np.array_equal(pairs, rp) and np.array_equal(off, ro)
 
 
+@pytest.mark.parametrize("T,k", [(4999, 7), (4096, 8), (4097, 6)])
+def test_route_many_pairs(gpu, T, k):
+    """More pairs than one grouping round of 24,576 takes (the later rounds
+    reload their ids), and pair counts that are not a multiple of 4."""
+    ds4q = gpu
+    E = 256
+    lg = synth.logits_zipf(synth.stream_key(12, T, k), T, E)
+    ids, w, cnt, off, pairs = _route_gpu(ds4q, lg, k)
+    rids, rw = oracle.route(lg, k)
+    assert np.array_equal(ids, rids)
+    rc, ro, rp = oracle.group(rids, E)
+    assert np.array_equal(cnt, rc) and np.array_equal(off, ro) and np.array_equal(pairs, rp)
+
+
 # ---------------------------------------------------------------- decode MoE
 
 def _decode(ds4q, lay, x, lg, flags=0, y0=None, in_place=False):
