@@ -207,56 +207,95 @@ __device__ __forceinline__ float4 load4(const uint16_t *o, int64_t off) {
   return make_float4(bf16_to_f32(u.x & 0xFFFFu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFFu),
                      bf16_to_f32(u.y >> 16));
 }
+// V consecutive values from offset off (a multiple of V): f32 rows four at a
+// time, bf16 rows four or eight (one 16-byte request).
+template <int V>
+__device__ __forceinline__ void loadv(const float *o, int64_t off, float v[V]) {
+  static_assert(V == 4, "f32 rows: four values per request");
+  const float4 f = load4(o, off);
+  v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+}
+template <int V>
+__device__ __forceinline__ void loadv(const uint16_t *o, int64_t off, float v[V]) {
+  if constexpr (V == 4) {
+    const float4 f = load4(o, off);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    static_assert(V == 8, "bf16 rows: four or eight values per request");
+    const uint4 u = *reinterpret_cast<const uint4 *>(o + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+}
 
-// y[t] (+)= sum_j w[t][j] * o[row(t, j)] in slot order.
-template <typename OT, bool BY_POS, int KC>
+// y[t] (+)= sum_j w[t][j] * o[row(t, j)] in slot order; each thread takes V
+// consecutive values of one token row (D a multiple of V).
+template <typename OT, bool BY_POS, int KC, int V>
 __global__ __launch_bounds__(256) void combine_kernel(const OT *__restrict__ o, RouteBufs rb,
                                                       int T, int k_rt, int D,
                                                       float *__restrict__ y, int accumulate) {
-  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int D4 = D / 4;
-  if (i4 >= (int64_t)T * D4) return;
-  const int t = (int)(i4 / D4), c = (int)(i4 % D4);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 *yp = reinterpret_cast<float4 *>(y + (int64_t)t * D + 4 * c);
+  const int64_t iv = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int DV = D / V;
+  if (iv >= (int64_t)T * DV) return;
+  const int t = (int)(iv / DV), c = (int)(iv % DV);
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  float4 *yp = reinterpret_cast<float4 *>(y + (int64_t)t * D + V * c);
+  float old[V];
   if constexpr (KC > 0) {
     // the slot count known at compile time: straight-line code requests every
     // slot's position, then every slot's row (and the old y row), before the
     // sum in slot order
-    const float4 old = accumulate ? *yp : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (accumulate) {
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        const float4 f = yp[q];
+        old[4 * q] = f.x; old[4 * q + 1] = f.y; old[4 * q + 2] = f.z; old[4 * q + 3] = f.w;
+      }
+    }
     int64_t row[KC];
 #pragma unroll
     for (int j = 0; j < KC; ++j) row[j] = BY_POS ? rb.pair_pos[t * KC + j] : t * KC + j;
-    float4 v[KC];
+    float v[KC][V];
     float w[KC];
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-      v[j] = load4(o, row[j] * D + 4 * c);
+      loadv<V>(o, row[j] * D + V * c, v[j]);
       w[j] = rb.w[t * KC + j];
     }
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      acc.x = fmaf(w[j], v[j].x, acc.x); acc.y = fmaf(w[j], v[j].y, acc.y);
-      acc.z = fmaf(w[j], v[j].z, acc.z); acc.w = fmaf(w[j], v[j].w, acc.w);
-    }
-    if (accumulate) {
-      acc.x += old.x; acc.y += old.y; acc.z += old.z; acc.w += old.w;
-    }
+    for (int j = 0; j < KC; ++j)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
   } else {
     for (int j = 0; j < k_rt; ++j) {
       const int p = t * k_rt + j;
       const int64_t row = BY_POS ? rb.pair_pos[p] : p;
-      const float4 v = load4(o, row * D + 4 * c);
+      float v[V];
+      loadv<V>(o, row * D + V * c, v);
       const float w = rb.w[p];
-      acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(w, v[i], acc[i]);
     }
     if (accumulate) {
-      const float4 old = *yp;
-      acc.x += old.x; acc.y += old.y; acc.z += old.z; acc.w += old.w;
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        const float4 f = yp[q];
+        old[4 * q] = f.x; old[4 * q + 1] = f.y; old[4 * q + 2] = f.z; old[4 * q + 3] = f.w;
+      }
     }
   }
-  *yp = acc;
+  if (accumulate) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] += old[i];
+  }
+#pragma unroll
+  for (int q = 0; q < V / 4; ++q) yp[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
 }
 
 // Combine with directional steering: one workgroup per token row (D <= 4096,
@@ -402,14 +441,18 @@ hipError_t combine_any(const OT *o, const RouteBufs &rb, int T, int k, int D, bo
 #undef DS4Q_STEER
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((n4 + 255) / 256));
+  // bf16 rows: eight values per thread (one 16-byte request per slot)
+  constexpr int V = sizeof(OT) == 2 ? 8 : 4;
+  if (D % V) return hipErrorInvalidValue;
+  const int64_t nv = (int64_t)T * (D / V);
+  const dim3 grid((unsigned)((nv + 255) / 256));
   const int acc = accumulate ? 1 : 0;
 #define DS4Q_COMBINE(KC)                                                                           \
   do {                                                                                             \
     if (by_pos)                                                                                    \
-      hipLaunchKernelGGL((combine_kernel<OT, true, KC>), grid, dim3(256), 0, s, o, rb, T, k, D, y, acc); \
+      hipLaunchKernelGGL((combine_kernel<OT, true, KC, V>), grid, dim3(256), 0, s, o, rb, T, k, D, y, acc); \
     else                                                                                           \
-      hipLaunchKernelGGL((combine_kernel<OT, false, KC>), grid, dim3(256), 0, s, o, rb, T, k, D, y, acc); \
+      hipLaunchKernelGGL((combine_kernel<OT, false, KC, V>), grid, dim3(256), 0, s, o, rb, T, k, D, y, acc); \
   } while (0)
   switch (k) {
     case 6: DS4Q_COMBINE(6); break;
